@@ -1,0 +1,192 @@
+/*
+ * tq.h - C ABI of the TurboQuant compressed KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * The method follows the AI Heartland news article "Apple Silicon向けSwiftLM、
+ * TurboQuant KVキャッシュ圧縮とSSD Expert Streamingを実装", section 技術的な詳細:
+ *   - "K-Cache圧縮: 3-bit PolarQuant + 1-bit QJL = 4.25 bits/dim", flow steps 1-5:
+ *     L2 norm and normalisation, fast Walsh-Hadamard rotation, 3-bit non-linear
+ *     Lloyd-Max code per coordinate, residual, 1-bit signs of a Johnson-Lindenstrauss
+ *     projection of the residual (kept so that inner-product scoring stays accurate);
+ *   - "V-Cache圧縮: 3-bit PolarQuant = 3.125 bits/dim" (V is not scored, so no QJL);
+ *   - "TurboQuant KVキャッシュ圧縮アーキテクチャ" (Lloyd-Max codebook in a native
+ *     encode path, dequantisation fused into the attention kernel).
+ * The techfi24 article "SwiftLM : serveur d'inférence MLX natif pour Apple Silicon",
+ * section "Contexte Technique", names the same pair: polar quantisation plus QJL
+ * residual correction.
+ *
+ * Conventions for every entry point
+ *   - Return a tq_status; negative values are errors. Argument checks run on the
+ *     host before any HIP call, so a rejected call has enqueued nothing.
+ *   - Device work is enqueued asynchronously on `stream` (a hipStream_t, 0 = the
+ *     null stream); the call returns before the GPU finishes.
+ *   - The caller owns every buffer. The library allocates no device memory, frees
+ *     nothing and keeps no mutable global state; calls on different streams that
+ *     touch disjoint outputs may run concurrently.
+ *   - Device-side contract violations (slot, page id or sequence length out of
+ *     range, NaN/Inf inputs) are undefined behaviour.
+ *
+ * Symbols: d = head_dim, m = d (QJL rows), P = page_size, Hkv = KV heads,
+ * Hq = query heads (a multiple of Hkv; query head h reads KV head h / (Hq/Hkv)),
+ * Pi = H_d / sqrt(d) (Sylvester Hadamard, natural order), c[0..7] / t[0..6] the
+ * ascending codebook levels / thresholds, S the m x d QJL matrix.
+ *
+ * Packed page format (frozen; one section per (page, KV head), sections stored
+ * [n_pages][n_kv_heads], slot = page * P + offset, little-endian words):
+ *   K section, k_page_bytes = P*d/2 + 4*P:
+ *     record of token t at byte t*d/2, d/2 bytes: for each coordinate group
+ *     s = 0..d/32-1 four u32 words [code bit 0, code bit 1, code bit 2, QJL sign];
+ *     bit e of a word belongs to coordinate 32*s + e; sign bit = [ (S r)_l >= 0 ];
+ *     N[t] (fp16, ||x||) at byte P*d/2 + 2t; G[t] (fp16, ||r||) at P*d/2 + 2P + 2t.
+ *   V section, v_page_bytes = 3*d*P/8 + 2*P:
+ *     for plane j = 0..2 and coordinate i a P-bit row at byte (j*d + i)*P/8;
+ *     bit t of the row (bit t%32 of u32 word t/32) is bit j of token t's code of
+ *     coordinate i; N[t] (fp16) at byte 3*d*P/8 + 2t.
+ *   At d = 128 that is 544 bits per K vector (4.25 bits/dim) and 400 bits per V
+ *   vector (3.125 bits/dim); at d = 256, 4.125 and 3.0625 bits/dim.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,       /* null pointer, non-positive or inconsistent size        */
+  TQ_EUNSUPPORTED = -2, /* valid request outside what the kernels implement       */
+  TQ_EALIGN = -3,       /* pool not 256-byte aligned or I/O not 16-byte aligned    */
+  TQ_EWORKSPACE = -4,   /* workspace smaller than *workspace_bytes (size written)  */
+  TQ_EHIP = -5          /* a HIP launch or runtime call failed                     */
+} tq_status;
+
+typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+#define TQ_PAGE_SIZE 256   /* the only page size the kernels implement */
+#define TQ_MAX_GROUP 16    /* max query rows per KV head per sequence (Hq/Hkv * n_q) */
+
+/* Cache descriptor: plain data, owned by the caller, read by every call. */
+typedef struct {
+  int32_t head_dim;     /* d: 128 or 256                                         */
+  int32_t n_kv_heads;   /* Hkv >= 1                                              */
+  int32_t page_size;    /* P: must be TQ_PAGE_SIZE                               */
+  int32_t n_pages;      /* pool capacity in pages                                */
+  void *k_pool;         /* device, n_pages * Hkv * k_page_bytes, 256-B aligned    */
+  void *v_pool;         /* device, n_pages * Hkv * v_page_bytes, 256-B aligned    */
+  const float *qjl;     /* device, S as m x d float32 row-major (m = d)           */
+  float levels[8];      /* c[0..7], ascending (from tq_build_codebook)            */
+  float thresholds[7];  /* t[0..6], midpoints, thresholds[3] == 0                 */
+} tq_cache;
+
+/* Bytes of one (page, KV head) section; 0 for unsupported d or P. */
+size_t tq_k_page_bytes(int32_t head_dim, int32_t page_size);
+size_t tq_v_page_bytes(int32_t head_dim, int32_t page_size);
+
+/*
+ * Lloyd-Max codebook and QJL matrix ("TurboQuant KVキャッシュ圧縮アーキテクチャ",
+ * item 1; "K-Cache圧縮" steps 3 and 5). Host only, no GPU needed.
+ *   levels[8], thresholds[7] (host out): the 8-level MSE quantiser of N(0, 1/d),
+ *     found by Lloyd iteration in float64 from the Gaussian quantiles
+ *     sigma*Phi^-1((k+1/2)/8) until no level moves by 1e-14*sigma, symmetrised,
+ *     thresholds at midpoints, then rounded to float32.
+ *   qjl_host (host out, d*d floats, may be NULL): S[l][i] row-major; SplitMix64
+ *     seeded with qjl_seed gives pairs (x1, x2) -> u = ((x>>11)+1)*2^-53, Box-Muller
+ *     sqrt(-2 ln u1) cos(2 pi u2) then sin(...), filled in order, rounded to float32.
+ *     The caller uploads it and points tq_cache.qjl at the device copy.
+ * Errors: TQ_EINVAL (null levels/thresholds, head_dim < 2 or not a power of two),
+ * TQ_EUNSUPPORTED (bits != 3).
+ */
+int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed,
+                      float *levels, float *thresholds, float *qjl_host);
+
+/*
+ * K encode ("K-Cache圧縮" flow steps 1-5): for each token i and KV head h,
+ * x = k[i][h][:] (float32 or bfloat16, [n_tokens][Hkv][d] row-major, 16-B aligned):
+ * n = ||x||, x_hat = x/n (0 if n = 0), y = Pi x_hat, code_j = #{k: t_k <= y_j},
+ * r = y - c[code], z = S r; writes the K record, N = fp16(n), G = fp16(||r||) at
+ * slot slots[i] (device int32 [n_tokens]) of head h. Only the addressed records
+ * change. n_tokens == 0 is a no-op.
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED (d, P, dtype), TQ_EALIGN, TQ_EHIP.
+ */
+int tq_encode_k(const tq_cache *c, const void *k, int32_t dtype,
+                const int32_t *slots, int32_t n_tokens, void *stream);
+
+/*
+ * V encode ("V-Cache圧縮"): steps 1-3 of the K flow, then the V record and
+ * N = fp16(n). Bits of other tokens sharing the same V rows are preserved
+ * (the rows are updated with per-bit atomics). Same arguments and errors as
+ * tq_encode_k.
+ */
+int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype,
+                const int32_t *slots, int32_t n_tokens, void *stream);
+
+/*
+ * Query preparation (the query is rotated once per step instead of each key
+ * being dequantised): for each of n_rows query vectors q (float32 or bfloat16,
+ * [n_rows][d]) writes prep[row][0][:] = Pi q and prep[row][1][:] = S Pi q
+ * (device float32 [n_rows][2][d], 16-B aligned).
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EHIP.
+ */
+int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t n_rows,
+                     float *prep, void *stream);
+
+/*
+ * Decode attention over the packed cache, dequantisation fused in
+ * ("TurboQuant KVキャッシュ圧縮アーキテクチャ" item 2; "K-Cache圧縮", reason for QJL).
+ * For query row (b, t, h) of q [batch][n_q][Hq][d], KV head kv = h / (Hq/Hkv) and
+ * visible tokens j < L_b = seq_lens[b] (causal_tail = 0) or
+ * j < L_b - (n_q - 1 - t) (causal_tail = 1):
+ *   score_j = scale * N_j * (<Pi q, c[code_j]> + sqrt(pi/2)/m * G_j * <S Pi q, sigma_j>)
+ *   w = softmax(score),  out = Pi( sum_j w_j N^V_j c[codeV_j] )   (float32)
+ * Token j of sequence b lives at slot block_table[b][j / P] * P + j % P
+ * (block_table: device int32 [batch][max_pages]). An empty visible range gives
+ * a zero row. Hq / Hkv * n_q must not exceed TQ_MAX_GROUP.
+ * Workspace: call with workspace == NULL to get the size in *workspace_bytes
+ * (nothing is launched). The workspace must be zero-filled once before its
+ * first use; every call leaves its counters at zero again, so it can be reused
+ * by later calls on the same stream. Calls that share a workspace must not
+ * overlap. A workspace smaller than needed returns TQ_EWORKSPACE with the size
+ * written back.
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP.
+ */
+int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype,
+                   int32_t batch, int32_t n_q, int32_t n_q_heads,
+                   const int32_t *block_table, int32_t max_pages,
+                   const int32_t *seq_lens, int32_t causal_tail, float scale,
+                   float *out, void *workspace, size_t *workspace_bytes, void *stream);
+
+/*
+ * The attention part of tq_attn_decode alone, on queries already prepared by
+ * tq_query_prepare (prep: device float32 [batch][n_q][Hq][2][d]). Same
+ * semantics, workspace rules and errors; its workspace is smaller (no query
+ * region).
+ */
+int tq_attn_decode_prepared(const tq_cache *c, const float *prep,
+                            int32_t batch, int32_t n_q, int32_t n_q_heads,
+                            const int32_t *block_table, int32_t max_pages,
+                            const int32_t *seq_lens, int32_t causal_tail, float scale,
+                            float *out, void *workspace, size_t *workspace_bytes,
+                            void *stream);
+
+/*
+ * Dequantise records back to the original domain (float32 [n_tokens][Hkv][d]):
+ *   which = 0 (K): N * Pi(c[code] + sqrt(pi/2)/m * G * S^T sigma)  (with_qjl = 1)
+ *                  N * Pi c[code]                                    (with_qjl = 0)
+ *   which = 1 (V): N * Pi c[code]
+ * so that <q, K_tilde_j> equals the attention score estimate of token j.
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EHIP.
+ */
+int tq_dequant(const tq_cache *c, int32_t which, int32_t with_qjl,
+               const int32_t *slots, int32_t n_tokens, float *out, void *stream);
+
+/* Static description of a status code. */
+const char *tq_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

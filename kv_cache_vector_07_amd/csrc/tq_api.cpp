@@ -1,0 +1,320 @@
+// C-ABI entry points: argument checks, the host-side codebook / QJL matrix,
+// the decode split plan and workspace sizing. Device work lives in *.hip.
+#include <math.h>
+#include <string.h>
+
+#include "tq_internal.h"
+
+using tq::Codebook;
+
+namespace {
+
+bool supported_dim(int d) { return d == 128 || d == 256; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int check_cache(const tq_cache *c) {
+  if (!c) return TQ_EINVAL;
+  if (c->head_dim <= 0 || c->n_kv_heads <= 0 || c->page_size <= 0 || c->n_pages <= 0)
+    return TQ_EINVAL;
+  if (!supported_dim(c->head_dim) || c->page_size != TQ_PAGE_SIZE) return TQ_EUNSUPPORTED;
+  if (!c->k_pool || !c->v_pool) return TQ_EINVAL;
+  if (!aligned(c->k_pool, 256) || !aligned(c->v_pool, 256)) return TQ_EALIGN;
+  return TQ_OK;
+}
+
+Codebook codebook_of(const tq_cache *c) {
+  Codebook cb;
+  memcpy(cb.levels, c->levels, sizeof cb.levels);
+  memcpy(cb.thresholds, c->thresholds, sizeof cb.thresholds);
+  return cb;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+// ---- Lloyd-Max for N(0, sigma^2), float64 -------------------------------------
+double std_pdf(double u) { return isinf(u) ? 0.0 : exp(-0.5 * u * u) / sqrt(2.0 * M_PI); }
+
+// P(a < Z <= b), Z ~ N(0,1); upper-tail form when a >= 0 to avoid cancellation.
+double std_mass(double a, double b) {
+  auto upper = [](double x) { return 0.5 * erfc(x / M_SQRT2); };  // P(Z > x)
+  if (a >= 0) return upper(a) - upper(b);
+  return upper(-b) - upper(-a);
+}
+
+// Phi^-1(p) by bisection on erfc (only used for the starting levels).
+double std_quantile(double p) {
+  double lo = -40.0, hi = 40.0;
+  for (int i = 0; i < 200; ++i) {
+    double mid = 0.5 * (lo + hi);
+    double cdf = 0.5 * erfc(-mid / M_SQRT2);
+    (cdf < p ? lo : hi) = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+void lloyd_max(double sigma, double *c, double *t) {
+  const int n = 8;
+  for (int k = 0; k < n; ++k) c[k] = sigma * std_quantile((k + 0.5) / n);
+  for (int it = 0; it < 10000; ++it) {
+    for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+    double delta = 0.0;
+    for (int k = 0; k < n; ++k) {
+      double a = k == 0 ? -INFINITY : t[k - 1] / sigma;
+      double b = k == n - 1 ? INFINITY : t[k] / sigma;
+      double nc = sigma * (std_pdf(a) - std_pdf(b)) / std_mass(a, b);
+      delta = fmax(delta, fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (delta < 1e-14 * sigma) break;
+  }
+  double s[8];
+  for (int k = 0; k < n; ++k) s[k] = 0.5 * (c[k] - c[n - 1 - k]);
+  for (int k = 0; k < n; ++k) c[k] = s[k];
+  for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+  t[n / 2 - 1] = 0.0;
+}
+
+uint64_t splitmix64_next(uint64_t &state) {
+  uint64_t z = (state += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+namespace tq {
+
+DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages) {
+  DecodePlan p;
+  p.group = n_q_heads / n_kv_heads * n_q;
+  // Aim for about 2048 workgroups (8 per CU); each split keeps whole pages so a
+  // workgroup streams at least one 256-token page per KV head.
+  long work = (long)batch * n_kv_heads * max_pages;
+  int pps = (int)(work / 2048);
+  if (pps < 1) pps = 1;
+  p.pages_per_split = pps;
+  p.n_split = (max_pages + pps - 1) / pps;
+  p.counter_bytes = round_up((size_t)batch * n_kv_heads * sizeof(uint32_t), 256);
+  p.partial_bytes = round_up((size_t)batch * n_kv_heads * p.n_split * p.group * (d + 2) * sizeof(float), 256);
+  p.prep_bytes = round_up((size_t)batch * n_q * n_q_heads * 2 * d * sizeof(float), 256);
+  return p;
+}
+
+}  // namespace tq
+
+extern "C" {
+
+size_t tq_k_page_bytes(int32_t head_dim, int32_t page_size) {
+  if (head_dim <= 0 || head_dim % 32 || page_size <= 0 || page_size % 32) return 0;
+  return (size_t)page_size * head_dim / 2 + 4u * page_size;
+}
+
+size_t tq_v_page_bytes(int32_t head_dim, int32_t page_size) {
+  if (head_dim <= 0 || head_dim % 32 || page_size <= 0 || page_size % 32) return 0;
+  return (size_t)3 * head_dim * page_size / 8 + 2u * page_size;
+}
+
+const char *tq_status_string(int32_t s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_EUNSUPPORTED: return "unsupported configuration";
+    case TQ_EALIGN: return "misaligned buffer";
+    case TQ_EWORKSPACE: return "workspace too small";
+    case TQ_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed, float *levels,
+                      float *thresholds, float *qjl_host) {
+  if (!levels || !thresholds) return TQ_EINVAL;
+  if (head_dim < 2 || (head_dim & (head_dim - 1))) return TQ_EINVAL;
+  if (bits != 3) return TQ_EUNSUPPORTED;
+  double c[8], t[7];
+  lloyd_max(1.0 / sqrt((double)head_dim), c, t);
+  for (int k = 0; k < 8; ++k) levels[k] = (float)c[k];
+  for (int k = 0; k < 7; ++k) thresholds[k] = (float)t[k];
+  if (qjl_host) {
+    uint64_t state = qjl_seed;
+    const size_t n = (size_t)head_dim * head_dim;
+    for (size_t i = 0; i < n; i += 2) {
+      uint64_t x1 = splitmix64_next(state), x2 = splitmix64_next(state);
+      double u1 = (double)((x1 >> 11) + 1) * 0x1.0p-53;
+      double u2 = (double)((x2 >> 11) + 1) * 0x1.0p-53;
+      double rad = sqrt(-2.0 * log(u1));
+      double ang = 2.0 * M_PI * u2;
+      qjl_host[i] = (float)(rad * cos(ang));
+      if (i + 1 < n) qjl_host[i + 1] = (float)(rad * sin(ang));
+    }
+  }
+  return TQ_OK;
+}
+
+static int encode_common(const tq_cache *c, const void *x, int32_t dtype, const int32_t *slots,
+                         int32_t n_tokens, void *stream, bool is_k) {
+  int st = check_cache(c);
+  if (st) return st;
+  if (n_tokens < 0) return TQ_EINVAL;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
+  if (n_tokens == 0) return TQ_OK;
+  if (!x || !slots || (is_k && !c->qjl)) return TQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(slots, 4) || (is_k && !aligned(c->qjl, 16))) return TQ_EALIGN;
+  tq::EncodeArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.slots = slots;
+  a.n_tokens = n_tokens;
+  a.n_heads = c->n_kv_heads;
+  a.pool = (uint8_t *)(is_k ? c->k_pool : c->v_pool);
+  a.qjl = c->qjl;
+  a.cb = codebook_of(c);
+  hipStream_t s = (hipStream_t)stream;
+  return hip_status(is_k ? tq::launch_encode_k(a, c->head_dim, s)
+                         : tq::launch_encode_v(a, c->head_dim, s));
+}
+
+int tq_encode_k(const tq_cache *c, const void *k, int32_t dtype, const int32_t *slots,
+                int32_t n_tokens, void *stream) {
+  return encode_common(c, k, dtype, slots, n_tokens, stream, true);
+}
+
+int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype, const int32_t *slots,
+                int32_t n_tokens, void *stream) {
+  return encode_common(c, v, dtype, slots, n_tokens, stream, false);
+}
+
+int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t n_rows,
+                     float *prep, void *stream) {
+  if (!c) return TQ_EINVAL;
+  if (c->head_dim <= 0) return TQ_EINVAL;
+  if (!supported_dim(c->head_dim)) return TQ_EUNSUPPORTED;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
+  if (n_rows < 0) return TQ_EINVAL;
+  if (n_rows == 0) return TQ_OK;
+  if (!q || !prep || !c->qjl) return TQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(prep, 16) || !aligned(c->qjl, 16)) return TQ_EALIGN;
+  tq::PrepArgs a{q, dtype, n_rows, c->qjl, prep};
+  return hip_status(tq::launch_prepare(a, c->head_dim, (hipStream_t)stream));
+}
+
+static int decode_checks(const tq_cache *c, int32_t batch, int32_t n_q, int32_t n_q_heads,
+                         const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens,
+                         int32_t causal_tail, float *out, size_t *workspace_bytes) {
+  int st = check_cache(c);
+  if (st) return st;
+  if (!workspace_bytes) return TQ_EINVAL;
+  if (batch <= 0 || n_q <= 0 || n_q_heads <= 0 || max_pages <= 0) return TQ_EINVAL;
+  if (n_q_heads % c->n_kv_heads) return TQ_EINVAL;
+  if (causal_tail != 0 && causal_tail != 1) return TQ_EINVAL;
+  if (n_q_heads / c->n_kv_heads * n_q > TQ_MAX_GROUP) return TQ_EUNSUPPORTED;
+  if (!block_table || !seq_lens || !out || !c->qjl) return TQ_EINVAL;
+  if (!aligned(out, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4)) return TQ_EALIGN;
+  return TQ_OK;
+}
+
+static int decode_run(const tq_cache *c, const float *prep, int32_t batch, int32_t n_q,
+                      int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
+                      const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
+                      uint8_t *ws, const tq::DecodePlan &plan, hipStream_t s) {
+  tq::DecodeArgs a;
+  a.k_pool = (const uint8_t *)c->k_pool;
+  a.v_pool = (const uint8_t *)c->v_pool;
+  a.prep = prep;
+  a.block_table = block_table;
+  a.max_pages = max_pages;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.counters = (uint32_t *)ws;
+  a.partials = (float *)(ws + plan.counter_bytes);
+  a.batch = batch;
+  a.n_q = n_q;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = c->n_kv_heads;
+  a.causal_tail = causal_tail;
+  a.scale = scale;
+  a.plan = plan;
+  a.cb = codebook_of(c);
+  return hip_status(tq::launch_decode(a, c->head_dim, s));
+}
+
+int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype, int32_t batch, int32_t n_q,
+                   int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
+                   const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
+                   void *workspace, size_t *workspace_bytes, void *stream) {
+  int st = decode_checks(c, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+                         out, workspace_bytes);
+  if (st) return st;
+  if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
+  tq::DecodePlan plan =
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+  size_t need = plan.counter_bytes + plan.partial_bytes + plan.prep_bytes;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return TQ_OK;
+  }
+  if (*workspace_bytes < need) {
+    *workspace_bytes = need;
+    return TQ_EWORKSPACE;
+  }
+  if (!q) return TQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
+  uint8_t *ws = (uint8_t *)workspace;
+  float *prep = (float *)(ws + plan.counter_bytes + plan.partial_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  tq::PrepArgs pa{q, dtype, batch * n_q * n_q_heads, c->qjl, prep};
+  hipError_t e = tq::launch_prepare(pa, c->head_dim, s);
+  if (e != hipSuccess) return TQ_EHIP;
+  return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+                    scale, out, ws, plan, s);
+}
+
+int tq_attn_decode_prepared(const tq_cache *c, const float *prep, int32_t batch, int32_t n_q,
+                            int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
+                            const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
+                            void *workspace, size_t *workspace_bytes, void *stream) {
+  int st = decode_checks(c, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+                         out, workspace_bytes);
+  if (st) return st;
+  tq::DecodePlan plan =
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+  size_t need = plan.counter_bytes + plan.partial_bytes;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return TQ_OK;
+  }
+  if (*workspace_bytes < need) {
+    *workspace_bytes = need;
+    return TQ_EWORKSPACE;
+  }
+  if (!prep) return TQ_EINVAL;
+  if (!aligned(prep, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
+  return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+                    scale, out, (uint8_t *)workspace, plan, (hipStream_t)stream);
+}
+
+int tq_dequant(const tq_cache *c, int32_t which, int32_t with_qjl, const int32_t *slots,
+               int32_t n_tokens, float *out, void *stream) {
+  int st = check_cache(c);
+  if (st) return st;
+  if ((which != 0 && which != 1) || (with_qjl != 0 && with_qjl != 1) || n_tokens < 0)
+    return TQ_EINVAL;
+  if (n_tokens == 0) return TQ_OK;
+  if (!slots || !out || (which == 0 && with_qjl && !c->qjl)) return TQ_EINVAL;
+  if (!aligned(out, 16) || !aligned(slots, 4)) return TQ_EALIGN;
+  tq::DequantArgs a;
+  a.pool = (const uint8_t *)(which == 0 ? c->k_pool : c->v_pool);
+  a.slots = slots;
+  a.n_tokens = n_tokens;
+  a.n_heads = c->n_kv_heads;
+  a.with_qjl = which == 0 ? with_qjl : 0;
+  a.qjl = c->qjl;
+  a.out = out;
+  a.cb = codebook_of(c);
+  return hip_status(tq::launch_dequant(a, c->head_dim, which, (hipStream_t)stream));
+}
+
+}  // extern "C"

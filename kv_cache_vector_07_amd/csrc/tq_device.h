@@ -1,0 +1,103 @@
+// Device helpers shared by the TurboQuant kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int D>
+__device__ constexpr float rsqrt_dim() {
+  return D == 128 ? 0.08838834764831845f : (D == 256 ? 0.0625f : 0.0f);
+}
+
+// sqrt(pi/2) / m with m = D rows in the QJL matrix.
+template <int D>
+__device__ constexpr float qjl_kappa() {
+  return 1.2533141373155003f / (float)D;
+}
+
+template <int DT>
+__device__ inline float load_elem(const void *p, size_t i) {
+  if constexpr (DT == TQ_F32) {
+    return reinterpret_cast<const float *>(p)[i];
+  } else {
+    uint32_t b = reinterpret_cast<const uint16_t *>(p)[i];
+    return __uint_as_float(b << 16);
+  }
+}
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+// Unnormalised Walsh-Hadamard butterflies over D = 64*R values held by one
+// wave, coordinate i = lane + 64*r in v[r]. Pair distance h < 64 crosses lanes,
+// h >= 64 stays inside a lane's registers.
+template <int R>
+__device__ inline void fwht_wave(float (&v)[R]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1) {
+    const bool upper = lane & h;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float o = __shfl_xor(v[r], h, 64);
+      v[r] = upper ? (o - v[r]) : (v[r] + o);
+    }
+  }
+#pragma unroll
+  for (int hh = 1; hh < R; hh <<= 1) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (!(r & hh)) {
+        float x = v[r], y = v[r | hh];
+        v[r] = x + y;
+        v[r | hh] = x - y;
+      }
+    }
+  }
+}
+
+// c[idx] by a select tree (idx in 0..7) over the levels held in SGPRs.
+__device__ inline float level_of(const Codebook &cb, int idx) {
+  const bool b0 = idx & 1, b1 = idx & 2, b2 = idx & 4;
+  float l01 = b0 ? cb.levels[1] : cb.levels[0];
+  float l23 = b0 ? cb.levels[3] : cb.levels[2];
+  float l45 = b0 ? cb.levels[5] : cb.levels[4];
+  float l67 = b0 ? cb.levels[7] : cb.levels[6];
+  float l03 = b1 ? l23 : l01;
+  float l47 = b1 ? l67 : l45;
+  return b2 ? l47 : l03;
+}
+
+// Code = number of thresholds t_k <= y (a tie goes to the upper cell).
+__device__ inline int quantize_code(const Codebook &cb, float y) {
+  int idx = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) idx += (y >= cb.thresholds[k]) ? 1 : 0;
+  return idx;
+}
+
+__device__ inline uint16_t f32_to_f16_bits(float x) {
+  _Float16 h = (_Float16)x;  // round to nearest even, overflow to inf
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ inline float f16_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+}  // namespace tq

@@ -1,0 +1,233 @@
+"""ctypes binding of libtq.so: one Python function per C entry point, same names.
+
+Only argument marshalling happens here: every step of encode, decode and
+dequantisation runs in the HIP kernels behind the C ABI. torch supplies device
+memory and the current HIP stream. If the library is not built this module
+raises instead of computing anything another way.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+_lib = None
+
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2, -3, -4, -5
+TQ_F32, TQ_BF16 = 0, 1
+TQ_PAGE_SIZE = 256
+TQ_MAX_GROUP = 16
+EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_encode_k",
+           "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_prepared",
+           "tq_dequant", "tq_status_string")
+
+
+class TqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+class TqCacheDesc(C.Structure):
+    """Mirror of struct tq_cache."""
+    _fields_ = [("head_dim", C.c_int32), ("n_kv_heads", C.c_int32), ("page_size", C.c_int32),
+                ("n_pages", C.c_int32), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
+                ("qjl", C.c_void_p), ("levels", C.c_float * 8), ("thresholds", C.c_float * 7)]
+
+
+def lib():
+    """Load libtq.so once; raise loudly when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with "
+                          "`python -m kv_cache_vector_07_amd.build` (hipcc, gfx950)")
+    L = C.CDLL(_LIB_PATH)
+    vp, i32, f32, sz = C.c_void_p, C.c_int32, C.c_float, C.c_size_t
+    L.tq_k_page_bytes.argtypes = [i32, i32]
+    L.tq_k_page_bytes.restype = sz
+    L.tq_v_page_bytes.argtypes = [i32, i32]
+    L.tq_v_page_bytes.restype = sz
+    L.tq_status_string.argtypes = [i32]
+    L.tq_status_string.restype = C.c_char_p
+    L.tq_build_codebook.argtypes = [i32, i32, C.c_uint64, vp, vp, vp]
+    L.tq_encode_k.argtypes = [vp, vp, i32, vp, i32, vp]
+    L.tq_encode_v.argtypes = [vp, vp, i32, vp, i32, vp]
+    L.tq_query_prepare.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.tq_attn_decode.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
+                                 C.POINTER(sz), vp]
+    L.tq_attn_decode_prepared.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
+                                          C.POINTER(sz), vp]
+    L.tq_dequant.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    for name in ("tq_build_codebook", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
+                 "tq_attn_decode", "tq_attn_decode_prepared", "tq_dequant"):
+        getattr(L, name).restype = i32
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().tq_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        raise TqError(status, where)
+
+
+def _stream(stream) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return TQ_F32
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def tq_k_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE) -> int:
+    return int(lib().tq_k_page_bytes(head_dim, page_size))
+
+
+def tq_v_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE) -> int:
+    return int(lib().tq_v_page_bytes(head_dim, page_size))
+
+
+def tq_build_codebook(head_dim: int, bits: int = 3, qjl_seed: int = 12345, with_qjl: bool = True):
+    """Host-only: (levels float32[8], thresholds float32[7], S float32[d][d] or None)."""
+    levels = np.zeros(8, np.float32)
+    thr = np.zeros(7, np.float32)
+    S = np.zeros((head_dim, head_dim), np.float32) if with_qjl and head_dim > 0 else None
+    st = lib().tq_build_codebook(head_dim, bits, qjl_seed, levels.ctypes.data, thr.ctypes.data,
+                                 S.ctypes.data if S is not None else None)
+    _check(st, "tq_build_codebook")
+    return levels, thr, S
+
+
+class Cache:
+    """Caller-side owner of one packed cache: device pools, the QJL matrix and
+    the descriptor passed to every call. Pools are allocated with torch."""
+
+    def __init__(self, head_dim: int, n_kv_heads: int, n_pages: int, qjl_seed: int = 12345,
+                 device="cuda", codebook=None, zero: bool = True):
+        import torch
+        self.head_dim, self.n_kv_heads, self.n_pages = head_dim, n_kv_heads, n_pages
+        self.page_size = TQ_PAGE_SIZE
+        levels, thr, S = codebook if codebook is not None else tq_build_codebook(head_dim, 3, qjl_seed)
+        self.levels, self.thresholds, self.qjl_host = levels, thr, S
+        kpb, vpb = tq_k_page_bytes(head_dim), tq_v_page_bytes(head_dim)
+        alloc = torch.zeros if zero else torch.empty
+        self.k_pool = alloc(n_pages * n_kv_heads * kpb, dtype=torch.uint8, device=device)
+        self.v_pool = alloc(n_pages * n_kv_heads * vpb, dtype=torch.uint8, device=device)
+        self.qjl = torch.from_numpy(S).to(device)
+        self.desc = TqCacheDesc(head_dim, n_kv_heads, self.page_size, n_pages,
+                                self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.qjl.data_ptr(),
+                                (C.c_float * 8)(*levels.tolist()), (C.c_float * 7)(*thr.tolist()))
+        self._ws = None
+
+    @property
+    def ref(self):
+        return C.byref(self.desc)
+
+    def workspace(self, nbytes: int):
+        """A zero-initialised decode workspace of at least nbytes, reused across calls."""
+        import torch
+        if self._ws is None or self._ws.numel() < nbytes:
+            self._ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.k_pool.device)
+        return self._ws
+
+
+def tq_encode_k(cache: Cache, k, slots, stream=None) -> None:
+    """k: [n_tokens][Hkv][d] float32/bfloat16 on the device; slots: int32 [n_tokens]."""
+    st = lib().tq_encode_k(cache.ref, k.data_ptr(), _dtype_code(k), slots.data_ptr(),
+                           int(slots.numel()), _stream(stream))
+    _check(st, "tq_encode_k")
+
+
+def tq_encode_v(cache: Cache, v, slots, stream=None) -> None:
+    st = lib().tq_encode_v(cache.ref, v.data_ptr(), _dtype_code(v), slots.data_ptr(),
+                           int(slots.numel()), _stream(stream))
+    _check(st, "tq_encode_v")
+
+
+def tq_query_prepare(cache: Cache, q, prep=None, stream=None):
+    """q: [..., d] -> prep [..., 2, d] float32 (rotated query, then S times it)."""
+    import torch
+    d = cache.head_dim
+    rows = q.numel() // d
+    if prep is None:
+        prep = torch.empty(*q.shape[:-1], 2, d, dtype=torch.float32, device=q.device)
+    st = lib().tq_query_prepare(cache.ref, q.data_ptr(), _dtype_code(q), rows, prep.data_ptr(),
+                                _stream(stream))
+    _check(st, "tq_query_prepare")
+    return prep
+
+
+def _decode_ws(cache, fn, args, workspace):
+    size = C.c_size_t(0)
+    st = fn(*args(None), C.byref(size), None)
+    _check(st, fn.__name__ + " (workspace query)")
+    ws = workspace if workspace is not None else cache.workspace(size.value)
+    return ws, size
+
+
+def tq_attn_decode(cache: Cache, q, block_table, seq_lens, causal_tail: int = 0, scale=None,
+                   out=None, workspace=None, stream=None):
+    """q: [B][n_q][Hq][d]; block_table: int32 [B][max_pages]; seq_lens: int32 [B]."""
+    import torch
+    B, n_q, Hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=q.device)
+    L = lib()
+    args = lambda ws: (cache.ref, q.data_ptr(), _dtype_code(q), B, n_q, Hq, block_table.data_ptr(),
+                       int(block_table.shape[1]), seq_lens.data_ptr(), int(causal_tail), scale,
+                       out.data_ptr(), ws)
+    ws, size = _decode_ws(cache, L.tq_attn_decode, args, workspace)
+    size = C.c_size_t(ws.numel())
+    st = L.tq_attn_decode(*args(ws.data_ptr()), C.byref(size), _stream(stream))
+    _check(st, "tq_attn_decode")
+    return out
+
+
+def tq_attn_decode_prepared(cache: Cache, prep, block_table, seq_lens, causal_tail: int = 0,
+                            scale=None, out=None, workspace=None, stream=None):
+    """prep: [B][n_q][Hq][2][d] float32 from tq_query_prepare."""
+    import torch
+    B, n_q, Hq, _, d = prep.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=prep.device)
+    L = lib()
+    args = lambda ws: (cache.ref, prep.data_ptr(), B, n_q, Hq, block_table.data_ptr(),
+                       int(block_table.shape[1]), seq_lens.data_ptr(), int(causal_tail), scale,
+                       out.data_ptr(), ws)
+    ws, size = _decode_ws(cache, L.tq_attn_decode_prepared, args, workspace)
+    size = C.c_size_t(ws.numel())
+    st = L.tq_attn_decode_prepared(*args(ws.data_ptr()), C.byref(size), _stream(stream))
+    _check(st, "tq_attn_decode_prepared")
+    return out
+
+
+def tq_dequant(cache: Cache, which: int, with_qjl: int, slots, out=None, stream=None):
+    """which 0 = K, 1 = V; returns float32 [n_tokens][Hkv][d] in the original domain."""
+    import torch
+    n = int(slots.numel())
+    if out is None:
+        out = torch.empty(n, cache.n_kv_heads, cache.head_dim, dtype=torch.float32,
+                          device=slots.device)
+    st = lib().tq_dequant(cache.ref, int(which), int(with_qjl), slots.data_ptr(), n,
+                          out.data_ptr(), _stream(stream))
+    _check(st, "tq_dequant")
+    return out
