@@ -1,0 +1,294 @@
+"""Benchmark of the TurboQuant KV-cache hot path on one MI355X.
+
+One step = the whole path for one decode step of the workload: encode the
+step's new K and V token of every KV head into the cache (append), prepare
+the queries (rotation + QJL projection), and run split-K decode attention over
+the full compressed context. Steps read rotating device copies of the cache
+(together at least 1 GiB, four times the 256 MB Infinity Cache) so the stream
+comes from HBM. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes as C
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "compressed-KV decode attention GB/s (% HBM peak) + ctx tokens/s; encode vec/s"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
+
+
+def kv_bytes_per_token_head(d: int) -> int:
+    """Algorithmic compressed bytes read per (token, KV head): K record + its
+    two fp16 sidecars, V record + its fp16 sidecar."""
+    return (d // 2 + 4) + (3 * d // 8 + 2)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "kv_cache_vector_07_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per decode launch measured with rocprofv3 counters, if they were
+    taken on the current kernel sources (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.strip().split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash() or kv.get("workload") != workload:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0):
+    """The CPU reference (numpy float64, as it stands) timed on this host on a
+    bounded sample: whole decode steps over every KV head of sequence 0, and
+    an encode of a slice of the K/V inputs."""
+    import oracle as O
+    from kv_cache_vector_07_amd import inputs as I
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cb = O.codebook(w.head_dim)
+    S = O.qjl_matrix(w.head_dim, w.qjl_seed)
+    d, H = w.head_dim, w.n_kv_heads
+    L = int(lens[0])
+    t0 = time.perf_counter()
+    heads_done = 0
+    while time.perf_counter() - t0 < budget_s and heads_done < 3 * H:
+        O.attn_decode(kp, vp, cb, S, q[:1].astype(np.float64), table[:1], lens[:1], H,
+                      w.page_size, 1 / math.sqrt(d), pairs=[(0, heads_done % H)])
+        heads_done += 1
+    dt = time.perf_counter() - t0
+    gbs = heads_done * L * kv_bytes_per_token_head(d) / dt / 1e9
+    n_enc = 2048
+    x = I.kv_tokens(w, "k", 0, 0, n_enc // H + 1)[: n_enc // H].astype(np.float64)
+    t1 = time.perf_counter()
+    O.encode(x, cb, S)
+    O.encode(x, cb)
+    enc_dt = time.perf_counter() - t1
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads_done} (sequence, KV head) decode passes over L={L} "
+                      f"({heads_done * w.group} query rows) in {dt:.1f} s; "
+                      f"encode of {x.shape[0] * H} K and V vectors",
+            "encode_vec_per_s": round(2 * x.shape[0] * H / enc_dt, 1)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-launches", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+
+    from kv_cache_vector_07_amd import inputs as I
+    from kv_cache_vector_07_amd import tq
+
+    L_ = tq.lib()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    w = I.workload(args.workload)
+    d, H, Hq, B, nq = w.head_dim, w.n_kv_heads, w.n_q_heads, w.batch, w.n_q
+    lens = I.seq_lens(w)
+    table_np, n_pages = I.page_table(w, lens, shuffle=w.batch > 1)
+    kpb, vpb = tq.tq_k_page_bytes(d), tq.tq_v_page_bytes(d)
+    copy_bytes = n_pages * H * (kpb + vpb)
+    R = max(1, math.ceil(ROTATE_BYTES / copy_bytes))
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log(f"[bench] workload {w.name}: B={B} Hq={Hq} Hkv={H} d={d} n_q={nq} "
+        f"L={lens.tolist() if B <= 4 else (int(lens.min()), int(lens.max()))}, "
+        f"{n_pages} pages, {R} rotating copies of {copy_bytes / 1e6:.1f} MB")
+
+    # ---- build the compressed cache once (timed: encode vec/s), then copy it
+    base = tq.Cache(d, H, n_pages, qjl_seed=w.qjl_seed, device=dev)
+    table = torch.from_numpy(table_np).to(dev)
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    stream = torch.cuda.current_stream()
+    enc_k_ms = enc_v_ms = 0.0
+    n_vec = 0
+    chunk = 32768
+    for b in range(B):
+        Lb = int(lens[b])
+        for t0 in range(0, Lb, chunk):
+            t1 = min(Lb, t0 + chunk)
+            k = torch.from_numpy(I.kv_tokens(w, "k", b, t0, t1)).to(dev, tdt)
+            v = torch.from_numpy(I.kv_tokens(w, "v", b, t0, t1)).to(dev, tdt)
+            t = torch.arange(t0, t1, device=dev)
+            slots = (table[b, t // 256] * 256 + t % 256).to(torch.int32)
+            e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+            e0.record()
+            tq.tq_encode_k(base, k, slots)
+            e1.record()
+            tq.tq_encode_v(base, v, slots)
+            e2.record()
+            e2.synchronize()
+            enc_k_ms += e0.elapsed_time(e1)
+            enc_v_ms += e1.elapsed_time(e2)
+            n_vec += (t1 - t0) * H
+    log(f"[bench] cache encoded: {n_vec} K and V vectors")
+    copies = [base]
+    for _ in range(R - 1):
+        c = tq.Cache(d, H, n_pages, device=dev, zero=False,
+                     codebook=(base.levels, base.thresholds, base.qjl_host))
+        c.k_pool.copy_(base.k_pool)
+        c.v_pool.copy_(base.v_pool)
+        copies.append(c)
+    torch.cuda.synchronize()
+
+    # ---- per-step inputs: fresh queries and one new K/V token per sequence
+    n_q_sets = 16
+    qs = [torch.from_numpy(I.queries(w, s)).to(dev, tdt) for s in range(n_q_sets)]
+    app_k = [torch.from_numpy(I.kv_tokens(w, "k", b, int(lens[b]) - 1, int(lens[b]))).to(dev, tdt)
+             for b in range(B)]
+    app_v = [torch.from_numpy(I.kv_tokens(w, "v", b, int(lens[b]) - 1, int(lens[b]))).to(dev, tdt)
+             for b in range(B)]
+    new_k = torch.cat(app_k, 0).contiguous()
+    new_v = torch.cat(app_v, 0).contiguous()
+    last = torch.from_numpy(lens - 1).to(dev)
+    app_slots = (table[torch.arange(B, device=dev), last // 256] * 256 + last % 256).to(torch.int32)
+    size = C.c_size_t(0)
+    scale = 1.0 / math.sqrt(d)
+    out = torch.empty(B, nq, Hq, d, dtype=torch.float32, device=dev)
+    st = L_.tq_attn_decode(copies[0].ref, qs[0].data_ptr(), tq._dtype_code(qs[0]), B, nq, Hq,
+                           table.data_ptr(), table.shape[1], seq.data_ptr(), 0, scale,
+                           out.data_ptr(), None, C.byref(size), None)
+    assert st == 0, st
+    ws = torch.zeros(size.value, dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+    qdt = tq._dtype_code(qs[0])
+    mp = table.shape[1]
+
+    def step(i):
+        c = copies[i % R]
+        q = qs[i % n_q_sets]
+        r = L_.tq_encode_k(c.ref, new_k.data_ptr(), qdt, app_slots.data_ptr(), B, sh)
+        r |= L_.tq_encode_v(c.ref, new_v.data_ptr(), qdt, app_slots.data_ptr(), B, sh)
+        sz = C.c_size_t(ws.numel())
+        r |= L_.tq_attn_decode(c.ref, q.data_ptr(), qdt, B, nq, Hq, table.data_ptr(), mp,
+                               seq.data_ptr(), 0, scale, out.data_ptr(), ws.data_ptr(),
+                               C.byref(sz), sh)
+        if r:
+            raise RuntimeError(f"launch failed with status {r}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {step_ms * 1e3:.2f} us/step (host wall {wall:.3f} s)")
+
+    # ---- decode kernel alone (the dominant kernel): back-to-back launches
+    prep = tq.tq_query_prepare(copies[0], qs[0])
+    size_p = C.c_size_t(0)
+    L_.tq_attn_decode_prepared(copies[0].ref, prep.data_ptr(), B, nq, Hq, table.data_ptr(), mp,
+                               seq.data_ptr(), 0, scale, out.data_ptr(), None, C.byref(size_p), None)
+    ws_p = torch.zeros(size_p.value, dtype=torch.uint8, device=dev)
+
+    def dec(i):
+        c = copies[i % R]
+        sz = C.c_size_t(ws_p.numel())
+        r = L_.tq_attn_decode_prepared(c.ref, prep.data_ptr(), B, nq, Hq, table.data_ptr(), mp,
+                                       seq.data_ptr(), 0, scale, out.data_ptr(), ws_p.data_ptr(),
+                                       C.byref(sz), sh)
+        if r:
+            raise RuntimeError(f"decode launch failed with status {r}")
+
+    for i in range(16):
+        dec(i)
+    torch.cuda.synchronize()
+    ev0.record()
+    for i in range(args.decode_launches):
+        dec(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    dec_ms = ev0.elapsed_time(ev1) / args.decode_launches
+
+    ctx_tokens = int(lens.sum())
+    kv_bytes = ctx_tokens * H * kv_bytes_per_token_head(d)
+    app_bytes = B * H * (2 * d * (2 if w.dtype == "bf16" else 4) + kv_bytes_per_token_head(d))
+    step_s = step_ms / 1e3
+    value = (kv_bytes + app_bytes) / step_s / 1e9
+    dec_gbs = kv_bytes / (dec_ms / 1e3) / 1e9
+    traffic = read_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; outlier-channel K where the workload says so)",
+        "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": H,
+                   "head_dim": d, "n_q": nq, "context": int(lens.max()) if B == 1 else
+                   [int(lens.min()), int(lens.max())], "ctx_tokens": ctx_tokens,
+                   "input_dtype": w.dtype, "page_size": 256, "rotating_copies": R,
+                   "step": "append 1 token/seq (encode K+V) + query prep + split-K decode"},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "ctx_tokens_per_s": round(ctx_tokens / step_s, 1),
+        "encode_k_vec_per_s": round(n_vec / (enc_k_ms / 1e3), 1),
+        "encode_v_vec_per_s": round(n_vec / (enc_v_ms / 1e3), 1),
+        "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel",
+                     "bytes_per_launch": kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU reference on a bounded sample")
+        kp = base.k_pool.cpu().numpy()
+        vp = base.v_pool.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(w, lens, n_pages, kp, vp, table_np,
+                                              I.queries(w, 0))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,13 +125,19 @@ int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype,
 
 /*
  * Query preparation (the query is rotated once per step instead of each key
- * being dequantised): for each of n_rows query vectors q (float32 or bfloat16,
- * [n_rows][d]) writes prep[row][0][:] = Pi q and prep[row][1][:] = S Pi q
- * (device float32 [n_rows][2][d], 16-B aligned).
- * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EHIP.
+ * being dequantised) for one decode call over q [batch][n_q][n_q_heads][d]
+ * (float32 or bfloat16, 16-B aligned). Writes into `prep` (device, 256-B
+ * aligned, *prep_bytes bytes):
+ *   [rows][2][d] float32 with rows in (b, t, h) order: Pi q, then S Pi q;
+ *   then, when Hq/Hkv * n_q <= 4, the packed int8 scoring operand of each
+ *   (sequence, KV head) used by the MFMA decode kernel (internal layout).
+ * prep == NULL returns the size in *prep_bytes and launches nothing; a short
+ * buffer returns TQ_EWORKSPACE with the size written back.
+ * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP.
  */
-int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t n_rows,
-                     float *prep, void *stream);
+int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t batch,
+                     int32_t n_q, int32_t n_q_heads, void *prep, size_t *prep_bytes,
+                     void *stream);
 
 /*
  * Decode attention over the packed cache, dequantisation fused in
@@ -145,11 +151,11 @@ int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t n_
  * (block_table: device int32 [batch][max_pages]). An empty visible range gives
  * a zero row. Hq / Hkv * n_q must not exceed TQ_MAX_GROUP.
  * Workspace: call with workspace == NULL to get the size in *workspace_bytes
- * (nothing is launched). The workspace must be zero-filled once before its
- * first use; every call leaves its counters at zero again, so it can be reused
- * by later calls on the same stream. Calls that share a workspace must not
- * overlap. A workspace smaller than needed returns TQ_EWORKSPACE with the size
- * written back.
+ * (nothing is launched). It holds split partials and the prepared queries; its
+ * contents need no initialisation and are scratch after the call. Calls that
+ * share a workspace must not overlap. A workspace smaller than needed returns
+ * TQ_EWORKSPACE with the size written back. Two kernels are enqueued after the
+ * query preparation: the split-K pass and a small merge.
  * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP.
  */
 int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype,
@@ -159,12 +165,12 @@ int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype,
                    float *out, void *workspace, size_t *workspace_bytes, void *stream);
 
 /*
- * The attention part of tq_attn_decode alone, on queries already prepared by
- * tq_query_prepare (prep: device float32 [batch][n_q][Hq][2][d]). Same
- * semantics, workspace rules and errors; its workspace is smaller (no query
- * region).
+ * The attention part of tq_attn_decode alone (one kernel launch), on queries
+ * already prepared by tq_query_prepare with the same batch, n_q and n_q_heads.
+ * Same semantics, workspace rules and errors; its workspace is smaller (no
+ * query region).
  */
-int tq_attn_decode_prepared(const tq_cache *c, const float *prep,
+int tq_attn_decode_prepared(const tq_cache *c, const void *prep,
                             int32_t batch, int32_t n_q, int32_t n_q_heads,
                             const int32_t *block_table, int32_t max_pages,
                             const int32_t *seq_lens, int32_t causal_tail, float scale,

@@ -90,6 +90,7 @@ namespace tq {
 DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages) {
   DecodePlan p;
   p.group = n_q_heads / n_kv_heads * n_q;
+  p.mfma = p.group <= kMfmaMaxGroup;
   // Aim for about 2048 workgroups (8 per CU); each split keeps whole pages so a
   // workgroup streams at least one 256-token page per KV head.
   long work = (long)batch * n_kv_heads * max_pages;
@@ -97,9 +98,10 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
   if (pps < 1) pps = 1;
   p.pages_per_split = pps;
   p.n_split = (max_pages + pps - 1) / pps;
-  p.counter_bytes = round_up((size_t)batch * n_kv_heads * sizeof(uint32_t), 256);
-  p.partial_bytes = round_up((size_t)batch * n_kv_heads * p.n_split * p.group * (d + 2) * sizeof(float), 256);
-  p.prep_bytes = round_up((size_t)batch * n_q * n_q_heads * 2 * d * sizeof(float), 256);
+  p.counter_bytes = 0;
+  p.partial_bytes =
+      round_up((size_t)batch * n_kv_heads * p.n_split * p.group * (d + 4) * sizeof(float), 256);
+  p.prep_bytes = prep_region_bytes(d, batch, n_q, n_q_heads, n_kv_heads);
   return p;
 }
 
@@ -187,18 +189,52 @@ int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype, const int32_t *
   return encode_common(c, v, dtype, slots, n_tokens, stream, false);
 }
 
-int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t n_rows,
-                     float *prep, void *stream) {
+static int prepare_checks(const tq_cache *c, int32_t dtype, int32_t batch, int32_t n_q,
+                          int32_t n_q_heads) {
   if (!c) return TQ_EINVAL;
-  if (c->head_dim <= 0) return TQ_EINVAL;
+  if (c->head_dim <= 0 || c->n_kv_heads <= 0) return TQ_EINVAL;
   if (!supported_dim(c->head_dim)) return TQ_EUNSUPPORTED;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
-  if (n_rows < 0) return TQ_EINVAL;
-  if (n_rows == 0) return TQ_OK;
-  if (!q || !prep || !c->qjl) return TQ_EINVAL;
-  if (!aligned(q, 16) || !aligned(prep, 16) || !aligned(c->qjl, 16)) return TQ_EALIGN;
-  tq::PrepArgs a{q, dtype, n_rows, c->qjl, prep};
-  return hip_status(tq::launch_prepare(a, c->head_dim, (hipStream_t)stream));
+  if (batch <= 0 || n_q <= 0 || n_q_heads <= 0 || n_q_heads % c->n_kv_heads) return TQ_EINVAL;
+  if (n_q_heads / c->n_kv_heads * n_q > TQ_MAX_GROUP) return TQ_EUNSUPPORTED;
+  return TQ_OK;
+}
+
+static hipError_t run_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t batch,
+                              int32_t n_q, int32_t n_q_heads, uint8_t *prep, hipStream_t s) {
+  tq::PrepArgs a;
+  a.q = q;
+  a.dtype = dtype;
+  a.batch = batch;
+  a.n_q = n_q;
+  a.n_q_heads = n_q_heads;
+  a.n_kv_heads = c->n_kv_heads;
+  a.qjl = c->qjl;
+  a.prep = (float *)prep;
+  const bool mfma = n_q_heads / c->n_kv_heads * n_q <= tq::kMfmaMaxGroup;
+  a.packed = mfma ? prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads) : nullptr;
+  a.cb = codebook_of(c);
+  return tq::launch_prepare(a, c->head_dim, s);
+}
+
+int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t batch, int32_t n_q,
+                     int32_t n_q_heads, void *prep, size_t *prep_bytes, void *stream) {
+  int st = prepare_checks(c, dtype, batch, n_q, n_q_heads);
+  if (st) return st;
+  if (!prep_bytes) return TQ_EINVAL;
+  const size_t need = tq::prep_region_bytes(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads);
+  if (!prep) {
+    *prep_bytes = need;
+    return TQ_OK;
+  }
+  if (*prep_bytes < need) {
+    *prep_bytes = need;
+    return TQ_EWORKSPACE;
+  }
+  if (!q || !c->qjl) return TQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(prep, 256) || !aligned(c->qjl, 16)) return TQ_EALIGN;
+  return hip_status(run_prepare(c, q, dtype, batch, n_q, n_q_heads, (uint8_t *)prep,
+                                (hipStream_t)stream));
 }
 
 static int decode_checks(const tq_cache *c, int32_t batch, int32_t n_q, int32_t n_q_heads,
@@ -216,14 +252,15 @@ static int decode_checks(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   return TQ_OK;
 }
 
-static int decode_run(const tq_cache *c, const float *prep, int32_t batch, int32_t n_q,
+static int decode_run(const tq_cache *c, const uint8_t *prep, int32_t batch, int32_t n_q,
                       int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
                       const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
                       uint8_t *ws, const tq::DecodePlan &plan, hipStream_t s) {
   tq::DecodeArgs a;
   a.k_pool = (const uint8_t *)c->k_pool;
   a.v_pool = (const uint8_t *)c->v_pool;
-  a.prep = prep;
+  a.prep = (const float *)prep;
+  a.packed = prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads);
   a.block_table = block_table;
   a.max_pages = max_pages;
   a.seq_lens = seq_lens;
@@ -263,16 +300,14 @@ int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype, int32_t batc
   if (!q) return TQ_EINVAL;
   if (!aligned(q, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
   uint8_t *ws = (uint8_t *)workspace;
-  float *prep = (float *)(ws + plan.counter_bytes + plan.partial_bytes);
+  uint8_t *prep = ws + plan.counter_bytes + plan.partial_bytes;
   hipStream_t s = (hipStream_t)stream;
-  tq::PrepArgs pa{q, dtype, batch * n_q * n_q_heads, c->qjl, prep};
-  hipError_t e = tq::launch_prepare(pa, c->head_dim, s);
-  if (e != hipSuccess) return TQ_EHIP;
+  if (run_prepare(c, q, dtype, batch, n_q, n_q_heads, prep, s) != hipSuccess) return TQ_EHIP;
   return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
                     scale, out, ws, plan, s);
 }
 
-int tq_attn_decode_prepared(const tq_cache *c, const float *prep, int32_t batch, int32_t n_q,
+int tq_attn_decode_prepared(const tq_cache *c, const void *prep, int32_t batch, int32_t n_q,
                             int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
                             const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
                             void *workspace, size_t *workspace_bytes, void *stream) {
@@ -291,8 +326,8 @@ int tq_attn_decode_prepared(const tq_cache *c, const float *prep, int32_t batch,
     return TQ_EWORKSPACE;
   }
   if (!prep) return TQ_EINVAL;
-  if (!aligned(prep, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
-  return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+  if (!aligned(prep, 256) || !aligned(workspace, 256)) return TQ_EALIGN;
+  return decode_run(c, (const uint8_t *)prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
                     scale, out, (uint8_t *)workspace, plan, (hipStream_t)stream);
 }
 

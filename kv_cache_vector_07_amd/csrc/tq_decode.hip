@@ -1,25 +1,181 @@
-// Split-K decode attention over the packed TurboQuant cache.
+// Query preparation and split-K decode attention over the packed TurboQuant cache.
 //
 // Method: AI Heartland news "Apple Silicon向けSwiftLM、TurboQuant KVキャッシュ圧縮と
 // SSD Expert Streamingを実装", section 技術的な詳細: "K-Cache圧縮" (QJL signs keep the
-// inner-product score accurate), "V-Cache圧縮" (V is only accumulated), and
+// inner-product score accurate), "V-Cache圧縮" (V is only accumulated) and
 // "TurboQuant KVキャッシュ圧縮アーキテクチャ" item 2 (dequantisation fused into the
-// attention kernel: no dequantised K/V ever reaches memory).
+// attention kernel: no dequantised K/V ever reaches memory). The query is rotated
+// and projected once per step; scores and the V sum live in the rotated domain
+// and one inverse rotation is applied per output row.
 //
-// Grid (split, kv_head, sequence); a workgroup streams whole 256-token pages of
-// one (sequence, KV head), scores every token against all query rows of that KV
-// head (Hq/Hkv heads x n_q tokens) in the rotated domain, keeps an online softmax
-// and accumulates V in the rotated domain. The last workgroup of a (sequence, KV
-// head) to finish merges the split partials by log-sum-exp, applies the single
-// inverse rotation and writes float32 outputs.
+// Grid (split, KV head, sequence). A workgroup streams whole 256-token pages of
+// one (sequence, KV head) for every query row of that KV head, keeps an online
+// softmax, and writes (max, sum, V numerator) partials; a second, small kernel
+// merges the partials of each (sequence, KV head) by log-sum-exp and writes
+// float32 rows. (Merging in the last-arriving workgroup would need a device-scope
+// release per workgroup, which on this GPU writes back and invalidates the whole
+// L2 of the XCD every time.)
+//
+// Two kernels implement the same arithmetic:
+//  - decode_mfma_kernel (<= 4 query rows per KV head). Scores are an int8 MFMA
+//    contraction: with beta_j = 2 b_j - 1 the 3-bit code satisfies
+//    c[idx] = 2 (a0 b0 + a1 b1 + a2 b2 + a3 (b0^b1^b2)) - c7 because the codebook
+//    is odd (c[7-k] = -c[k]), so each key bit plane becomes an int8 operand with
+//    one AND per four coordinates; the query side is exact to fp32 precision as
+//    four int8 limbs laid along the 16 MFMA rows (4 rows x 4 limbs). V is
+//    accumulated with f16 MFMAs in the zero-mean form c[idx] = sum_j a_j beta_j
+//    (beta_3 = beta0 beta1 beta2 = 2 (b0^b1^b2) - 1): each key bit becomes the sign
+//    of a constant fp16 value, so the fp16 rounding of the weights does not add up
+//    coherently over coordinates.
+//  - decode_valu_kernel (up to 16 rows): plain VALU loops, one token per thread.
 #include "tq_device.h"
 
 namespace tq {
 namespace {
 
-template <int D, int GT>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kPartHead = 4;   // partial record: m, l, mU, pad, then acc[d]
+
+// Weights of the odd-codebook bit planes: c[idx] = sum_j 2 a_j plane_j - c7 with
+// planes (b0, b1, b2, b0^b1^b2).
+__device__ inline void plane_weights(const Codebook &cb, float (&w)[4]) {
+  const float c4 = cb.levels[4], c5 = cb.levels[5], c6 = cb.levels[6], c7 = cb.levels[7];
+  const float a2 = 0.25f * (c4 + c5 + c6 + c7);
+  w[0] = 2.f * (0.5f * (c5 + c7) - a2);
+  w[1] = 2.f * (0.5f * (c6 + c7) - a2);
+  w[2] = 2.f * a2;
+  w[3] = 2.f * (0.5f * (c4 + c7) - a2);
+}
+
+// ------------------------------------------------------------------ prepare
+// One workgroup per (sequence, KV head): rotate and project its query rows,
+// then (MFMA path) write the packed int8 scoring operand of the group.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   constexpr int R = D / 64;
+  constexpr int NMU = 10 * (D / 128);
+  __shared__ float s_v[kMfmaMaxGroup][2][D];
+  __shared__ float s_const[kMfmaMaxGroup][4];
+  __shared__ float s_q[4][D];
+  const int kvh = blockIdx.x, b = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = a.n_q_heads / a.n_kv_heads, G = g * a.n_q;
+  const bool pack = a.packed != nullptr;
+
+  for (int qq = wave; qq < G; qq += 4) {
+    const int t = qq / g, hh = qq % g;
+    const size_t row = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
+    float v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[r] = load_elem<DT>(a.q, row * D + lane + 64 * r);
+    fwht_wave<R>(v);
+    float *dst = a.prep + row * 2 * D;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      v[r] *= rsqrt_dim<D>();
+      dst[lane + 64 * r] = v[r];
+      s_q[wave][lane + 64 * r] = v[r];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // p_l = sum_i S[l][i] q~_i for rows l = lane + 64 r
+    float p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) p[r] = 0.f;
+    const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
+    const float4 *q4 = reinterpret_cast<const float4 *>(s_q[wave]);
+#pragma unroll 16
+    for (int i4 = 0; i4 < D / 4; ++i4) {
+      const float4 qv = q4[i4];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const float4 s = S4[(size_t)(lane + 64 * r) * (D / 4) + i4];
+        p[r] = fmaf(s.x, qv.x, p[r]);
+        p[r] = fmaf(s.y, qv.y, p[r]);
+        p[r] = fmaf(s.z, qv.z, p[r]);
+        p[r] = fmaf(s.w, qv.w, p[r]);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) dst[D + lane + 64 * r] = p[r];
+    if (pack) {
+      float w[4];
+      plane_weights(a.cb, w);
+      const float wmax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
+      float mq = 0.f, mp = 0.f, sq = 0.f, sp = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        s_v[qq][0][lane + 64 * r] = v[r];
+        s_v[qq][1][lane + 64 * r] = p[r];
+        mq = fmaxf(mq, fabsf(v[r]));
+        mp = fmaxf(mp, fabsf(p[r]));
+        sq += v[r];
+        sp += p[r];
+      }
+      mq = wave_max(mq);
+      mp = wave_max(mp);
+      sq = wave_sum(sq);
+      sp = wave_sum(sp);
+      if (lane == 0) {
+        // integer scales: |value / delta| < 2^30 so four balanced base-256 limbs hold it
+        s_const[qq][0] = mq > 0.f ? wmax * mq * 0x1p-30f : 1.f;
+        s_const[qq][1] = mp > 0.f ? 2.f * mp * 0x1p-30f : 1.f;
+        s_const[qq][2] = sq;
+        s_const[qq][3] = sp;
+      }
+    }
+  }
+  if (!pack) return;
+  __syncthreads();
+
+  // Operand byte (mu, lane = 16 kg + n, 4 r' + bb): row n = 4 q + limb, MFMA mu of a
+  // 16-token tile: group s = kg + 4 (mu / 10); mu % 10 < 8 -> code plane j = (mu%10)/2,
+  // else the sign plane; half h = mu % 2; coordinate 32 s + 8 bb + 4 h + r' with
+  // key-side value 2^r'.
+  float w[4];
+  plane_weights(a.cb, w);
+  uint8_t *grp = a.packed + ((size_t)b * a.n_kv_heads + kvh) * packed_group_bytes(D);
+  for (int e = threadIdx.x; e < NMU * 64 * 4; e += 256) {
+    const int mu = e / 256, ln = (e / 4) % 64, rr = e % 4;
+    const int n = ln & 15, kg = ln >> 4, q = n >> 2, limb = n & 3;
+    const int s = kg + 4 * (mu / 10), m10 = mu % 10, h = m10 & 1;
+    uint32_t word = 0;
+    if (q < G) {
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const int i = 32 * s + 8 * bb + 4 * h + rr;
+        float u;
+        if (m10 < 8)
+          u = w[m10 >> 1] * s_v[q][0][i] / s_const[q][0];
+        else
+          u = 2.f * s_v[q][1][i] / s_const[q][1];
+        int X = (int)rintf(u * (1.0f / (float)(1 << rr)));
+        int dgt = 0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int lo = (int)(int8_t)(X & 0xFF);
+          if (k == limb) dgt = lo;
+          X = (X - lo) >> 8;
+        }
+        word |= (uint32_t)(uint8_t)(int8_t)dgt << (8 * bb);
+      }
+    }
+    reinterpret_cast<uint32_t *>(grp)[(size_t)mu * 256 + ln * 4 + rr] = word;
+  }
+  if (threadIdx.x < kMfmaMaxGroup * 4) {
+    const int q = threadIdx.x >> 2;
+    reinterpret_cast<float *>(grp + (size_t)NMU * 1024)[threadIdx.x] =
+        q < G ? s_const[q][threadIdx.x & 3] : 0.f;
+  }
+}
+
+// ------------------------------------------------------------------ VALU kernel
+template <int D, int GT>
+__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
   constexpr int KREC = D / 2;
   constexpr size_t KCODES = (size_t)kPage * KREC;
   constexpr size_t KSEC = KCODES + 4 * kPage;
@@ -33,7 +189,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   __shared__ float s_w[kPage][GT];          // scores, then softmax numerators
   __shared__ float s_nv[kPage];
   __shared__ float s_m[GT], s_l[GT], s_alpha[GT];
-  __shared__ int s_last;
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -80,8 +235,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const uint8_t *vsec = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
-
-    // ---- scores: one thread per token of the page
     {
       const int t = tid;
       float s1[GT], s2[GT];
@@ -119,8 +272,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();
-
-    // ---- online softmax update: wave w owns rows w, w+4, ...
     for (int qq = wave; qq < GT; qq += 4) {
       float mx = kNegInf;
 #pragma unroll
@@ -145,8 +296,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
       }
     }
     __syncthreads();
-
-    // ---- V accumulation: thread (coordinate i, query set) walks the page's tokens
     {
       const int i = tid % D, set = tid / D;
 #pragma unroll
@@ -183,83 +332,425 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     __syncthreads();
   }
 
-  // ---- partials: [B*Hkv][n_split][GT... group rows] x (m, l, acc[D])
   const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * G;
   {
     const int i = tid % D, set = tid / D;
 #pragma unroll
     for (int k = 0; k < QPS; ++k) {
       const int qq = set + NS * k;
-      if (qq < G) a.partials[(pbase + qq) * (D + 2) + 2 + i] = acc[k];
+      if (qq < G) a.partials[(pbase + qq) * (D + kPartHead) + kPartHead + i] = acc[k];
     }
     if (tid < G) {
-      a.partials[(pbase + tid) * (D + 2) + 0] = s_m[tid];
-      a.partials[(pbase + tid) * (D + 2) + 1] = s_l[tid];
+      float *pr = a.partials + (pbase + tid) * (D + kPartHead);
+      pr[0] = s_m[tid];
+      pr[1] = s_l[tid];
+      pr[2] = s_m[tid];    // V numerator is in units of exp(-m)
+      pr[3] = 0.f;
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[b * H + kvh], 1u);
-    s_last = prev == (uint32_t)(nsplit - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // ---- merge (last workgroup): one wave per query row
-  const size_t mbase = ((size_t)b * H + kvh) * nsplit * G;
-  for (int qq = wave; qq < G; qq += 4) {
-    float M = kNegInf;
-    for (int sp = lane; sp < nsplit; sp += 64) {
-      const float *pr = a.partials + (mbase + (size_t)sp * G + qq) * (D + 2);
-      if (pr[1] > 0.f) M = fmaxf(M, pr[0]);
+// ------------------------------------------------------------------ MFMA kernel
+__device__ inline float quad_sum(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+  return x;
+}
+
+// Reductions over the four lanes l, l^16, l^32, l^48 (same MFMA column).
+__device__ inline float xmax_kg(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  return fmaxf(x, __shfl_xor(x, 32, 64));
+}
+
+__device__ inline float xsum_kg(float x) {
+  x += __shfl_xor(x, 16, 64);
+  return x + __shfl_xor(x, 32, 64);
+}
+
+// int8 operand of one bit plane word: byte b of register r is bit 8b + r of w,
+// valued 2^r.
+__device__ inline v4i bit_operand(uint32_t w) {
+  v4i o;
+  o.x = (int)(w & 0x01010101u);
+  o.y = (int)(w & 0x02020202u);
+  o.z = (int)(w & 0x04040404u);
+  o.w = (int)(w & 0x08080808u);
+  return o;
+}
+
+// Each wave owns 64-token blocks (block w of every page of the split) from the
+// loads to the V accumulation, with its own online softmax; the four waves of
+// the workgroup combine once at the end into one partial per query row.
+template <int D>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+  constexpr int NGRP = D / 128;             // 32-coordinate groups per lane in scoring
+  constexpr int NMU = 10 * NGRP;            // int8 MFMAs per 16-token tile
+  constexpr int KREC = D / 2;
+  constexpr size_t KCODES = (size_t)kPage * KREC;
+  constexpr size_t KSEC = KCODES + 4 * kPage;
+  constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
+  constexpr size_t VSEC = VCODES + 2 * kPage;
+  constexpr int NB = D / 16;                // 16-coordinate V column blocks
+  constexpr bool kPrefetchV = D == 128;     // V words of the block loaded with the keys
+
+  __shared__ float s_wm[4][3][kMfmaMaxGroup];     // per wave: m, l, mU of each row
+  __shared__ float s_wacc[4][kMfmaMaxGroup][D];   // per wave V numerators
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  const int q = n >> 2, limb = n & 3;                  // scoring-output role of this lane
+  const int H = a.n_kv_heads, Hq = a.n_q_heads, g = Hq / H, G = a.plan.group;
+  const int L = a.seq_lens[b];
+
+  const uint8_t *grp = a.packed + ((size_t)b * H + kvh) * packed_group_bytes(D);
+  v4i qop[NMU];
+#pragma unroll
+  for (int mu = 0; mu < NMU; ++mu) qop[mu] = reinterpret_cast<const v4i *>(grp)[mu * 64 + lane];
+  const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * 1024)[q];
+  const float lsc1 = rc.x * (float)(1 << (8 * limb));
+  const float lsc2 = rc.y * (float)(1 << (8 * limb));
+  const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w;
+  const int vis = q < G ? (a.causal_tail ? L - (a.n_q - 1 - q / g) : L) : 0;
+  const float kappa = qjl_kappa<D>();
+  float wpl[4];
+  plane_weights(a.cb, wpl);
+  // V operand: key side is -2^-14 * beta (sign bit = key bit), query side is
+  // -U * a_j * 2^14, so every product is U * a_j * beta.
+  float cw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cw[j] = -0.5f * wpl[j] * 16384.f;
+  const int rot = (4 * kg - 12) & 31;   // brings bit 4 kg + 3 to 15 and 4 kg + 19 to 31
+  const int src = 16 * kg + 4 * (n & 3); // scoring lane that holds row n's weights
+
+  float m_run = kNegInf, l_run = 0.f, mu_run = kNegInf;
+  v4f acc[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) acc[k] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  const int n_pages_seq = min((L + kPage - 1) / kPage, a.max_pages);
+  const int pg0 = split * a.plan.pages_per_split;
+  const int pg1 = min(pg0 + a.plan.pages_per_split, n_pages_seq);
+  const int blk0 = 64 * wave;
+
+  for (int pg = pg0; pg < pg1; ++pg) {
+    const int tok0 = pg * kPage;
+    const int ntok = min(kPage, L - tok0);
+    if (blk0 >= ntok) continue;                       // wave-uniform
+    const int phys = a.block_table[(size_t)b * a.max_pages + pg];
+    const uint8_t *ksec = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
+    const uint8_t *vsec = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
+    const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vsec);
+
+    // ---- issue every load of the block first
+    uint4 kw[4][NGRP];
+    uint2 nb[4], gb[4], vb[4];
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      const uint4 *rec = reinterpret_cast<const uint4 *>(ksec + (size_t)(blk0 + 16 * tau + n) * KREC);
+#pragma unroll
+      for (int gi = 0; gi < NGRP; ++gi) kw[tau][gi] = rec[kg + 4 * gi];
+      const int tb = blk0 + 16 * tau + 4 * kg;
+      nb[tau] = *reinterpret_cast<const uint2 *>(ksec + KCODES + 2 * tb);
+      gb[tau] = *reinterpret_cast<const uint2 *>(ksec + KCODES + 2 * kPage + 2 * tb);
+      vb[tau] = *reinterpret_cast<const uint2 *>(vsec + VCODES + 2 * tb);
     }
-    M = wave_max(M);
-    float x[R];
+    uint2 vw[kPrefetchV ? NB : 1][3];
+    if constexpr (kPrefetchV) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] = 0.f;
-    float lsum = 0.f;
-    for (int sp = 0; sp < nsplit; ++sp) {
-      const float *pr = a.partials + (mbase + (size_t)sp * G + qq) * (D + 2);
-      const float l = pr[1];
-      if (l > 0.f) {
-        const float f = __expf(pr[0] - M);
-        lsum += l * f;
+      for (int k = 0; k < NB; ++k)
 #pragma unroll
-        for (int r = 0; r < R; ++r) x[r] = fmaf(f, pr[2 + lane + 64 * r], x[r]);
+        for (int j = 0; j < 3; ++j)
+          vw[k][j] = *reinterpret_cast<const uint2 *>(vrow + (size_t)(j * D + 16 * k + n) * (kPage / 32) + blk0 / 32);
+    }
+
+    // ---- scores of the block's 4 tiles of 16 tokens
+    float sc[4][4], sv[4][4];
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      v4i c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0};
+#pragma unroll
+      for (int gi = 0; gi < NGRP; ++gi) {
+        const uint4 w = kw[tau][gi];
+        const uint32_t pl[4] = {w.x, w.y, w.z, w.x ^ w.y ^ w.z};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(pl[j]), qop[10 * gi + 2 * j], c1, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(pl[j] >> 4), qop[10 * gi + 2 * j + 1], c1, 0, 0, 0);
+        }
+        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(w.w), qop[10 * gi + 8], c2, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(w.w >> 4), qop[10 * gi + 9], c2, 0, 0, 0);
+      }
+      const int tb = blk0 + 16 * tau + 4 * kg;   // output tokens tb + r
+      const uint32_t nw[2] = {nb[tau].x, nb[tau].y}, gw[2] = {gb[tau].x, gb[tau].y},
+                     vw2[2] = {vb[tau].x, vb[tau].y};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float s1 = quad_sum((float)c1[r] * lsc1) - off1;
+        const float s2 = quad_sum((float)c2[r] * lsc2) - off2;
+        const int tok = tb + r;
+        const bool valid = q < G && tok < ntok && tok0 + tok < vis;
+        const float N = f16_bits_to_f32((uint16_t)(nw[r >> 1] >> (16 * (r & 1))));
+        const float Gm = f16_bits_to_f32((uint16_t)(gw[r >> 1] >> (16 * (r & 1))));
+        const float NV = f16_bits_to_f32((uint16_t)(vw2[r >> 1] >> (16 * (r & 1))));
+        const float sco = a.scale * N * fmaf(kappa * Gm, s2, s1);
+        sc[tau][r] = valid ? sco : kNegInf;
+        sv[tau][r] = valid ? sco + __logf(NV) : kNegInf;
       }
     }
-    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+
+    // ---- online softmax of this wave (scores, and scores + ln N^V for V)
+    float mx = kNegInf, mxu = kNegInf;
 #pragma unroll
-    for (int r = 0; r < R; ++r) x[r] *= inv;
-    fwht_wave<R>(x);
-    const int t = qq / g, hh = qq % g;
-    float *o = a.out + (((size_t)b * a.n_q + t) * Hq + kvh * g + hh) * D;
+    for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
-    for (int r = 0; r < R; ++r) o[lane + 64 * r] = x[r] * rsqrt_dim<D>();
+      for (int r = 0; r < 4; ++r) {
+        mx = fmaxf(mx, sc[tau][r]);
+        mxu = fmaxf(mxu, sv[tau][r]);
+      }
+    const float m_new = fmaxf(m_run, xmax_kg(mx));
+    const float mu_new = fmaxf(mu_run, xmax_kg(mxu));
+    const float alpha = m_run == kNegInf ? 0.f : __expf(m_run - m_new);
+    const float alphaU = mu_run == kNegInf ? 0.f : __expf(mu_run - mu_new);
+    float ps = 0.f;
+    float U[4][4];
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ps += sc[tau][r] == kNegInf ? 0.f : __expf(sc[tau][r] - m_new);
+        U[tau][r] = sv[tau][r] == kNegInf ? 0.f : __expf(sv[tau][r] - mu_new);
+      }
+    l_run = l_run * alpha + xsum_kg(ps);
+    m_run = m_new;
+    mu_run = mu_new;
+
+    // rows of the V accumulator: lane (column n, kg = 0) holds rows 0..3 = query rows
+    const float al0 = __shfl(alphaU, 0, 64), al1 = __shfl(alphaU, 4, 64);
+    const float al2 = __shfl(alphaU, 8, 64), al3 = __shfl(alphaU, 12, 64);
+    if (kg == 0) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        acc[k].x *= al0;
+        acc[k].y *= al1;
+        acc[k].z *= al2;
+        acc[k].w *= al3;
+      }
+    }
+
+    // ---- V numerator: two 32-token K-blocks, rows = query rows (n < 4)
+#pragma unroll
+    for (int kap = 0; kap < 2; ++kap) {
+      v8h A[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float ua = __shfl(U[2 * kap][r], src, 64);
+        float ub = __shfl(U[2 * kap + 1][r], src, 64);
+        if (n >= kMfmaMaxGroup) ua = ub = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          A[j][2 * r] = (_Float16)(ua * cw[j]);
+          A[j][2 * r + 1] = (_Float16)(ub * cw[j]);
+        }
+      }
+      if (32 * kap + blk0 >= ntok) break;   // wave-uniform: rest of the block is past the end
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        uint32_t w0, w1, w2;
+        if constexpr (kPrefetchV) {
+          w0 = kap ? vw[k][0].y : vw[k][0].x;
+          w1 = kap ? vw[k][1].y : vw[k][1].x;
+          w2 = kap ? vw[k][2].y : vw[k][2].x;
+        } else {
+          const size_t base = (size_t)(16 * k + n) * (kPage / 32) + blk0 / 32 + kap;
+          w0 = vrow[base];
+          w1 = vrow[base + (size_t)D * (kPage / 32)];
+          w2 = vrow[base + (size_t)2 * D * (kPage / 32)];
+        }
+        const uint32_t pl[4] = {w0, w1, w2, w0 ^ w1 ^ w2};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // tokens 4 kg + r and 4 kg + 16 + r sit at bits 12 + r and 28 + r of wr
+          const uint32_t wr = __builtin_amdgcn_alignbit(pl[j], pl[j], rot);
+          v4i bi;
+          bi.x = (int)(((wr << 3) & 0x80008000u) | 0x04000400u);
+          bi.y = (int)(((wr << 2) & 0x80008000u) | 0x04000400u);
+          bi.z = (int)(((wr << 1) & 0x80008000u) | 0x04000400u);
+          bi.w = (int)((wr & 0x80008000u) | 0x04000400u);
+          acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], __builtin_bit_cast(v8h, bi), acc[k], 0, 0, 0);
+        }
+      }
+    }
   }
-  if (tid == 0) a.counters[b * H + kvh] = 0u;
+
+  // ---- combine the four waves into one partial per query row
+  if (kg == 0 && limb == 0) {
+    s_wm[wave][0][q] = m_run;
+    s_wm[wave][1][q] = l_run;
+    s_wm[wave][2][q] = mu_run;
+  }
+  if (kg == 0) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      s_wacc[wave][0][16 * k + n] = acc[k].x;
+      s_wacc[wave][1][16 * k + n] = acc[k].y;
+      s_wacc[wave][2][16 * k + n] = acc[k].z;
+      s_wacc[wave][3][16 * k + n] = acc[k].w;
+    }
+  }
+  __syncthreads();
+  const int nsplit = a.plan.n_split;
+  const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * G;
+  for (int qq = wave; qq < G; qq += 4) {
+    float M = kNegInf, MU = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_wm[w][1][qq] > 0.f) {
+        M = fmaxf(M, s_wm[w][0][qq]);
+        MU = fmaxf(MU, s_wm[w][2][qq]);
+      }
+    float lsum = 0.f, fw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bool live = s_wm[w][1][qq] > 0.f;
+      lsum += live ? s_wm[w][1][qq] * __expf(s_wm[w][0][qq] - M) : 0.f;
+      fw[w] = (live && s_wm[w][2][qq] != kNegInf) ? __expf(s_wm[w][2][qq] - MU) : 0.f;
+    }
+    float *pr = a.partials + (pbase + qq) * (D + kPartHead);
+    if (lane == 0) {
+      pr[0] = M;
+      pr[1] = lsum;
+      pr[2] = MU;
+      pr[3] = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) {
+      const int i = lane + 64 * r;
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x = fmaf(fw[w], s_wacc[w][qq][i], x);
+      pr[kPartHead + i] = x;
+    }
+  }
+}
+
+// One workgroup per (query row, KV head, sequence): four waves split the split
+// partials, then combine in LDS, apply the inverse rotation and write the row.
+template <int D>
+__global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
+  constexpr int R = D / 64;
+  __shared__ float s_stat[4][3];
+  __shared__ float s_x[4][D];
+  __shared__ float s_f[4][64];
+  const int qq = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int H = a.n_kv_heads, Hq = a.n_q_heads, g = Hq / H, G = a.plan.group;
+  const int nsplit = a.plan.n_split;
+  const size_t stride = (size_t)G * (D + kPartHead);
+  const float *part = a.partials + (((size_t)b * H + kvh) * nsplit * G + qq) * (D + kPartHead);
+  // global maxima over all splits (every wave computes them)
+  float M = kNegInf, MU = kNegInf;
+  for (int sp = lane; sp < nsplit; sp += 64) {
+    const float *pr = part + sp * stride;
+    if (pr[1] > 0.f) {
+      M = fmaxf(M, pr[0]);
+      MU = fmaxf(MU, pr[2]);
+    }
+  }
+  M = wave_max(M);
+  MU = wave_max(MU);
+  float x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = 0.f;
+  float lpart = 0.f;
+  // wave w takes chunks of 64 splits w, w + 4, ...
+  for (int c0 = 64 * wave; c0 < nsplit; c0 += 256) {
+    const int sp = c0 + lane;
+    float f = 0.f;
+    if (sp < nsplit) {
+      const float *pr = part + sp * stride;
+      const float l = pr[1];
+      if (l > 0.f) {
+        lpart += l * __expf(pr[0] - M);
+        if (MU != kNegInf && pr[2] != kNegInf) f = __expf(pr[2] - MU);
+      }
+    }
+    s_f[wave][lane] = f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    const int cnt = min(64, nsplit - c0);
+#pragma unroll 8
+    for (int j = 0; j < cnt; ++j) {
+      const float fj = s_f[wave][j];
+      const float *row = part + (size_t)(c0 + j) * stride + kPartHead;
+#pragma unroll
+      for (int r = 0; r < R; ++r) x[r] = fmaf(fj, row[lane + 64 * r], x[r]);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+  }
+  const float lw = wave_sum(lpart);
+#pragma unroll
+  for (int r = 0; r < R; ++r) s_x[wave][lane + 64 * r] = x[r];
+  if (lane == 0) s_stat[wave][0] = lw;
+  __syncthreads();
+  if (wave != 0) return;
+  const float lsum = s_stat[0][0] + s_stat[1][0] + s_stat[2][0] + s_stat[3][0];
+  const float inv = (lsum > 0.f && MU != kNegInf) ? __expf(MU - M) / lsum : 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int i = lane + 64 * r;
+    x[r] = (s_x[0][i] + s_x[1][i] + s_x[2][i] + s_x[3][i]) * inv;
+  }
+  fwht_wave<R>(x);
+  const int t = qq / g, hh = qq % g;
+  float *o = a.out + (((size_t)b * a.n_q + t) * Hq + kvh * g + hh) * D;
+#pragma unroll
+  for (int r = 0; r < R; ++r) o[lane + 64 * r] = x[r] * rsqrt_dim<D>();
 }
 
 template <int D>
 hipError_t launch_dim(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch);
   const int G = a.plan.group;
-  if (G <= 1)
-    hipLaunchKernelGGL((decode_kernel<D, 1>), grid, dim3(256), 0, s, a);
-  else if (G <= 2)
-    hipLaunchKernelGGL((decode_kernel<D, 2>), grid, dim3(256), 0, s, a);
-  else if (G <= 4)
-    hipLaunchKernelGGL((decode_kernel<D, 4>), grid, dim3(256), 0, s, a);
+  if (a.plan.mfma)
+    hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
   else if (G <= 8)
-    hipLaunchKernelGGL((decode_kernel<D, 8>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_valu_kernel<D, 8>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, 16>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((decode_valu_kernel<D, 16>), grid, dim3(256), 0, s, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.plan.group, a.n_kv_heads, a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads) {
+  size_t bytes = prep_float_bytes(d, batch, n_q, n_q_heads);
+  if (n_q_heads / n_kv_heads * n_q <= kMfmaMaxGroup)
+    bytes += ((size_t)batch * n_kv_heads * packed_group_bytes(d) + 255) / 256 * 256;
+  return bytes;
+}
+
+hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
+  const dim3 grid(a.n_kv_heads, a.batch);
+  if (d == 128) {
+    if (a.dtype == TQ_F32)
+      hipLaunchKernelGGL((prepare_kernel<128, TQ_F32>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prepare_kernel<128, TQ_BF16>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.dtype == TQ_F32)
+      hipLaunchKernelGGL((prepare_kernel<256, TQ_F32>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((prepare_kernel<256, TQ_BF16>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s) {
   return d == 128 ? launch_dim<128>(a, s) : launch_dim<256>(a, s);

@@ -1,4 +1,4 @@
-// Encode (K and V), dequantise and query-preparation kernels.
+// Encode (K and V) and dequantise kernels.
 //
 // Method: AI Heartland news "Apple Silicon向けSwiftLM、TurboQuant KVキャッシュ圧縮と
 // SSD Expert Streamingを実装", section 技術的な詳細, "K-Cache圧縮" flow steps 1-5 and
@@ -93,6 +93,7 @@ __global__ __launch_bounds__(256) void encode_k_kernel(EncodeArgs a) {
 #pragma unroll
     for (int k = 0; k < R; ++k) z[v][k] = 0.f;
   const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
+#pragma unroll 8
   for (int i4 = 0; i4 < D / 4; ++i4) {
     float4 s[R];
 #pragma unroll
@@ -236,47 +237,6 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
   for (int r = 0; r < R; ++r) o[lane + 64 * r] = v[r] * scale;
 }
 
-template <int D, int DT>
-__global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
-  constexpr int R = D / 64;
-  __shared__ float qbuf[kWaves][D];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long row = (long)blockIdx.x * kWaves + wave;
-  const bool live = row < a.rows;
-  float v[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) v[r] = live ? load_elem<DT>(a.q, (size_t)row * D + lane + 64 * r) : 0.f;
-  fwht_wave<R>(v);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    v[r] *= rsqrt_dim<D>();
-    qbuf[wave][lane + 64 * r] = v[r];
-  }
-  __syncthreads();
-  if (!live) return;
-  float *dst = a.prep + (size_t)row * 2 * D;
-#pragma unroll
-  for (int r = 0; r < R; ++r) dst[lane + 64 * r] = v[r];
-  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
-  const float4 *q4 = reinterpret_cast<const float4 *>(qbuf[wave]);
-  float p[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) p[r] = 0.f;
-  for (int i4 = 0; i4 < D / 4; ++i4) {
-    const float4 qv = q4[i4];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const float4 s = S4[(size_t)(lane + 64 * r) * (D / 4) + i4];
-      p[r] = fmaf(s.x, qv.x, p[r]);
-      p[r] = fmaf(s.y, qv.y, p[r]);
-      p[r] = fmaf(s.z, qv.z, p[r]);
-      p[r] = fmaf(s.w, qv.w, p[r]);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < R; ++r) dst[D + lane + 64 * r] = p[r];
-}
-
 template <typename F>
 hipError_t by_dim_dtype(int d, int dtype, F &&f) {
   if (d == 128) {
@@ -316,14 +276,6 @@ hipError_t launch_dequant(const DequantArgs &a, int d, int which, hipStream_t s)
   else
     hipLaunchKernelGGL((dequant_kernel<256>), grid, dim3(256), 0, s, a, which);
   return hipGetLastError();
-}
-
-hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
-  const dim3 grid((unsigned)((a.rows + kWaves - 1) / kWaves));
-  return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
-    hipLaunchKernelGGL((prepare_kernel<D.value, DT.value>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-  });
 }
 
 }  // namespace tq

@@ -41,28 +41,48 @@ struct DequantArgs {
   Codebook cb;
 };
 
+// Query preparation for one decode call: rotation, QJL projection and, for
+// the MFMA decode path, the packed int8 scoring operand of each (sequence, KV head).
 struct PrepArgs {
-  const void *q;          // [rows][d]
+  const void *q;          // [batch][n_q][Hq][d]
   int dtype;
-  int rows;
+  int batch, n_q, n_q_heads, n_kv_heads;
   const float *qjl;
-  float *prep;            // [rows][2][d]
+  float *prep;            // [rows][2][d]: Pi q, then S Pi q
+  uint8_t *packed;        // per (sequence, KV head): int8 operand + row constants (or null)
+  Codebook cb;
 };
+
+// Bytes of the packed scoring operand of one (sequence, KV head): per 16-token
+// tile a wave issues mfma_per_tile int8 MFMAs whose query operand (16 B per
+// lane) is stored lane-major, then 4 rows x {delta1, delta2, sum q~, sum p}.
+__host__ __device__ inline int mfma_per_tile(int d) { return 10 * (d / 128); }
+__host__ __device__ inline size_t packed_group_bytes(int d) { return (size_t)mfma_per_tile(d) * 64 * 16 + 64; }
+constexpr int kMfmaMaxGroup = 4;   // query rows per (sequence, KV head) on the MFMA path
 
 // Split-K plan of one decode call.
 struct DecodePlan {
   int group;              // query rows per (sequence, KV head) = Hq/Hkv * n_q
   int pages_per_split;
   int n_split;
-  size_t counter_bytes;   // [B*Hkv] u32, padded
-  size_t partial_bytes;   // [B*Hkv][n_split][group] x (d + 2) float32
-  size_t prep_bytes;      // [B*n_q*Hq][2][d] float32 (tq_attn_decode only)
+  size_t counter_bytes;   // reserved (0)
+  size_t partial_bytes;   // [B*Hkv][n_split][group] x (d + 4) float32
+  size_t prep_bytes;      // query region (tq_attn_decode only)
+  bool mfma;              // int8/f16 MFMA kernel (group <= kMfmaMaxGroup) or the VALU kernel
 };
+
+// Query region of a decode call: [rows][2][d] float32, then (MFMA path) the
+// packed operands of the B*Hkv groups.
+size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads);
+inline size_t prep_float_bytes(int d, int batch, int n_q, int n_q_heads) {
+  return ((size_t)batch * n_q * n_q_heads * 2 * d * sizeof(float) + 255) / 256 * 256;
+}
 
 struct DecodeArgs {
   const uint8_t *k_pool;
   const uint8_t *v_pool;
   const float *prep;      // [B][n_q][Hq][2][d]
+  const uint8_t *packed;  // packed scoring operands (MFMA path)
   const int32_t *block_table;
   int max_pages;
   const int32_t *seq_lens;

@@ -58,7 +58,7 @@ def lib():
     L.tq_build_codebook.argtypes = [i32, i32, C.c_uint64, vp, vp, vp]
     L.tq_encode_k.argtypes = [vp, vp, i32, vp, i32, vp]
     L.tq_encode_v.argtypes = [vp, vp, i32, vp, i32, vp]
-    L.tq_query_prepare.argtypes = [vp, vp, i32, i32, vp, vp]
+    L.tq_query_prepare.argtypes = [vp, vp, i32, i32, i32, i32, vp, C.POINTER(sz), vp]
     L.tq_attn_decode.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
                                  C.POINTER(sz), vp]
     L.tq_attn_decode_prepared.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
@@ -162,16 +162,27 @@ def tq_encode_v(cache: Cache, v, slots, stream=None) -> None:
 
 
 def tq_query_prepare(cache: Cache, q, prep=None, stream=None):
-    """q: [..., d] -> prep [..., 2, d] float32 (rotated query, then S times it)."""
+    """q: [B][n_q][Hq][d] -> the prepared-query buffer (uint8 device tensor) whose
+    first B*n_q*Hq*2*d float32 values are (Pi q, S Pi q) per row."""
     import torch
-    d = cache.head_dim
-    rows = q.numel() // d
+    B, n_q, Hq, d = q.shape
+    size = C.c_size_t(0)
+    L = lib()
+    _check(L.tq_query_prepare(cache.ref, q.data_ptr(), _dtype_code(q), B, n_q, Hq, None,
+                              C.byref(size), None), "tq_query_prepare (size query)")
     if prep is None:
-        prep = torch.empty(*q.shape[:-1], 2, d, dtype=torch.float32, device=q.device)
-    st = lib().tq_query_prepare(cache.ref, q.data_ptr(), _dtype_code(q), rows, prep.data_ptr(),
-                                _stream(stream))
-    _check(st, "tq_query_prepare")
+        prep = torch.empty(size.value, dtype=torch.uint8, device=q.device)
+    size = C.c_size_t(prep.numel())
+    _check(L.tq_query_prepare(cache.ref, q.data_ptr(), _dtype_code(q), B, n_q, Hq, prep.data_ptr(),
+                              C.byref(size), _stream(stream)), "tq_query_prepare")
     return prep
+
+
+def prepared_rows(prep, shape):
+    """View of the (Pi q, S Pi q) rows of a prepared-query buffer: [..., 2, d] float32."""
+    B, n_q, Hq, d = shape
+    n = B * n_q * Hq * 2 * d
+    return prep[: 4 * n].view(dtype=__import__("torch").float32).view(B, n_q, Hq, 2, d)
 
 
 def _decode_ws(cache, fn, args, workspace):
@@ -201,11 +212,12 @@ def tq_attn_decode(cache: Cache, q, block_table, seq_lens, causal_tail: int = 0,
     return out
 
 
-def tq_attn_decode_prepared(cache: Cache, prep, block_table, seq_lens, causal_tail: int = 0,
-                            scale=None, out=None, workspace=None, stream=None):
-    """prep: [B][n_q][Hq][2][d] float32 from tq_query_prepare."""
+def tq_attn_decode_prepared(cache: Cache, prep, q_shape, block_table, seq_lens,
+                            causal_tail: int = 0, scale=None, out=None, workspace=None,
+                            stream=None):
+    """prep: buffer from tq_query_prepare for queries of shape q_shape = (B, n_q, Hq, d)."""
     import torch
-    B, n_q, Hq, _, d = prep.shape
+    B, n_q, Hq, d = q_shape
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=prep.device)

@@ -93,9 +93,24 @@ def test_dequant_and_prepare_validation(L):
     assert L.tq_dequant(r, 0, 3, FAKE, 4, FAKE, None) == tq.TQ_EINVAL
     assert L.tq_dequant(r, 1, 0, FAKE, 0, FAKE, None) == tq.TQ_OK
     assert L.tq_dequant(r, 1, 0, FAKE, 4, FAKE + 8, None) == tq.TQ_EALIGN
-    assert L.tq_query_prepare(r, FAKE, 0, 0, FAKE, None) == tq.TQ_OK
-    assert L.tq_query_prepare(r, FAKE, 5, 3, FAKE, None) == tq.TQ_EUNSUPPORTED
-    assert L.tq_query_prepare(r, None, 0, 3, FAKE, None) == tq.TQ_EINVAL
+    sz = C.c_size_t(0)
+    assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, None, C.byref(sz), None) == tq.TQ_OK
+    need = sz.value
+    # rows of (Pi q, S Pi q) plus the packed operands of the 2 x 2 (sequence, KV head) groups
+    assert need >= 2 * 8 * 2 * 128 * 4 + 4 * (10 * 1024 + 64)
+    sz = C.c_size_t(need - 1)
+    assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE, C.byref(sz), None) == tq.TQ_EWORKSPACE
+    assert sz.value == need
+    sz = C.c_size_t(need)
+    assert L.tq_query_prepare(r, FAKE, 5, 2, 1, 8, FAKE, C.byref(sz), None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_query_prepare(r, None, 0, 2, 1, 8, FAKE, C.byref(sz), None) == tq.TQ_EINVAL
+    assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 7, FAKE, C.byref(sz), None) == tq.TQ_EINVAL
+    assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE + 16, C.byref(sz), None) == tq.TQ_EALIGN
+    assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE, None, None) == tq.TQ_EINVAL
+    # 16 rows per KV head: no packed operand (VALU decode path)
+    sz16 = C.c_size_t(0)
+    assert L.tq_query_prepare(r, FAKE, 0, 2, 2, 16, None, C.byref(sz16), None) == tq.TQ_OK
+    assert sz16.value == 2 * 2 * 16 * 2 * 128 * 4
 
 
 def _decode(L, dsc, ws=None, size=None, B=2, nq=1, Hq=8, maxp=16, causal=0, q=FAKE):

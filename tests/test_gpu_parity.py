@@ -142,6 +142,9 @@ DEC_CASES = [
     (256, 8, 32, 4, [600, 300], "bf16", "outlier", 0, 5),             # d=256, 16 rows per KV head
     (256, 8, 32, 4, [600, 3], "bf16", "outlier", 1, 6),               # causal tail
     (128, 2, 6, 1, [513], "bf16", "normal", 0, 7),                    # g=3 (padded group)
+    (256, 4, 16, 1, [700, 256], "bf16", "outlier", 0, 8),             # d=256, MFMA path
+    (128, 4, 8, 2, [400, 2, 257], "bf16", "outlier", 1, 9),           # n_q=2 causal, MFMA path
+    (128, 2, 16, 1, [300], "bf16", "normal", 0, 10),                  # 8 rows: VALU path
 ]
 
 
@@ -169,19 +172,20 @@ def test_decode_parity(tq, case):
     assert torch.equal(out, out2)
     # the prepared-query path gives the same bits
     prep = tq.tq_query_prepare(cache, qt)
-    out3 = tq.tq_attn_decode_prepared(cache, prep, bt, sl, causal_tail=causal)
+    out3 = tq.tq_attn_decode_prepared(cache, prep, tuple(qt.shape), bt, sl, causal_tail=causal)
     torch.cuda.synchronize()
     assert torch.equal(out, out3)
 
 
-def test_query_prepare_parity(tq):
-    d = 256
-    cache = tq.Cache(d, 1, 1)
-    q = np.random.default_rng(3).standard_normal((37, d)).astype(np.float32)
-    prep = tq.tq_query_prepare(cache, torch.from_numpy(q).cuda()).cpu().numpy()
+@pytest.mark.parametrize("d", [128, 256])
+def test_query_prepare_parity(tq, d):
+    cache = tq.Cache(d, 2, 1)
+    q = np.random.default_rng(3).standard_normal((3, 2, 4, d)).astype(np.float32)
+    prep = tq.tq_query_prepare(cache, torch.from_numpy(q).cuda())
+    rows = tq.prepared_rows(prep, q.shape).cpu().numpy()
     qt, p = O.rotate_query(q.astype(np.float64), cache.qjl_host)
-    assert np.max(np.abs(prep[:, 0] - qt)) < 1e-5 * np.max(np.abs(qt))
-    assert np.max(np.abs(prep[:, 1] - p)) < 1e-5 * np.max(np.abs(p))
+    assert np.max(np.abs(rows[..., 0, :] - qt)) < 1e-5 * np.max(np.abs(qt))
+    assert np.max(np.abs(rows[..., 1, :] - p)) < 1e-5 * np.max(np.abs(p))
 
 
 @pytest.mark.parametrize("d", [128, 256])
