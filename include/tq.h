@@ -38,9 +38,11 @@
  *     bit e of a word belongs to coordinate 32*s + e; sign bit = [ (S r)_l >= 0 ];
  *     N[t] (fp16, ||x||) at byte P*d/2 + 2t; G[t] (fp16, ||r||) at P*d/2 + 2P + 2t.
  *   V section, v_page_bytes = 3*d*P/8 + 2*P:
- *     for plane j = 0..2 and coordinate i a P-bit row at byte (j*d + i)*P/8;
- *     bit t of the row (bit t%32 of u32 word t/32) is bit j of token t's code of
- *     coordinate i; N[t] (fp16) at byte 3*d*P/8 + 2t.
+ *     for plane j = 0..2 and coordinate i a row of P/32 u32 words at byte
+ *     (j*d + i)*P/8; word w holds tokens 32w..32w+31, token 32w + u at bit
+ *     8*(u%4) + u/4 (bit j of that token's code of coordinate i), so one AND
+ *     with 0x01010101 << k gathers the bits of four tokens into four bytes;
+ *     N[t] (fp16) at byte 3*d*P/8 + 2t.
  *   At d = 128 that is 544 bits per K vector (4.25 bits/dim) and 400 bits per V
  *   vector (3.125 bits/dim); at d = 256, 4.125 and 3.0625 bits/dim.
  */

@@ -90,12 +90,14 @@ namespace tq {
 DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages) {
   DecodePlan p;
   p.group = n_q_heads / n_kv_heads * n_q;
-  p.mfma = p.group <= kMfmaMaxGroup;
-  // Aim for about 2048 workgroups (8 per CU); each split keeps whole pages so a
-  // workgroup streams at least one 256-token page per KV head.
+  p.mfma = mfma_path(d, p.group);
+  // About 512 workgroups (two per CU, one occupancy round) so that every
+  // workgroup streams several pages with its loads overlapped; whole pages per
+  // split; at most 256 pages (65536 tokens) per split.
   long work = (long)batch * n_kv_heads * max_pages;
-  int pps = (int)(work / 2048);
+  int pps = (int)((work + 511) / 512);
   if (pps < 1) pps = 1;
+  if (pps > 256) pps = 256;
   p.pages_per_split = pps;
   p.n_split = (max_pages + pps - 1) / pps;
   p.counter_bytes = 0;
@@ -211,7 +213,7 @@ static hipError_t run_prepare(const tq_cache *c, const void *q, int32_t dtype, i
   a.n_kv_heads = c->n_kv_heads;
   a.qjl = c->qjl;
   a.prep = (float *)prep;
-  const bool mfma = n_q_heads / c->n_kv_heads * n_q <= tq::kMfmaMaxGroup;
+  const bool mfma = tq::mfma_path(c->head_dim, n_q_heads / c->n_kv_heads * n_q);
   a.packed = mfma ? prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads) : nullptr;
   a.cb = codebook_of(c);
   return tq::launch_prepare(a, c->head_dim, s);

@@ -59,6 +59,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   constexpr int NMU = 10 * (D / 128);
   __shared__ float s_v[kMfmaMaxGroup][2][D];
   __shared__ float s_const[kMfmaMaxGroup][4];
+  __shared__ float s_inv[kMfmaMaxGroup][2];
   __shared__ float s_q[4][D];
   const int kvh = blockIdx.x, b = blockIdx.y;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -126,6 +127,8 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
         s_const[qq][1] = mp > 0.f ? 2.f * mp * 0x1p-30f : 1.f;
         s_const[qq][2] = sq;
         s_const[qq][3] = sp;
+        s_inv[qq][0] = 1.0f / s_const[qq][0];
+        s_inv[qq][1] = 1.0f / s_const[qq][1];
       }
     }
   }
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   // Operand byte (mu, lane = 16 kg + n, 4 r' + bb): row n = 4 q + limb, MFMA mu of a
   // 16-token tile: group s = kg + 4 (mu / 10); mu % 10 < 8 -> code plane j = (mu%10)/2,
   // else the sign plane; half h = mu % 2; coordinate 32 s + 8 bb + 4 h + r' with
-  // key-side value 2^r'.
+  // key-side byte value 2^(4h + r') (-128 for bit 7).
   float w[4];
   plane_weights(a.cb, w);
   uint8_t *grp = a.packed + ((size_t)b * a.n_kv_heads + kvh) * packed_group_bytes(D);
@@ -143,28 +146,23 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
     const int mu = e / 256, ln = (e / 4) % 64, rr = e % 4;
     const int n = ln & 15, kg = ln >> 4, q = n >> 2, limb = n & 3;
     const int s = kg + 4 * (mu / 10), m10 = mu % 10, h = m10 & 1;
-    uint32_t word = 0;
+    uint32_t word = 0x80808080u;   // all-zero limbs
     if (q < G) {
+      // value / (delta * 2^rr) as an integer X; limb bytes of X + 0x80808080
+      // are the digits of X in base 256 offset by 128 (X = sum (byte_l - 128) 256^l)
+      const int kb = 4 * h + rr;   // key byte value 2^kb, the top bit reads as -128
+      const float vkey = kb == 7 ? -128.f : (float)(1 << kb);
+      const float f = (m10 < 8 ? w[m10 >> 1] * s_inv[q][0] : 2.f * s_inv[q][1]) / vkey;
+      const float *src = s_v[q][m10 < 8 ? 0 : 1];
+      word = 0;
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
-        const int i = 32 * s + 8 * bb + 4 * h + rr;
-        float u;
-        if (m10 < 8)
-          u = w[m10 >> 1] * s_v[q][0][i] / s_const[q][0];
-        else
-          u = 2.f * s_v[q][1][i] / s_const[q][1];
-        int X = (int)rintf(u * (1.0f / (float)(1 << rr)));
-        int dgt = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int lo = (int)(int8_t)(X & 0xFF);
-          if (k == limb) dgt = lo;
-          X = (X - lo) >> 8;
-        }
-        word |= (uint32_t)(uint8_t)(int8_t)dgt << (8 * bb);
+        const int X = (int)rintf(src[32 * s + 8 * bb + 4 * h + rr] * f);
+        const uint32_t byte = (((uint32_t)X + 0x80808080u) >> (8 * limb)) & 0xFFu;
+        word |= byte << (8 * bb);
       }
     }
-    reinterpret_cast<uint32_t *>(grp)[(size_t)mu * 256 + ln * 4 + rr] = word;
+    reinterpret_cast<uint32_t *>(grp)[(size_t)mu * 256 + ln * 4 + rr] = word ^ 0x80808080u;
   }
   if (threadIdx.x < kMfmaMaxGroup * 4) {
     const int q = threadIdx.x >> 2;
@@ -319,7 +317,8 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll 4
         for (int e = 0; e < 32; ++e) {
           const int t = tb + e;
-          const int idx = ((w0 >> e) & 1) | (((w1 >> e) & 1) << 1) | (((w2 >> e) & 1) << 2);
+          const int pos = 8 * (e & 3) + (e >> 2);   // storage bit of token e of the word
+          const int idx = ((w0 >> pos) & 1) | (((w1 >> pos) & 1) << 1) | (((w2 >> pos) & 1) << 2);
           const float val = s_nv[t] * level_of(a.cb, idx);
 #pragma unroll
           for (int k = 0; k < QPS; ++k) {
@@ -351,253 +350,266 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------ MFMA kernel
-__device__ inline float quad_sum(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
-  return x;
-}
+__device__ inline int dpp_swap1(int x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); }
+__device__ inline int dpp_swap2(int x) { return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); }
+__device__ inline float dpp_swap1f(float x) { return __builtin_bit_cast(float, dpp_swap1(__builtin_bit_cast(int, x))); }
+__device__ inline float dpp_swap2f(float x) { return __builtin_bit_cast(float, dpp_swap2(__builtin_bit_cast(int, x))); }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 (same MFMA column).
-__device__ inline float xmax_kg(float x) {
+// Reductions over the 16 lanes of one query row: the quad (lanes 4q..4q+3 of a
+// 16-lane row) and the four rows l, l^16, l^32, l^48.
+__device__ inline float rowmax16(float x) {
+  x = fmaxf(x, dpp_swap1f(x));
+  x = fmaxf(x, dpp_swap2f(x));
   x = fmaxf(x, __shfl_xor(x, 16, 64));
   return fmaxf(x, __shfl_xor(x, 32, 64));
 }
-
-__device__ inline float xsum_kg(float x) {
+__device__ inline float rowsum16(float x) {
+  x += dpp_swap1f(x);
+  x += dpp_swap2f(x);
   x += __shfl_xor(x, 16, 64);
   return x + __shfl_xor(x, 32, 64);
 }
 
-// int8 operand of one bit plane word: byte b of register r is bit 8b + r of w,
-// valued 2^r.
-__device__ inline v4i bit_operand(uint32_t w) {
-  v4i o;
-  o.x = (int)(w & 0x01010101u);
-  o.y = (int)(w & 0x02020202u);
-  o.z = (int)(w & 0x04040404u);
-  o.w = (int)(w & 0x08080808u);
-  return o;
+// 4x4 byte transpose inside a quad: lane L holds the four bytes of token L; on
+// return lane L holds byte L of tokens 0..3.
+__device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
+  const uint32_t p1 = (uint32_t)dpp_swap1((int)d);
+  const uint32_t e = __builtin_amdgcn_perm(p1, d, (lam & 1) ? 0x03070105u : 0x06020400u);
+  const uint32_t p2 = (uint32_t)dpp_swap2((int)e);
+  return __builtin_amdgcn_perm(p2, e, (lam & 2) ? 0x03020706u : 0x05040100u);
 }
 
 // Each wave owns 64-token blocks (block w of every page of the split) from the
 // loads to the V accumulation, with its own online softmax; the four waves of
 // the workgroup combine once at the end into one partial per query row.
+//
+// Scores: int8 MFMA over the key bit planes (A: key bytes, 16 tokens x 64 slots;
+// B: query limbs, 16 rows = 4 query rows x 4 limbs). The limb partials of a
+// token sit in the four lanes of a quad; a transpose-reduce leaves lane L of the
+// quad with the full score of token L, so every later per-score step runs once.
+// V: int8 MFMA with the softmax weight (times each plane weight) as 4 int8 limbs
+// on the 16 rows and the V bit planes (storage order puts the four tokens of a
+// lane in the four bytes of one AND) on the columns; per 64-token block the
+// int32 sums are folded into a float accumulator.
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NGRP = D / 128;             // 32-coordinate groups per lane in scoring
-  constexpr int NMU = 10 * NGRP;            // int8 MFMAs per 16-token tile
+  static_assert(D == 128, "MFMA decode path is built for head_dim 128");
+  constexpr int NMU = 10;                   // int8 MFMAs per 16-token scoring tile
   constexpr int KREC = D / 2;
   constexpr size_t KCODES = (size_t)kPage * KREC;
   constexpr size_t KSEC = KCODES + 4 * kPage;
   constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
   constexpr size_t VSEC = VCODES + 2 * kPage;
   constexpr int NB = D / 16;                // 16-coordinate V column blocks
-  constexpr bool kPrefetchV = D == 128;     // V words of the block loaded with the keys
 
-  __shared__ float s_wm[4][3][kMfmaMaxGroup];     // per wave: m, l, mU of each row
+  __shared__ float s_wm[4][4][kMfmaMaxGroup];     // per wave: m, l, mU, sum U of each row
   __shared__ float s_wacc[4][kMfmaMaxGroup][D];   // per wave V numerators
+  __shared__ v4i s_qop[10 * 64];                   // packed query operand, [mfma][lane]
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
-  const int q = n >> 2, limb = n & 3;                  // scoring-output role of this lane
+  const int q = n >> 2, lam = n & 3;   // query row of this lane's 16-lane row slot, limb / token
   const int H = a.n_kv_heads, Hq = a.n_q_heads, g = Hq / H, G = a.plan.group;
   const int L = a.seq_lens[b];
 
   const uint8_t *grp = a.packed + ((size_t)b * H + kvh) * packed_group_bytes(D);
-  v4i qop[NMU];
-#pragma unroll
-  for (int mu = 0; mu < NMU; ++mu) qop[mu] = reinterpret_cast<const v4i *>(grp)[mu * 64 + lane];
+  // the packed query operand is shared by the four waves: keep it in LDS
+  for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
   const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * 1024)[q];
-  const float lsc1 = rc.x * (float)(1 << (8 * limb));
-  const float lsc2 = rc.y * (float)(1 << (8 * limb));
-  const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w;
+  const float lsc1 = rc.x * (float)(1 << (8 * lam));
+  const float lsc2 = rc.y * (float)(1 << (8 * lam)) * qjl_kappa<D>();
+  const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w * qjl_kappa<D>();
   const int vis = q < G ? (a.causal_tail ? L - (a.n_q - 1 - q / g) : L) : 0;
-  const float kappa = qjl_kappa<D>();
   float wpl[4];
   plane_weights(a.cb, wpl);
-  // V operand: key side is -2^-14 * beta (sign bit = key bit), query side is
-  // -U * a_j * 2^14, so every product is U * a_j * beta.
-  float cw[4];
+  const float wmax = fmaxf(fmaxf(fabsf(wpl[0]), fabsf(wpl[1])), fmaxf(fabsf(wpl[2]), fabsf(wpl[3])));
+  // weight limbs: X = U * (w_j / wmax) * 2^30 / v, v = value of the V key byte
+  // (2^(4 (tau&1) + kg), or -128 for the top bit)
+  float cx[4][2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cw[j] = -0.5f * wpl[j] * 16384.f;
-  const int rot = (4 * kg - 12) & 31;   // brings bit 4 kg + 3 to 15 and 4 kg + 19 to 31
-  const int src = 16 * kg + 4 * (n & 3); // scoring lane that holds row n's weights
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int k = 4 * hh + kg;
+      const float v = k == 7 ? -128.f : (float)(1 << k);
+      cx[j][hh] = wpl[j] / wmax * 1073741824.f / v;
+    }
+  const float delta_u = wmax * 0x1p-30f;
+  const uint32_t vmask0 = 0x01010101u << kg, vmask1 = 0x10101010u << kg;
+  const float kNaN = __builtin_nanf("");
+  (void)kNaN;
 
-  float m_run = kNegInf, l_run = 0.f, mu_run = kNegInf;
-  v4f acc[NB];
+  float m_run = kNegInf, mu_run = kNegInf, l_lane = 0.f, us_lane = 0.f;
+  float facc[NB];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) acc[k] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NB; ++k) facc[k] = 0.f;
 
   const int n_pages_seq = min((L + kPage - 1) / kPage, a.max_pages);
   const int pg0 = split * a.plan.pages_per_split;
-  const int pg1 = min(pg0 + a.plan.pages_per_split, n_pages_seq);
+  int pg1 = min(pg0 + a.plan.pages_per_split, n_pages_seq);
   const int blk0 = 64 * wave;
+  // pages whose block of this wave holds no token are skipped (only the last can)
+  if (pg1 > pg0 && blk0 >= L - (pg1 - 1) * kPage) --pg1;
+  __syncthreads();   // s_qop
+
+  // key words of the next block are loaded while the current block computes
+  uint4 kw_n[4];
+  uint2 gb_n[4];
+  uint16_t nh_n[4], vh_n[4];
+  auto load_keys = [&](int pg) {
+    const int phys = a.block_table[(size_t)b * a.max_pages + pg];
+    const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
+    const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      kw_n[tau] = reinterpret_cast<const uint4 *>(ks + (size_t)(blk0 + 16 * tau + n) * KREC)[kg];
+      const int tb = blk0 + 16 * tau + 4 * kg;
+      gb_n[tau] = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * kPage + 2 * tb);
+      nh_n[tau] = reinterpret_cast<const uint16_t *>(ks + KCODES)[tb + lam];
+      vh_n[tau] = reinterpret_cast<const uint16_t *>(vs + VCODES)[tb + lam];
+    }
+  };
+  if (pg0 < pg1) load_keys(pg0);
 
   for (int pg = pg0; pg < pg1; ++pg) {
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
-    if (blk0 >= ntok) continue;                       // wave-uniform
     const int phys = a.block_table[(size_t)b * a.max_pages + pg];
-    const uint8_t *ksec = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
     const uint8_t *vsec = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
     const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vsec);
-
-    // ---- issue every load of the block first
-    uint4 kw[4][NGRP];
-    uint2 nb[4], gb[4], vb[4];
+    uint4 kw[4];
+    uint2 gb[4];
+    uint16_t nh[4], vh[4];
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      const uint4 *rec = reinterpret_cast<const uint4 *>(ksec + (size_t)(blk0 + 16 * tau + n) * KREC);
-#pragma unroll
-      for (int gi = 0; gi < NGRP; ++gi) kw[tau][gi] = rec[kg + 4 * gi];
-      const int tb = blk0 + 16 * tau + 4 * kg;
-      nb[tau] = *reinterpret_cast<const uint2 *>(ksec + KCODES + 2 * tb);
-      gb[tau] = *reinterpret_cast<const uint2 *>(ksec + KCODES + 2 * kPage + 2 * tb);
-      vb[tau] = *reinterpret_cast<const uint2 *>(vsec + VCODES + 2 * tb);
+      kw[tau] = kw_n[tau];
+      gb[tau] = gb_n[tau];
+      nh[tau] = nh_n[tau];
+      vh[tau] = vh_n[tau];
     }
-    uint2 vw[kPrefetchV ? NB : 1][3];
-    if constexpr (kPrefetchV) {
+    uint2 vw[NB][3];
 #pragma unroll
-      for (int k = 0; k < NB; ++k)
+    for (int k = 0; k < NB; ++k)
 #pragma unroll
-        for (int j = 0; j < 3; ++j)
-          vw[k][j] = *reinterpret_cast<const uint2 *>(vrow + (size_t)(j * D + 16 * k + n) * (kPage / 32) + blk0 / 32);
-    }
+      for (int j = 0; j < 3; ++j)
+        vw[k][j] = *reinterpret_cast<const uint2 *>(vrow + (size_t)(j * D + 16 * k + n) * (kPage / 32) + blk0 / 32);
+    if (pg + 1 < pg1) load_keys(pg + 1);
 
-    // ---- scores of the block's 4 tiles of 16 tokens
-    float sc[4][4], sv[4][4];
+    // ---- scores: lane (n, kg) ends with the score of token blk0 + 16 tau + 4 kg + lam
+    float sc[4], sv[4];
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       v4i c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0};
+      const uint4 w = kw[tau];
+      const uint32_t pl[4] = {w.x, w.y, w.z, w.x ^ w.y ^ w.z};
 #pragma unroll
-      for (int gi = 0; gi < NGRP; ++gi) {
-        const uint4 w = kw[tau][gi];
-        const uint32_t pl[4] = {w.x, w.y, w.z, w.x ^ w.y ^ w.z};
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(pl[j]), qop[10 * gi + 2 * j], c1, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(pl[j] >> 4), qop[10 * gi + 2 * j + 1], c1, 0, 0, 0);
+        for (int hh = 0; hh < 2; ++hh) {
+          v4i op;
+          op.x = (int)(pl[j] & (0x01010101u << (4 * hh)));
+          op.y = (int)(pl[j] & (0x02020202u << (4 * hh)));
+          op.z = (int)(pl[j] & (0x04040404u << (4 * hh)));
+          op.w = (int)(pl[j] & (0x08080808u << (4 * hh)));
+          c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(2 * j + hh) * 64 + lane], c1, 0, 0, 0);
         }
-        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(w.w), qop[10 * gi + 8], c2, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_operand(w.w >> 4), qop[10 * gi + 9], c2, 0, 0, 0);
       }
-      const int tb = blk0 + 16 * tau + 4 * kg;   // output tokens tb + r
-      const uint32_t nw[2] = {nb[tau].x, nb[tau].y}, gw[2] = {gb[tau].x, gb[tau].y},
-                     vw2[2] = {vb[tau].x, vb[tau].y};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        v4i op;
+        op.x = (int)(w.w & (0x01010101u << (4 * hh)));
+        op.y = (int)(w.w & (0x02020202u << (4 * hh)));
+        op.z = (int)(w.w & (0x04040404u << (4 * hh)));
+        op.w = (int)(w.w & (0x08080808u << (4 * hh)));
+        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(8 + hh) * 64 + lane], c2, 0, 0, 0);
+      }
+      // this lane's limb of (S1 + kappa G S2) for the 4 tokens r of the column group
+      const uint32_t gw[2] = {gb[tau].x, gb[tau].y};
+      float t[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float s1 = quad_sum((float)c1[r] * lsc1) - off1;
-        const float s2 = quad_sum((float)c2[r] * lsc2) - off2;
-        const int tok = tb + r;
-        const bool valid = q < G && tok < ntok && tok0 + tok < vis;
-        const float N = f16_bits_to_f32((uint16_t)(nw[r >> 1] >> (16 * (r & 1))));
-        const float Gm = f16_bits_to_f32((uint16_t)(gw[r >> 1] >> (16 * (r & 1))));
-        const float NV = f16_bits_to_f32((uint16_t)(vw2[r >> 1] >> (16 * (r & 1))));
-        const float sco = a.scale * N * fmaf(kappa * Gm, s2, s1);
-        sc[tau][r] = valid ? sco : kNegInf;
-        sv[tau][r] = valid ? sco + __logf(NV) : kNegInf;
+        const float Gr = f16_bits_to_f32((uint16_t)(gw[r >> 1] >> (16 * (r & 1))));
+        t[r] = fmaf((float)c2[r] * lsc2, Gr, (float)c1[r] * lsc1);
       }
+      // transpose-reduce over the quad: lane lam keeps token lam
+      const bool o1 = lam & 1, o2 = lam & 2;
+      const float u0 = (o1 ? t[1] : t[0]) + dpp_swap1f(o1 ? t[0] : t[1]);
+      const float u1 = (o1 ? t[3] : t[2]) + dpp_swap1f(o1 ? t[2] : t[3]);
+      const float T = (o2 ? u1 : u0) + dpp_swap2f(o2 ? u0 : u1);
+      const uint32_t gsel = gw[lam >> 1] >> (16 * (lam & 1));
+      const float Gm = f16_bits_to_f32((uint16_t)gsel);
+      const float N = f16_bits_to_f32(nh[tau]);
+      const int tok = blk0 + 16 * tau + 4 * kg + lam;
+      const bool valid = q < G && tok < ntok && tok0 + tok < vis;
+      const float sco = a.scale * N * (T - off1 - Gm * off2);
+      sc[tau] = valid ? sco : kNegInf;
+      sv[tau] = valid ? sco + __logf(f16_bits_to_f32(vh[tau])) : kNegInf;
     }
 
     // ---- online softmax of this wave (scores, and scores + ln N^V for V)
-    float mx = kNegInf, mxu = kNegInf;
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        mx = fmaxf(mx, sc[tau][r]);
-        mxu = fmaxf(mxu, sv[tau][r]);
-      }
-    const float m_new = fmaxf(m_run, xmax_kg(mx));
-    const float mu_new = fmaxf(mu_run, xmax_kg(mxu));
+    const float m_new = fmaxf(m_run, rowmax16(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
+    const float mu_new = fmaxf(mu_run, rowmax16(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
     const float alpha = m_run == kNegInf ? 0.f : __expf(m_run - m_new);
     const float alphaU = mu_run == kNegInf ? 0.f : __expf(mu_run - mu_new);
-    float ps = 0.f;
-    float U[4][4];
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        ps += sc[tau][r] == kNegInf ? 0.f : __expf(sc[tau][r] - m_new);
-        U[tau][r] = sv[tau][r] == kNegInf ? 0.f : __expf(sv[tau][r] - mu_new);
-      }
-    l_run = l_run * alpha + xsum_kg(ps);
     m_run = m_new;
     mu_run = mu_new;
-
-    // rows of the V accumulator: lane (column n, kg = 0) holds rows 0..3 = query rows
-    const float al0 = __shfl(alphaU, 0, 64), al1 = __shfl(alphaU, 4, 64);
-    const float al2 = __shfl(alphaU, 8, 64), al3 = __shfl(alphaU, 12, 64);
-    if (kg == 0) {
+    float ps = 0.f, us = 0.f;
+    v4i A[4];   // per plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
 #pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        acc[k].x *= al0;
-        acc[k].y *= al1;
-        acc[k].z *= al2;
-        acc[k].w *= al3;
+    for (int tau = 0; tau < 4; ++tau) {
+      ps += sc[tau] == kNegInf ? 0.f : __expf(sc[tau] - m_new);
+      const float U = sv[tau] == kNegInf ? 0.f : __expf(sv[tau] - mu_new);
+      us += U;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int X = (int)rintf(U * cx[j][tau & 1]);
+        const uint32_t t4 = quad_byte_transpose((uint32_t)X + 0x80808080u, lam) ^ 0x80808080u;
+        A[j][tau] = (int)t4;
       }
     }
+    l_lane = l_lane * alpha + ps;
+    us_lane = us_lane * alphaU + us;
 
-    // ---- V numerator: two 32-token K-blocks, rows = query rows (n < 4)
+    // ---- V: one 64-token K block, 8 column blocks x 4 planes
+    // the accumulator row of this lane's column lane is query row kg
+    const float aU_row = __shfl(alphaU, 4 * (kg & 3), 64);
 #pragma unroll
-    for (int kap = 0; kap < 2; ++kap) {
-      v8h A[4];
+    for (int k = 0; k < NB; ++k) {
+      const uint32_t x0 = vw[k][0].x ^ vw[k][1].x ^ vw[k][2].x;
+      const uint32_t x1 = vw[k][0].y ^ vw[k][1].y ^ vw[k][2].y;
+      const uint32_t w0[4] = {vw[k][0].x, vw[k][1].x, vw[k][2].x, x0};
+      const uint32_t w1[4] = {vw[k][0].y, vw[k][1].y, vw[k][2].y, x1};
+      v4i c = {0, 0, 0, 0};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float ua = __shfl(U[2 * kap][r], src, 64);
-        float ub = __shfl(U[2 * kap + 1][r], src, 64);
-        if (n >= kMfmaMaxGroup) ua = ub = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          A[j][2 * r] = (_Float16)(ua * cw[j]);
-          A[j][2 * r + 1] = (_Float16)(ub * cw[j]);
-        }
+      for (int j = 0; j < 4; ++j) {
+        v4i bop;
+        bop.x = (int)(w0[j] & vmask0);   // tokens 4 kg + r       (tile 0)
+        bop.y = (int)(w0[j] & vmask1);   // tokens 16 + 4 kg + r  (tile 1)
+        bop.z = (int)(w1[j] & vmask0);   // tokens 32 + 4 kg + r  (tile 2)
+        bop.w = (int)(w1[j] & vmask1);   // tokens 48 + 4 kg + r  (tile 3)
+        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bop, c, 0, 0, 0);
       }
-      if (32 * kap + blk0 >= ntok) break;   // wave-uniform: rest of the block is past the end
-#pragma unroll
-      for (int k = 0; k < NB; ++k) {
-        uint32_t w0, w1, w2;
-        if constexpr (kPrefetchV) {
-          w0 = kap ? vw[k][0].y : vw[k][0].x;
-          w1 = kap ? vw[k][1].y : vw[k][1].x;
-          w2 = kap ? vw[k][2].y : vw[k][2].x;
-        } else {
-          const size_t base = (size_t)(16 * k + n) * (kPage / 32) + blk0 / 32 + kap;
-          w0 = vrow[base];
-          w1 = vrow[base + (size_t)D * (kPage / 32)];
-          w2 = vrow[base + (size_t)2 * D * (kPage / 32)];
-        }
-        const uint32_t pl[4] = {w0, w1, w2, w0 ^ w1 ^ w2};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          // tokens 4 kg + r and 4 kg + 16 + r sit at bits 12 + r and 28 + r of wr
-          const uint32_t wr = __builtin_amdgcn_alignbit(pl[j], pl[j], rot);
-          v4i bi;
-          bi.x = (int)(((wr << 3) & 0x80008000u) | 0x04000400u);
-          bi.y = (int)(((wr << 2) & 0x80008000u) | 0x04000400u);
-          bi.z = (int)(((wr << 1) & 0x80008000u) | 0x04000400u);
-          bi.w = (int)((wr & 0x80008000u) | 0x04000400u);
-          acc[k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], __builtin_bit_cast(v8h, bi), acc[k], 0, 0, 0);
-        }
-      }
+      // rows 4 kg + r are (query kg, limb r)
+      const float v = (float)c[0] + 256.f * (float)c[1] + 65536.f * (float)c[2] + 16777216.f * (float)c[3];
+      facc[k] = fmaf(facc[k], aU_row, delta_u * v);
     }
   }
 
   // ---- combine the four waves into one partial per query row
-  if (kg == 0 && limb == 0) {
+  const float l_row = rowsum16(l_lane), us_row = rowsum16(us_lane);
+  if (kg == 0 && lam == 0) {
     s_wm[wave][0][q] = m_run;
-    s_wm[wave][1][q] = l_run;
+    s_wm[wave][1][q] = l_row;
     s_wm[wave][2][q] = mu_run;
+    s_wm[wave][3][q] = us_row;
   }
-  if (kg == 0) {
+  __syncthreads();
+  {
+    const float c7 = a.cb.levels[7];
+    const float usq = s_wm[wave][3][kg & 3];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      s_wacc[wave][0][16 * k + n] = acc[k].x;
-      s_wacc[wave][1][16 * k + n] = acc[k].y;
-      s_wacc[wave][2][16 * k + n] = acc[k].z;
-      s_wacc[wave][3][16 * k + n] = acc[k].w;
-    }
+    for (int k = 0; k < NB; ++k) s_wacc[wave][kg & 3][16 * k + n] = facc[k] - c7 * usq;
   }
   __syncthreads();
   const int nsplit = a.plan.n_split;
@@ -664,15 +676,15 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) x[r] = 0.f;
   float lpart = 0.f;
-  // wave w takes chunks of 64 splits w, w + 4, ...
-  for (int c0 = 64 * wave; c0 < nsplit; c0 += 256) {
+  // split weights, 64 at a time across lanes; wave w then sums splits w, w+4, ...
+  for (int c0 = 0; c0 < nsplit; c0 += 64) {
     const int sp = c0 + lane;
     float f = 0.f;
     if (sp < nsplit) {
       const float *pr = part + sp * stride;
       const float l = pr[1];
       if (l > 0.f) {
-        lpart += l * __expf(pr[0] - M);
+        if ((sp & 3) == wave) lpart += l * __expf(pr[0] - M);
         if (MU != kNegInf && pr[2] != kNegInf) f = __expf(pr[2] - MU);
       }
     }
@@ -681,8 +693,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     const int cnt = min(64, nsplit - c0);
-#pragma unroll 8
-    for (int j = 0; j < cnt; ++j) {
+#pragma unroll 16
+    for (int j = wave; j < cnt; j += 4) {
       const float fj = s_f[wave][j];
       const float *row = part + (size_t)(c0 + j) * stride + kPartHead;
 #pragma unroll
@@ -715,9 +727,11 @@ template <int D>
 hipError_t launch_dim(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch);
   const int G = a.plan.group;
-  if (a.plan.mfma)
-    hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
-  else if (G <= 8)
+  if constexpr (D == 128) {
+    if (a.plan.mfma) hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
+  }
+  if (a.plan.mfma) {
+  } else if (G <= 8)
     hipLaunchKernelGGL((decode_valu_kernel<D, 8>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode_valu_kernel<D, 16>), grid, dim3(256), 0, s, a);
@@ -731,7 +745,7 @@ hipError_t launch_dim(const DecodeArgs &a, hipStream_t s) {
 
 size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads) {
   size_t bytes = prep_float_bytes(d, batch, n_q, n_q_heads);
-  if (n_q_heads / n_kv_heads * n_q <= kMfmaMaxGroup)
+  if (mfma_path(d, n_q_heads / n_kv_heads * n_q))
     bytes += ((size_t)batch * n_kv_heads * packed_group_bytes(d) + 255) / 256 * 256;
   return bytes;
 }

@@ -11,7 +11,6 @@ namespace tq {
 namespace {
 
 constexpr int kWaves = 4;      // waves per workgroup
-constexpr int kKVecPerWave = 4; // K vectors a wave keeps in flight for the S r product
 
 // Steps 1-3 for one vector: norm, rotation, codes. Returns y (rotated, unit
 // norm) in y[], the codes in idx[] and the norm.
@@ -40,7 +39,9 @@ __device__ inline float encode_front(const void *x, size_t base, const Codebook 
   return n;
 }
 
-template <int D, int DT>
+// VPW K vectors per wave share each load of S in the S r product: 4 for bulk
+// encodes, 1 for short appends (where latency, not S traffic, dominates).
+template <int D, int DT, int kKVecPerWave>
 __global__ __launch_bounds__(256) void encode_k_kernel(EncodeArgs a) {
   constexpr int R = D / 64;
   constexpr int NWORD = D / 8;              // u32 words per K record
@@ -156,7 +157,8 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
   uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * VSEC;
   const int off = slot % kPage;
   uint32_t *rows = reinterpret_cast<uint32_t *>(sec);
-  const uint32_t bit = 1u << (off & 31);
+  // token u of a 32-token word sits at bit 8 (u % 4) + u / 4
+  const uint32_t bit = 1u << (8 * (off & 3) + ((off & 31) >> 2));
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = lane + 64 * r;
@@ -225,7 +227,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
       int idx = 0;
 #pragma unroll
       for (int j = 0; j < 3; ++j)
-        idx |= ((rows[(size_t)(j * D + i) * (kPage / 32) + (off >> 5)] >> (off & 31)) & 1) << j;
+        idx |= ((rows[(size_t)(j * D + i) * (kPage / 32) + (off >> 5)] >> (8 * (off & 3) + ((off & 31) >> 2))) & 1) << j;
       v[r] = level_of(a.cb, idx);
     }
     scale = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + VCODES)[off]);
@@ -251,10 +253,15 @@ hipError_t by_dim_dtype(int d, int dtype, F &&f) {
 
 hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
   const long total = (long)a.n_tokens * a.n_heads;
-  const long per_block = kWaves * kKVecPerWave;
-  const dim3 grid((unsigned)((total + per_block - 1) / per_block));
   return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
-    hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value>), grid, dim3(256), 0, s, a);
+    if (total < 4096) {
+      const dim3 grid((unsigned)((total + kWaves - 1) / kWaves));
+      hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 1>), grid, dim3(256), 0, s, a);
+    } else {
+      const long per_block = kWaves * 4;
+      const dim3 grid((unsigned)((total + per_block - 1) / per_block));
+      hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 4>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
   });
 }

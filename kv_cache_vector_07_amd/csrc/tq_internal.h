@@ -59,6 +59,11 @@ struct PrepArgs {
 __host__ __device__ inline int mfma_per_tile(int d) { return 10 * (d / 128); }
 __host__ __device__ inline size_t packed_group_bytes(int d) { return (size_t)mfma_per_tile(d) * 64 * 16 + 64; }
 constexpr int kMfmaMaxGroup = 4;   // query rows per (sequence, KV head) on the MFMA path
+// The MFMA decode kernel covers head_dim 128 with at most 4 query rows per KV
+// head; other shapes run the VALU decode kernel.
+__host__ __device__ inline bool mfma_path(int d, int group) {
+  return d == 128 && group <= kMfmaMaxGroup;
+}
 
 // Split-K plan of one decode call.
 struct DecodePlan {

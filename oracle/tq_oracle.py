@@ -265,11 +265,29 @@ def encode(x, cb: Codebook, S=None) -> dict:
 #     bit e of a word belongs to coordinate 32 s + e;
 #     then N[P] fp16 at P*d/2, then G[P] fp16 at P*d/2 + 2P.
 #   V section of one (page, kv-head):
-#     for plane j = 0..2 and coordinate i: a P-bit little-endian row at byte
-#     ((j*d + i) * P/8); bit t is bit j of token t's code for coordinate i;
-#     then N[P] fp16 at 3*d*P/8.
+#     for plane j = 0..2 and coordinate i: a row of P/32 little-endian u32 words
+#     at byte ((j*d + i) * P/8); word w covers tokens 32w .. 32w+31 and token
+#     32w + u sits at bit 8*(u mod 4) + u div 4 of it (bit j of that token's
+#     code for coordinate i); then N[P] fp16 at 3*d*P/8.
 #   Pools are [n_pages][n_kv_heads][section bytes]; slot = page * P + offset.
 # --------------------------------------------------------------------------
+# storage bit p of a 32-token V word holds token u = 4 (p mod 8) + p div 8
+_V_TOKEN_OF_BIT = np.array([4 * (p % 8) + p // 8 for p in range(32)])
+_V_BIT_OF_TOKEN = np.argsort(_V_TOKEN_OF_BIT)
+
+
+def _v_to_storage(bits):
+    """[..., P] bits in token order -> [..., P] in storage order."""
+    lead, P = bits.shape[:-1], bits.shape[-1]
+    return bits.reshape(*lead, P // 32, 32)[..., _V_TOKEN_OF_BIT].reshape(*lead, P)
+
+
+def _v_from_storage(bits):
+    """[..., P] bits in storage order -> [..., P] in token order."""
+    lead, P = bits.shape[:-1], bits.shape[-1]
+    return bits.reshape(*lead, P // 32, 32)[..., _V_BIT_OF_TOKEN].reshape(*lead, P)
+
+
 def k_page_bytes(d: int, P: int) -> int:
     return P * d // 2 + 4 * P
 
@@ -312,10 +330,11 @@ def pack_v(pool: np.ndarray, slots, idx, N, P: int) -> None:
         for h in range(H):
             base = (int(pg) * H + h) * vpb
             region = pool[base:base + cbytes].reshape(3, d, P // 8)
-            bits = np.unpackbits(region, axis=-1, bitorder="little")     # [3][d][P]
+            bits = _v_from_storage(np.unpackbits(region, axis=-1, bitorder="little"))  # [3][d][P]
             for j in range(3):
                 bits[j][:, off[sel]] = ((idx[sel, h, :] >> j) & 1).T
-            pool[base:base + cbytes] = np.packbits(bits, axis=-1, bitorder="little").reshape(-1)
+            pool[base:base + cbytes] = np.packbits(_v_to_storage(bits), axis=-1,
+                                                   bitorder="little").reshape(-1)
             nb = np.asarray(N, dtype=np.float16)[sel, h].view(np.uint8).reshape(-1, 2)
             pos = base + cbytes + 2 * off[sel]
             pool[pos[:, None] + np.arange(2)] = nb
@@ -351,8 +370,8 @@ def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
         sel = np.nonzero(page == pg)[0]
         for h in range(H):
             base = (int(pg) * H + h) * vpb
-            bits = np.unpackbits(pool[base:base + cbytes].reshape(3, d, P // 8), axis=-1,
-                                 bitorder="little")                        # [3][d][P]
+            bits = _v_from_storage(np.unpackbits(pool[base:base + cbytes].reshape(3, d, P // 8),
+                                                 axis=-1, bitorder="little"))  # [3][d][P]
             sub = bits[:, :, off[sel]]                                     # [3][d][k]
             idx[sel, h, :] = (sub[0] | (sub[1] << 1) | (sub[2] << 2)).T
             pos = base + cbytes + 2 * off[sel]
@@ -390,7 +409,7 @@ def gather_v(pool, block_table_row, L, kv_head, H, d, P):
     pages = np.asarray(block_table_row, dtype=np.int64)[:npg]
     base = (pages * H + kv_head) * vpb
     codes = pool[base[:, None] + np.arange(cbytes)].reshape(npg, 3, d, P // 8)
-    bits = np.unpackbits(codes, axis=-1, bitorder="little")                # [pg][3][d][P]
+    bits = _v_from_storage(np.unpackbits(codes, axis=-1, bitorder="little"))  # [pg][3][d][P]
     idx = bits[:, 0] | (bits[:, 1] << 1) | (bits[:, 2] << 2)               # [pg][d][P]
     idx = idx.transpose(0, 2, 1).reshape(npg * P, d)[:L]
     t = np.arange(L, dtype=np.int64)

@@ -260,7 +260,7 @@ def test_pack_layout_hand_fixture():
     for j in range(3):
         for c in range(d):
             if ((c % 8) >> j) & 1:
-                wantv[4 * (32 * j + c)] = 0x02
+                wantv[4 * (32 * j + c) + 1] = 0x01
     for off, hx in g["v_n_bytes"].items():
         wantv[int(off)] = int(hx, 16)
     assert np.array_equal(vp, wantv)
