@@ -461,13 +461,17 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
         idx, sign, N, G = gather_k(k_pool, block_table[b], L, kvh, n_kv_heads, d, page_size)
         vidx, NV = gather_v(v_pool, block_table[b], L, kvh, n_kv_heads, d, page_size)
         vals = NV[:, None] * cb.levels[vidx]                               # [L][d]
+        ckey = cb.levels[idx]                                              # [L][d]
+        sig = np.where(sign, 1.0, -1.0)
         for t in range(n_q):
             vis = L - (n_q - 1 - t) if causal_tail else L
             if vis <= 0:
                 continue
             for h in range(kvh * g, (kvh + 1) * g):
                 qt, p = rotate_query(q[b, t, h], S64)
-                logits = scale * score(qt, p, idx[:vis], sign[:vis], N[:vis], G[:vis], cb, m)
+                # the estimate of score() with c[idx] and sigma evaluated once per head
+                est = N[:vis] * (ckey[:vis] @ qt + (QJL_KAPPA_NUM / m) * G[:vis] * (sig[:vis] @ p))
+                logits = scale * est
                 w = np.exp(logits - logits.max())
                 w /= w.sum()
                 out[b, t, h] = fwht(w @ vals[:vis])
