@@ -235,31 +235,41 @@ def main():
     step_ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] timed {args.steps} steps: {step_ms * 1e3:.2f} us/step (host wall {wall:.3f} s)")
 
-    # ---- decode kernel alone (the dominant kernel): back-to-back launches
+    # ---- the split-K decode kernel alone (the dominant kernel): back-to-back launches
     prep = tq.tq_query_prepare(copies[0], qs[0])
     size_p = C.c_size_t(0)
-    L_.tq_attn_decode_prepared(copies[0].ref, prep.data_ptr(), B, nq, Hq, table.data_ptr(), mp,
-                               seq.data_ptr(), 0, scale, out.data_ptr(), None, C.byref(size_p), None)
+    L_.tq_attn_decode_split(copies[0].ref, prep.data_ptr(), B, nq, Hq, table.data_ptr(), mp,
+                            seq.data_ptr(), 0, scale, None, C.byref(size_p), None)
     ws_p = torch.zeros(size_p.value, dtype=torch.uint8, device=dev)
 
     def dec(i):
         c = copies[i % R]
         sz = C.c_size_t(ws_p.numel())
-        r = L_.tq_attn_decode_prepared(c.ref, prep.data_ptr(), B, nq, Hq, table.data_ptr(), mp,
-                                       seq.data_ptr(), 0, scale, out.data_ptr(), ws_p.data_ptr(),
-                                       C.byref(sz), sh)
+        r = L_.tq_attn_decode_split(c.ref, prep.data_ptr(), B, nq, Hq, table.data_ptr(), mp,
+                                    seq.data_ptr(), 0, scale, ws_p.data_ptr(), C.byref(sz), sh)
         if r:
             raise RuntimeError(f"decode launch failed with status {r}")
 
-    for i in range(16):
-        dec(i)
-    torch.cuda.synchronize()
-    ev0.record()
-    for i in range(args.decode_launches):
-        dec(i)
-    ev1.record()
-    torch.cuda.synchronize()
-    dec_ms = ev0.elapsed_time(ev1) / args.decode_launches
+    def merge(i):
+        r = L_.tq_attn_decode_merge(copies[0].ref, B, nq, Hq, mp, out.data_ptr(), ws_p.data_ptr(),
+                                    ws_p.numel(), sh)
+        if r:
+            raise RuntimeError(f"merge launch failed with status {r}")
+
+    def timed(fn, n):
+        for i in range(8):
+            fn(i)
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(n):
+            fn(i)
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n
+
+    dec_ms = timed(dec, args.decode_launches)
+    merge_ms = timed(merge, 64)
+    dec_kernel = "decode_mfma_kernel" if (w.head_dim == 128 and w.group <= 4) else "decode_valu_kernel"
 
     ctx_tokens = int(lens.sum())
     kv_bytes = ctx_tokens * H * kv_bytes_per_token_head(d)
@@ -291,9 +301,10 @@ def main():
         "encode_k_vec_per_s": round(n_vec / (enc_k_ms / 1e3), 1),
         "encode_v_vec_per_s": round(n_vec / (enc_v_ms / 1e3), 1),
         "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "merge_kernel_us": round(merge_ms * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel",
+                     "traffic": traffic, "kernel": dec_kernel,
                      "bytes_per_launch": kv_bytes},
     }
     if not args.no_cpu_baseline:

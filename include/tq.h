@@ -31,18 +31,22 @@
  * ascending codebook levels / thresholds, S the m x d QJL matrix.
  *
  * Packed page format (frozen; one section per (page, KV head), sections stored
- * [n_pages][n_kv_heads], slot = page * P + offset, little-endian words):
+ * [n_pages][n_kv_heads], slot = page * P + offset, little-endian words). An
+ * offset is split as t = 64*b + 16*tau + 4*k + r (b: 64-token block; tau, k,
+ * r = 0..3); per-token fp16 arrays are kept in side order, token t at entry
+ * e(t) = 64*b + 16*k + 4*r + tau.
  *   K section, k_page_bytes = P*d/2 + 4*P:
  *     record of token t at byte t*d/2, d/2 bytes: for each coordinate group
  *     s = 0..d/32-1 four u32 words [code bit 0, code bit 1, code bit 2, QJL sign];
  *     bit e of a word belongs to coordinate 32*s + e; sign bit = [ (S r)_l >= 0 ];
- *     N[t] (fp16, ||x||) at byte P*d/2 + 2t; G[t] (fp16, ||r||) at P*d/2 + 2P + 2t.
+ *     N (fp16, ||x||) at byte P*d/2 + 2*e(t); G (fp16, ||r||) at P*d/2 + 2*P + 2*e(t).
  *   V section, v_page_bytes = 3*d*P/8 + 2*P:
- *     for plane j = 0..2 and coordinate i a row of P/32 u32 words at byte
- *     (j*d + i)*P/8; word w holds tokens 32w..32w+31, token 32w + u at bit
- *     8*(u%4) + u/4 (bit j of that token's code of coordinate i), so one AND
- *     with 0x01010101 << k gathers the bits of four tokens into four bytes;
- *     N[t] (fp16) at byte 3*d*P/8 + 2t.
+ *     code bits as u32 words: bit j of the code of coordinate i = 16*(2*kp + h) + n
+ *     (h = 0..1, n = 0..15) of token t is bit 8*r + 4*h + tau of word
+ *     b*6d + j*2d + (16*k + n)*(d/32) + kp. So for one block and plane the words
+ *     of "lane" 16*k + n are contiguous, and a shift by 4*h plus one AND with
+ *     0x01010101 << tau gathers the bits of four tokens into four bytes;
+ *     N (fp16) at byte 3*d*P/8 + 2*e(t).
  *   At d = 128 that is 544 bits per K vector (4.25 bits/dim) and 400 bits per V
  *   vector (3.125 bits/dim); at d = 256, 4.125 and 3.0625 bits/dim.
  */
@@ -79,7 +83,9 @@ typedef struct {
   void *k_pool;         /* device, n_pages * Hkv * k_page_bytes, 256-B aligned    */
   void *v_pool;         /* device, n_pages * Hkv * v_page_bytes, 256-B aligned    */
   const float *qjl;     /* device, S as m x d float32 row-major (m = d)           */
-  float levels[8];      /* c[0..7], ascending (from tq_build_codebook)            */
+  float levels[8];      /* c[0..7], strictly ascending and odd, c[7-k] = -c[k]
+                           (from tq_build_codebook); otherwise calls return
+                           TQ_EINVAL                                              */
   float thresholds[7];  /* t[0..6], midpoints, thresholds[3] == 0                 */
 } tq_cache;
 
@@ -178,6 +184,25 @@ int tq_attn_decode_prepared(const tq_cache *c, const void *prep,
                             const int32_t *seq_lens, int32_t causal_tail, float scale,
                             float *out, void *workspace, size_t *workspace_bytes,
                             void *stream);
+
+/*
+ * The two launches of tq_attn_decode_prepared, for callers that overlap or time
+ * them separately. tq_attn_decode_split runs the split-K pass (one kernel) and
+ * leaves per-split partials (running max, softmax sum, V numerator) in the
+ * workspace; tq_attn_decode_merge (one small kernel) combines them by
+ * log-sum-exp, applies the inverse rotation and writes `out`. Both must be called
+ * with the same batch, n_q, n_q_heads and max_pages (the split plan is a
+ * function of these and of the cache shape) and the same workspace, on the
+ * same stream. Workspace rules and errors as for tq_attn_decode_prepared.
+ */
+int tq_attn_decode_split(const tq_cache *c, const void *prep,
+                         int32_t batch, int32_t n_q, int32_t n_q_heads,
+                         const int32_t *block_table, int32_t max_pages,
+                         const int32_t *seq_lens, int32_t causal_tail, float scale,
+                         void *workspace, size_t *workspace_bytes, void *stream);
+int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t n_q_heads,
+                         int32_t max_pages, float *out, const void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 /*
  * Dequantise records back to the original domain (float32 [n_tokens][Hkv][d]):

@@ -19,6 +19,12 @@ int check_cache(const tq_cache *c) {
   if (!supported_dim(c->head_dim) || c->page_size != TQ_PAGE_SIZE) return TQ_EUNSUPPORTED;
   if (!c->k_pool || !c->v_pool) return TQ_EINVAL;
   if (!aligned(c->k_pool, 256) || !aligned(c->v_pool, 256)) return TQ_EALIGN;
+  // the decode kernels split each level into odd bit-plane weights: the
+  // codebook must be strictly increasing and odd (c[7-k] = -c[k])
+  for (int k = 0; k < 8; ++k) {
+    if (!isfinite(c->levels[k]) || c->levels[7 - k] != -c->levels[k]) return TQ_EINVAL;
+    if (k > 0 && !(c->levels[k] > c->levels[k - 1])) return TQ_EINVAL;
+  }
   return TQ_OK;
 }
 
@@ -254,20 +260,21 @@ static int decode_checks(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   return TQ_OK;
 }
 
-static int decode_run(const tq_cache *c, const uint8_t *prep, int32_t batch, int32_t n_q,
-                      int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
-                      const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
-                      uint8_t *ws, const tq::DecodePlan &plan, hipStream_t s) {
+static tq::DecodeArgs decode_args(const tq_cache *c, const uint8_t *prep, int32_t batch,
+                                  int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
+                                  int32_t max_pages, const int32_t *seq_lens, int32_t causal_tail,
+                                  float scale, float *out, uint8_t *ws,
+                                  const tq::DecodePlan &plan) {
   tq::DecodeArgs a;
   a.k_pool = (const uint8_t *)c->k_pool;
   a.v_pool = (const uint8_t *)c->v_pool;
   a.prep = (const float *)prep;
-  a.packed = prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads);
+  a.packed = prep ? prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads) : nullptr;
   a.block_table = block_table;
   a.max_pages = max_pages;
   a.seq_lens = seq_lens;
   a.out = out;
-  a.counters = (uint32_t *)ws;
+  a.counters = nullptr;
   a.partials = (float *)(ws + plan.counter_bytes);
   a.batch = batch;
   a.n_q = n_q;
@@ -277,7 +284,17 @@ static int decode_run(const tq_cache *c, const uint8_t *prep, int32_t batch, int
   a.scale = scale;
   a.plan = plan;
   a.cb = codebook_of(c);
-  return hip_status(tq::launch_decode(a, c->head_dim, s));
+  return a;
+}
+
+static int decode_run(const tq_cache *c, const uint8_t *prep, int32_t batch, int32_t n_q,
+                      int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
+                      const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
+                      uint8_t *ws, const tq::DecodePlan &plan, hipStream_t s) {
+  tq::DecodeArgs a = decode_args(c, prep, batch, n_q, n_q_heads, block_table, max_pages,
+                                 seq_lens, causal_tail, scale, out, ws, plan);
+  if (tq::launch_decode_split(a, c->head_dim, s) != hipSuccess) return TQ_EHIP;
+  return hip_status(tq::launch_decode_merge(a, c->head_dim, s));
 }
 
 int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype, int32_t batch, int32_t n_q,
@@ -331,6 +348,51 @@ int tq_attn_decode_prepared(const tq_cache *c, const void *prep, int32_t batch, 
   if (!aligned(prep, 256) || !aligned(workspace, 256)) return TQ_EALIGN;
   return decode_run(c, (const uint8_t *)prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
                     scale, out, (uint8_t *)workspace, plan, (hipStream_t)stream);
+}
+
+int tq_attn_decode_split(const tq_cache *c, const void *prep, int32_t batch, int32_t n_q,
+                         int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
+                         const int32_t *seq_lens, int32_t causal_tail, float scale,
+                         void *workspace, size_t *workspace_bytes, void *stream) {
+  float dummy_out[4] __attribute__((aligned(16)));
+  int st = decode_checks(c, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+                         dummy_out, workspace_bytes);
+  if (st) return st;
+  tq::DecodePlan plan =
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+  size_t need = plan.counter_bytes + plan.partial_bytes;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return TQ_OK;
+  }
+  if (*workspace_bytes < need) {
+    *workspace_bytes = need;
+    return TQ_EWORKSPACE;
+  }
+  if (!prep) return TQ_EINVAL;
+  if (!aligned(prep, 256) || !aligned(workspace, 256)) return TQ_EALIGN;
+  tq::DecodeArgs a = decode_args(c, (const uint8_t *)prep, batch, n_q, n_q_heads, block_table,
+                                 max_pages, seq_lens, causal_tail, scale, nullptr,
+                                 (uint8_t *)workspace, plan);
+  return hip_status(tq::launch_decode_split(a, c->head_dim, (hipStream_t)stream));
+}
+
+int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t n_q_heads,
+                         int32_t max_pages, float *out, const void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  int st = check_cache(c);
+  if (st) return st;
+  if (batch <= 0 || n_q <= 0 || n_q_heads <= 0 || max_pages <= 0) return TQ_EINVAL;
+  if (n_q_heads % c->n_kv_heads) return TQ_EINVAL;
+  if (n_q_heads / c->n_kv_heads * n_q > TQ_MAX_GROUP) return TQ_EUNSUPPORTED;
+  if (!out || !workspace) return TQ_EINVAL;
+  if (!aligned(out, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
+  tq::DecodePlan plan =
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+  if (workspace_bytes < plan.counter_bytes + plan.partial_bytes) return TQ_EWORKSPACE;
+  tq::DecodeArgs a = decode_args(c, nullptr, batch, n_q, n_q_heads, nullptr, max_pages, nullptr, 0,
+                                 0.f, out, (uint8_t *)workspace, plan);
+  return hip_status(tq::launch_decode_merge(a, c->head_dim, (hipStream_t)stream));
 }
 
 int tq_dequant(const tq_cache *c, int32_t which, int32_t with_qjl, const int32_t *slots,

@@ -37,7 +37,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
-constexpr int kPartHead = 4;   // partial record: m, l, mU, pad, then acc[d]
+constexpr int kPartHead = 4;   // partial record: m, l, mU (log2 units), pad, then acc[d]
 
 // Weights of the odd-codebook bit planes: c[idx] = sum_j 2 a_j plane_j - c7 with
 // planes (b0, b1, b2, b0^b1^b2).
@@ -217,6 +217,7 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
     vis[qq] = qq < G ? (a.causal_tail ? L - (a.n_q - 1 - t) : L) : 0;
   }
   const float kappa = qjl_kappa<D>();
+  const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
   float acc[QPS];
 #pragma unroll
   for (int k = 0; k < QPS; ++k) acc[k] = 0.f;
@@ -255,14 +256,15 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
             }
           }
         }
-        const float N = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(ksec + KCODES)[t]);
-        const float Gm = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(ksec + KCODES + 2 * kPage)[t]);
+        const int e = side_entry(t);
+        const float N = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(ksec + KCODES)[e]);
+        const float Gm = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(ksec + KCODES + 2 * kPage)[e]);
 #pragma unroll
         for (int qq = 0; qq < GT; ++qq) {
-          const float sc = a.scale * N * fmaf(kappa * Gm, s2[qq], s1[qq]);
+          const float sc = scale2 * N * fmaf(kappa * Gm, s2[qq], s1[qq]);
           s_w[t][qq] = (tok0 + t < vis[qq]) ? sc : kNegInf;
         }
-        s_nv[t] = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(vsec + VCODES)[t]);
+        s_nv[t] = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(vsec + VCODES)[e]);
       } else {
 #pragma unroll
         for (int qq = 0; qq < GT; ++qq) s_w[t][qq] = kNegInf;
@@ -281,13 +283,13 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < kPage / 64; ++k) {
         const int t = lane + 64 * k;
-        const float e = m_new == kNegInf ? 0.f : __expf(s_w[t][qq] - m_new);
+        const float e = m_new == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s_w[t][qq] - m_new);
         s_w[t][qq] = e;
         sum += e;
       }
       sum = wave_sum(sum);
       if (lane == 0) {
-        const float alpha = m_old == kNegInf ? 0.f : __expf(m_old - m_new);
+        const float alpha = m_old == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
         s_alpha[qq] = alpha;
         s_l[qq] = s_l[qq] * alpha + sum;
         s_m[qq] = m_new;
@@ -301,23 +303,18 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
         const int qq = set + NS * k;
         if (qq < GT) acc[k] *= s_alpha[qq];
       }
-      const uint4 *r0 = reinterpret_cast<const uint4 *>(vsec + (size_t)(0 * D + i) * (kPage / 8));
-      const uint4 *r1 = reinterpret_cast<const uint4 *>(vsec + (size_t)(1 * D + i) * (kPage / 8));
-      const uint4 *r2 = reinterpret_cast<const uint4 *>(vsec + (size_t)(2 * D + i) * (kPage / 8));
-      const uint4 p0[2] = {r0[0], r0[1]}, p1[2] = {r1[0], r1[1]}, p2[2] = {r2[0], r2[1]};
+      // coordinate i: the (b, k) token groups of 16 each give one word per plane
+      const uint32_t *vw32 = reinterpret_cast<const uint32_t *>(vsec);
+      const int hsh = 4 * ((i >> 4) & 1);
+      for (int grp = 0; grp < kPage / 16; ++grp) {
+        const int t0 = 64 * (grp >> 2) + 4 * (grp & 3);   // lowest token of the group
+        if (t0 >= ntok) continue;
+        const int w = v_word<D>(t0, i, 0);
+        const uint32_t w0 = vw32[w] >> hsh, w1 = vw32[w + 2 * D] >> hsh, w2 = vw32[w + 4 * D] >> hsh;
 #pragma unroll
-      for (int wi = 0; wi < kPage / 32; ++wi) {
-        const int tb = wi * 32;
-        if (tb >= ntok) break;
-        const uint4 &q0 = p0[wi >> 2], &q1 = p1[wi >> 2], &q2 = p2[wi >> 2];
-        const int c = wi & 3;
-        const uint32_t w0 = c == 0 ? q0.x : c == 1 ? q0.y : c == 2 ? q0.z : q0.w;
-        const uint32_t w1 = c == 0 ? q1.x : c == 1 ? q1.y : c == 2 ? q1.z : q1.w;
-        const uint32_t w2 = c == 0 ? q2.x : c == 1 ? q2.y : c == 2 ? q2.z : q2.w;
-#pragma unroll 4
-        for (int e = 0; e < 32; ++e) {
-          const int t = tb + e;
-          const int pos = 8 * (e & 3) + (e >> 2);   // storage bit of token e of the word
+        for (int e = 0; e < 16; ++e) {
+          const int tau = e >> 2, r = e & 3, pos = 8 * r + tau;
+          const int t = t0 + 16 * tau + r;
           const int idx = ((w0 >> pos) & 1) | (((w1 >> pos) & 1) << 1) | (((w2 >> pos) & 1) << 2);
           const float val = s_nv[t] * level_of(a.cb, idx);
 #pragma unroll
@@ -388,9 +385,21 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // token sit in the four lanes of a quad; a transpose-reduce leaves lane L of the
 // quad with the full score of token L, so every later per-score step runs once.
 // V: int8 MFMA with the softmax weight (times each plane weight) as 4 int8 limbs
-// on the 16 rows and the V bit planes (storage order puts the four tokens of a
-// lane in the four bytes of one AND) on the columns; per 64-token block the
-// int32 sums are folded into a float accumulator.
+// on the 16 rows and the V bit planes on the columns: lane (n, k) reads its 16
+// tokens x 2 coordinates per u32 word, and a shift plus one AND per 4 tokens
+// makes the B operand. Per 64-token block the int32 sums are folded into a
+// float accumulator.
+//
+// Everything one block needs (key records, sidecars, V words: 40 registers) is
+// loaded one block ahead; two register sets alternate between even and odd
+// pages so that no copy is needed.
+struct MfmaBlock {
+  uint4 kw[4];   // key record chunk k of tokens 16 tau + n
+  uint4 g[2];    // G of side entries 16 k + 0..15 (r = 0..3, tau = 0..3)
+  uint2 nk, nv;  // N^K, N^V of side entries 16 k + 4 lam + 0..3 (tau = 0..3)
+  uint4 v[3];    // V words of plane j: coordinate pairs kp = 0..3
+};
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   static_assert(D == 128, "MFMA decode path is built for head_dim 128");
@@ -404,13 +413,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   __shared__ float s_wm[4][4][kMfmaMaxGroup];     // per wave: m, l, mU, sum U of each row
   __shared__ float s_wacc[4][kMfmaMaxGroup][D];   // per wave V numerators
-  __shared__ v4i s_qop[10 * 64];                   // packed query operand, [mfma][lane]
+  __shared__ v4i s_qop[NMU * 64];                  // packed query operand, [mfma][lane]
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
   const int q = n >> 2, lam = n & 3;   // query row of this lane's 16-lane row slot, limb / token
-  const int H = a.n_kv_heads, Hq = a.n_q_heads, g = Hq / H, G = a.plan.group;
+  const int H = a.n_kv_heads, G = a.plan.group, g = a.n_q_heads / H;
   const int L = a.seq_lens[b];
 
   const uint8_t *grp = a.packed + ((size_t)b * H + kvh) * packed_group_bytes(D);
@@ -421,24 +430,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const float lsc2 = rc.y * (float)(1 << (8 * lam)) * qjl_kappa<D>();
   const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w * qjl_kappa<D>();
   const int vis = q < G ? (a.causal_tail ? L - (a.n_q - 1 - q / g) : L) : 0;
+  const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
   float wpl[4];
   plane_weights(a.cb, wpl);
   const float wmax = fmaxf(fmaxf(fabsf(wpl[0]), fabsf(wpl[1])), fmaxf(fabsf(wpl[2]), fabsf(wpl[3])));
-  // weight limbs: X = U * (w_j / wmax) * 2^30 / v, v = value of the V key byte
-  // (2^(4 (tau&1) + kg), or -128 for the top bit)
-  float cx[4][2];
+  // weight limbs: X = U * 2^-tau * (w_j / wmax) * 2^30, where 2^tau is the value
+  // the V bit of token 16 tau + 4 k + r takes in byte r of the B operand
+  float cx[4], half[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int k = 4 * hh + kg;
-      const float v = k == 7 ? -128.f : (float)(1 << k);
-      cx[j][hh] = wpl[j] / wmax * 1073741824.f / v;
-    }
+  for (int j = 0; j < 4; ++j) {
+    half[j] = wpl[j] < 0.f ? -0.5f : 0.5f;   // round to nearest with a truncating convert
+    cx[j] = wpl[j] / wmax * 1073741824.f;
+  }
   const float delta_u = wmax * 0x1p-30f;
-  const uint32_t vmask0 = 0x01010101u << kg, vmask1 = 0x10101010u << kg;
-  const float kNaN = __builtin_nanf("");
-  (void)kNaN;
 
   float m_run = kNegInf, mu_run = kNegInf, l_lane = 0.f, us_lane = 0.f;
   float facc[NB];
@@ -453,55 +457,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   if (pg1 > pg0 && blk0 >= L - (pg1 - 1) * kPage) --pg1;
   __syncthreads();   // s_qop
 
-  // key words of the next block are loaded while the current block computes
-  uint4 kw_n[4];
-  uint2 gb_n[4];
-  uint16_t nh_n[4], vh_n[4];
-  auto load_keys = [&](int pg) {
+  auto load_block = [&](MfmaBlock &d, int pg) {
     const int phys = a.block_table[(size_t)b * a.max_pages + pg];
     const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
     const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      kw_n[tau] = reinterpret_cast<const uint4 *>(ks + (size_t)(blk0 + 16 * tau + n) * KREC)[kg];
-      const int tb = blk0 + 16 * tau + 4 * kg;
-      gb_n[tau] = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * kPage + 2 * tb);
-      nh_n[tau] = reinterpret_cast<const uint16_t *>(ks + KCODES)[tb + lam];
-      vh_n[tau] = reinterpret_cast<const uint16_t *>(vs + VCODES)[tb + lam];
-    }
+    for (int tau = 0; tau < 4; ++tau)
+      d.kw[tau] = reinterpret_cast<const uint4 *>(ks + (size_t)(blk0 + 16 * tau + n) * KREC)[kg];
+    const int se = blk0 + 16 * kg;   // first side entry of this lane's tokens
+    d.g[0] = reinterpret_cast<const uint4 *>(ks + KCODES + 2 * kPage + 2 * se)[0];
+    d.g[1] = reinterpret_cast<const uint4 *>(ks + KCODES + 2 * kPage + 2 * se)[1];
+    d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * (se + 4 * lam));
+    d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * (se + 4 * lam));
+    const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) d.v[j] = vw[j * 2 * D * 4 / 16];
   };
-  if (pg0 < pg1) load_keys(pg0);
 
-  for (int pg = pg0; pg < pg1; ++pg) {
+  auto process = [&](const MfmaBlock &d, int pg) {
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
-    const int phys = a.block_table[(size_t)b * a.max_pages + pg];
-    const uint8_t *vsec = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
-    const uint32_t *vrow = reinterpret_cast<const uint32_t *>(vsec);
-    uint4 kw[4];
-    uint2 gb[4];
-    uint16_t nh[4], vh[4];
-#pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      kw[tau] = kw_n[tau];
-      gb[tau] = gb_n[tau];
-      nh[tau] = nh_n[tau];
-      vh[tau] = vh_n[tau];
-    }
-    uint2 vw[NB][3];
-#pragma unroll
-    for (int k = 0; k < NB; ++k)
-#pragma unroll
-      for (int j = 0; j < 3; ++j)
-        vw[k][j] = *reinterpret_cast<const uint2 *>(vrow + (size_t)(j * D + 16 * k + n) * (kPage / 32) + blk0 / 32);
-    if (pg + 1 < pg1) load_keys(pg + 1);
-
     // ---- scores: lane (n, kg) ends with the score of token blk0 + 16 tau + 4 kg + lam
+    const uint32_t gw[8] = {d.g[0].x, d.g[0].y, d.g[0].z, d.g[0].w, d.g[1].x, d.g[1].y, d.g[1].z, d.g[1].w};
     float sc[4], sv[4];
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       v4i c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0};
-      const uint4 w = kw[tau];
+      const uint4 w = d.kw[tau];
       const uint32_t pl[4] = {w.x, w.y, w.z, w.x ^ w.y ^ w.z};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -524,12 +506,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         op.w = (int)(w.w & (0x08080808u << (4 * hh)));
         c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(8 + hh) * 64 + lane], c2, 0, 0, 0);
       }
-      // this lane's limb of (S1 + kappa G S2) for the 4 tokens r of the column group
-      const uint32_t gw[2] = {gb[tau].x, gb[tau].y};
+      // this lane's limb of (S1 + kappa G S2) for the 4 tokens r of the column group;
+      // G of (tau, r) is side entry 4 r + tau of the lane's 16
       float t[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float Gr = f16_bits_to_f32((uint16_t)(gw[r >> 1] >> (16 * (r & 1))));
+        const float Gr = f16_bits_to_f32((uint16_t)(gw[2 * r + (tau >> 1)] >> (16 * (tau & 1))));
         t[r] = fmaf((float)c2[r] * lsc2, Gr, (float)c1[r] * lsc1);
       }
       // transpose-reduce over the quad: lane lam keeps token lam
@@ -537,63 +519,86 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       const float u0 = (o1 ? t[1] : t[0]) + dpp_swap1f(o1 ? t[0] : t[1]);
       const float u1 = (o1 ? t[3] : t[2]) + dpp_swap1f(o1 ? t[2] : t[3]);
       const float T = (o2 ? u1 : u0) + dpp_swap2f(o2 ? u0 : u1);
-      const uint32_t gsel = gw[lam >> 1] >> (16 * (lam & 1));
-      const float Gm = f16_bits_to_f32((uint16_t)gsel);
-      const float N = f16_bits_to_f32(nh[tau]);
+      const uint32_t gsel = (lam & 2) ? ((lam & 1) ? gw[6 + (tau >> 1)] : gw[4 + (tau >> 1)])
+                                      : ((lam & 1) ? gw[2 + (tau >> 1)] : gw[tau >> 1]);
+      const float Gm = f16_bits_to_f32((uint16_t)(gsel >> (16 * (tau & 1))));
+      const uint32_t nkw = (tau >> 1) ? d.nk.y : d.nk.x, nvw = (tau >> 1) ? d.nv.y : d.nv.x;
+      const float N = f16_bits_to_f32((uint16_t)(nkw >> (16 * (tau & 1))));
+      const float NV = f16_bits_to_f32((uint16_t)(nvw >> (16 * (tau & 1))));
       const int tok = blk0 + 16 * tau + 4 * kg + lam;
       const bool valid = q < G && tok < ntok && tok0 + tok < vis;
-      const float sco = a.scale * N * (T - off1 - Gm * off2);
+      const float sco = scale2 * N * (T - off1 - Gm * off2);
       sc[tau] = valid ? sco : kNegInf;
-      sv[tau] = valid ? sco + __logf(f16_bits_to_f32(vh[tau])) : kNegInf;
+      sv[tau] = valid ? sco + __builtin_amdgcn_logf(NV) : kNegInf;   // + log2 N^V
     }
 
-    // ---- online softmax of this wave (scores, and scores + ln N^V for V)
+    // ---- online softmax of this wave (log2 units; scores, and scores + log2 N^V for V)
     const float m_new = fmaxf(m_run, rowmax16(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
     const float mu_new = fmaxf(mu_run, rowmax16(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
-    const float alpha = m_run == kNegInf ? 0.f : __expf(m_run - m_new);
-    const float alphaU = mu_run == kNegInf ? 0.f : __expf(mu_run - mu_new);
+    const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float alphaU = mu_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mu_run - mu_new);
     m_run = m_new;
     mu_run = mu_new;
     float ps = 0.f, us = 0.f;
     v4i A[4];   // per plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      ps += sc[tau] == kNegInf ? 0.f : __expf(sc[tau] - m_new);
-      const float U = sv[tau] == kNegInf ? 0.f : __expf(sv[tau] - mu_new);
+      ps += sc[tau] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[tau] - m_new);
+      const float U = sv[tau] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[tau] - mu_new);
       us += U;
+      const float Ut = __builtin_amdgcn_ldexpf(U, -tau);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int X = (int)rintf(U * cx[j][tau & 1]);
+        const int X = (int)fmaf(Ut, cx[j], half[j]);
         const uint32_t t4 = quad_byte_transpose((uint32_t)X + 0x80808080u, lam) ^ 0x80808080u;
         A[j][tau] = (int)t4;
       }
     }
     l_lane = l_lane * alpha + ps;
     us_lane = us_lane * alphaU + us;
-
-    // ---- V: one 64-token K block, 8 column blocks x 4 planes
     // the accumulator row of this lane's column lane is query row kg
     const float aU_row = __shfl(alphaU, 4 * (kg & 3), 64);
+
+    // ---- V: one 64-token K block, 8 column blocks x 4 planes
+    uint32_t xw[4];
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const uint32_t a0 = kp == 0 ? d.v[0].x : kp == 1 ? d.v[0].y : kp == 2 ? d.v[0].z : d.v[0].w;
+      const uint32_t a1 = kp == 0 ? d.v[1].x : kp == 1 ? d.v[1].y : kp == 2 ? d.v[1].z : d.v[1].w;
+      const uint32_t a2 = kp == 0 ? d.v[2].x : kp == 1 ? d.v[2].y : kp == 2 ? d.v[2].z : d.v[2].w;
+      xw[kp] = a0 ^ a1 ^ a2;
+    }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
-      const uint32_t x0 = vw[k][0].x ^ vw[k][1].x ^ vw[k][2].x;
-      const uint32_t x1 = vw[k][0].y ^ vw[k][1].y ^ vw[k][2].y;
-      const uint32_t w0[4] = {vw[k][0].x, vw[k][1].x, vw[k][2].x, x0};
-      const uint32_t w1[4] = {vw[k][0].y, vw[k][1].y, vw[k][2].y, x1};
+      const int kp = k >> 1, sh = 4 * (k & 1);
+      const uint32_t w0 = (kp == 0 ? d.v[0].x : kp == 1 ? d.v[0].y : kp == 2 ? d.v[0].z : d.v[0].w) >> sh;
+      const uint32_t w1 = (kp == 0 ? d.v[1].x : kp == 1 ? d.v[1].y : kp == 2 ? d.v[1].z : d.v[1].w) >> sh;
+      const uint32_t w2 = (kp == 0 ? d.v[2].x : kp == 1 ? d.v[2].y : kp == 2 ? d.v[2].z : d.v[2].w) >> sh;
+      const uint32_t wj[4] = {w0, w1, w2, xw[kp] >> sh};
       v4i c = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        v4i bop;
-        bop.x = (int)(w0[j] & vmask0);   // tokens 4 kg + r       (tile 0)
-        bop.y = (int)(w0[j] & vmask1);   // tokens 16 + 4 kg + r  (tile 1)
-        bop.z = (int)(w1[j] & vmask0);   // tokens 32 + 4 kg + r  (tile 2)
-        bop.w = (int)(w1[j] & vmask1);   // tokens 48 + 4 kg + r  (tile 3)
+        v4i bop;   // VGPR tau, byte r: token 16 tau + 4 kg + r, bit value 2^tau
+        bop.x = (int)(wj[j] & 0x01010101u);
+        bop.y = (int)(wj[j] & 0x02020202u);
+        bop.z = (int)(wj[j] & 0x04040404u);
+        bop.w = (int)(wj[j] & 0x08080808u);
         c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bop, c, 0, 0, 0);
       }
       // rows 4 kg + r are (query kg, limb r)
       const float v = (float)c[0] + 256.f * (float)c[1] + 65536.f * (float)c[2] + 16777216.f * (float)c[3];
       facc[k] = fmaf(facc[k], aU_row, delta_u * v);
     }
+  };
+
+  MfmaBlock d0, d1;
+  if (pg0 < pg1) load_block(d0, pg0);
+  for (int pg = pg0; pg < pg1; pg += 2) {
+    if (pg + 1 < pg1) load_block(d1, pg + 1);
+    process(d0, pg);
+    if (pg + 1 >= pg1) break;
+    if (pg + 2 < pg1) load_block(d0, pg + 2);
+    process(d1, pg + 1);
   }
 
   // ---- combine the four waves into one partial per query row
@@ -626,8 +631,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       const bool live = s_wm[w][1][qq] > 0.f;
-      lsum += live ? s_wm[w][1][qq] * __expf(s_wm[w][0][qq] - M) : 0.f;
-      fw[w] = (live && s_wm[w][2][qq] != kNegInf) ? __expf(s_wm[w][2][qq] - MU) : 0.f;
+      lsum += live ? s_wm[w][1][qq] * __builtin_amdgcn_exp2f(s_wm[w][0][qq] - M) : 0.f;
+      fw[w] = (live && s_wm[w][2][qq] != kNegInf) ? __builtin_amdgcn_exp2f(s_wm[w][2][qq] - MU) : 0.f;
     }
     float *pr = a.partials + (pbase + qq) * (D + kPartHead);
     if (lane == 0) {
@@ -684,8 +689,8 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
       const float *pr = part + sp * stride;
       const float l = pr[1];
       if (l > 0.f) {
-        if ((sp & 3) == wave) lpart += l * __expf(pr[0] - M);
-        if (MU != kNegInf && pr[2] != kNegInf) f = __expf(pr[2] - MU);
+        if ((sp & 3) == wave) lpart += l * __builtin_amdgcn_exp2f(pr[0] - M);
+        if (MU != kNegInf && pr[2] != kNegInf) f = __builtin_amdgcn_exp2f(pr[2] - MU);
       }
     }
     s_f[wave][lane] = f;
@@ -710,7 +715,7 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   __syncthreads();
   if (wave != 0) return;
   const float lsum = s_stat[0][0] + s_stat[1][0] + s_stat[2][0] + s_stat[3][0];
-  const float inv = (lsum > 0.f && MU != kNegInf) ? __expf(MU - M) / lsum : 0.f;
+  const float inv = (lsum > 0.f && MU != kNegInf) ? __builtin_amdgcn_exp2f(MU - M) / lsum : 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = lane + 64 * r;
@@ -724,20 +729,19 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 }
 
 template <int D>
-hipError_t launch_dim(const DecodeArgs &a, hipStream_t s) {
+hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch);
   const int G = a.plan.group;
   if constexpr (D == 128) {
-    if (a.plan.mfma) hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
+    if (a.plan.mfma) {
+      hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
   }
-  if (a.plan.mfma) {
-  } else if (G <= 8)
+  if (G <= 8)
     hipLaunchKernelGGL((decode_valu_kernel<D, 8>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((decode_valu_kernel<D, 16>), grid, dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((merge_kernel<D>), dim3(a.plan.group, a.n_kv_heads, a.batch), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -766,8 +770,17 @@ hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s) {
-  return d == 128 ? launch_dim<128>(a, s) : launch_dim<256>(a, s);
+hipError_t launch_decode_split(const DecodeArgs &a, int d, hipStream_t s) {
+  return d == 128 ? launch_split_dim<128>(a, s) : launch_split_dim<256>(a, s);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &a, int d, hipStream_t s) {
+  const dim3 grid(a.plan.group, a.n_kv_heads, a.batch);
+  if (d == 128)
+    hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((merge_kernel<256>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace tq

@@ -91,6 +91,23 @@ __device__ inline int quantize_code(const Codebook &cb, float y) {
   return idx;
 }
 
+// Page offsets are split as t = 64 b + 16 tau + 4 k + r (b: 64-token block;
+// tau, k, r = 0..3). The per-page N / G arrays hold token t at entry
+// 64 b + 16 k + 4 r + tau, so the 16 tokens with one (b, k) are adjacent.
+__host__ __device__ inline int side_entry(int t) {
+  return (t & ~63) | ((t & 12) << 2) | ((t & 3) << 2) | ((t >> 4) & 3);
+}
+
+// V code bits: bit j of the code of coordinate i = 16 (2 kp + h) + n of token
+// t is bit 8 r + 4 h + tau of u32 word b*6D + j*2D + (16 k + n)*(D/32) + kp.
+// One lane of the decode kernel (k, n) reads its D/32 words of a plane as one
+// contiguous run, and the words of one plane and block are contiguous.
+template <int D>
+__device__ inline int v_word(int t, int i, int j) {
+  return (t >> 6) * 6 * D + j * 2 * D + (16 * ((t >> 2) & 3) + (i & 15)) * (D / 32) + (i >> 5);
+}
+__device__ inline int v_bit(int t, int i) { return 8 * (t & 3) + 4 * ((i >> 4) & 1) + ((t >> 4) & 3); }
+
 __device__ inline uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;  // round to nearest even, overflow to inf
   return __builtin_bit_cast(uint16_t, h);

@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256) void encode_k_kernel(EncodeArgs a) {
     }
     if (lane < NWORD) reinterpret_cast<uint32_t *>(sec + (size_t)off * (D / 2))[lane] = w;
     if (lane == 0) {
-      reinterpret_cast<uint16_t *>(sec + KCODES)[off] = f32_to_f16_bits(nrm[v]);
-      reinterpret_cast<uint16_t *>(sec + KCODES + 2 * kPage)[off] = f32_to_f16_bits(gam[v]);
+      reinterpret_cast<uint16_t *>(sec + KCODES)[side_entry(off)] = f32_to_f16_bits(nrm[v]);
+      reinterpret_cast<uint16_t *>(sec + KCODES + 2 * kPage)[side_entry(off)] = f32_to_f16_bits(gam[v]);
     }
   }
 }
@@ -157,21 +157,20 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
   uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * VSEC;
   const int off = slot % kPage;
   uint32_t *rows = reinterpret_cast<uint32_t *>(sec);
-  // token u of a 32-token word sits at bit 8 (u % 4) + u / 4
-  const uint32_t bit = 1u << (8 * (off & 3) + ((off & 31) >> 2));
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = lane + 64 * r;
+    const uint32_t bit = 1u << v_bit(off, i);
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
-      uint32_t *w = rows + (size_t)(j * D + i) * (kPage / 32) + (off >> 5);
+      uint32_t *w = rows + v_word<D>(off, i, j);
       if ((idx[r] >> j) & 1)
         atomicOr(w, bit);
       else
         atomicAnd(w, ~bit);
     }
   }
-  if (lane == 0) reinterpret_cast<uint16_t *>(sec + VCODES)[off] = f32_to_f16_bits(n);
+  if (lane == 0) reinterpret_cast<uint16_t *>(sec + VCODES)[side_entry(off)] = f32_to_f16_bits(n);
 }
 
 template <int D>
@@ -200,9 +199,9 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
                       (((rec[4 * s + 2] >> e) & 1) << 2);
       v[r] = level_of(a.cb, idx);
     }
-    scale = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + KCODES)[off]);
+    scale = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + KCODES)[side_entry(off)]);
     if (a.with_qjl) {
-      const float G = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + KCODES + 2 * kPage)[off]);
+      const float G = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + KCODES + 2 * kPage)[side_entry(off)]);
       float t[R];
 #pragma unroll
       for (int r = 0; r < R; ++r) t[r] = 0.f;
@@ -223,14 +222,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
     const uint32_t *rows = reinterpret_cast<const uint32_t *>(sec);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int i = lane + 64 * r;
+      const int i = lane + 64 * r, bit = v_bit(off, i);
       int idx = 0;
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
-        idx |= ((rows[(size_t)(j * D + i) * (kPage / 32) + (off >> 5)] >> (8 * (off & 3) + ((off & 31) >> 2))) & 1) << j;
+      for (int j = 0; j < 3; ++j) idx |= ((rows[v_word<D>(off, i, j)] >> bit) & 1) << j;
       v[r] = level_of(a.cb, idx);
     }
-    scale = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + VCODES)[off]);
+    scale = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + VCODES)[side_entry(off)]);
   }
   fwht_wave<R>(v);
   scale *= rsqrt_dim<D>();

@@ -107,6 +107,7 @@ hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s);
 hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, int d, int which, hipStream_t s);
 hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s);
-hipError_t launch_decode(const DecodeArgs &a, int d, hipStream_t s);
+hipError_t launch_decode_split(const DecodeArgs &a, int d, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeArgs &a, int d, hipStream_t s);
 
 }  // namespace tq

@@ -23,7 +23,7 @@ TQ_PAGE_SIZE = 256
 TQ_MAX_GROUP = 16
 EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_encode_k",
            "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_prepared",
-           "tq_dequant", "tq_status_string")
+           "tq_attn_decode_split", "tq_attn_decode_merge", "tq_dequant", "tq_status_string")
 
 
 class TqError(RuntimeError):
@@ -63,9 +63,13 @@ def lib():
                                  C.POINTER(sz), vp]
     L.tq_attn_decode_prepared.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
                                           C.POINTER(sz), vp]
+    L.tq_attn_decode_split.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp,
+                                       C.POINTER(sz), vp]
+    L.tq_attn_decode_merge.argtypes = [vp, i32, i32, i32, i32, vp, vp, sz, vp]
     L.tq_dequant.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     for name in ("tq_build_codebook", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
-                 "tq_attn_decode", "tq_attn_decode_prepared", "tq_dequant"):
+                 "tq_attn_decode", "tq_attn_decode_prepared", "tq_attn_decode_split",
+                 "tq_attn_decode_merge", "tq_dequant"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -229,6 +233,30 @@ def tq_attn_decode_prepared(cache: Cache, prep, q_shape, block_table, seq_lens,
     size = C.c_size_t(ws.numel())
     st = L.tq_attn_decode_prepared(*args(ws.data_ptr()), C.byref(size), _stream(stream))
     _check(st, "tq_attn_decode_prepared")
+    return out
+
+
+def tq_attn_decode_split(cache: Cache, prep, q_shape, block_table, seq_lens, workspace,
+                         causal_tail: int = 0, scale=None, stream=None) -> None:
+    """Split-K pass only: partials land in `workspace` (uint8 device tensor)."""
+    B, n_q, Hq, d = q_shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    size = C.c_size_t(workspace.numel())
+    st = lib().tq_attn_decode_split(cache.ref, prep.data_ptr(), B, n_q, Hq, block_table.data_ptr(),
+                                    int(block_table.shape[1]), seq_lens.data_ptr(), int(causal_tail),
+                                    scale, workspace.data_ptr(), C.byref(size), _stream(stream))
+    _check(st, "tq_attn_decode_split")
+
+
+def tq_attn_decode_merge(cache: Cache, q_shape, max_pages: int, workspace, out=None, stream=None):
+    """Merge pass only: combines the partials in `workspace` into out [B][n_q][Hq][d]."""
+    import torch
+    B, n_q, Hq, d = q_shape
+    if out is None:
+        out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=workspace.device)
+    st = lib().tq_attn_decode_merge(cache.ref, B, n_q, Hq, int(max_pages), out.data_ptr(),
+                                    workspace.data_ptr(), int(workspace.numel()), _stream(stream))
+    _check(st, "tq_attn_decode_merge")
     return out
 
 

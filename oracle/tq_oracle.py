@@ -40,6 +40,7 @@ notes; the ones that shape arithmetic are restated where they are used:
 
 from __future__ import annotations
 
+import functools
 import math
 from dataclasses import dataclass
 
@@ -259,33 +260,43 @@ def encode(x, cb: Codebook, S=None) -> dict:
 
 # --------------------------------------------------------------------------
 # Packed page layout (frozen format of this library; not given by the pages)
+#   Offsets t within a page are split as t = 64 b + 16 tau + 4 k + r
+#   (b = 64-token block, tau, k, r = 0..3).
 #   K section of one (page, kv-head), P tokens:
 #     token t record (d/2 bytes) at t*d/2: for group s = 0..d/32-1 four
 #     little-endian u32 words [code bit0, code bit1, code bit2, QJL sign];
 #     bit e of a word belongs to coordinate 32 s + e;
-#     then N[P] fp16 at P*d/2, then G[P] fp16 at P*d/2 + 2P.
-#   V section of one (page, kv-head):
-#     for plane j = 0..2 and coordinate i: a row of P/32 little-endian u32 words
-#     at byte ((j*d + i) * P/8); word w covers tokens 32w .. 32w+31 and token
-#     32w + u sits at bit 8*(u mod 4) + u div 4 of it (bit j of that token's
-#     code for coordinate i); then N[P] fp16 at 3*d*P/8.
+#     then N[P] fp16 at P*d/2, then G[P] fp16 at P*d/2 + 2P, each array in
+#     side order: token t at entry 64 b + 16 k + 4 r + tau.
+#   V section of one (page, kv-head): code bits, then N[P] fp16 at 3*d*P/8 in
+#     side order. Code bits are little-endian u32 words; bit j of the code of
+#     coordinate i = 16 (2 kp + h) + n (h = 0..1, n = 0..15) of token t is bit
+#     8 r + 4 h + tau of word  b*(6 d) + j*(2 d) + (16 k + n)*(d/32) + kp.
 #   Pools are [n_pages][n_kv_heads][section bytes]; slot = page * P + offset.
 # --------------------------------------------------------------------------
-# storage bit p of a 32-token V word holds token u = 4 (p mod 8) + p div 8
-_V_TOKEN_OF_BIT = np.array([4 * (p % 8) + p // 8 for p in range(32)])
-_V_BIT_OF_TOKEN = np.argsort(_V_TOKEN_OF_BIT)
+def _split_offset(t):
+    t = np.asarray(t, dtype=np.int64)
+    return t // 64, (t % 64) // 16, (t % 16) // 4, t % 4        # b, tau, k, r
 
 
-def _v_to_storage(bits):
-    """[..., P] bits in token order -> [..., P] in storage order."""
-    lead, P = bits.shape[:-1], bits.shape[-1]
-    return bits.reshape(*lead, P // 32, 32)[..., _V_TOKEN_OF_BIT].reshape(*lead, P)
+def side_entry(t):
+    """Entry of offset t in the per-page N / G arrays."""
+    b, tau, k, r = _split_offset(t)
+    return 64 * b + 16 * k + 4 * r + tau
 
 
-def _v_from_storage(bits):
-    """[..., P] bits in storage order -> [..., P] in token order."""
-    lead, P = bits.shape[:-1], bits.shape[-1]
-    return bits.reshape(*lead, P // 32, 32)[..., _V_BIT_OF_TOKEN].reshape(*lead, P)
+@functools.lru_cache(maxsize=None)
+def _v_bit_table(d: int, P: int) -> np.ndarray:
+    """[3][d][P] -> index of that bit in the section's code bits (as a flat
+    little-endian bit string, bit 32 w + p = bit p of word w)."""
+    j = np.arange(3)[:, None, None]
+    i = np.arange(d)[None, :, None]
+    b, tau, k, r = _split_offset(np.arange(P)[None, None, :])
+    kk, n = i // 16, i % 16
+    kp, h = kk // 2, kk % 2
+    word = b * (6 * d) + j * (2 * d) + (16 * k + n) * (d // 32) + kp
+    bit = 8 * r + 4 * h + tau
+    return (32 * word + bit).astype(np.int64)
 
 
 def k_page_bytes(d: int, P: int) -> int:
@@ -311,7 +322,7 @@ def pack_k(pool: np.ndarray, slots, idx, sign, N, G, P: int) -> None:
     pool[(base + off[:, None] * (d // 2))[..., None] + np.arange(d // 2)] = rec
     nb = np.asarray(N, dtype=np.float16).reshape(n, H, 1).view(np.uint8)
     gb = np.asarray(G, dtype=np.float16).reshape(n, H, 1).view(np.uint8)
-    side = base + P * d // 2 + 2 * off[:, None]
+    side = base + P * d // 2 + 2 * side_entry(off)[:, None]
     pool[side[..., None] + np.arange(2)] = nb
     pool[(side + 2 * P)[..., None] + np.arange(2)] = gb
 
@@ -323,20 +334,19 @@ def pack_v(pool: np.ndarray, slots, idx, N, P: int) -> None:
     n, H, d = idx.shape
     vpb = v_page_bytes(d, P)
     cbytes = 3 * d * P // 8
+    tab = _v_bit_table(d, P)
     slots = np.asarray(slots, dtype=np.int64)
     page, off = slots // P, slots % P
     for pg in np.unique(page):
         sel = np.nonzero(page == pg)[0]
         for h in range(H):
             base = (int(pg) * H + h) * vpb
-            region = pool[base:base + cbytes].reshape(3, d, P // 8)
-            bits = _v_from_storage(np.unpackbits(region, axis=-1, bitorder="little"))  # [3][d][P]
+            bits = np.unpackbits(pool[base:base + cbytes], bitorder="little")
             for j in range(3):
-                bits[j][:, off[sel]] = ((idx[sel, h, :] >> j) & 1).T
-            pool[base:base + cbytes] = np.packbits(_v_to_storage(bits), axis=-1,
-                                                   bitorder="little").reshape(-1)
+                bits[tab[j][:, off[sel]]] = ((idx[sel, h, :] >> j) & 1).T
+            pool[base:base + cbytes] = np.packbits(bits, bitorder="little")
             nb = np.asarray(N, dtype=np.float16)[sel, h].view(np.uint8).reshape(-1, 2)
-            pos = base + cbytes + 2 * off[sel]
+            pos = base + cbytes + 2 * side_entry(off[sel])
             pool[pos[:, None] + np.arange(2)] = nb
 
 
@@ -351,7 +361,7 @@ def unpack_k(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
                          bitorder="little")                                # [n][H][S][4][32]
     bits = bits.transpose(0, 1, 3, 2, 4).reshape(len(slots), H, 4, d)
     idx = bits[:, :, 0] | (bits[:, :, 1] << 1) | (bits[:, :, 2] << 2)
-    side = base + P * d // 2 + 2 * off[:, None]
+    side = base + P * d // 2 + 2 * side_entry(off)[:, None]
     N = pool[side[..., None] + np.arange(2)].copy().view(np.float16)[..., 0]
     G = pool[(side + 2 * P)[..., None] + np.arange(2)].copy().view(np.float16)[..., 0]
     return {"idx": idx.astype(np.uint8), "sign": bits[:, :, 3].astype(bool), "N": N, "G": G}
@@ -361,6 +371,7 @@ def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
     """Read V records of `slots` for all heads: idx [n][H][d], N [n][H]."""
     vpb = v_page_bytes(d, P)
     cbytes = 3 * d * P // 8
+    tab = _v_bit_table(d, P)
     slots = np.asarray(slots, dtype=np.int64)
     page, off = slots // P, slots % P
     n = len(slots)
@@ -370,11 +381,10 @@ def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
         sel = np.nonzero(page == pg)[0]
         for h in range(H):
             base = (int(pg) * H + h) * vpb
-            bits = _v_from_storage(np.unpackbits(pool[base:base + cbytes].reshape(3, d, P // 8),
-                                                 axis=-1, bitorder="little"))  # [3][d][P]
-            sub = bits[:, :, off[sel]]                                     # [3][d][k]
+            bits = np.unpackbits(pool[base:base + cbytes], bitorder="little")
+            sub = bits[tab[:, :, off[sel]]]                                # [3][d][k]
             idx[sel, h, :] = (sub[0] | (sub[1] << 1) | (sub[2] << 2)).T
-            pos = base + cbytes + 2 * off[sel]
+            pos = base + cbytes + 2 * side_entry(off[sel])
             N[sel, h] = pool[pos[:, None] + np.arange(2)].copy().view(np.float16)[:, 0]
     return {"idx": idx, "N": N}
 
@@ -395,7 +405,7 @@ def gather_k(pool, block_table_row, L, kv_head, H, d, P):
     bits = np.unpackbits(rec.reshape(L, d // 32, 4, 4), axis=-1, bitorder="little")
     bits = bits.transpose(0, 2, 1, 3).reshape(L, 4, d)
     idx = bits[:, 0] | (bits[:, 1] << 1) | (bits[:, 2] << 2)
-    side = base + P * d // 2 + 2 * off
+    side = base + P * d // 2 + 2 * side_entry(off)
     N = pool[side[:, None] + np.arange(2)].copy().view(np.float16)[:, 0]
     G = pool[(side + 2 * P)[:, None] + np.arange(2)].copy().view(np.float16)[:, 0]
     return idx, bits[:, 3].astype(bool), N.astype(np.float64), G.astype(np.float64)
@@ -408,12 +418,12 @@ def gather_v(pool, block_table_row, L, kv_head, H, d, P):
     npg = (L + P - 1) // P
     pages = np.asarray(block_table_row, dtype=np.int64)[:npg]
     base = (pages * H + kv_head) * vpb
-    codes = pool[base[:, None] + np.arange(cbytes)].reshape(npg, 3, d, P // 8)
-    bits = _v_from_storage(np.unpackbits(codes, axis=-1, bitorder="little"))  # [pg][3][d][P]
+    codes = pool[base[:, None] + np.arange(cbytes)]                     # [pg][cbytes]
+    bits = np.unpackbits(codes, axis=-1, bitorder="little")[:, _v_bit_table(d, P)]  # [pg][3][d][P]
     idx = bits[:, 0] | (bits[:, 1] << 1) | (bits[:, 2] << 2)               # [pg][d][P]
     idx = idx.transpose(0, 2, 1).reshape(npg * P, d)[:L]
     t = np.arange(L, dtype=np.int64)
-    side = base[t // P] + cbytes + 2 * (t % P)
+    side = base[t // P] + cbytes + 2 * side_entry(t % P)
     N = pool[side[:, None] + np.arange(2)].copy().view(np.float16)[:, 0]
     return idx, N.astype(np.float64)
 

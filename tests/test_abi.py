@@ -141,3 +141,23 @@ def test_decode_validation_and_workspace(L):
                             None, None) == tq.TQ_EINVAL
     st, _ = _decode(L, dsc, ws=FAKE + 16, size=need)
     assert st == tq.TQ_EALIGN
+
+
+def test_split_and_merge_validation(L):
+    dsc = _desc(H=2)
+    r = C.byref(dsc)
+    sz = C.c_size_t(0)
+    assert L.tq_attn_decode_split(r, FAKE, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, None, C.byref(sz),
+                                  None) == tq.TQ_OK
+    need = sz.value
+    sz2 = C.c_size_t(0)
+    assert L.tq_attn_decode_prepared(r, FAKE, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE, None,
+                                     C.byref(sz2), None) == tq.TQ_OK
+    assert need == sz2.value
+    small = C.c_size_t(need - 256)
+    assert L.tq_attn_decode_split(r, FAKE, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE, C.byref(small),
+                                  None) == tq.TQ_EWORKSPACE
+    assert L.tq_attn_decode_merge(r, 2, 1, 8, 16, FAKE, FAKE, need - 256, None) == tq.TQ_EWORKSPACE
+    assert L.tq_attn_decode_merge(r, 2, 1, 8, 16, None, FAKE, need, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode_merge(r, 2, 1, 7, 16, FAKE, FAKE, need, None) == tq.TQ_EINVAL
+    assert L.tq_attn_decode_merge(r, 2, 1, 8, 16, FAKE + 4, FAKE, need, None) == tq.TQ_EALIGN

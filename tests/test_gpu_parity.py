@@ -173,8 +173,13 @@ def test_decode_parity(tq, case):
     # the prepared-query path gives the same bits
     prep = tq.tq_query_prepare(cache, qt)
     out3 = tq.tq_attn_decode_prepared(cache, prep, tuple(qt.shape), bt, sl, causal_tail=causal)
+    # the split pass and the merge as separate calls
+    ws = torch.empty(cache.workspace(0).numel(), dtype=torch.uint8, device="cuda")
+    tq.tq_attn_decode_split(cache, prep, tuple(qt.shape), bt, sl, ws, causal_tail=causal)
+    out4 = tq.tq_attn_decode_merge(cache, tuple(qt.shape), bt.shape[1], ws)
     torch.cuda.synchronize()
     assert torch.equal(out, out3)
+    assert torch.equal(out, out4)
 
 
 @pytest.mark.parametrize("d", [128, 256])

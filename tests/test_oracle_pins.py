@@ -241,8 +241,8 @@ def test_zero_vector():
 
 # ---------------------------------------------------------------- packed format
 def test_pack_layout_hand_fixture():
-    g = _golden("pack_layout_d32_p32.json")
-    d, P, slot = g["head_dim"], g["page_size"], g["slot"]
+    g = _golden("pack_layout_d32_p64.json")
+    d, P, slot = g["head_dim"], g["page_size"], g["k_slot"]
     assert O.k_page_bytes(d, P) == g["k_section_bytes"]
     assert O.v_page_bytes(d, P) == g["v_section_bytes"]
     i = np.arange(d)
@@ -255,13 +255,10 @@ def test_pack_layout_hand_fixture():
         want[int(off)] = int(hx, 16)
     assert np.array_equal(kp, want)
     vp = np.zeros(g["v_section_bytes"], np.uint8)
-    O.pack_v(vp, [slot], idx, np.array([[1.0]], np.float16), P)
+    idx3 = np.stack([idx[0], np.full((1, d), 7, np.uint8), np.full((1, d), 7, np.uint8)])
+    O.pack_v(vp, [1, 13, 37], idx3, np.array([[1.0], [2.0], [0.5]], np.float16), P)
     wantv = np.zeros_like(vp)
-    for j in range(3):
-        for c in range(d):
-            if ((c % 8) >> j) & 1:
-                wantv[4 * (32 * j + c) + 1] = 0x01
-    for off, hx in g["v_n_bytes"].items():
+    for off, hx in g["v_nonzero"].items():
         wantv[int(off)] = int(hx, 16)
     assert np.array_equal(vp, wantv)
 
@@ -298,7 +295,7 @@ def test_pack_unpack_roundtrip_and_isolation(d):
 
 
 # ---------------------------------------------------------------- attention
-def _small_cache(d=32, L=40, H=2, P=32, seed=0, nq=3, g=2, B=2):
+def _small_cache(d=32, L=150, H=2, P=64, seed=0, nq=3, g=2, B=2):
     rng = np.random.default_rng(seed)
     cb = O.codebook(d)
     S = O.qjl_matrix(d, 77).astype(np.float64)
