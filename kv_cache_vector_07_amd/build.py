@@ -28,6 +28,8 @@ COMMON = [
     "-I", INCLUDE, "-I", CSRC,
     # packed FP32 VALU forms stay off; ordinary float code is compiled unpacked
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results go straight to VGPRs (no AGPR copies before VALU use)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

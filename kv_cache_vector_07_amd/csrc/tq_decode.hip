@@ -37,6 +37,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
+constexpr float kFltMax = 3.402823466e38f;
 constexpr int kPartHead = 4;   // partial record: m, l, mU (log2 units), pad, then acc[d]
 
 // Weights of the odd-codebook bit planes: c[idx] = sum_j 2 a_j plane_j - c7 with
@@ -444,7 +445,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   }
   const float delta_u = wmax * 0x1p-30f;
 
-  float m_run = kNegInf, mu_run = kNegInf, l_lane = 0.f, us_lane = 0.f;
+  // running maxima start finite, so exp2 of a masked (-inf) score is 0 and no
+  // per-token guard is needed; a row with no visible token keeps l = 0
+  float m_run = -kFltMax, mu_run = -kFltMax, l_lane = 0.f, us_lane = 0.f;
   float facc[NB];
 #pragma unroll
   for (int k = 0; k < NB; ++k) facc[k] = 0.f;
@@ -535,16 +538,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // ---- online softmax of this wave (log2 units; scores, and scores + log2 N^V for V)
     const float m_new = fmaxf(m_run, rowmax16(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
     const float mu_new = fmaxf(mu_run, rowmax16(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
-    const float alpha = m_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float alphaU = mu_run == kNegInf ? 0.f : __builtin_amdgcn_exp2f(mu_run - mu_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    const float alphaU = __builtin_amdgcn_exp2f(mu_run - mu_new);
     m_run = m_new;
     mu_run = mu_new;
     float ps = 0.f, us = 0.f;
     v4i A[4];   // per plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      ps += sc[tau] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sc[tau] - m_new);
-      const float U = sv[tau] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(sv[tau] - mu_new);
+      ps += __builtin_amdgcn_exp2f(sc[tau] - m_new);
+      const float U = __builtin_amdgcn_exp2f(sv[tau] - mu_new);
       us += U;
       const float Ut = __builtin_amdgcn_ldexpf(U, -tau);
 #pragma unroll
@@ -632,7 +635,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     for (int w = 0; w < 4; ++w) {
       const bool live = s_wm[w][1][qq] > 0.f;
       lsum += live ? s_wm[w][1][qq] * __builtin_amdgcn_exp2f(s_wm[w][0][qq] - M) : 0.f;
-      fw[w] = (live && s_wm[w][2][qq] != kNegInf) ? __builtin_amdgcn_exp2f(s_wm[w][2][qq] - MU) : 0.f;
+      fw[w] = live ? __builtin_amdgcn_exp2f(s_wm[w][2][qq] - MU) : 0.f;
     }
     float *pr = a.partials + (pbase + qq) * (D + kPartHead);
     if (lane == 0) {
