@@ -52,123 +52,132 @@ __device__ inline void plane_weights(const Codebook &cb, float (&w)[4]) {
 }
 
 // ------------------------------------------------------------------ prepare
-// One workgroup per (sequence, KV head): rotate and project its query rows,
-// then (MFMA path) write the packed int8 scoring operand of the group.
+// One workgroup per query row qq of a (sequence, KV head) group: rotate the
+// row, project it with S, write q~ and p, and on the MFMA path pack this row's
+// four limb columns of the int8 scoring operand. The four waves split the m
+// rows of S, and every S load of a chunk is issued before the row is rotated.
 template <int D, int DT>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   constexpr int R = D / 64;
   constexpr int NMU = 10 * (D / 128);
-  __shared__ float s_v[kMfmaMaxGroup][2][D];
-  __shared__ float s_const[kMfmaMaxGroup][4];
-  __shared__ float s_inv[kMfmaMaxGroup][2];
-  __shared__ float s_q[4][D];
-  const int kvh = blockIdx.x, b = blockIdx.y;
+  constexpr int RPW = D / 4;         // rows of S per wave
+  constexpr int LPR = 64 / RPW;      // lanes per row of S: 2 (d = 128) or 1 (d = 256)
+  constexpr int EPL = D / LPR;       // elements of a row per lane
+  constexpr int CH = 16;             // float4 loads in flight per lane
+  constexpr int NCH = EPL / 4 / CH;  // chunks: 1 (d = 128) or 4 (d = 256)
+  __shared__ float s_q[D], s_p[D];
+  const int qq = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = a.n_q_heads / a.n_kv_heads, G = g * a.n_q;
-  const bool pack = a.packed != nullptr;
-
-  for (int qq = wave; qq < G; qq += 4) {
-    const int t = qq / g, hh = qq % g;
-    const size_t row = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
-    float v[R];
+  const int t = qq / g, hh = qq % g;
+  const size_t row = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
+  const int srow = wave * RPW + lane / LPR, part = lane % LPR;
+  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl) + (size_t)srow * (D / 4) + part * (EPL / 4);
+  float4 sv[CH];
 #pragma unroll
-    for (int r = 0; r < R; ++r) v[r] = load_elem<DT>(a.q, row * D + lane + 64 * r);
-    fwht_wave<R>(v);
-    float *dst = a.prep + row * 2 * D;
+  for (int k = 0; k < CH; ++k) sv[k] = S4[k];
+
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = load_elem<DT>(a.q, row * D + lane + 64 * r);
+  fwht_wave<R>(v);
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] *= rsqrt_dim<D>();
+  float *dst = a.prep + row * 2 * D;
+  if (wave == 0) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      v[r] *= rsqrt_dim<D>();
+      s_q[lane + 64 * r] = v[r];
       dst[lane + 64 * r] = v[r];
-      s_q[wave][lane + 64 * r] = v[r];
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    // p_l = sum_i S[l][i] q~_i for rows l = lane + 64 r
-    float p[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) p[r] = 0.f;
-    const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
-    const float4 *q4 = reinterpret_cast<const float4 *>(s_q[wave]);
-#pragma unroll 16
-    for (int i4 = 0; i4 < D / 4; ++i4) {
-      const float4 qv = q4[i4];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float4 s = S4[(size_t)(lane + 64 * r) * (D / 4) + i4];
-        p[r] = fmaf(s.x, qv.x, p[r]);
-        p[r] = fmaf(s.y, qv.y, p[r]);
-        p[r] = fmaf(s.z, qv.z, p[r]);
-        p[r] = fmaf(s.w, qv.w, p[r]);
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r) dst[D + lane + 64 * r] = p[r];
-    if (pack) {
-      float w[4];
-      plane_weights(a.cb, w);
-      const float wmax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
-      float mq = 0.f, mp = 0.f, sq = 0.f, sp = 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        s_v[qq][0][lane + 64 * r] = v[r];
-        s_v[qq][1][lane + 64 * r] = p[r];
-        mq = fmaxf(mq, fabsf(v[r]));
-        mp = fmaxf(mp, fabsf(p[r]));
-        sq += v[r];
-        sp += p[r];
-      }
-      mq = wave_max(mq);
-      mp = wave_max(mp);
-      sq = wave_sum(sq);
-      sp = wave_sum(sp);
-      if (lane == 0) {
-        // integer scales: |value / delta| < 2^30 so four balanced base-256 limbs hold it
-        s_const[qq][0] = mq > 0.f ? wmax * mq * 0x1p-30f : 1.f;
-        s_const[qq][1] = mp > 0.f ? 2.f * mp * 0x1p-30f : 1.f;
-        s_const[qq][2] = sq;
-        s_const[qq][3] = sp;
-        s_inv[qq][0] = 1.0f / s_const[qq][0];
-        s_inv[qq][1] = 1.0f / s_const[qq][1];
-      }
     }
   }
-  if (!pack) return;
   __syncthreads();
 
-  // Operand byte (mu, lane = 16 kg + n, 4 r' + bb): row n = 4 q + limb, MFMA mu of a
-  // 16-token tile: group s = kg + 4 (mu / 10); mu % 10 < 8 -> code plane j = (mu%10)/2,
-  // else the sign plane; half h = mu % 2; coordinate 32 s + 8 bb + 4 h + r' with
-  // key-side byte value 2^(4h + r') (-128 for bit 7).
+  // p_l = sum_i S[l][i] q~_i
+  const float4 *q4 = reinterpret_cast<const float4 *>(s_q) + part * (EPL / 4);
+  float acc = 0.f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c > 0) {
+#pragma unroll
+      for (int k = 0; k < CH; ++k) sv[k] = S4[c * CH + k];
+    }
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float4 qv = q4[c * CH + k];
+      acc = fmaf(sv[k].x, qv.x, acc);
+      acc = fmaf(sv[k].y, qv.y, acc);
+      acc = fmaf(sv[k].z, qv.z, acc);
+      acc = fmaf(sv[k].w, qv.w, acc);
+    }
+  }
+  if (LPR == 2) acc += __shfl_xor(acc, 1, 64);
+  if (part == 0) {
+    s_p[srow] = acc;
+    dst[D + srow] = acc;
+  }
+  if (a.packed == nullptr) return;
+  __syncthreads();
+
+  // scales of this row (every wave computes them): |value / delta| < 2^30, so
+  // four balanced base-256 limbs hold each scaled value
   float w[4];
   plane_weights(a.cb, w);
+  const float wmax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
+  float mq = 0.f, mp = 0.f, sq = 0.f, sp = 0.f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float x = s_q[lane + 64 * r], y = s_p[lane + 64 * r];
+    mq = fmaxf(mq, fabsf(x));
+    mp = fmaxf(mp, fabsf(y));
+    sq += x;
+    sp += y;
+  }
+  mq = wave_max(mq);
+  mp = wave_max(mp);
+  sq = wave_sum(sq);
+  sp = wave_sum(sp);
+  const float d1 = mq > 0.f ? wmax * mq * 0x1p-30f : 1.f;
+  const float d2 = mp > 0.f ? 2.f * mp * 0x1p-30f : 1.f;
+  const float i1 = 1.0f / d1, i2 = 1.0f / d2;
+
+  // Operand byte (mu, lane = 16 kg + n, 4 r' + bb): column n = 4 q + limb, MFMA mu of a
+  // 16-token tile: group s = kg + 4 (mu / 10); mu % 10 < 8 -> code plane j = (mu%10)/2,
+  // else the sign plane; half h = mu % 2; coordinate 32 s + 8 bb + 4 h + r' with
+  // key-side byte value 2^(4h + r') (-128 for bit 7). This row writes columns 4 qq .. 4 qq + 3;
+  // row 0 also clears the columns of rows G .. 3.
   uint8_t *grp = a.packed + ((size_t)b * a.n_kv_heads + kvh) * packed_group_bytes(D);
-  for (int e = threadIdx.x; e < NMU * 64 * 4; e += 256) {
-    const int mu = e / 256, ln = (e / 4) % 64, rr = e % 4;
-    const int n = ln & 15, kg = ln >> 4, q = n >> 2, limb = n & 3;
+  const int ncol = (qq == 0) ? 4 * (kMfmaMaxGroup - G) + 4 : 4;
+  for (int e = threadIdx.x; e < NMU * 4 * 4 * ncol; e += 256) {
+    const int rr = e & 3, kg = (e >> 2) & 3, c = (e >> 4) % ncol, mu = (e >> 4) / ncol;
+    const int n = c < 4 ? 4 * qq + c : 4 * G + (c - 4);   // column; c >= 4: an unused row
+    const int limb = n & 3;
     const int s = kg + 4 * (mu / 10), m10 = mu % 10, h = m10 & 1;
-    uint32_t word = 0x80808080u;   // all-zero limbs
-    if (q < G) {
-      // value / (delta * 2^rr) as an integer X; limb bytes of X + 0x80808080
+    uint32_t word = 0;
+    if (c < 4) {
+      // value / (delta * key byte value) as an integer X; limb bytes of X + 0x80808080
       // are the digits of X in base 256 offset by 128 (X = sum (byte_l - 128) 256^l)
-      const int kb = 4 * h + rr;   // key byte value 2^kb, the top bit reads as -128
+      const int kb = 4 * h + rr;
       const float vkey = kb == 7 ? -128.f : (float)(1 << kb);
-      const float f = (m10 < 8 ? w[m10 >> 1] * s_inv[q][0] : 2.f * s_inv[q][1]) / vkey;
-      const float *src = s_v[q][m10 < 8 ? 0 : 1];
-      word = 0;
+      const float f = (m10 < 8 ? w[m10 >> 1] * i1 : 2.f * i2) / vkey;
+      const float *src = m10 < 8 ? s_q : s_p;
+      uint32_t bytes = 0;
 #pragma unroll
       for (int bb = 0; bb < 4; ++bb) {
         const int X = (int)rintf(src[32 * s + 8 * bb + 4 * h + rr] * f);
         const uint32_t byte = (((uint32_t)X + 0x80808080u) >> (8 * limb)) & 0xFFu;
-        word |= byte << (8 * bb);
+        bytes |= byte << (8 * bb);
       }
+      word = bytes ^ 0x80808080u;
     }
-    reinterpret_cast<uint32_t *>(grp)[(size_t)mu * 256 + ln * 4 + rr] = word ^ 0x80808080u;
+    reinterpret_cast<uint32_t *>(grp)[(size_t)mu * 256 + (16 * kg + n) * 4 + rr] = word;
   }
-  if (threadIdx.x < kMfmaMaxGroup * 4) {
-    const int q = threadIdx.x >> 2;
-    reinterpret_cast<float *>(grp + (size_t)NMU * 1024)[threadIdx.x] =
-        q < G ? s_const[q][threadIdx.x & 3] : 0.f;
+  float *rc = reinterpret_cast<float *>(grp + (size_t)NMU * 1024);
+  if (threadIdx.x < 4) {
+    const float cv[4] = {d1, d2, sq, sp};
+    rc[4 * qq + threadIdx.x] = cv[threadIdx.x];
+  } else if (qq == 0 && threadIdx.x < 4 * kMfmaMaxGroup && threadIdx.x >= 4 * G) {
+    rc[threadIdx.x] = 0.f;
   }
 }
 
@@ -424,8 +433,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int L = a.seq_lens[b];
 
   const uint8_t *grp = a.packed + ((size_t)b * H + kvh) * packed_group_bytes(D);
-  // the packed query operand is shared by the four waves: keep it in LDS
-  for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
   const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * 1024)[q];
   const float lsc1 = rc.x * (float)(1 << (8 * lam));
   const float lsc2 = rc.y * (float)(1 << (8 * lam)) * qjl_kappa<D>();
@@ -458,7 +465,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int blk0 = 64 * wave;
   // pages whose block of this wave holds no token are skipped (only the last can)
   if (pg1 > pg0 && blk0 >= L - (pg1 - 1) * kPage) --pg1;
-  __syncthreads();   // s_qop
 
   auto load_block = [&](MfmaBlock &d, int pg) {
     const int phys = a.block_table[(size_t)b * a.max_pages + pg];
@@ -594,8 +600,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
+  // the first block's loads go out before the query operand is staged, so the
+  // two fetches overlap
   MfmaBlock d0, d1;
   if (pg0 < pg1) load_block(d0, pg0);
+  // the packed query operand is shared by the four waves: keep it in LDS
+  for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
+  __syncthreads();
   for (int pg = pg0; pg < pg1; pg += 2) {
     if (pg + 1 < pg1) load_block(d1, pg + 1);
     process(d0, pg);
@@ -758,7 +769,7 @@ size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_head
 }
 
 hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
-  const dim3 grid(a.n_kv_heads, a.batch);
+  const dim3 grid(a.n_q * (a.n_q_heads / a.n_kv_heads), a.n_kv_heads, a.batch);
   if (d == 128) {
     if (a.dtype == TQ_F32)
       hipLaunchKernelGGL((prepare_kernel<128, TQ_F32>), grid, dim3(256), 0, s, a);
