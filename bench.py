@@ -138,22 +138,9 @@ def main():
     table = torch.from_numpy(table_np).to(dev)
     seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
     stream = torch.cuda.current_stream()
-    enc_k_ms = enc_v_ms = 0.0
-    n_vec = 0
-
-    def encode_call(k, v, slots):
-        nonlocal enc_k_ms, enc_v_ms, n_vec
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        e0.record()
-        tq.tq_encode_k(base, k, slots)
-        e1.record()
-        tq.tq_encode_v(base, v, slots)
-        e2.record()
-        e2.synchronize()
-        enc_k_ms += e0.elapsed_time(e1)
-        enc_v_ms += e1.elapsed_time(e2)
-        n_vec += slots.numel() * H
-
+    # every chunk's inputs are staged on the device first, so the timed region
+    # holds only back-to-back encode launches (all K calls, then all V calls)
+    calls = []
     if w.prefill_chunk:
         # chunked prefill: one call per chunk position covers every sequence
         CH = w.prefill_chunk
@@ -162,7 +149,7 @@ def main():
             slots = torch.cat([(table[b, t // 256] * 256 + t % 256) for b in range(B)]).to(torch.int32)
             k = torch.from_numpy(np.concatenate([I.kv_tokens(w, "k", b, t0, t0 + CH) for b in range(B)])).to(dev, tdt)
             v = torch.from_numpy(np.concatenate([I.kv_tokens(w, "v", b, t0, t0 + CH) for b in range(B)])).to(dev, tdt)
-            encode_call(k, v, slots)
+            calls.append((k, v, slots))
     else:
         chunk = 32768
         for b in range(B):
@@ -173,7 +160,24 @@ def main():
                 v = torch.from_numpy(I.kv_tokens(w, "v", b, t0, t1)).to(dev, tdt)
                 t = torch.arange(t0, t1, device=dev)
                 slots = (table[b, t // 256] * 256 + t % 256).to(torch.int32)
-                encode_call(k, v, slots)
+                calls.append((k, v, slots))
+    n_vec = sum(c[2].numel() for c in calls) * H
+    # one untimed call first (encoding is idempotent): the first launch of a
+    # kernel also loads its code object
+    tq.tq_encode_k(base, *calls[0][0::2])
+    tq.tq_encode_v(base, *calls[0][1:])
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    torch.cuda.synchronize()
+    e0.record()
+    for k, v, slots in calls:
+        tq.tq_encode_k(base, k, slots)
+    e1.record()
+    for k, v, slots in calls:
+        tq.tq_encode_v(base, v, slots)
+    e2.record()
+    e2.synchronize()
+    enc_k_ms, enc_v_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
+    del calls
     log(f"[bench] cache encoded: {n_vec} K and V vectors")
     copies = [base]
     for _ in range(R - 1):

@@ -39,138 +39,234 @@ __device__ inline float encode_front(const void *x, size_t base, const Codebook 
   return n;
 }
 
-// VPW K vectors per wave share each load of S in the S r product: 4 for bulk
-// encodes, 1 for short appends (where latency, not S traffic, dominates).
-template <int D, int DT, int kKVecPerWave>
+// K encode: VPW vectors per wave (16 for bulk encodes, 1 for short appends
+// where latency rules). Each wave runs steps 1-4 on its vectors (codes by
+// ballot, residual into LDS); the QJL product Z = R S^T over the workgroup's
+// residuals then runs on fp32 MFMA (16x16x4), with S read from L2 once per
+// workgroup; signs come back by ballot. Rows of R past the last vector are
+// zero and their records are not written.
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+template <int D, int DT, int VPW>
 __global__ __launch_bounds__(256) void encode_k_kernel(EncodeArgs a) {
   constexpr int R = D / 64;
   constexpr int NWORD = D / 8;              // u32 words per K record
+  constexpr int VB = kWaves * VPW;          // vectors per workgroup
+  constexpr int VT = (VB + 15) / 16;        // 16-vector MFMA tiles
+  constexpr int RT = D / 16 / kWaves;       // 16-row tiles of S per wave: 2 or 4
   constexpr size_t KSEC = (size_t)kPage * D / 2 + 4 * kPage;
   constexpr size_t KCODES = (size_t)kPage * D / 2;
-  __shared__ float4 rbuf[kWaves][kKVecPerWave][D / 4];
+  __shared__ float4 s_r[16 * VT][D / 4];    // residuals
+  __shared__ uint64_t s_code[VB][3][R];     // code bit planes
+  __shared__ uint16_t s_sign[VB][D / 16];   // sign bits, 16 rows of S per entry
+  __shared__ float s_ng[VB][2];             // N, G
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
   const long total = (long)a.n_tokens * a.n_heads;
-  const long v0 = ((long)blockIdx.x * kWaves + wave) * kKVecPerWave;
+  const long v0 = (long)blockIdx.x * VB;
+  const int nv = (int)min((long)VB, total - v0);
 
-  float nrm[kKVecPerWave], gam[kKVecPerWave];
-  uint64_t code[kKVecPerWave][R][3];
+  // S rows of this wave's tiles: the loads do not depend on the data, so for
+  // d = 128 they are all issued before the encode starts
+  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
+  constexpr bool kHoist = D == 128;
+  float4 sreg[kHoist ? RT * (D / 16) : 1];
+  if constexpr (kHoist) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        sreg[t * (D / 16) + c] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
+  }
 
+  for (int u = wave; u < 16 * VT; u += kWaves) {
+    float4 *rrow = s_r[u];
+    if (u >= nv) {
+      for (int e = lane; e < D / 4; e += 64) rrow[e] = make_float4(0.f, 0.f, 0.f, 0.f);
+      continue;
+    }
+    float y[R];
+    int idx[R];
+    const float n = encode_front<D, DT>(a.x, (size_t)(v0 + u) * D, a.cb, y, idx);
+    float rr = 0.f;
 #pragma unroll
-  for (int v = 0; v < kKVecPerWave; ++v) {
-    const long vec = v0 + v;
-    float r[R];
-    if (vec < total) {
-      int idx[R];
-      nrm[v] = encode_front<D, DT>(a.x, (size_t)vec * D, a.cb, r, idx);
-      float rr = 0.f;
+    for (int k = 0; k < R; ++k) {
+      y[k] -= level_of(a.cb, idx[k]);
+      rr += y[k] * y[k];
+      reinterpret_cast<float *>(rrow)[lane + 64 * k] = y[k];
 #pragma unroll
-      for (int k = 0; k < R; ++k) {
-        r[k] -= level_of(a.cb, idx[k]);
-        rr += r[k] * r[k];
-#pragma unroll
-        for (int j = 0; j < 3; ++j) code[v][k][j] = __ballot((idx[k] >> j) & 1);
-      }
-      gam[v] = sqrtf(wave_sum(rr));
-    } else {
-      nrm[v] = gam[v] = 0.f;
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        r[k] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 3; ++j) code[v][k][j] = 0;
+      for (int j = 0; j < 3; ++j) {
+        const uint64_t m = __ballot((idx[k] >> j) & 1);
+        if (lane == 0) s_code[u][j][k] = m;
       }
     }
-    float *rb = reinterpret_cast<float *>(rbuf[wave][v]);
-#pragma unroll
-    for (int k = 0; k < R; ++k) rb[lane + 64 * k] = r[k];
+    const float gm = sqrtf(wave_sum(rr));
+    if (lane == 0) {
+      s_ng[u][0] = n;
+      s_ng[u][1] = gm;
+    }
   }
   __syncthreads();
 
-  // z_l = sum_i S[l][i] r_i for rows l = lane + 64 k of each of the wave's vectors.
-  float z[kKVecPerWave][R];
+  // Z tile (vector tile vt, row tile rt) = sum over i of R[16 vt + .][i] S[16 rt + .][i].
+  // MFMA m of a 16-wide i step uses i = i0 + 4 kq + m in lane group kq, for A and B alike.
+  v4f acc[VT][RT];
 #pragma unroll
-  for (int v = 0; v < kKVecPerWave; ++v)
+  for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-    for (int k = 0; k < R; ++k) z[v][k] = 0.f;
-  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
-#pragma unroll 8
-  for (int i4 = 0; i4 < D / 4; ++i4) {
-    float4 s[R];
+    for (int t = 0; t < RT; ++t) acc[vt][t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < R; ++k) s[k] = S4[(size_t)(lane + 64 * k) * (D / 4) + i4];
+  for (int c = 0; c < D / 16; ++c) {
+    float4 bv[RT], av[VT];
 #pragma unroll
-    for (int v = 0; v < kKVecPerWave; ++v) {
-      const float4 rv = rbuf[wave][v][i4];
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        z[v][k] = fmaf(s[k].x, rv.x, z[v][k]);
-        z[v][k] = fmaf(s[k].y, rv.y, z[v][k]);
-        z[v][k] = fmaf(s[k].z, rv.z, z[v][k]);
-        z[v][k] = fmaf(s[k].w, rv.w, z[v][k]);
-      }
+    for (int t = 0; t < RT; ++t) {
+      if constexpr (kHoist)
+        bv[t] = sreg[t * (D / 16) + c];
+      else
+        bv[t] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
     }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt) av[vt] = s_r[16 * vt + l16][4 * c + kq];
+    // independent tiles between the dependent steps of one accumulator
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+          acc[vt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[vt][m], bv[t][m], acc[vt][t], 0, 0, 0);
   }
+  // lane (l16, kq), register r of a tile: vector 16 vt + 4 kq + r, row 16 rt + l16
+#pragma unroll
+  for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint64_t m = __ballot(acc[vt][t][r] >= 0.f);
+        const int u = 16 * vt + 4 * kq + r;
+        if (l16 == 0 && u < VB) s_sign[u][wave * RT + t] = (uint16_t)(m >> (16 * kq));
+      }
+  __syncthreads();
 
-#pragma unroll
-  for (int v = 0; v < kKVecPerWave; ++v) {
-    const long vec = v0 + v;
-    uint64_t sgn[R];
-#pragma unroll
-    for (int k = 0; k < R; ++k) sgn[k] = __ballot(z[v][k] >= 0.f);
-    if (vec >= total) continue;
+  // records: wave w writes vectors w, w + 4, ...
+  for (int u = wave; u < nv; u += kWaves) {
+    const long vec = v0 + u;
     const long tok = vec / a.n_heads;
     const int head = (int)(vec % a.n_heads);
     const int slot = a.slots[tok];
     uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * KSEC;
     const int off = slot % kPage;
-    uint32_t w = 0;
-#pragma unroll
-    for (int kk = 0; kk < NWORD; ++kk) {
-      const int s = kk >> 2, j = kk & 3;
-      const uint64_t m = j < 3 ? code[v][s >> 1][j] : sgn[s >> 1];
-      const uint32_t word = (s & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
-      if (lane == kk) w = word;
+    if (lane < NWORD) {
+      const int s = lane >> 2, j = lane & 3;
+      uint32_t w;
+      if (j < 3) {
+        const uint64_t m = s_code[u][j][s >> 1];
+        w = (s & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
+      } else {
+        w = (uint32_t)s_sign[u][2 * s] | ((uint32_t)s_sign[u][2 * s + 1] << 16);
+      }
+      reinterpret_cast<uint32_t *>(sec + (size_t)off * (D / 2))[lane] = w;
     }
-    if (lane < NWORD) reinterpret_cast<uint32_t *>(sec + (size_t)off * (D / 2))[lane] = w;
     if (lane == 0) {
-      reinterpret_cast<uint16_t *>(sec + KCODES)[side_entry(off)] = f32_to_f16_bits(nrm[v]);
-      reinterpret_cast<uint16_t *>(sec + KCODES + 2 * kPage)[side_entry(off)] = f32_to_f16_bits(gam[v]);
+      reinterpret_cast<uint16_t *>(sec + KCODES)[side_entry(off)] = f32_to_f16_bits(s_ng[u][0]);
+      reinterpret_cast<uint16_t *>(sec + KCODES + 2 * kPage)[side_entry(off)] = f32_to_f16_bits(s_ng[u][1]);
     }
   }
 }
 
-template <int D, int DT>
+// V encode: 64 tokens of one KV head per workgroup. Codes go to LDS by ballot;
+// when the 64 slots are one whole aligned 64-token block of a page, the block's
+// words are assembled and stored whole (coalesced, no atomics). Otherwise each
+// token's bits are set one by one with atomics, which leaves the neighbours in
+// the same words intact.
+template <int D, int DT, int VPW>
 __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
   constexpr int R = D / 64;
+  constexpr int VB = kWaves * VPW;   // tokens per workgroup: 64 (whole blocks possible) or 4
   constexpr size_t VSEC = (size_t)3 * D * kPage / 8 + 2 * kPage;
   constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
+  __shared__ uint64_t s_code[VB][3][R];
+  __shared__ float s_n[VB];
+  __shared__ int s_whole;
+
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const long vec = (long)blockIdx.x * kWaves + wave;
-  if (vec >= (long)a.n_tokens * a.n_heads) return;
-  float y[R];
-  int idx[R];
-  const float n = encode_front<D, DT>(a.x, (size_t)vec * D, a.cb, y, idx);
-  const long tok = vec / a.n_heads;
-  const int head = (int)(vec % a.n_heads);
-  const int slot = a.slots[tok];
-  uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * VSEC;
-  const int off = slot % kPage;
-  uint32_t *rows = reinterpret_cast<uint32_t *>(sec);
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int i = lane + 64 * r;
-    const uint32_t bit = 1u << v_bit(off, i);
-#pragma unroll
-    for (int j = 0; j < 3; ++j) {
-      uint32_t *w = rows + v_word<D>(off, i, j);
-      if ((idx[r] >> j) & 1)
-        atomicOr(w, bit);
-      else
-        atomicAnd(w, ~bit);
-    }
+  const int head = blockIdx.y;
+  const int t0 = blockIdx.x * VB;
+  const int nt = min(VB, a.n_tokens - t0);
+  if (threadIdx.x == 0) {
+    const int s0 = a.slots[t0];
+    s_whole = (VB == 64 && nt == VB && (s0 & 63) == 0);
   }
-  if (lane == 0) reinterpret_cast<uint16_t *>(sec + VCODES)[side_entry(off)] = f32_to_f16_bits(n);
+  __syncthreads();
+  if (threadIdx.x < VB && threadIdx.x < nt && a.slots[t0 + threadIdx.x] != a.slots[t0] + threadIdx.x)
+    s_whole = 0;   // benign race: every writer stores 0
+
+  for (int u = wave; u < nt; u += kWaves) {
+    float y[R];
+    int idx[R];
+    const float n = encode_front<D, DT>(a.x, ((size_t)(t0 + u) * a.n_heads + head) * D, a.cb, y, idx);
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        const uint64_t m = __ballot((idx[k] >> j) & 1);
+        if (lane == 0) s_code[u][j][k] = m;
+      }
+    if (lane == 0) s_n[u] = n;
+  }
+  __syncthreads();
+
+  if (VB == 64 && s_whole) {
+    const int s0 = a.slots[t0];
+    uint8_t *sec = a.pool + ((size_t)(s0 / kPage) * a.n_heads + head) * VSEC;
+    const int bofs = s0 % kPage;   // offset of the block in the page (a multiple of 64)
+    uint32_t *words = reinterpret_cast<uint32_t *>(sec) + (bofs >> 6) * 6 * D;
+    // word e = j*2D + (16 k + n)*(D/32) + kp; bit 8 r + 4 h + tau <- token 16 tau + 4 k + r,
+    // coordinate 32 kp + 16 h + n (both coordinates in the same 64-bit ballot)
+    for (int e = threadIdx.x; e < 6 * D; e += 256) {
+      const int j = e / (2 * D), rem = e % (2 * D);
+      const int c = rem / (D / 32), kp = rem % (D / 32);
+      const int k = c >> 4, n = c & 15;
+      const int i0 = 32 * kp + n;
+      const int sh = i0 & 63;
+      uint32_t w = 0;
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint64_t m = s_code[16 * tau + 4 * k + r][j][i0 >> 6];
+          w |= (uint32_t)((m >> sh) & 1) << (8 * r + tau);
+          w |= (uint32_t)((m >> (sh + 16)) & 1) << (8 * r + 4 + tau);
+        }
+      words[e] = w;
+    }
+    if (threadIdx.x < VB)
+      reinterpret_cast<uint16_t *>(sec + VCODES)[side_entry(bofs + threadIdx.x)] = f32_to_f16_bits(s_n[threadIdx.x]);
+    return;
+  }
+
+  for (int u = wave; u < nt; u += kWaves) {
+    const int slot = a.slots[t0 + u];
+    uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * VSEC;
+    const int off = slot % kPage;
+    uint32_t *rows = reinterpret_cast<uint32_t *>(sec);
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      const int i = lane + 64 * k;
+      const uint32_t bit = 1u << v_bit(off, i);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        uint32_t *w = rows + v_word<D>(off, i, j);
+        if ((s_code[u][j][k] >> lane) & 1)
+          atomicOr(w, bit);
+        else
+          atomicAnd(w, ~bit);
+      }
+    }
+    if (lane == 0) reinterpret_cast<uint16_t *>(sec + VCODES)[side_entry(off)] = f32_to_f16_bits(s_n[u]);
+  }
 }
 
 template <int D>
@@ -249,6 +345,8 @@ hipError_t by_dim_dtype(int d, int dtype, F &&f) {
 
 }  // namespace
 
+// Bulk calls use 16 vectors per wave; short appends (below 4096 vectors) one,
+// so that the work spreads over more workgroups.
 hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
   const long total = (long)a.n_tokens * a.n_heads;
   return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
@@ -256,9 +354,8 @@ hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
       const dim3 grid((unsigned)((total + kWaves - 1) / kWaves));
       hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 1>), grid, dim3(256), 0, s, a);
     } else {
-      const long per_block = kWaves * 4;
-      const dim3 grid((unsigned)((total + per_block - 1) / per_block));
-      hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 4>), grid, dim3(256), 0, s, a);
+      const dim3 grid((unsigned)((total + 63) / 64));
+      hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 16>), grid, dim3(256), 0, s, a);
     }
     return hipGetLastError();
   });
@@ -266,9 +363,14 @@ hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
 
 hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s) {
   const long total = (long)a.n_tokens * a.n_heads;
-  const dim3 grid((unsigned)((total + kWaves - 1) / kWaves));
   return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
-    hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value>), grid, dim3(256), 0, s, a);
+    if (total < 4096) {
+      const dim3 grid((unsigned)((a.n_tokens + kWaves - 1) / kWaves), (unsigned)a.n_heads);
+      hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 1>), grid, dim3(256), 0, s, a);
+    } else {
+      const dim3 grid((unsigned)((a.n_tokens + 63) / 64), (unsigned)a.n_heads);
+      hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 16>), grid, dim3(256), 0, s, a);
+    }
     return hipGetLastError();
   });
 }
