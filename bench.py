@@ -273,7 +273,7 @@ def main():
 
     dec_ms = timed(dec, args.decode_launches)
     merge_ms = timed(merge, 64)
-    dec_kernel = "decode_mfma_kernel" if (w.head_dim == 128 and w.group <= 4) else "decode_valu_kernel"
+    dec_kernel = "decode_mfma_kernel"
 
     ctx_tokens = int(lens.sum())
     kv_bytes = ctx_tokens * H * kv_bytes_per_token_head(d)

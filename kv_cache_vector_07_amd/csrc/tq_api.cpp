@@ -97,10 +97,11 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
   DecodePlan p;
   p.group = n_q_heads / n_kv_heads * n_q;
   p.mfma = mfma_path(d, p.group);
+  p.qgroups = p.mfma ? query_groups(p.group) : 1;
   // About 512 workgroups (two per CU, one occupancy round) so that every
   // workgroup streams several pages with its loads overlapped; whole pages per
   // split; at most 256 pages (65536 tokens) per split.
-  long work = (long)batch * n_kv_heads * max_pages;
+  long work = (long)batch * n_kv_heads * max_pages * p.qgroups;
   int pps = (int)((work + 511) / 512);
   if (pps < 1) pps = 1;
   if (pps > 256) pps = 256;

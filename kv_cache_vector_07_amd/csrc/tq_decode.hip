@@ -16,18 +16,14 @@
 // release per workgroup, which on this GPU writes back and invalidates the whole
 // L2 of the XCD every time.)
 //
-// Two kernels implement the same arithmetic:
-//  - decode_mfma_kernel (<= 4 query rows per KV head). Scores are an int8 MFMA
-//    contraction: with beta_j = 2 b_j - 1 the 3-bit code satisfies
-//    c[idx] = 2 (a0 b0 + a1 b1 + a2 b2 + a3 (b0^b1^b2)) - c7 because the codebook
-//    is odd (c[7-k] = -c[k]), so each key bit plane becomes an int8 operand with
-//    one AND per four coordinates; the query side is exact to fp32 precision as
-//    four int8 limbs laid along the 16 MFMA rows (4 rows x 4 limbs). V is
-//    accumulated with f16 MFMAs in the zero-mean form c[idx] = sum_j a_j beta_j
-//    (beta_3 = beta0 beta1 beta2 = 2 (b0^b1^b2) - 1): each key bit becomes the sign
-//    of a constant fp16 value, so the fp16 rounding of the weights does not add up
-//    coherently over coordinates.
-//  - decode_valu_kernel (up to 16 rows): plain VALU loops, one token per thread.
+// Scores are an int8 MFMA contraction. The codebook is odd (c[7-k] = -c[k]),
+// so the 3-bit code splits over four binary planes,
+// c[idx] = 2 (a0 b0 + a1 b1 + a2 b2 + a3 (b0^b1^b2)) - c7, and each key bit plane
+// becomes an int8 operand with one AND per four coordinates; the query side is
+// exact to fp32 precision as four balanced int8 limbs on the MFMA columns
+// (4 query rows x 4 limbs per query group). V is accumulated with the same
+// planes on int8 MFMA: the softmax weight times each plane weight, as four int8
+// limbs, against the V bit planes. Every product is exact in int32.
 #include "tq_device.h"
 
 namespace tq {
@@ -35,7 +31,6 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 constexpr float kFltMax = 3.402823466e38f;
 constexpr int kPartHead = 4;   // partial record: m, l, mU (log2 units), pad, then acc[d]
@@ -146,11 +141,14 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   // else the sign plane; half h = mu % 2; coordinate 32 s + 8 bb + 4 h + r' with
   // key-side byte value 2^(4h + r') (-128 for bit 7). This row writes columns 4 qq .. 4 qq + 3;
   // row 0 also clears the columns of rows G .. 3.
-  uint8_t *grp = a.packed + ((size_t)b * a.n_kv_heads + kvh) * packed_group_bytes(D);
-  const int ncol = (qq == 0) ? 4 * (kMfmaMaxGroup - G) + 4 : 4;
+  // query group rho = qq / 4 has its own operand; this row is its column group qloc
+  const int QG = query_groups(G), rho = qq / kMfmaMaxGroup, qloc = qq % kMfmaMaxGroup;
+  const int Gr = min(kMfmaMaxGroup, G - kMfmaMaxGroup * rho);   // rows of the group
+  uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * packed_group_bytes(D);
+  const int ncol = (qloc == 0) ? 4 * (kMfmaMaxGroup - Gr) + 4 : 4;
   for (int e = threadIdx.x; e < NMU * 4 * 4 * ncol; e += 256) {
     const int rr = e & 3, kg = (e >> 2) & 3, c = (e >> 4) % ncol, mu = (e >> 4) / ncol;
-    const int n = c < 4 ? 4 * qq + c : 4 * G + (c - 4);   // column; c >= 4: an unused row
+    const int n = c < 4 ? 4 * qloc + c : 4 * Gr + (c - 4);   // column; c >= 4: an unused row
     const int limb = n & 3;
     const int s = kg + 4 * (mu / 10), m10 = mu % 10, h = m10 & 1;
     uint32_t word = 0;
@@ -175,184 +173,9 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
   float *rc = reinterpret_cast<float *>(grp + (size_t)NMU * 1024);
   if (threadIdx.x < 4) {
     const float cv[4] = {d1, d2, sq, sp};
-    rc[4 * qq + threadIdx.x] = cv[threadIdx.x];
-  } else if (qq == 0 && threadIdx.x < 4 * kMfmaMaxGroup && threadIdx.x >= 4 * G) {
+    rc[4 * qloc + threadIdx.x] = cv[threadIdx.x];
+  } else if (qloc == 0 && threadIdx.x < 4 * kMfmaMaxGroup && threadIdx.x >= 4 * Gr) {
     rc[threadIdx.x] = 0.f;
-  }
-}
-
-// ------------------------------------------------------------------ VALU kernel
-template <int D, int GT>
-__global__ __launch_bounds__(256) void decode_valu_kernel(DecodeArgs a) {
-  constexpr int KREC = D / 2;
-  constexpr size_t KCODES = (size_t)kPage * KREC;
-  constexpr size_t KSEC = KCODES + 4 * kPage;
-  constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
-  constexpr size_t VSEC = VCODES + 2 * kPage;
-  constexpr int NS = 256 / D;               // query sets in the V phase
-  constexpr int QPS = (GT + NS - 1) / NS;   // query rows per thread in the V phase
-
-  __shared__ float s_qt[D][GT];             // rotated queries, [coordinate][row]
-  __shared__ float s_pp[D][GT];             // S * rotated queries
-  __shared__ float s_w[kPage][GT];          // scores, then softmax numerators
-  __shared__ float s_nv[kPage];
-  __shared__ float s_m[GT], s_l[GT], s_alpha[GT];
-
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int H = a.n_kv_heads, Hq = a.n_q_heads, g = Hq / H, G = a.plan.group;
-  const int nsplit = a.plan.n_split;
-  const int L = a.seq_lens[b];
-
-  for (int e = tid; e < GT * D; e += 256) {
-    const int qq = e / D, i = e % D;
-    float qv = 0.f, pv = 0.f;
-    if (qq < G) {
-      const int t = qq / g, hh = qq % g;
-      const size_t row = ((size_t)b * a.n_q + t) * Hq + kvh * g + hh;
-      qv = a.prep[row * 2 * D + i];
-      pv = a.prep[row * 2 * D + D + i];
-    }
-    s_qt[i][qq] = qv;
-    s_pp[i][qq] = pv;
-  }
-  if (tid < GT) {
-    s_m[tid] = kNegInf;
-    s_l[tid] = 0.f;
-  }
-  int vis[GT];
-#pragma unroll
-  for (int qq = 0; qq < GT; ++qq) {
-    const int t = qq / g;
-    vis[qq] = qq < G ? (a.causal_tail ? L - (a.n_q - 1 - t) : L) : 0;
-  }
-  const float kappa = qjl_kappa<D>();
-  const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
-  float acc[QPS];
-#pragma unroll
-  for (int k = 0; k < QPS; ++k) acc[k] = 0.f;
-
-  // pages beyond the block table's width are never read
-  const int n_pages_seq = min((L + kPage - 1) / kPage, a.max_pages);
-  const int pg0 = split * a.plan.pages_per_split;
-  const int pg1 = min(pg0 + a.plan.pages_per_split, n_pages_seq);
-  __syncthreads();
-
-  for (int pg = pg0; pg < pg1; ++pg) {
-    const int phys = a.block_table[(size_t)b * a.max_pages + pg];
-    const uint8_t *ksec = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
-    const uint8_t *vsec = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
-    const int tok0 = pg * kPage;
-    const int ntok = min(kPage, L - tok0);
-    {
-      const int t = tid;
-      float s1[GT], s2[GT];
-#pragma unroll
-      for (int qq = 0; qq < GT; ++qq) s1[qq] = s2[qq] = 0.f;
-      if (t < ntok) {
-        const uint4 *rec = reinterpret_cast<const uint4 *>(ksec + (size_t)t * KREC);
-        for (int s = 0; s < D / 32; ++s) {
-          const uint4 w = rec[s];
-#pragma unroll 8
-          for (int e = 0; e < 32; ++e) {
-            const int i = 32 * s + e;
-            const int idx = ((w.x >> e) & 1) | (((w.y >> e) & 1) << 1) | (((w.z >> e) & 1) << 2);
-            const float cv = level_of(a.cb, idx);
-            const float sg = ((w.w >> e) & 1) ? 1.f : -1.f;
-#pragma unroll
-            for (int qq = 0; qq < GT; ++qq) {
-              s1[qq] = fmaf(s_qt[i][qq], cv, s1[qq]);
-              s2[qq] = fmaf(s_pp[i][qq], sg, s2[qq]);
-            }
-          }
-        }
-        const int e = side_entry(t);
-        const float N = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(ksec + KCODES)[e]);
-        const float Gm = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(ksec + KCODES + 2 * kPage)[e]);
-#pragma unroll
-        for (int qq = 0; qq < GT; ++qq) {
-          const float sc = scale2 * N * fmaf(kappa * Gm, s2[qq], s1[qq]);
-          s_w[t][qq] = (tok0 + t < vis[qq]) ? sc : kNegInf;
-        }
-        s_nv[t] = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(vsec + VCODES)[e]);
-      } else {
-#pragma unroll
-        for (int qq = 0; qq < GT; ++qq) s_w[t][qq] = kNegInf;
-        s_nv[t] = 0.f;
-      }
-    }
-    __syncthreads();
-    for (int qq = wave; qq < GT; qq += 4) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int k = 0; k < kPage / 64; ++k) mx = fmaxf(mx, s_w[lane + 64 * k][qq]);
-      mx = wave_max(mx);
-      const float m_old = s_m[qq];
-      const float m_new = fmaxf(m_old, mx);
-      float sum = 0.f;
-#pragma unroll
-      for (int k = 0; k < kPage / 64; ++k) {
-        const int t = lane + 64 * k;
-        const float e = m_new == kNegInf ? 0.f : __builtin_amdgcn_exp2f(s_w[t][qq] - m_new);
-        s_w[t][qq] = e;
-        sum += e;
-      }
-      sum = wave_sum(sum);
-      if (lane == 0) {
-        const float alpha = m_old == kNegInf ? 0.f : __builtin_amdgcn_exp2f(m_old - m_new);
-        s_alpha[qq] = alpha;
-        s_l[qq] = s_l[qq] * alpha + sum;
-        s_m[qq] = m_new;
-      }
-    }
-    __syncthreads();
-    {
-      const int i = tid % D, set = tid / D;
-#pragma unroll
-      for (int k = 0; k < QPS; ++k) {
-        const int qq = set + NS * k;
-        if (qq < GT) acc[k] *= s_alpha[qq];
-      }
-      // coordinate i: the (b, k) token groups of 16 each give one word per plane
-      const uint32_t *vw32 = reinterpret_cast<const uint32_t *>(vsec);
-      const int hsh = 4 * ((i >> 4) & 1);
-      for (int grp = 0; grp < kPage / 16; ++grp) {
-        const int t0 = 64 * (grp >> 2) + 4 * (grp & 3);   // lowest token of the group
-        if (t0 >= ntok) continue;
-        const int w = v_word<D>(t0, i, 0);
-        const uint32_t w0 = vw32[w] >> hsh, w1 = vw32[w + 2 * D] >> hsh, w2 = vw32[w + 4 * D] >> hsh;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int tau = e >> 2, r = e & 3, pos = 8 * r + tau;
-          const int t = t0 + 16 * tau + r;
-          const int idx = ((w0 >> pos) & 1) | (((w1 >> pos) & 1) << 1) | (((w2 >> pos) & 1) << 2);
-          const float val = s_nv[t] * level_of(a.cb, idx);
-#pragma unroll
-          for (int k = 0; k < QPS; ++k) {
-            const int qq = set + NS * k;
-            if (qq < GT) acc[k] = fmaf(s_w[t][qq], val, acc[k]);
-          }
-        }
-      }
-    }
-    __syncthreads();
-  }
-
-  const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * G;
-  {
-    const int i = tid % D, set = tid / D;
-#pragma unroll
-    for (int k = 0; k < QPS; ++k) {
-      const int qq = set + NS * k;
-      if (qq < G) a.partials[(pbase + qq) * (D + kPartHead) + kPartHead + i] = acc[k];
-    }
-    if (tid < G) {
-      float *pr = a.partials + (pbase + tid) * (D + kPartHead);
-      pr[0] = s_m[tid];
-      pr[1] = s_l[tid];
-      pr[2] = s_m[tid];    // V numerator is in units of exp(-m)
-      pr[3] = 0.f;
-    }
   }
 }
 
@@ -400,20 +223,26 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // makes the B operand. Per 64-token block the int32 sums are folded into a
 // float accumulator.
 //
-// Everything one block needs (key records, sidecars, V words: 40 registers) is
-// loaded one block ahead; two register sets alternate between even and odd
-// pages so that no copy is needed.
+// Up to 16 query rows per KV head run as query groups of 4 rows (4 rows x 4
+// limbs fill the 16 MFMA columns); each group is its own workgroup, and the
+// groups of one split sit in blockIdx.z next to each other, so with n_split * Hkv
+// a multiple of 8 they land on the same XCD and share its L2.
+//
+// Everything one block needs (key records, sidecars, V words) is loaded one
+// block ahead; two register sets alternate between even and odd pages so that
+// no copy is needed.
+template <int D>
 struct MfmaBlock {
-  uint4 kw[4];   // key record chunk k of tokens 16 tau + n
-  uint4 g[2];    // G of side entries 16 k + 0..15 (r = 0..3, tau = 0..3)
-  uint2 nk, nv;  // N^K, N^V of side entries 16 k + 4 lam + 0..3 (tau = 0..3)
-  uint4 v[3];    // V words of plane j: coordinate pairs kp = 0..3
+  uint4 kw[4][D / 128];   // key record chunks k, k + 4 of tokens 16 tau + n
+  uint4 g[2];             // G of side entries 16 k + 0..15 (r = 0..3, tau = 0..3)
+  uint2 nk, nv;           // N^K, N^V of side entries 16 k + 4 lam + 0..3 (tau = 0..3)
+  uint4 v[3][D / 128];    // V words of plane j: coordinate pairs kp = 0 .. D/32 - 1
 };
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
-  static_assert(D == 128, "MFMA decode path is built for head_dim 128");
-  constexpr int NMU = 10;                   // int8 MFMAs per 16-token scoring tile
+  constexpr int NMU = 10 * (D / 128);       // int8 MFMAs per 16-token scoring tile
+  constexpr int NCH = D / 128;              // 16-byte key chunks per lane and token
   constexpr int KREC = D / 2;
   constexpr size_t KCODES = (size_t)kPage * KREC;
   constexpr size_t KSEC = KCODES + 4 * kPage;
@@ -425,19 +254,22 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   __shared__ float s_wacc[4][kMfmaMaxGroup][D];   // per wave V numerators
   __shared__ v4i s_qop[NMU * 64];                  // packed query operand, [mfma][lane]
 
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int QG = a.plan.qgroups;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / QG, rho = blockIdx.z % QG;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;
-  const int q = n >> 2, lam = n & 3;   // query row of this lane's 16-lane row slot, limb / token
-  const int H = a.n_kv_heads, G = a.plan.group, g = a.n_q_heads / H;
+  const int q = n >> 2, lam = n & 3;   // query row (in the group) of this lane's 16-lane row slot, limb / token
+  const int H = a.n_kv_heads, g = a.n_q_heads / H;
+  const int qbase = kMfmaMaxGroup * rho;                   // first query row of the group
+  const int G = min(kMfmaMaxGroup, a.plan.group - qbase);  // rows in this group
   const int L = a.seq_lens[b];
 
-  const uint8_t *grp = a.packed + ((size_t)b * H + kvh) * packed_group_bytes(D);
+  const uint8_t *grp = a.packed + (((size_t)b * H + kvh) * QG + rho) * packed_group_bytes(D);
   const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * 1024)[q];
   const float lsc1 = rc.x * (float)(1 << (8 * lam));
   const float lsc2 = rc.y * (float)(1 << (8 * lam)) * qjl_kappa<D>();
   const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w * qjl_kappa<D>();
-  const int vis = q < G ? (a.causal_tail ? L - (a.n_q - 1 - q / g) : L) : 0;
+  const int vis = q < G ? (a.causal_tail ? L - (a.n_q - 1 - (qbase + q) / g) : L) : 0;
   const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
   float wpl[4];
   plane_weights(a.cb, wpl);
@@ -466,13 +298,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   // pages whose block of this wave holds no token are skipped (only the last can)
   if (pg1 > pg0 && blk0 >= L - (pg1 - 1) * kPage) --pg1;
 
-  auto load_block = [&](MfmaBlock &d, int pg) {
+  auto load_block = [&](MfmaBlock<D> &d, int pg) {
     const int phys = a.block_table[(size_t)b * a.max_pages + pg];
     const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
     const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau)
-      d.kw[tau] = reinterpret_cast<const uint4 *>(ks + (size_t)(blk0 + 16 * tau + n) * KREC)[kg];
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+        d.kw[tau][c] = reinterpret_cast<const uint4 *>(ks + (size_t)(blk0 + 16 * tau + n) * KREC)[kg + 4 * c];
     const int se = blk0 + 16 * kg;   // first side entry of this lane's tokens
     d.g[0] = reinterpret_cast<const uint4 *>(ks + KCODES + 2 * kPage + 2 * se)[0];
     d.g[1] = reinterpret_cast<const uint4 *>(ks + KCODES + 2 * kPage + 2 * se)[1];
@@ -480,10 +314,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * (se + 4 * lam));
     const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
 #pragma unroll
-    for (int j = 0; j < 3; ++j) d.v[j] = vw[j * 2 * D * 4 / 16];
+    for (int j = 0; j < 3; ++j)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) d.v[j][c] = vw[j * 2 * D * 4 / 16 + c];
   };
 
-  auto process = [&](const MfmaBlock &d, int pg) {
+  auto process = [&](const MfmaBlock<D> &d, int pg) {
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
     // ---- scores: lane (n, kg) ends with the score of token blk0 + 16 tau + 4 kg + lam
@@ -492,28 +328,31 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       v4i c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0};
-      const uint4 w = d.kw[tau];
-      const uint32_t pl[4] = {w.x, w.y, w.z, w.x ^ w.y ^ w.z};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int c = 0; c < NCH; ++c) {
+        const uint4 w = d.kw[tau][c];
+        const uint32_t pl[4] = {w.x, w.y, w.z, w.x ^ w.y ^ w.z};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            v4i op;
+            op.x = (int)(pl[j] & (0x01010101u << (4 * hh)));
+            op.y = (int)(pl[j] & (0x02020202u << (4 * hh)));
+            op.z = (int)(pl[j] & (0x04040404u << (4 * hh)));
+            op.w = (int)(pl[j] & (0x08080808u << (4 * hh)));
+            c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 2 * j + hh) * 64 + lane], c1, 0, 0, 0);
+          }
+        }
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
           v4i op;
-          op.x = (int)(pl[j] & (0x01010101u << (4 * hh)));
-          op.y = (int)(pl[j] & (0x02020202u << (4 * hh)));
-          op.z = (int)(pl[j] & (0x04040404u << (4 * hh)));
-          op.w = (int)(pl[j] & (0x08080808u << (4 * hh)));
-          c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(2 * j + hh) * 64 + lane], c1, 0, 0, 0);
+          op.x = (int)(w.w & (0x01010101u << (4 * hh)));
+          op.y = (int)(w.w & (0x02020202u << (4 * hh)));
+          op.z = (int)(w.w & (0x04040404u << (4 * hh)));
+          op.w = (int)(w.w & (0x08080808u << (4 * hh)));
+          c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 8 + hh) * 64 + lane], c2, 0, 0, 0);
         }
-      }
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        v4i op;
-        op.x = (int)(w.w & (0x01010101u << (4 * hh)));
-        op.y = (int)(w.w & (0x02020202u << (4 * hh)));
-        op.z = (int)(w.w & (0x04040404u << (4 * hh)));
-        op.w = (int)(w.w & (0x08080808u << (4 * hh)));
-        c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(8 + hh) * 64 + lane], c2, 0, 0, 0);
       }
       // this lane's limb of (S1 + kappa G S2) for the 4 tokens r of the column group;
       // G of (tau, r) is side entry 4 r + tau of the lane's 16
@@ -568,22 +407,19 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // the accumulator row of this lane's column lane is query row kg
     const float aU_row = __shfl(alphaU, 4 * (kg & 3), 64);
 
-    // ---- V: one 64-token K block, 8 column blocks x 4 planes
-    uint32_t xw[4];
+    // ---- V: one 64-token K block, D/16 column blocks x 4 planes
+    auto vword = [&](int j, int kp) -> uint32_t {
+      const uint4 &u = d.v[j][kp >> 2];
+      const int e = kp & 3;
+      return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
+    };
+    uint32_t xw[D / 32];
 #pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-      const uint32_t a0 = kp == 0 ? d.v[0].x : kp == 1 ? d.v[0].y : kp == 2 ? d.v[0].z : d.v[0].w;
-      const uint32_t a1 = kp == 0 ? d.v[1].x : kp == 1 ? d.v[1].y : kp == 2 ? d.v[1].z : d.v[1].w;
-      const uint32_t a2 = kp == 0 ? d.v[2].x : kp == 1 ? d.v[2].y : kp == 2 ? d.v[2].z : d.v[2].w;
-      xw[kp] = a0 ^ a1 ^ a2;
-    }
+    for (int kp = 0; kp < D / 32; ++kp) xw[kp] = vword(0, kp) ^ vword(1, kp) ^ vword(2, kp);
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       const int kp = k >> 1, sh = 4 * (k & 1);
-      const uint32_t w0 = (kp == 0 ? d.v[0].x : kp == 1 ? d.v[0].y : kp == 2 ? d.v[0].z : d.v[0].w) >> sh;
-      const uint32_t w1 = (kp == 0 ? d.v[1].x : kp == 1 ? d.v[1].y : kp == 2 ? d.v[1].z : d.v[1].w) >> sh;
-      const uint32_t w2 = (kp == 0 ? d.v[2].x : kp == 1 ? d.v[2].y : kp == 2 ? d.v[2].z : d.v[2].w) >> sh;
-      const uint32_t wj[4] = {w0, w1, w2, xw[kp] >> sh};
+      const uint32_t wj[4] = {vword(0, kp) >> sh, vword(1, kp) >> sh, vword(2, kp) >> sh, xw[kp] >> sh};
       v4i c = {0, 0, 0, 0};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -602,7 +438,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   // the first block's loads go out before the query operand is staged, so the
   // two fetches overlap
-  MfmaBlock d0, d1;
+  MfmaBlock<D> d0, d1;
   if (pg0 < pg1) load_block(d0, pg0);
   // the packed query operand is shared by the four waves: keep it in LDS
   for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
@@ -632,7 +468,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const int nsplit = a.plan.n_split;
-  const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * G;
+  const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * a.plan.group + qbase;
   for (int qq = wave; qq < G; qq += 4) {
     float M = kNegInf, MU = kNegInf;
 #pragma unroll
@@ -744,18 +580,10 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 
 template <int D>
 hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
-  const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch);
   const int G = a.plan.group;
-  if constexpr (D == 128) {
-    if (a.plan.mfma) {
-      hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
-      return hipGetLastError();
-    }
-  }
-  if (G <= 8)
-    hipLaunchKernelGGL((decode_valu_kernel<D, 8>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_valu_kernel<D, 16>), grid, dim3(256), 0, s, a);
+  if (!a.plan.mfma || G > TQ_MAX_GROUP) return hipErrorInvalidValue;
+  const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.qgroups);
+  hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -763,8 +591,9 @@ hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
 
 size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads) {
   size_t bytes = prep_float_bytes(d, batch, n_q, n_q_heads);
-  if (mfma_path(d, n_q_heads / n_kv_heads * n_q))
-    bytes += ((size_t)batch * n_kv_heads * packed_group_bytes(d) + 255) / 256 * 256;
+  const int group = n_q_heads / n_kv_heads * n_q;
+  if (mfma_path(d, group))
+    bytes += ((size_t)batch * n_kv_heads * query_groups(group) * packed_group_bytes(d) + 255) / 256 * 256;
   return bytes;
 }
 

@@ -58,22 +58,24 @@ struct PrepArgs {
 // lane) is stored lane-major, then 4 rows x {delta1, delta2, sum q~, sum p}.
 __host__ __device__ inline int mfma_per_tile(int d) { return 10 * (d / 128); }
 __host__ __device__ inline size_t packed_group_bytes(int d) { return (size_t)mfma_per_tile(d) * 64 * 16 + 64; }
-constexpr int kMfmaMaxGroup = 4;   // query rows per (sequence, KV head) on the MFMA path
-// The MFMA decode kernel covers head_dim 128 with at most 4 query rows per KV
-// head; other shapes run the VALU decode kernel.
+constexpr int kMfmaMaxGroup = 4;   // query rows per MFMA query group (4 rows x 4 limbs)
+__host__ __device__ inline int query_groups(int group) { return (group + kMfmaMaxGroup - 1) / kMfmaMaxGroup; }
+// The MFMA decode kernel covers head_dim 128 and 256 with up to TQ_MAX_GROUP
+// query rows per KV head, as query groups of 4 rows.
 __host__ __device__ inline bool mfma_path(int d, int group) {
-  return d == 128 && group <= kMfmaMaxGroup;
+  return (d == 128 || d == 256) && group <= TQ_MAX_GROUP;
 }
 
 // Split-K plan of one decode call.
 struct DecodePlan {
   int group;              // query rows per (sequence, KV head) = Hq/Hkv * n_q
+  int qgroups;            // MFMA query groups of 4 rows (MFMA path)
   int pages_per_split;
   int n_split;
   size_t counter_bytes;   // reserved (0)
   size_t partial_bytes;   // [B*Hkv][n_split][group] x (d + 4) float32
   size_t prep_bytes;      // query region (tq_attn_decode only)
-  bool mfma;              // int8/f16 MFMA kernel (group <= kMfmaMaxGroup) or the VALU kernel
+  bool mfma;              // the shape is one the MFMA decode kernel covers
 };
 
 // Query region of a decode call: [rows][2][d] float32, then (MFMA path) the

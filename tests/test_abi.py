@@ -107,10 +107,10 @@ def test_dequant_and_prepare_validation(L):
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 7, FAKE, C.byref(sz), None) == tq.TQ_EINVAL
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE + 16, C.byref(sz), None) == tq.TQ_EALIGN
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE, None, None) == tq.TQ_EINVAL
-    # 16 rows per KV head: no packed operand (VALU decode path)
+    # 16 rows per KV head: four query groups of 4 rows, each with its own operand
     sz16 = C.c_size_t(0)
     assert L.tq_query_prepare(r, FAKE, 0, 2, 2, 16, None, C.byref(sz16), None) == tq.TQ_OK
-    assert sz16.value == 2 * 2 * 16 * 2 * 128 * 4
+    assert sz16.value == 2 * 2 * 16 * 2 * 128 * 4 + 2 * 2 * 4 * (10 * 1024 + 64)
 
 
 def _decode(L, dsc, ws=None, size=None, B=2, nq=1, Hq=8, maxp=16, causal=0, q=FAKE):

@@ -142,9 +142,9 @@ DEC_CASES = [
     (256, 8, 32, 4, [600, 300], "bf16", "outlier", 0, 5),             # d=256, 16 rows per KV head
     (256, 8, 32, 4, [600, 3], "bf16", "outlier", 1, 6),               # causal tail
     (128, 2, 6, 1, [513], "bf16", "normal", 0, 7),                    # g=3 (padded group)
-    (256, 4, 16, 1, [700, 256], "bf16", "outlier", 0, 8),             # d=256, MFMA path
+    (256, 4, 16, 1, [700, 256], "bf16", "outlier", 0, 8),             # d=256, one query group
     (128, 4, 8, 2, [400, 2, 257], "bf16", "outlier", 1, 9),           # n_q=2 causal, MFMA path
-    (128, 2, 16, 1, [300], "bf16", "normal", 0, 10),                  # 8 rows: VALU path
+    (128, 2, 16, 1, [300], "bf16", "normal", 0, 10),                  # 8 rows: two query groups
 ]
 
 
