@@ -231,12 +231,15 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // Everything one block needs (key records, sidecars, V words) is loaded one
 // block ahead; two register sets alternate between even and odd pages so that
 // no copy is needed.
+// (At d = 256 the V words are loaded at the start of the block instead, to keep
+// two waves per SIMD.)
 template <int D>
 struct MfmaBlock {
-  uint4 kw[4][D / 128];   // key record chunks k, k + 4 of tokens 16 tau + n
-  uint4 g[2];             // G of side entries 16 k + 0..15 (r = 0..3, tau = 0..3)
-  uint2 nk, nv;           // N^K, N^V of side entries 16 k + 4 lam + 0..3 (tau = 0..3)
-  uint4 v[3][D / 128];    // V words of plane j: coordinate pairs kp = 0 .. D/32 - 1
+  static constexpr bool kPrefetchV = D == 128;
+  uint4 kw[4][D / 128];            // key record chunks k, k + 4 of tokens 16 tau + n
+  uint4 g[2];                      // G of side entries 16 k + 0..15 (r = 0..3, tau = 0..3)
+  uint2 nk, nv;                    // N^K, N^V of side entries 16 k + 4 lam + 0..3 (tau = 0..3)
+  uint4 v[kPrefetchV ? 3 : 1][D / 128];   // V words of plane j: coordinate pairs kp
 };
 
 template <int D>
@@ -312,14 +315,35 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     d.g[1] = reinterpret_cast<const uint4 *>(ks + KCODES + 2 * kPage + 2 * se)[1];
     d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * (se + 4 * lam));
     d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * (se + 4 * lam));
-    const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
+    if constexpr (MfmaBlock<D>::kPrefetchV) {
+      const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < 3; ++j)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) d.v[j][c] = vw[j * 2 * D * 4 / 16 + c];
+        for (int c = 0; c < NCH; ++c) d.v[j][c] = vw[j * 2 * D * 4 / 16 + c];
+    }
   };
 
   auto process = [&](const MfmaBlock<D> &d, int pg) {
+    // at d = 256 the query operand (20 MFMA operands, 80 registers) is read from
+    // LDS where it is used: an opaque lane offset keeps it from being hoisted
+    int qo = lane;
+    if constexpr (D == 256) asm volatile("" : "+v"(qo));
+    uint4 vcur[3][NCH];
+    if constexpr (MfmaBlock<D>::kPrefetchV) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) vcur[j][c] = d.v[j][c];
+    } else {
+      const int phys = a.block_table[(size_t)b * a.max_pages + pg];
+      const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
+      const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) vcur[j][c] = vw[j * 2 * D * 4 / 16 + c];
+    }
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
     // ---- scores: lane (n, kg) ends with the score of token blk0 + 16 tau + 4 kg + lam
@@ -341,7 +365,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
             op.y = (int)(pl[j] & (0x02020202u << (4 * hh)));
             op.z = (int)(pl[j] & (0x04040404u << (4 * hh)));
             op.w = (int)(pl[j] & (0x08080808u << (4 * hh)));
-            c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 2 * j + hh) * 64 + lane], c1, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 2 * j + hh) * 64 + qo], c1, 0, 0, 0);
           }
         }
 #pragma unroll
@@ -351,7 +375,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           op.y = (int)(w.w & (0x02020202u << (4 * hh)));
           op.z = (int)(w.w & (0x04040404u << (4 * hh)));
           op.w = (int)(w.w & (0x08080808u << (4 * hh)));
-          c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 8 + hh) * 64 + lane], c2, 0, 0, 0);
+          c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 8 + hh) * 64 + qo], c2, 0, 0, 0);
         }
       }
       // this lane's limb of (S1 + kappa G S2) for the 4 tokens r of the column group;
@@ -409,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
     // ---- V: one 64-token K block, D/16 column blocks x 4 planes
     auto vword = [&](int j, int kp) -> uint32_t {
-      const uint4 &u = d.v[j][kp >> 2];
+      const uint4 &u = vcur[j][kp >> 2];
       const int e = kp & 3;
       return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
     };
@@ -438,17 +462,28 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   // the first block's loads go out before the query operand is staged, so the
   // two fetches overlap
-  MfmaBlock<D> d0, d1;
-  if (pg0 < pg1) load_block(d0, pg0);
-  // the packed query operand is shared by the four waves: keep it in LDS
-  for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
-  __syncthreads();
-  for (int pg = pg0; pg < pg1; pg += 2) {
-    if (pg + 1 < pg1) load_block(d1, pg + 1);
-    process(d0, pg);
-    if (pg + 1 >= pg1) break;
-    if (pg + 2 < pg1) load_block(d0, pg + 2);
-    process(d1, pg + 1);
+  if constexpr (D == 128) {
+    MfmaBlock<D> d0, d1;
+    if (pg0 < pg1) load_block(d0, pg0);
+    // the packed query operand is shared by the four waves: keep it in LDS
+    for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
+    __syncthreads();
+    for (int pg = pg0; pg < pg1; pg += 2) {
+      if (pg + 1 < pg1) load_block(d1, pg + 1);
+      process(d0, pg);
+      if (pg + 1 >= pg1) break;
+      if (pg + 2 < pg1) load_block(d0, pg + 2);
+      process(d1, pg + 1);
+    }
+  } else {
+    // d = 256: one register set (two would cost the second wave per SIMD)
+    for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
+    __syncthreads();
+    for (int pg = pg0; pg < pg1; ++pg) {
+      MfmaBlock<D> d0;
+      load_block(d0, pg);
+      process(d0, pg);
+    }
   }
 
   // ---- combine the four waves into one partial per query row
