@@ -214,12 +214,12 @@ def main():
     def step(i):
         c = copies[i % R]
         q = qs[i % n_q_sets]
-        r = L_.tq_encode_k(c.ref, new_k.data_ptr(), qdt, app_slots.data_ptr(), B, sh)
-        r |= L_.tq_encode_v(c.ref, new_v.data_ptr(), qdt, app_slots.data_ptr(), B, sh)
+        # append one token per sequence (encode K and V), then decode: one call
         sz = C.c_size_t(ws.numel())
-        r |= L_.tq_attn_decode(c.ref, q.data_ptr(), qdt, B, nq, Hq, table.data_ptr(), mp,
-                               seq.data_ptr(), 0, scale, out.data_ptr(), ws.data_ptr(),
-                               C.byref(sz), sh)
+        r = L_.tq_append_decode(c.ref, new_k.data_ptr(), new_v.data_ptr(), qdt, app_slots.data_ptr(),
+                                B, q.data_ptr(), qdt, B, nq, Hq, table.data_ptr(), mp,
+                                seq.data_ptr(), 0, scale, out.data_ptr(), ws.data_ptr(),
+                                C.byref(sz), sh)
         if r:
             raise RuntimeError(f"launch failed with status {r}")
 
@@ -299,7 +299,7 @@ def main():
                    "head_dim": d, "n_q": nq, "context": int(lens.max()) if B == 1 else
                    [int(lens.min()), int(lens.max())], "ctx_tokens": ctx_tokens,
                    "input_dtype": w.dtype, "page_size": 256, "rotating_copies": R,
-                   "step": "append 1 token/seq (encode K+V) + query prep + split-K decode"},
+                   "step": "tq_append_decode: append 1 token/seq (encode K+V) and decode (prologue, split-K, merge)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "ctx_tokens_per_s": round(ctx_tokens / step_s, 1),
         "encode_k_vec_per_s": round(n_vec / (enc_k_ms / 1e3), 1),

@@ -173,6 +173,24 @@ int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype,
                    float *out, void *workspace, size_t *workspace_bytes, void *stream);
 
 /*
+ * One decode step with an append: encode n_new new K and V vectors
+ * ([n_new][Hkv][d], kv_dtype) into `slots` exactly as tq_encode_k and
+ * tq_encode_v do, then run tq_attn_decode over the updated cache (seq_lens
+ * must already count the new tokens). The same workspace as tq_attn_decode.
+ * Short appends (n_new * Hkv < 4096) with q_dtype == kv_dtype encode and
+ * prepare the query in a single launch; otherwise the separate kernels run in
+ * order. n_new = 0 is a plain decode.
+ * Same passages as tq_encode_k / tq_encode_v and tq_attn_decode. Errors: as
+ * tq_encode_k and tq_attn_decode (TQ_EINVAL for null k_new / v_new / slots
+ * with n_new > 0).
+ */
+int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, int32_t kv_dtype,
+                     const int32_t *slots, int32_t n_new, const void *q, int32_t q_dtype,
+                     int32_t batch, int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
+                     int32_t max_pages, const int32_t *seq_lens, int32_t causal_tail, float scale,
+                     float *out, void *workspace, size_t *workspace_bytes, void *stream);
+
+/*
  * The attention part of tq_attn_decode alone (one kernel launch), on queries
  * already prepared by tq_query_prepare with the same batch, n_q and n_q_heads.
  * Same semantics, workspace rules and errors; its workspace is smaller (no

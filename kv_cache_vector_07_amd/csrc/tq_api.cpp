@@ -327,6 +327,72 @@ int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype, int32_t batc
                     scale, out, ws, plan, s);
 }
 
+int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, int32_t kv_dtype,
+                     const int32_t *slots, int32_t n_new, const void *q, int32_t q_dtype,
+                     int32_t batch, int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
+                     int32_t max_pages, const int32_t *seq_lens, int32_t causal_tail, float scale,
+                     float *out, void *workspace, size_t *workspace_bytes, void *stream) {
+  int st = decode_checks(c, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+                         out, workspace_bytes);
+  if (st) return st;
+  if (kv_dtype != TQ_F32 && kv_dtype != TQ_BF16) return TQ_EUNSUPPORTED;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EUNSUPPORTED;
+  if (n_new < 0) return TQ_EINVAL;
+  tq::DecodePlan plan =
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+  size_t need = plan.counter_bytes + plan.partial_bytes + plan.prep_bytes;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return TQ_OK;
+  }
+  if (*workspace_bytes < need) {
+    *workspace_bytes = need;
+    return TQ_EWORKSPACE;
+  }
+  if (!q || !c->qjl) return TQ_EINVAL;
+  if (n_new > 0 && (!k_new || !v_new || !slots)) return TQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(workspace, 256) || !aligned(c->qjl, 16)) return TQ_EALIGN;
+  if (n_new > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slots, 4)))
+    return TQ_EALIGN;
+  uint8_t *ws = (uint8_t *)workspace;
+  uint8_t *prep = ws + plan.counter_bytes + plan.partial_bytes;
+  hipStream_t s = (hipStream_t)stream;
+
+  tq::EncodeArgs ek, ev;
+  ek.x = k_new;
+  ek.dtype = kv_dtype;
+  ek.slots = slots;
+  ek.n_tokens = n_new;
+  ek.n_heads = c->n_kv_heads;
+  ek.pool = (uint8_t *)c->k_pool;
+  ek.qjl = c->qjl;
+  ek.cb = codebook_of(c);
+  ev = ek;
+  ev.x = v_new;
+  ev.pool = (uint8_t *)c->v_pool;
+  tq::PrepArgs pa;
+  pa.q = q;
+  pa.dtype = q_dtype;
+  pa.batch = batch;
+  pa.n_q = n_q;
+  pa.n_q_heads = n_q_heads;
+  pa.n_kv_heads = c->n_kv_heads;
+  pa.qjl = c->qjl;
+  pa.prep = (float *)prep;
+  pa.packed = prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads);
+  pa.cb = codebook_of(c);
+  if (n_new > 0 && tq::step_prologue_fits(ek, pa)) {
+    if (tq::launch_step_prologue(ek, ev, pa, c->head_dim, s) != hipSuccess) return TQ_EHIP;
+  } else {
+    if (n_new > 0 && (tq::launch_encode_k(ek, c->head_dim, s) != hipSuccess ||
+                      tq::launch_encode_v(ev, c->head_dim, s) != hipSuccess))
+      return TQ_EHIP;
+    if (tq::launch_prepare(pa, c->head_dim, s) != hipSuccess) return TQ_EHIP;
+  }
+  return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
+                    scale, out, ws, plan, s);
+}
+
 int tq_attn_decode_prepared(const tq_cache *c, const void *prep, int32_t batch, int32_t n_q,
                             int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
                             const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,

@@ -35,149 +35,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr float kFltMax = 3.402823466e38f;
 constexpr int kPartHead = 4;   // partial record: m, l, mU (log2 units), pad, then acc[d]
 
-// Weights of the odd-codebook bit planes: c[idx] = sum_j 2 a_j plane_j - c7 with
-// planes (b0, b1, b2, b0^b1^b2).
-__device__ inline void plane_weights(const Codebook &cb, float (&w)[4]) {
-  const float c4 = cb.levels[4], c5 = cb.levels[5], c6 = cb.levels[6], c7 = cb.levels[7];
-  const float a2 = 0.25f * (c4 + c5 + c6 + c7);
-  w[0] = 2.f * (0.5f * (c5 + c7) - a2);
-  w[1] = 2.f * (0.5f * (c6 + c7) - a2);
-  w[2] = 2.f * a2;
-  w[3] = 2.f * (0.5f * (c4 + c7) - a2);
-}
-
-// ------------------------------------------------------------------ prepare
-// One workgroup per query row qq of a (sequence, KV head) group: rotate the
-// row, project it with S, write q~ and p, and on the MFMA path pack this row's
-// four limb columns of the int8 scoring operand. The four waves split the m
-// rows of S, and every S load of a chunk is issued before the row is rotated.
-template <int D, int DT>
-__global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
-  constexpr int R = D / 64;
-  constexpr int NMU = 10 * (D / 128);
-  constexpr int RPW = D / 4;         // rows of S per wave
-  constexpr int LPR = 64 / RPW;      // lanes per row of S: 2 (d = 128) or 1 (d = 256)
-  constexpr int EPL = D / LPR;       // elements of a row per lane
-  constexpr int CH = 16;             // float4 loads in flight per lane
-  constexpr int NCH = EPL / 4 / CH;  // chunks: 1 (d = 128) or 4 (d = 256)
-  __shared__ float s_q[D], s_p[D];
-  const int qq = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = a.n_q_heads / a.n_kv_heads, G = g * a.n_q;
-  const int t = qq / g, hh = qq % g;
-  const size_t row = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
-  const int srow = wave * RPW + lane / LPR, part = lane % LPR;
-  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl) + (size_t)srow * (D / 4) + part * (EPL / 4);
-  float4 sv[CH];
-#pragma unroll
-  for (int k = 0; k < CH; ++k) sv[k] = S4[k];
-
-  float v[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) v[r] = load_elem<DT>(a.q, row * D + lane + 64 * r);
-  fwht_wave<R>(v);
-#pragma unroll
-  for (int r = 0; r < R; ++r) v[r] *= rsqrt_dim<D>();
-  float *dst = a.prep + row * 2 * D;
-  if (wave == 0) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      s_q[lane + 64 * r] = v[r];
-      dst[lane + 64 * r] = v[r];
-    }
-  }
-  __syncthreads();
-
-  // p_l = sum_i S[l][i] q~_i
-  const float4 *q4 = reinterpret_cast<const float4 *>(s_q) + part * (EPL / 4);
-  float acc = 0.f;
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c > 0) {
-#pragma unroll
-      for (int k = 0; k < CH; ++k) sv[k] = S4[c * CH + k];
-    }
-#pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const float4 qv = q4[c * CH + k];
-      acc = fmaf(sv[k].x, qv.x, acc);
-      acc = fmaf(sv[k].y, qv.y, acc);
-      acc = fmaf(sv[k].z, qv.z, acc);
-      acc = fmaf(sv[k].w, qv.w, acc);
-    }
-  }
-  if (LPR == 2) acc += __shfl_xor(acc, 1, 64);
-  if (part == 0) {
-    s_p[srow] = acc;
-    dst[D + srow] = acc;
-  }
-  if (a.packed == nullptr) return;
-  __syncthreads();
-
-  // scales of this row (every wave computes them): |value / delta| < 2^30, so
-  // four balanced base-256 limbs hold each scaled value
-  float w[4];
-  plane_weights(a.cb, w);
-  const float wmax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
-  float mq = 0.f, mp = 0.f, sq = 0.f, sp = 0.f;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float x = s_q[lane + 64 * r], y = s_p[lane + 64 * r];
-    mq = fmaxf(mq, fabsf(x));
-    mp = fmaxf(mp, fabsf(y));
-    sq += x;
-    sp += y;
-  }
-  mq = wave_max(mq);
-  mp = wave_max(mp);
-  sq = wave_sum(sq);
-  sp = wave_sum(sp);
-  const float d1 = mq > 0.f ? wmax * mq * 0x1p-30f : 1.f;
-  const float d2 = mp > 0.f ? 2.f * mp * 0x1p-30f : 1.f;
-  const float i1 = 1.0f / d1, i2 = 1.0f / d2;
-
-  // Operand byte (mu, lane = 16 kg + n, 4 r' + bb): column n = 4 q + limb, MFMA mu of a
-  // 16-token tile: group s = kg + 4 (mu / 10); mu % 10 < 8 -> code plane j = (mu%10)/2,
-  // else the sign plane; half h = mu % 2; coordinate 32 s + 8 bb + 4 h + r' with
-  // key-side byte value 2^(4h + r') (-128 for bit 7). This row writes columns 4 qq .. 4 qq + 3;
-  // row 0 also clears the columns of rows G .. 3.
-  // query group rho = qq / 4 has its own operand; this row is its column group qloc
-  const int QG = query_groups(G), rho = qq / kMfmaMaxGroup, qloc = qq % kMfmaMaxGroup;
-  const int Gr = min(kMfmaMaxGroup, G - kMfmaMaxGroup * rho);   // rows of the group
-  uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * packed_group_bytes(D);
-  const int ncol = (qloc == 0) ? 4 * (kMfmaMaxGroup - Gr) + 4 : 4;
-  for (int e = threadIdx.x; e < NMU * 4 * 4 * ncol; e += 256) {
-    const int rr = e & 3, kg = (e >> 2) & 3, c = (e >> 4) % ncol, mu = (e >> 4) / ncol;
-    const int n = c < 4 ? 4 * qloc + c : 4 * Gr + (c - 4);   // column; c >= 4: an unused row
-    const int limb = n & 3;
-    const int s = kg + 4 * (mu / 10), m10 = mu % 10, h = m10 & 1;
-    uint32_t word = 0;
-    if (c < 4) {
-      // value / (delta * key byte value) as an integer X; limb bytes of X + 0x80808080
-      // are the digits of X in base 256 offset by 128 (X = sum (byte_l - 128) 256^l)
-      const int kb = 4 * h + rr;
-      const float vkey = kb == 7 ? -128.f : (float)(1 << kb);
-      const float f = (m10 < 8 ? w[m10 >> 1] * i1 : 2.f * i2) / vkey;
-      const float *src = m10 < 8 ? s_q : s_p;
-      uint32_t bytes = 0;
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int X = (int)rintf(src[32 * s + 8 * bb + 4 * h + rr] * f);
-        const uint32_t byte = (((uint32_t)X + 0x80808080u) >> (8 * limb)) & 0xFFu;
-        bytes |= byte << (8 * bb);
-      }
-      word = bytes ^ 0x80808080u;
-    }
-    reinterpret_cast<uint32_t *>(grp)[(size_t)mu * 256 + (16 * kg + n) * 4 + rr] = word;
-  }
-  float *rc = reinterpret_cast<float *>(grp + (size_t)NMU * 1024);
-  if (threadIdx.x < 4) {
-    const float cv[4] = {d1, d2, sq, sp};
-    rc[4 * qloc + threadIdx.x] = cv[threadIdx.x];
-  } else if (qloc == 0 && threadIdx.x < 4 * kMfmaMaxGroup && threadIdx.x >= 4 * Gr) {
-    rc[threadIdx.x] = 0.f;
-  }
-}
 
 // ------------------------------------------------------------------ MFMA kernel
 __device__ inline int dpp_swap1(int x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); }
@@ -632,21 +489,6 @@ size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_head
   return bytes;
 }
 
-hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
-  const dim3 grid(a.n_q * (a.n_q_heads / a.n_kv_heads), a.n_kv_heads, a.batch);
-  if (d == 128) {
-    if (a.dtype == TQ_F32)
-      hipLaunchKernelGGL((prepare_kernel<128, TQ_F32>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((prepare_kernel<128, TQ_BF16>), grid, dim3(256), 0, s, a);
-  } else {
-    if (a.dtype == TQ_F32)
-      hipLaunchKernelGGL((prepare_kernel<256, TQ_F32>), grid, dim3(256), 0, s, a);
-    else
-      hipLaunchKernelGGL((prepare_kernel<256, TQ_BF16>), grid, dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
-}
 
 hipError_t launch_decode_split(const DecodeArgs &a, int d, hipStream_t s) {
   return d == 128 ? launch_split_dim<128>(a, s) : launch_split_dim<256>(a, s);

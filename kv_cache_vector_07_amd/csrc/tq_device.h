@@ -108,6 +108,17 @@ __device__ inline int v_word(int t, int i, int j) {
 }
 __device__ inline int v_bit(int t, int i) { return 8 * (t & 3) + 4 * ((i >> 4) & 1) + ((t >> 4) & 3); }
 
+// Weights of the odd-codebook bit planes: c[idx] = sum_j 2 a_j plane_j - c7 with
+// planes (b0, b1, b2, b0^b1^b2).
+__device__ inline void plane_weights(const Codebook &cb, float (&w)[4]) {
+  const float c4 = cb.levels[4], c5 = cb.levels[5], c6 = cb.levels[6], c7 = cb.levels[7];
+  const float a2 = 0.25f * (c4 + c5 + c6 + c7);
+  w[0] = 2.f * (0.5f * (c5 + c7) - a2);
+  w[1] = 2.f * (0.5f * (c6 + c7) - a2);
+  w[2] = 2.f * a2;
+  w[3] = 2.f * (0.5f * (c4 + c7) - a2);
+}
+
 __device__ inline uint16_t f32_to_f16_bits(float x) {
   _Float16 h = (_Float16)x;  // round to nearest even, overflow to inf
   return __builtin_bit_cast(uint16_t, h);

@@ -109,6 +109,12 @@ hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s);
 hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, int d, int which, hipStream_t s);
 hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s);
+// Encode of a short append (k, v: same tokens and dtype) and the query prepare in
+// one launch; false when the shapes need the separate kernels (long appends, or
+// query and K/V in different dtypes).
+bool step_prologue_fits(const EncodeArgs &k, const PrepArgs &p);
+hipError_t launch_step_prologue(const EncodeArgs &k, const EncodeArgs &v, const PrepArgs &p, int d,
+                                hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs &a, int d, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, int d, hipStream_t s);
 

@@ -22,8 +22,9 @@ TQ_F32, TQ_BF16 = 0, 1
 TQ_PAGE_SIZE = 256
 TQ_MAX_GROUP = 16
 EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_encode_k",
-           "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_prepared",
-           "tq_attn_decode_split", "tq_attn_decode_merge", "tq_dequant", "tq_status_string")
+           "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_append_decode",
+           "tq_attn_decode_prepared", "tq_attn_decode_split", "tq_attn_decode_merge",
+           "tq_dequant", "tq_status_string")
 
 
 class TqError(RuntimeError):
@@ -61,6 +62,8 @@ def lib():
     L.tq_query_prepare.argtypes = [vp, vp, i32, i32, i32, i32, vp, C.POINTER(sz), vp]
     L.tq_attn_decode.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
                                  C.POINTER(sz), vp]
+    L.tq_append_decode.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, vp, i32, vp,
+                                   i32, f32, vp, vp, C.POINTER(sz), vp]
     L.tq_attn_decode_prepared.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
                                           C.POINTER(sz), vp]
     L.tq_attn_decode_split.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp,
@@ -68,7 +71,7 @@ def lib():
     L.tq_attn_decode_merge.argtypes = [vp, i32, i32, i32, i32, vp, vp, sz, vp]
     L.tq_dequant.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     for name in ("tq_build_codebook", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
-                 "tq_attn_decode", "tq_attn_decode_prepared", "tq_attn_decode_split",
+                 "tq_attn_decode", "tq_append_decode", "tq_attn_decode_prepared", "tq_attn_decode_split",
                  "tq_attn_decode_merge", "tq_dequant"):
         getattr(L, name).restype = i32
     _lib = L
@@ -213,6 +216,28 @@ def tq_attn_decode(cache: Cache, q, block_table, seq_lens, causal_tail: int = 0,
     size = C.c_size_t(ws.numel())
     st = L.tq_attn_decode(*args(ws.data_ptr()), C.byref(size), _stream(stream))
     _check(st, "tq_attn_decode")
+    return out
+
+
+def tq_append_decode(cache: Cache, k_new, v_new, slots, q, block_table, seq_lens,
+                     causal_tail: int = 0, scale=None, out=None, workspace=None, stream=None):
+    """Encode k_new / v_new ([n][Hkv][d]) into `slots`, then decode q ([B][n_q][Hq][d])
+    over the updated cache; seq_lens must already count the new tokens."""
+    import torch
+    B, n_q, Hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=q.device)
+    n_new = int(slots.numel())
+    L = lib()
+    args = lambda ws: (cache.ref, k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new),
+                       slots.data_ptr(), n_new, q.data_ptr(), _dtype_code(q), B, n_q, Hq,
+                       block_table.data_ptr(), int(block_table.shape[1]), seq_lens.data_ptr(),
+                       int(causal_tail), scale, out.data_ptr(), ws)
+    ws, size = _decode_ws(cache, L.tq_append_decode, args, workspace)
+    size = C.c_size_t(ws.numel())
+    st = L.tq_append_decode(*args(ws.data_ptr()), C.byref(size), _stream(stream))
+    _check(st, "tq_append_decode")
     return out
 
 

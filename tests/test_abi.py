@@ -161,3 +161,26 @@ def test_split_and_merge_validation(L):
     assert L.tq_attn_decode_merge(r, 2, 1, 8, 16, None, FAKE, need, None) == tq.TQ_EINVAL
     assert L.tq_attn_decode_merge(r, 2, 1, 7, 16, FAKE, FAKE, need, None) == tq.TQ_EINVAL
     assert L.tq_attn_decode_merge(r, 2, 1, 8, 16, FAKE + 4, FAKE, need, None) == tq.TQ_EALIGN
+
+
+def test_append_decode_validation(L):
+    dsc = _desc(H=2)
+    r = C.byref(dsc)
+    args = lambda ws, n_new=4, kdt=1, qdt=1, k=FAKE, q=FAKE: (
+        r, k, FAKE, kdt, FAKE, n_new, q, qdt, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE, ws)
+    sz = C.c_size_t(0)
+    assert L.tq_append_decode(*args(None), C.byref(sz), None) == tq.TQ_OK
+    need = sz.value
+    sz2 = C.c_size_t(0)
+    assert L.tq_attn_decode(r, FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE, None, C.byref(sz2),
+                            None) == tq.TQ_OK
+    assert need == sz2.value
+    small = C.c_size_t(need - 256)
+    assert L.tq_append_decode(*args(FAKE), C.byref(small), None) == tq.TQ_EWORKSPACE
+    ok = C.c_size_t(need)
+    assert L.tq_append_decode(*args(FAKE, kdt=3), C.byref(ok), None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_append_decode(*args(FAKE, n_new=-1), C.byref(ok), None) == tq.TQ_EINVAL
+    assert L.tq_append_decode(*args(FAKE, k=None), C.byref(ok), None) == tq.TQ_EINVAL
+    assert L.tq_append_decode(*args(FAKE, q=None), C.byref(ok), None) == tq.TQ_EINVAL
+    assert L.tq_append_decode(*args(FAKE, k=FAKE + 4), C.byref(ok), None) == tq.TQ_EALIGN
+    assert L.tq_append_decode(*args(FAKE + 16), C.byref(ok), None) == tq.TQ_EALIGN

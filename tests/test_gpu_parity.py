@@ -219,3 +219,75 @@ def test_dequant_parity(tq, d):
     s = O.score(qt_, p_, uk["idx"][:, 2], uk["sign"][:, 2], uk["N"][:, 2].astype(float),
                 uk["G"][:, 2].astype(float), cb, d)
     assert np.max(np.abs(Kt @ q - s)) < 1e-9 * np.max(np.abs(s))
+
+
+@pytest.mark.parametrize("start", [256, 288], ids=["aligned-blocks", "unaligned"])
+def test_encode_whole_blocks_and_unaligned(tq, start):
+    """Bulk encode into consecutive slots: from a 64-token boundary every block is
+    stored whole; from an unaligned start no block is whole (per-bit path)."""
+    d, H, n, seed = 128, 8, 640, 11
+    print(f"[encode blocks] start={start}", flush=True)
+    w, k, v = _enc_inputs(d, "bf16", "outlier", n, H, seed)
+    cache = tq.Cache(d, H, 5)
+    slots = np.arange(start, start + n, dtype=np.int32)
+    ts = torch.from_numpy(slots).cuda()
+    tq.tq_encode_k(cache, Hn.torch_input(k, "bf16"), ts)
+    tq.tq_encode_v(cache, Hn.torch_input(v, "bf16"), ts)
+    torch.cuda.synchronize()
+    kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+    cb = Hn.codebook_from_cache(cache)
+    Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k.astype(np.float64), cb, cache.qjl_host)
+    Hn.compare_encode_v(O.unpack_v(vp, slots, H, d, 256), v.astype(np.float64), cb)
+    # slots outside the written range stay zero
+    rest = np.setdiff1d(np.arange(5 * 256), slots).astype(np.int64)
+    assert np.all(O.unpack_v(vp, rest, H, d, 256)["idx"] == 0)
+    assert np.all(O.unpack_k(kp, rest, H, d, 256)["idx"] == 0)
+
+
+@pytest.mark.parametrize("d,Hq,nq", [(128, 32, 1), (256, 32, 4)])
+def test_append_decode_matches_separate_calls_and_reference(tq, d, Hq, nq):
+    """tq_append_decode (encode of the appended tokens and query prepare in one
+    launch) against tq_encode_k + tq_encode_v + tq_attn_decode on a twin cache,
+    bit for bit, and against the reference over the updated cache."""
+    H, lens0 = 8, np.array([700, 257, 64])
+    print(f"[append decode] d={d} Hq={Hq} n_q={nq}", flush=True)
+    w = I.Workload(f"app{d}", len(lens0), Hq, H, d, "bf16", "outlier", 31, n_q=nq, fixed_len=1)
+    table, n_pages = I.page_table(w, lens0, extra_tokens=1, shuffle=True)
+    caches = [tq.Cache(d, H, n_pages) for _ in range(2)]
+    bt = torch.from_numpy(table).cuda()
+    for c in caches:
+        for b, L in enumerate(lens0):
+            t = torch.arange(0, int(L), device="cuda")
+            sl = (bt[b, t // 256] * 256 + t % 256).to(torch.int32)
+            c_k = torch.from_numpy(I.kv_tokens(w, "k", b, 0, int(L))).to("cuda", torch.bfloat16)
+            c_v = torch.from_numpy(I.kv_tokens(w, "v", b, 0, int(L))).to("cuda", torch.bfloat16)
+            tq.tq_encode_k(c, c_k, sl)
+            tq.tq_encode_v(c, c_v, sl)
+    pos = torch.from_numpy(lens0).cuda()
+    slots = (bt[torch.arange(len(lens0), device="cuda"), pos // 256] * 256 + pos % 256).to(torch.int32)
+    nk = np.concatenate([I.kv_tokens(w, "k", b, int(L), int(L) + 1) for b, L in enumerate(lens0)])
+    nv = np.concatenate([I.kv_tokens(w, "v", b, int(L), int(L) + 1) for b, L in enumerate(lens0)])
+    nk_t = torch.from_numpy(nk).to("cuda", torch.bfloat16)
+    nv_t = torch.from_numpy(nv).to("cuda", torch.bfloat16)
+    lens = lens0 + 1
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = I.queries(w, 0)
+    qt = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    out_a = tq.tq_append_decode(caches[0], nk_t, nv_t, slots, qt, bt, sl)
+    tq.tq_encode_k(caches[1], nk_t, slots)
+    tq.tq_encode_v(caches[1], nv_t, slots)
+    out_b = tq.tq_attn_decode(caches[1], qt, bt, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].k_pool, caches[1].k_pool)
+    assert torch.equal(caches[0].v_pool, caches[1].v_pool)
+    assert torch.equal(out_a, out_b)
+    kp, vp = caches[0].k_pool.cpu().numpy(), caches[0].v_pool.cpu().numpy()
+    cb = Hn.codebook_from_cache(caches[0])
+    s_np = slots.cpu().numpy()
+    Hn.compare_encode_k(O.unpack_k(kp, s_np, H, d, 256), nk.astype(np.float64), cb, caches[0].qjl_host)
+    Hn.compare_encode_v(O.unpack_v(vp, s_np, H, d, 256), nv.astype(np.float64), cb)
+    ref = O.attn_decode(kp, vp, cb, caches[0].qjl_host, q.astype(np.float64), table, lens, H, 256,
+                        Hn.scale_of(d))
+    err = Hn.attn_rel_err(out_a.cpu().numpy(), ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= Hn.ATTN_TOL
