@@ -394,74 +394,84 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// One workgroup per (query row, KV head, sequence): four waves split the split
-// partials, then combine in LDS, apply the inverse rotation and write the row.
+// One workgroup per (query row, KV head, sequence). Wave w takes splits
+// w, w + 4, ...: it issues the loads of up to 8 of them at once (the headers are
+// wave-uniform) and folds them with a running log-sum-exp; the four waves then
+// combine in LDS, and wave 0 applies the inverse rotation and writes the row.
 template <int D>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int R = D / 64;
-  __shared__ float s_stat[4][3];
+  constexpr int CH = 8;   // splits per wave in flight
+  __shared__ float s_st[4][3];
   __shared__ float s_x[4][D];
-  __shared__ float s_f[4][64];
   const int qq = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int H = a.n_kv_heads, Hq = a.n_q_heads, g = Hq / H, G = a.plan.group;
   const int nsplit = a.plan.n_split;
   const size_t stride = (size_t)G * (D + kPartHead);
   const float *part = a.partials + (((size_t)b * H + kvh) * nsplit * G + qq) * (D + kPartHead);
-  // global maxima over all splits (every wave computes them)
-  float M = kNegInf, MU = kNegInf;
-  for (int sp = lane; sp < nsplit; sp += 64) {
-    const float *pr = part + sp * stride;
-    if (pr[1] > 0.f) {
-      M = fmaxf(M, pr[0]);
-      MU = fmaxf(MU, pr[2]);
-    }
-  }
-  M = wave_max(M);
-  MU = wave_max(MU);
-  float x[R];
+
+  float M = -kFltMax, MU = -kFltMax, l = 0.f, x[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) x[r] = 0.f;
-  float lpart = 0.f;
-  // split weights, 64 at a time across lanes; wave w then sums splits w, w+4, ...
-  for (int c0 = 0; c0 < nsplit; c0 += 64) {
-    const int sp = c0 + lane;
-    float f = 0.f;
-    if (sp < nsplit) {
-      const float *pr = part + sp * stride;
-      const float l = pr[1];
-      if (l > 0.f) {
-        if ((sp & 3) == wave) lpart += l * __builtin_amdgcn_exp2f(pr[0] - M);
-        if (MU != kNegInf && pr[2] != kNegInf) f = __builtin_amdgcn_exp2f(pr[2] - MU);
+  for (int base = wv; base < nsplit; base += 4 * CH) {
+    float4 hd[CH];
+    float v[CH][R];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int sp = base + 4 * c;
+      if (sp < nsplit) {
+        const float *pr = part + (size_t)sp * stride;
+        hd[c] = *reinterpret_cast<const float4 *>(pr);
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[c][r] = pr[kPartHead + lane + 64 * r];
+      } else {
+        hd[c] = make_float4(-kFltMax, 0.f, -kFltMax, 0.f);
+#pragma unroll
+        for (int r = 0; r < R; ++r) v[c][r] = 0.f;
       }
     }
-    s_f[wave][lane] = f;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    const int cnt = min(64, nsplit - c0);
-#pragma unroll 16
-    for (int j = wave; j < cnt; j += 4) {
-      const float fj = s_f[wave][j];
-      const float *row = part + (size_t)(c0 + j) * stride + kPartHead;
 #pragma unroll
-      for (int r = 0; r < R; ++r) x[r] = fmaf(fj, row[lane + 64 * r], x[r]);
+    for (int c = 0; c < CH; ++c) {
+      if (hd[c].y > 0.f) {   // a split with no visible token has l = 0
+        const float mn = fmaxf(M, hd[c].x), mun = fmaxf(MU, hd[c].z);
+        l = l * __builtin_amdgcn_exp2f(M - mn) + hd[c].y * __builtin_amdgcn_exp2f(hd[c].x - mn);
+        const float f0 = __builtin_amdgcn_exp2f(MU - mun), f1 = __builtin_amdgcn_exp2f(hd[c].z - mun);
+#pragma unroll
+        for (int r = 0; r < R; ++r) x[r] = fmaf(x[r], f0, v[c][r] * f1);
+        M = mn;
+        MU = mun;
+      }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
   }
-  const float lw = wave_sum(lpart);
+  if (lane == 0) {
+    s_st[wv][0] = M;
+    s_st[wv][1] = MU;
+    s_st[wv][2] = l;
+  }
 #pragma unroll
-  for (int r = 0; r < R; ++r) s_x[wave][lane + 64 * r] = x[r];
-  if (lane == 0) s_stat[wave][0] = lw;
+  for (int r = 0; r < R; ++r) s_x[wv][lane + 64 * r] = x[r];
   __syncthreads();
-  if (wave != 0) return;
-  const float lsum = s_stat[0][0] + s_stat[1][0] + s_stat[2][0] + s_stat[3][0];
-  const float inv = (lsum > 0.f && MU != kNegInf) ? __builtin_amdgcn_exp2f(MU - M) / lsum : 0.f;
+  if (wv != 0) return;
+  float Mg = -kFltMax, MUg = -kFltMax;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    if (s_st[w][2] > 0.f) {
+      Mg = fmaxf(Mg, s_st[w][0]);
+      MUg = fmaxf(MUg, s_st[w][1]);
+    }
+  float lsum = 0.f, fw[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const bool live = s_st[w][2] > 0.f;
+    lsum += live ? s_st[w][2] * __builtin_amdgcn_exp2f(s_st[w][0] - Mg) : 0.f;
+    fw[w] = live ? __builtin_amdgcn_exp2f(s_st[w][1] - MUg) : 0.f;
+  }
+  const float inv = lsum > 0.f ? __builtin_amdgcn_exp2f(MUg - Mg) / lsum : 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int i = lane + 64 * r;
-    x[r] = (s_x[0][i] + s_x[1][i] + s_x[2][i] + s_x[3][i]) * inv;
+    x[r] = (fw[0] * s_x[0][i] + fw[1] * s_x[1][i] + fw[2] * s_x[2][i] + fw[3] * s_x[3][i]) * inv;
   }
   fwht_wave<R>(x);
   const int t = qq / g, hh = qq % g;

@@ -31,16 +31,58 @@ __device__ inline float load_elem(const void *p, size_t i) {
   }
 }
 
+// Value of lane (lane ^ H) of the wave. H = 1, 2: one DPP quad permutation;
+// H = 4, 8: two DPP moves (a mirror inside 8 or 16 lanes composed with a
+// smaller xor); H = 16: ds_swizzle inside 32 lanes; H = 32: ds_bpermute.
+template <int H>
+__device__ inline float xor_lane(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int y;
+  if constexpr (H == 1) {
+    y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);        // quad_perm [1,0,3,2]
+  } else if constexpr (H == 2) {
+    y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);        // quad_perm [2,3,0,1]
+  } else if constexpr (H == 4) {
+    const int m = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);   // lane ^ 7 (half-row mirror)
+    y = __builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, true);        // then lane ^ 3 (quad_perm [3,2,1,0])
+  } else if constexpr (H == 8) {
+    const int m = __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);   // lane ^ 15 (row mirror)
+    y = __builtin_amdgcn_mov_dpp(m, 0x141, 0xF, 0xF, true);       // then lane ^ 7
+  } else if constexpr (H == 16) {
+    y = __builtin_amdgcn_ds_swizzle(x, 0x401F);                    // and 0x1f, xor 0x10
+  } else {
+    static_assert(H == 32, "lane xor distance");
+    y = __builtin_bit_cast(int, __shfl_xor(v, 32, 64));
+  }
+  return __builtin_bit_cast(float, y);
+}
+
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
+  x += xor_lane<32>(x);
+  x += xor_lane<16>(x);
+  x += xor_lane<8>(x);
+  x += xor_lane<4>(x);
+  x += xor_lane<2>(x);
+  return x + xor_lane<1>(x);
 }
 
 __device__ inline float wave_max(float x) {
+  x = fmaxf(x, xor_lane<32>(x));
+  x = fmaxf(x, xor_lane<16>(x));
+  x = fmaxf(x, xor_lane<8>(x));
+  x = fmaxf(x, xor_lane<4>(x));
+  x = fmaxf(x, xor_lane<2>(x));
+  return fmaxf(x, xor_lane<1>(x));
+}
+
+template <int H, int R>
+__device__ inline void fwht_stage(float (&v)[R], int lane) {
+  const bool upper = lane & H;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+  for (int r = 0; r < R; ++r) {
+    const float o = xor_lane<H>(v[r]);
+    v[r] = upper ? (o - v[r]) : (v[r] + o);
+  }
 }
 
 // Unnormalised Walsh-Hadamard butterflies over D = 64*R values held by one
@@ -49,15 +91,12 @@ __device__ inline float wave_max(float x) {
 template <int R>
 __device__ inline void fwht_wave(float (&v)[R]) {
   const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int h = 1; h < 64; h <<= 1) {
-    const bool upper = lane & h;
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float o = __shfl_xor(v[r], h, 64);
-      v[r] = upper ? (o - v[r]) : (v[r] + o);
-    }
-  }
+  fwht_stage<1>(v, lane);
+  fwht_stage<2>(v, lane);
+  fwht_stage<4>(v, lane);
+  fwht_stage<8>(v, lane);
+  fwht_stage<16>(v, lane);
+  fwht_stage<32>(v, lane);
 #pragma unroll
   for (int hh = 1; hh < R; hh <<= 1) {
 #pragma unroll
