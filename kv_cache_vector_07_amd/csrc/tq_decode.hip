@@ -33,6 +33,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr float kFltMax = 3.402823466e38f;
+// Headroom of a running softmax reference (log2 units): weights relative to it
+// stay below 2^0.8 = 1.74, so weight * 2^30 plus the limb offset 0x80808080
+// stays inside 32 bits.
+constexpr float kSlack = 0.8f;
 constexpr int kPartHead = 4;   // partial record: m, l, mU (log2 units), pad, then acc[d]
 
 
@@ -261,19 +265,35 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       sv[tau] = valid ? sco + __builtin_amdgcn_logf(NV) : kNegInf;   // + log2 N^V
     }
 
-    // ---- online softmax of this wave (log2 units; scores, and scores + log2 N^V for V)
-    const float m_new = fmaxf(m_run, rowmax16(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]))));
-    const float mu_new = fmaxf(mu_run, rowmax16(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    const float alphaU = __builtin_amdgcn_exp2f(mu_run - mu_new);
-    m_run = m_new;
-    mu_run = mu_new;
+    // ---- online softmax of this wave (log2 units; scores, and scores + log2 N^V for V).
+    // m_run / mu_run are references, not exact maxima: they move only when a
+    // score exceeds them by more than kSlack (log2 units), so every V weight
+    // stays below 2^kSlack (its int32 limbs cannot overflow) and most blocks
+    // skip the cross-lane maximum and the rescale.
+    {
+      const float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      const float vmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      if (__any(smax > m_run + kSlack || vmax > mu_run + kSlack)) {
+        const float m_new = fmaxf(m_run, rowmax16(smax));
+        const float mu_new = fmaxf(mu_run, rowmax16(vmax));
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        const float alphaU = __builtin_amdgcn_exp2f(mu_run - mu_new);
+        // the accumulator row of this lane's column lane is query row kg
+        const float aU_row = __shfl(alphaU, 4 * (kg & 3), 64);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) facc[k] *= aU_row;
+        l_lane *= alpha;
+        us_lane *= alphaU;
+        m_run = m_new;
+        mu_run = mu_new;
+      }
+    }
     float ps = 0.f, us = 0.f;
     v4i A[4];   // per plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      ps += __builtin_amdgcn_exp2f(sc[tau] - m_new);
-      const float U = __builtin_amdgcn_exp2f(sv[tau] - mu_new);
+      ps += __builtin_amdgcn_exp2f(sc[tau] - m_run);
+      const float U = __builtin_amdgcn_exp2f(sv[tau] - mu_run);
       us += U;
       const float Ut = __builtin_amdgcn_ldexpf(U, -tau);
 #pragma unroll
@@ -283,10 +303,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         A[j][tau] = (int)t4;
       }
     }
-    l_lane = l_lane * alpha + ps;
-    us_lane = us_lane * alphaU + us;
-    // the accumulator row of this lane's column lane is query row kg
-    const float aU_row = __shfl(alphaU, 4 * (kg & 3), 64);
+    l_lane += ps;
+    us_lane += us;
 
     // ---- V: one 64-token K block, D/16 column blocks x 4 planes
     auto vword = [&](int j, int kp) -> uint32_t {
@@ -313,7 +331,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       }
       // rows 4 kg + r are (query kg, limb r)
       const float v = (float)c[0] + 256.f * (float)c[1] + 65536.f * (float)c[2] + 16777216.f * (float)c[3];
-      facc[k] = fmaf(facc[k], aU_row, delta_u * v);
+      facc[k] = fmaf(delta_u, v, facc[k]);
     }
   };
 
