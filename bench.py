@@ -63,6 +63,49 @@ def read_traffic(workload: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
+def dense_baseline(dense, qs, seq, scale, tq_dec_ms, sh, log):
+    """The uncompressed bf16 decode kernel on the same K, V and queries, over
+    rotating device copies (>= 1 GiB), against the compressed split kernel."""
+    import torch
+    from kv_cache_vector_07_amd import tq
+    k0, v0 = dense
+    B, H, Lm, d = k0.shape
+    nbytes = 2 * k0.numel() * 2
+    R = max(1, math.ceil(ROTATE_BYTES / nbytes))
+    ks = [k0] + [k0.clone() for _ in range(R - 1)]
+    vs = [v0] + [v0.clone() for _ in range(R - 1)]
+    out = torch.empty(qs[0].shape, dtype=torch.float32, device=k0.device)
+    L_ = tq.lib()
+    size = C.c_size_t(0)
+    n_q, Hq = qs[0].shape[1], qs[0].shape[2]
+    qdt = tq._dtype_code(qs[0])
+    args = lambda i, ws: (ks[i % R].data_ptr(), vs[i % R].data_ptr(), d, H, Lm, qs[i % len(qs)].data_ptr(),
+                          qdt, B, n_q, Hq, seq.data_ptr(), scale, out.data_ptr(), ws)
+    assert L_.tq_dense_attn_decode(*args(0, None), C.byref(size), None) == 0
+    ws = torch.empty(size.value, dtype=torch.uint8, device=k0.device)
+    for i in range(8):
+        sz = C.c_size_t(ws.numel())
+        assert L_.tq_dense_attn_decode(*args(i, ws.data_ptr()), C.byref(sz), sh) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 64
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        sz = C.c_size_t(ws.numel())
+        L_.tq_dense_attn_decode(*args(i, ws.data_ptr()), C.byref(sz), sh)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    gbs = nbytes / (ms / 1e3) / 1e9
+    log(f"[bench] dense bf16 baseline: {ms * 1e3:.2f} us/step ({gbs:.0f} GB/s), {R} copies")
+    return {"kernel": "dense_decode_kernel + merge", "us_per_step": round(ms * 1e3, 3),
+            "bytes_per_step": nbytes, "achieved_GBps": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "rotating_copies": R,
+            "speedup_compressed_split_vs_dense": round(ms / tq_dec_ms, 3),
+            "speedup_vs_dense_at_hbm_peak": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e3 / tq_dec_ms, 3),
+            "ideal_byte_ratio": round(nbytes / (Lm * B * H * kv_bytes_per_token_head(d)), 3)}
+
+
 def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0):
     """The CPU reference (numpy float64, as it stands) timed on this host on a
     bounded sample: whole decode steps over every KV head of sequence 0, and
@@ -107,6 +150,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-launches", type=int, default=512)
+    ap.add_argument("--no-dense-baseline", action="store_true",
+                    help="skip the uncompressed bf16 decode baseline")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -177,6 +222,13 @@ def main():
     e2.record()
     e2.synchronize()
     enc_k_ms, enc_v_ms = e0.elapsed_time(e1), e1.elapsed_time(e2)
+    # the uncompressed bf16 baseline reads the same K and V densely (single
+    # sequence workloads: the staged chunks are the sequence in order)
+    dense = None
+    if B == 1 and not args.no_dense_baseline and tdt == torch.bfloat16:
+        # [1][Hkv][L][d]: each KV head's tokens contiguous
+        dense = tuple(torch.cat([c[i] for c in calls]).transpose(0, 1).contiguous().unsqueeze(0)
+                      for i in (0, 1))
     del calls
     log(f"[bench] cache encoded: {n_vec} K and V vectors")
     copies = [base]
@@ -311,6 +363,8 @@ def main():
                      "traffic": traffic, "kernel": dec_kernel,
                      "bytes_per_launch": kv_bytes},
     }
+    if dense is not None:
+        result["dense_bf16_baseline"] = dense_baseline(dense, qs, seq, scale, dec_ms, sh, log)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU reference on a bounded sample")
         kp = base.k_pool.cpu().numpy()

@@ -223,6 +223,22 @@ int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
                          size_t workspace_bytes, void *stream);
 
 /*
+ * Uncompressed baseline: decode attention over dense bf16 K and V
+ * ([batch][Hkv][max_len][d], d = head_dim), softmax(q K^T * scale) V, with the
+ * same split-K scheme and merge as tq_attn_decode. It exists to measure the
+ * compressed path against; it is not part of the compressed cache.
+ * q: [batch][n_q][Hq][d] fp32/bf16; every query sees seq_lens[b] tokens;
+ * out: [batch][n_q][Hq][d] fp32. At most 4 query rows per KV head
+ * (Hq/Hkv * n_q <= 4), else TQ_EUNSUPPORTED. Workspace as tq_attn_decode
+ * (workspace == NULL: size query). Errors: TQ_EINVAL (null pointer or bad size),
+ * TQ_EALIGN (k, v, q, out not 16-byte or workspace not 256-byte aligned).
+ */
+int tq_dense_attn_decode(const void *k, const void *v, int32_t head_dim, int32_t n_kv_heads,
+                         int32_t max_len, const void *q, int32_t q_dtype, int32_t batch,
+                         int32_t n_q, int32_t n_q_heads, const int32_t *seq_lens, float scale,
+                         float *out, void *workspace, size_t *workspace_bytes, void *stream);
+
+/*
  * Dequantise records back to the original domain (float32 [n_tokens][Hkv][d]):
  *   which = 0 (K): N * Pi(c[code] + sqrt(pi/2)/m * G * S^T sigma)  (with_qjl = 1)
  *                  N * Pi c[code]                                    (with_qjl = 0)

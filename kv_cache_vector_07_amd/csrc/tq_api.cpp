@@ -1,6 +1,8 @@
 // C-ABI entry points: argument checks, the host-side codebook / QJL matrix,
 // the decode split plan and workspace sizing. Device work lives in *.hip.
 #include <math.h>
+
+#include <algorithm>
 #include <string.h>
 
 #include "tq_internal.h"
@@ -460,6 +462,65 @@ int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   tq::DecodeArgs a = decode_args(c, nullptr, batch, n_q, n_q_heads, nullptr, max_pages, nullptr, 0,
                                  0.f, out, (uint8_t *)workspace, plan);
   return hip_status(tq::launch_decode_merge(a, c->head_dim, (hipStream_t)stream));
+}
+
+int tq_dense_attn_decode(const void *k, const void *v, int32_t head_dim, int32_t n_kv_heads,
+                         int32_t max_len, const void *q, int32_t q_dtype, int32_t batch,
+                         int32_t n_q, int32_t n_q_heads, const int32_t *seq_lens, float scale,
+                         float *out, void *workspace, size_t *workspace_bytes, void *stream) {
+  if (!workspace_bytes) return TQ_EINVAL;
+  if (head_dim <= 0 || n_kv_heads <= 0 || max_len <= 0 || batch <= 0 || n_q <= 0 ||
+      n_q_heads <= 0 || n_q_heads % n_kv_heads)
+    return TQ_EINVAL;
+  if (!supported_dim(head_dim) || (q_dtype != TQ_F32 && q_dtype != TQ_BF16)) return TQ_EUNSUPPORTED;
+  const int group = n_q_heads / n_kv_heads * n_q;
+  if (group > tq::kMfmaMaxGroup) return TQ_EUNSUPPORTED;
+  // about 512 workgroups, whole 256-token ranges per split
+  const long work = (long)batch * n_kv_heads * ((max_len + 255) / 256);
+  const int tps = (int)std::max(1L, (work + 511) / 512) * 256;
+  const int n_split = (max_len + tps - 1) / tps;
+  const size_t need =
+      round_up((size_t)batch * n_kv_heads * n_split * group * (head_dim + 4) * sizeof(float), 256);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return TQ_OK;
+  }
+  if (*workspace_bytes < need) {
+    *workspace_bytes = need;
+    return TQ_EWORKSPACE;
+  }
+  if (!k || !v || !q || !seq_lens || !out) return TQ_EINVAL;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(q, 16) || !aligned(out, 16) ||
+      !aligned(workspace, 256))
+    return TQ_EALIGN;
+  tq::DenseArgs da;
+  da.k = (const uint16_t *)k;
+  da.v = (const uint16_t *)v;
+  da.max_len = max_len;
+  da.q = q;
+  da.q_dtype = q_dtype;
+  da.seq_lens = seq_lens;
+  da.batch = batch;
+  da.n_q = n_q;
+  da.n_q_heads = n_q_heads;
+  da.n_kv_heads = n_kv_heads;
+  da.tokens_per_split = tps;
+  da.n_split = n_split;
+  da.scale = scale;
+  da.partials = (float *)workspace;
+  hipStream_t s = (hipStream_t)stream;
+  if (tq::launch_dense_split(da, head_dim, s) != hipSuccess) return TQ_EHIP;
+  tq::DecodeArgs ma = {};
+  ma.partials = (float *)workspace;
+  ma.out = out;
+  ma.batch = batch;
+  ma.n_q = n_q;
+  ma.n_q_heads = n_q_heads;
+  ma.n_kv_heads = n_kv_heads;
+  ma.plan.group = group;
+  ma.plan.n_split = n_split;
+  ma.plan.qgroups = 1;
+  return hip_status(tq::launch_decode_merge(ma, head_dim, s, false));
 }
 
 int tq_dequant(const tq_cache *c, int32_t which, int32_t with_qjl, const int32_t *slots,

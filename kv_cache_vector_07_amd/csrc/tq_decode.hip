@@ -210,42 +210,44 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // ---- scores: lane (n, kg) ends with the score of token blk0 + 16 tau + 4 kg + lam
     const uint32_t gw[8] = {d.g[0].x, d.g[0].y, d.g[0].z, d.g[0].w, d.g[1].x, d.g[1].y, d.g[1].z, d.g[1].w};
     float sc[4], sv[4];
+    // the four 16-token tiles' MFMAs are interleaved (consecutive MFMAs are
+    // independent); the query operand of each step is shared by the four
+    v4i c1[4], c2[4];
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      v4i c1 = {0, 0, 0, 0}, c2 = {0, 0, 0, 0};
+    for (int tau = 0; tau < 4; ++tau) c1[tau] = c2[tau] = v4i{0, 0, 0, 0};
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const uint4 w = d.kw[tau][c];
-        const uint32_t pl[4] = {w.x, w.y, w.z, w.x ^ w.y ^ w.z};
+    for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            v4i op;
-            op.x = (int)(pl[j] & (0x01010101u << (4 * hh)));
-            op.y = (int)(pl[j] & (0x02020202u << (4 * hh)));
-            op.z = (int)(pl[j] & (0x04040404u << (4 * hh)));
-            op.w = (int)(pl[j] & (0x08080808u << (4 * hh)));
-            c1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 2 * j + hh) * 64 + qo], c1, 0, 0, 0);
-          }
-        }
+      for (int j = 0; j < 5; ++j) {   // code planes b0, b1, b2, b0^b1^b2, then the sign plane
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          v4i op;
-          op.x = (int)(w.w & (0x01010101u << (4 * hh)));
-          op.y = (int)(w.w & (0x02020202u << (4 * hh)));
-          op.z = (int)(w.w & (0x04040404u << (4 * hh)));
-          op.w = (int)(w.w & (0x08080808u << (4 * hh)));
-          c2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, s_qop[(10 * c + 8 + hh) * 64 + qo], c2, 0, 0, 0);
+          const v4i qop = s_qop[(10 * c + 2 * j + hh) * 64 + qo];
+#pragma unroll
+          for (int tau = 0; tau < 4; ++tau) {
+            const uint4 w = d.kw[tau][c];
+            const uint32_t pl = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : j == 3 ? (w.x ^ w.y ^ w.z) : w.w;
+            v4i op;
+            op.x = (int)(pl & (0x01010101u << (4 * hh)));
+            op.y = (int)(pl & (0x02020202u << (4 * hh)));
+            op.z = (int)(pl & (0x04040404u << (4 * hh)));
+            op.w = (int)(pl & (0x08080808u << (4 * hh)));
+            if (j < 4)
+              c1[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, qop, c1[tau], 0, 0, 0);
+            else
+              c2[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, qop, c2[tau], 0, 0, 0);
+          }
         }
       }
+    }
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
       // this lane's limb of (S1 + kappa G S2) for the 4 tokens r of the column group;
       // G of (tau, r) is side entry 4 r + tau of the lane's 16
       float t[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float Gr = f16_bits_to_f32((uint16_t)(gw[2 * r + (tau >> 1)] >> (16 * (tau & 1))));
-        t[r] = fmaf((float)c2[r] * lsc2, Gr, (float)c1[r] * lsc1);
+        t[r] = fmaf((float)c2[tau][r] * lsc2, Gr, (float)c1[tau][r] * lsc1);
       }
       // transpose-reduce over the quad: lane lam keeps token lam
       const bool o1 = lam & 1, o2 = lam & 2;
@@ -315,23 +317,31 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     uint32_t xw[D / 32];
 #pragma unroll
     for (int kp = 0; kp < D / 32; ++kp) xw[kp] = vword(0, kp) ^ vword(1, kp) ^ vword(2, kp);
+    // column blocks 2 kp and 2 kp + 1 come from the low and high nibbles of the
+    // same words; their two accumulation chains are interleaved
 #pragma unroll
-    for (int k = 0; k < NB; ++k) {
-      const int kp = k >> 1, sh = 4 * (k & 1);
-      const uint32_t wj[4] = {vword(0, kp) >> sh, vword(1, kp) >> sh, vword(2, kp) >> sh, xw[kp] >> sh};
-      v4i c = {0, 0, 0, 0};
+    for (int kp = 0; kp < D / 32; ++kp) {
+      const uint32_t wj[4] = {vword(0, kp), vword(1, kp), vword(2, kp), xw[kp]};
+      v4i c[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v4i bop;   // VGPR tau, byte r: token 16 tau + 4 kg + r, bit value 2^tau
-        bop.x = (int)(wj[j] & 0x01010101u);
-        bop.y = (int)(wj[j] & 0x02020202u);
-        bop.z = (int)(wj[j] & 0x04040404u);
-        bop.w = (int)(wj[j] & 0x08080808u);
-        c = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bop, c, 0, 0, 0);
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w = wj[j] >> (4 * h);
+          v4i bop;   // VGPR tau, byte r: token 16 tau + 4 kg + r, bit value 2^tau
+          bop.x = (int)(w & 0x01010101u);
+          bop.y = (int)(w & 0x02020202u);
+          bop.z = (int)(w & 0x04040404u);
+          bop.w = (int)(w & 0x08080808u);
+          c[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bop, c[h], 0, 0, 0);
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // rows 4 kg + r are (query kg, limb r)
+        const float v = (float)c[h][0] + 256.f * (float)c[h][1] + 65536.f * (float)c[h][2] +
+                        16777216.f * (float)c[h][3];
+        facc[2 * kp + h] = fmaf(delta_u, v, facc[2 * kp + h]);
       }
-      // rows 4 kg + r are (query kg, limb r)
-      const float v = (float)c[0] + 256.f * (float)c[1] + 65536.f * (float)c[2] + 16777216.f * (float)c[3];
-      facc[k] = fmaf(delta_u, v, facc[k]);
     }
   };
 
@@ -416,7 +426,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 // w, w + 4, ...: it issues the loads of up to 8 of them at once (the headers are
 // wave-uniform) and folds them with a running log-sum-exp; the four waves then
 // combine in LDS, and wave 0 applies the inverse rotation and writes the row.
-template <int D>
+template <int D, bool kRotate>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int R = D / 64;
   constexpr int CH = 8;   // splits per wave in flight
@@ -491,11 +501,15 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
     const int i = lane + 64 * r;
     x[r] = (fw[0] * s_x[0][i] + fw[1] * s_x[1][i] + fw[2] * s_x[2][i] + fw[3] * s_x[3][i]) * inv;
   }
-  fwht_wave<R>(x);
+  if constexpr (kRotate) {
+    fwht_wave<R>(x);
+#pragma unroll
+    for (int r = 0; r < R; ++r) x[r] *= rsqrt_dim<D>();
+  }
   const int t = qq / g, hh = qq % g;
   float *o = a.out + (((size_t)b * a.n_q + t) * Hq + kvh * g + hh) * D;
 #pragma unroll
-  for (int r = 0; r < R; ++r) o[lane + 64 * r] = x[r] * rsqrt_dim<D>();
+  for (int r = 0; r < R; ++r) o[lane + 64 * r] = x[r];
 }
 
 template <int D>
@@ -522,12 +536,19 @@ hipError_t launch_decode_split(const DecodeArgs &a, int d, hipStream_t s) {
   return d == 128 ? launch_split_dim<128>(a, s) : launch_split_dim<256>(a, s);
 }
 
-hipError_t launch_decode_merge(const DecodeArgs &a, int d, hipStream_t s) {
+hipError_t launch_decode_merge(const DecodeArgs &a, int d, hipStream_t s, bool rotate) {
   const dim3 grid(a.plan.group, a.n_kv_heads, a.batch);
-  if (d == 128)
-    hipLaunchKernelGGL((merge_kernel<128>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((merge_kernel<256>), grid, dim3(256), 0, s, a);
+  if (d == 128) {
+    if (rotate)
+      hipLaunchKernelGGL((merge_kernel<128, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<128, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (rotate)
+      hipLaunchKernelGGL((merge_kernel<256, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((merge_kernel<256, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -116,6 +116,22 @@ bool step_prologue_fits(const EncodeArgs &k, const PrepArgs &p);
 hipError_t launch_step_prologue(const EncodeArgs &k, const EncodeArgs &v, const PrepArgs &p, int d,
                                 hipStream_t s);
 hipError_t launch_decode_split(const DecodeArgs &a, int d, hipStream_t s);
-hipError_t launch_decode_merge(const DecodeArgs &a, int d, hipStream_t s);
+// Merge of split partials; rotate = apply the inverse rotation (the compressed
+// path accumulates in the rotated domain, the dense baseline does not).
+hipError_t launch_decode_merge(const DecodeArgs &a, int d, hipStream_t s, bool rotate = true);
+
+// Uncompressed bf16 baseline: K and V dense as [batch][Hkv][max_len][d].
+struct DenseArgs {
+  const uint16_t *k, *v;
+  int max_len;
+  const void *q;
+  int q_dtype;
+  const int32_t *seq_lens;
+  int batch, n_q, n_q_heads, n_kv_heads;
+  int tokens_per_split, n_split;
+  float scale;
+  float *partials;
+};
+hipError_t launch_dense_split(const DenseArgs &a, int d, hipStream_t s);
 
 }  // namespace tq

@@ -24,7 +24,7 @@ TQ_MAX_GROUP = 16
 EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_encode_k",
            "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_append_decode",
            "tq_attn_decode_prepared", "tq_attn_decode_split", "tq_attn_decode_merge",
-           "tq_dequant", "tq_status_string")
+           "tq_dense_attn_decode", "tq_dequant", "tq_status_string")
 
 
 class TqError(RuntimeError):
@@ -70,9 +70,11 @@ def lib():
                                        C.POINTER(sz), vp]
     L.tq_attn_decode_merge.argtypes = [vp, i32, i32, i32, i32, vp, vp, sz, vp]
     L.tq_dequant.argtypes = [vp, i32, i32, vp, i32, vp, vp]
+    L.tq_dense_attn_decode.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, f32,
+                                       vp, vp, C.POINTER(sz), vp]
     for name in ("tq_build_codebook", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
                  "tq_attn_decode", "tq_append_decode", "tq_attn_decode_prepared", "tq_attn_decode_split",
-                 "tq_attn_decode_merge", "tq_dequant"):
+                 "tq_attn_decode_merge", "tq_dense_attn_decode", "tq_dequant"):
         getattr(L, name).restype = i32
     _lib = L
     return L
@@ -295,4 +297,24 @@ def tq_dequant(cache: Cache, which: int, with_qjl: int, slots, out=None, stream=
     st = lib().tq_dequant(cache.ref, int(which), int(with_qjl), slots.data_ptr(), n,
                           out.data_ptr(), _stream(stream))
     _check(st, "tq_dequant")
+    return out
+
+
+def tq_dense_attn_decode(k, v, q, seq_lens, scale=None, out=None, workspace=None, stream=None):
+    """Uncompressed baseline. k, v: bf16 [B][Hkv][max_len][d]; q: [B][n_q][Hq][d]."""
+    import torch
+    B, Hkv, max_len, d = k.shape
+    _, n_q, Hq, _ = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=q.device)
+    L = lib()
+    args = lambda ws: (k.data_ptr(), v.data_ptr(), d, Hkv, max_len, q.data_ptr(), _dtype_code(q), B,
+                       n_q, Hq, seq_lens.data_ptr(), scale, out.data_ptr(), ws)
+    size = C.c_size_t(0)
+    _check(L.tq_dense_attn_decode(*args(None), C.byref(size), None), "tq_dense_attn_decode (size)")
+    ws = workspace if workspace is not None else torch.empty(size.value, dtype=torch.uint8, device=q.device)
+    size = C.c_size_t(ws.numel())
+    _check(L.tq_dense_attn_decode(*args(ws.data_ptr()), C.byref(size), _stream(stream)),
+           "tq_dense_attn_decode")
     return out

@@ -52,7 +52,7 @@ __all__ = [
     "codebook", "splitmix64", "qjl_matrix", "fp16_rne", "quantize", "encode",
     "k_page_bytes", "v_page_bytes", "pack_k", "pack_v", "unpack_k", "unpack_v",
     "gather_k", "gather_v", "rotate_query", "score", "attn_decode", "dequant_k",
-    "dequant_v", "bf16_to_f64",
+    "dequant_v", "bf16_to_f64", "dense_attn_decode",
 ]
 
 # sqrt(pi/2): the QJL estimator constant numerator (R9); divided by m at use.
@@ -507,3 +507,27 @@ def bf16_to_f64(bits) -> np.ndarray:
     """Exact value of bfloat16 bit patterns (uint16) as float64."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return b.view(np.float32).astype(np.float64)
+
+
+def dense_attn_decode(k, v, q, seq_lens, scale):
+    """Plain softmax(q K^T * scale) V over dense, uncompressed K and V
+    ([B][max_len][Hkv][d]); q [B][n_q][Hq][d]; query head h reads KV head
+    h // (Hq / Hkv) (R15); every query sees seq_lens[b] tokens. The baseline the
+    compressed path is measured against, not part of the method."""
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    q = np.asarray(q, np.float64)
+    B, n_q, Hq, d = q.shape
+    H = k.shape[2]
+    g = Hq // H
+    out = np.zeros((B, n_q, Hq, d))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        for t in range(n_q):
+            for h in range(Hq):
+                lg = scale * (k[b, :L, h // g] @ q[b, t, h])
+                w = np.exp(lg - lg.max())
+                out[b, t, h] = (w / w.sum()) @ v[b, :L, h // g]
+    return out

@@ -291,3 +291,30 @@ def test_append_decode_matches_separate_calls_and_reference(tq, d, Hq, nq):
     err = Hn.attn_rel_err(out_a.cpu().numpy(), ref)
     print(f"  max rel err {err:.3e}", flush=True)
     assert err <= Hn.ATTN_TOL
+
+
+@pytest.mark.parametrize("d,Hq,nq,lens", [(128, 16, 1, [700, 257]), (128, 32, 1, [1000, 1]),
+                                          (256, 16, 2, [300, 64]), (128, 8, 2, [513, 0])])
+def test_dense_baseline_parity(tq, d, Hq, nq, lens):
+    """The uncompressed bf16 baseline kernel against plain softmax attention."""
+    H = 8
+    print(f"[dense baseline] d={d} Hq={Hq} n_q={nq} lens={lens}", flush=True)
+    w = I.Workload(f"dense{d}", len(lens), Hq, H, d, "bf16", "outlier", 41, n_q=nq, fixed_len=1)
+    Lm = max(max(lens), 1)
+    k = np.zeros((len(lens), Lm, H, d), np.float32)
+    v = np.zeros_like(k)
+    for b, L in enumerate(lens):
+        if L:
+            k[b, :L] = I.kv_tokens(w, "k", b, 0, L)
+            v[b, :L] = I.kv_tokens(w, "v", b, 0, L)
+    q = I.queries(w, 0)
+    # the kernel takes [B][Hkv][max_len][d]
+    kt = torch.from_numpy(k).to("cuda", torch.bfloat16).permute(0, 2, 1, 3).contiguous()
+    vt = torch.from_numpy(v).to("cuda", torch.bfloat16).permute(0, 2, 1, 3).contiguous()
+    qt = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = tq.tq_dense_attn_decode(kt, vt, qt, sl).cpu().numpy()
+    ref = O.dense_attn_decode(k, v, q, lens, Hn.scale_of(d))
+    err = Hn.attn_rel_err(out, ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= Hn.ATTN_TOL

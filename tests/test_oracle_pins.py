@@ -387,3 +387,33 @@ def test_dequant_without_qjl_drops_only_the_sign_term():
     rel = np.linalg.norm(mse - x, axis=1) / np.linalg.norm(x, axis=1)
     assert np.all(rel < 0.3)
     assert not np.allclose(full, mse)
+
+
+def test_dense_attention_matches_compressed_attention_over_dequantised_cache():
+    """Two independent formulas: the dense baseline run on the dequantised K and
+    V equals the compressed-cache attention (scores from the packed bits)."""
+    c = _small_cache()
+    scale = 1 / math.sqrt(c["d"])
+    out = O.attn_decode(c["kp"], c["vp"], c["cb"], c["S"], c["q"], c["table"], c["lens"],
+                        c["H"], c["P"], scale)
+    B = len(c["lens"])
+    Lm = int(max(c["lens"]))
+    k = np.zeros((B, Lm, c["H"], c["d"]))
+    v = np.zeros_like(k)
+    for b in range(B):
+        Kt, Vt = c["dense"][b]
+        k[b, :len(Kt)] = Kt
+        v[b, :len(Vt)] = Vt
+    ref = O.dense_attn_decode(k, v, c["q"], c["lens"], scale)
+    assert np.max(np.abs(out - ref)) < 1e-12
+
+
+def test_dense_attention_special_cases():
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((1, 5, 2, 8))
+    v = rng.standard_normal((1, 5, 2, 8))
+    q = rng.standard_normal((1, 1, 4, 8))
+    out = O.dense_attn_decode(k, v, q, [1], 0.3)
+    assert np.allclose(out[0, 0, 3], v[0, 0, 1])
+    out = O.dense_attn_decode(k, v, np.zeros_like(q), [5], 0.3)
+    assert np.allclose(out[0, 0, 0], v[0, :, 0].mean(0))
