@@ -16,20 +16,22 @@
 // release per workgroup, which on this GPU writes back and invalidates the whole
 // L2 of the XCD every time.)
 //
-// Scores are an int8 MFMA contraction. The codebook is odd (c[7-k] = -c[k]),
-// so the 3-bit code splits over four binary planes,
+// Scores are a block-scaled fp4 x fp8 MFMA contraction. The codebook is odd
+// (c[7-k] = -c[k]), so the 3-bit code splits over four binary planes,
 // c[idx] = 2 (a0 b0 + a1 b1 + a2 b2 + a3 (b0^b1^b2)) - c7, and each key bit plane
-// becomes an int8 operand with one AND per four coordinates; the query side is
-// exact to fp32 precision as four balanced int8 limbs on the MFMA columns
-// (4 query rows x 4 limbs per query group). V is accumulated with the same
-// planes on int8 MFMA: the softmax weight times each plane weight, as four int8
-// limbs, against the V bit planes. Every product is exact in int32.
+// becomes an fp4 operand (one AND per eight coordinates, the bit's position
+// folded into the fp4 value); the query side is four fp8 limbs with a power-of-two
+// scale per 32 coordinates on the MFMA columns (4 query rows x 4 limbs per query
+// group), about 2^-16 of the largest term per block. V is accumulated with the
+// same planes on int8 MFMA: the softmax weight times each plane weight, as four
+// int8 limbs, against the V bit planes; every product there is exact in int32.
 #include "tq_device.h"
 
 namespace tq {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr float kFltMax = 3.402823466e38f;
@@ -74,8 +76,8 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // loads to the V accumulation, with its own online softmax; the four waves of
 // the workgroup combine once at the end into one partial per query row.
 //
-// Scores: int8 MFMA over the key bit planes (A: key bytes, 16 tokens x 64 slots;
-// B: query limbs, 16 rows = 4 query rows x 4 limbs). The limb partials of a
+// Scores: scaled MFMA over the key bit planes (A: key nibbles, 16 tokens x 128
+// coordinates; B: query limbs, 16 columns = 4 query rows x 4 limbs). The limb partials of a
 // token sit in the four lanes of a quad; a transpose-reduce leaves lane L of the
 // quad with the full score of token L, so every later per-score step runs once.
 // V: int8 MFMA with the softmax weight (times each plane weight) as 4 int8 limbs
@@ -94,6 +96,17 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // no copy is needed.
 // (At d = 256 the V words are loaded at the start of the block instead, to keep
 // two waves per SIMD.)
+// Copies the packed scoring operand of a query group (NMU x 64 lanes x 32 bytes,
+// then NMU x 64 scale words) into LDS.
+template <int NMU>
+__device__ inline void stage_query(const uint8_t *grp, v8i *s_qop, int *s_qsc, int tid) {
+  const uint4 *src = reinterpret_cast<const uint4 *>(grp);
+  uint4 *dst = reinterpret_cast<uint4 *>(s_qop);
+  for (int e = tid; e < NMU * 128; e += 256) dst[e] = src[e];
+  const int *ssrc = reinterpret_cast<const int *>(grp + (size_t)NMU * 2048);
+  for (int e = tid; e < NMU * 64; e += 256) s_qsc[e] = ssrc[e];
+}
+
 template <int D>
 struct MfmaBlock {
   static constexpr bool kPrefetchV = D == 128;
@@ -105,7 +118,7 @@ struct MfmaBlock {
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NMU = 10 * (D / 128);       // int8 MFMAs per 16-token scoring tile
+  constexpr int NMU = 5 * (D / 128);        // scaled MFMAs per 16-token scoring tile
   constexpr int NCH = D / 128;              // 16-byte key chunks per lane and token
   constexpr int KREC = D / 2;
   constexpr size_t KCODES = (size_t)kPage * KREC;
@@ -116,7 +129,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 
   __shared__ float s_wm[4][4][kMfmaMaxGroup];     // per wave: m, l, mU, sum U of each row
   __shared__ float s_wacc[4][kMfmaMaxGroup][D];   // per wave V numerators
-  __shared__ v4i s_qop[NMU * 64];                  // packed query operand, [mfma][lane]
+  __shared__ v8i s_qop[NMU * 64];                  // packed query operand, [mfma][lane]
+  __shared__ int s_qsc[NMU * 64];                  // its block scales (E8M0), [mfma][lane]
 
   const int QG = a.plan.qgroups;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / QG, rho = blockIdx.z % QG;
@@ -129,9 +143,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int L = a.seq_lens[b];
 
   const uint8_t *grp = a.packed + (((size_t)b * H + kvh) * QG + rho) * packed_group_bytes(D);
-  const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * 1024)[q];
-  const float lsc1 = rc.x * (float)(1 << (8 * lam));
-  const float lsc2 = rc.y * (float)(1 << (8 * lam)) * qjl_kappa<D>();
+  const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * (2048 + 256))[q];
   const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w * qjl_kappa<D>();
   const int vis = q < G ? (a.causal_tail ? L - (a.n_q - 1 - (qbase + q) / g) : L) : 0;
   const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
@@ -211,31 +223,28 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     const uint32_t gw[8] = {d.g[0].x, d.g[0].y, d.g[0].z, d.g[0].w, d.g[1].x, d.g[1].y, d.g[1].z, d.g[1].w};
     float sc[4], sv[4];
     // the four 16-token tiles' MFMAs are interleaved (consecutive MFMAs are
-    // independent); the query operand of each step is shared by the four
-    v4i c1[4], c2[4];
+    // independent); the query operand of each step is shared by the four.
+    // Key operand (fp4 e2m1): nibble m of dword v holds plane bit 4 m + v, as
+    // 0.5, 1, 2, 2 (bit 3 shifted down one place); the query side carries 1 / value.
+    v4f c1[4], c2[4];
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) c1[tau] = c2[tau] = v4i{0, 0, 0, 0};
+    for (int tau = 0; tau < 4; ++tau) c1[tau] = c2[tau] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
       for (int j = 0; j < 5; ++j) {   // code planes b0, b1, b2, b0^b1^b2, then the sign plane
+        const v8i qop = s_qop[(5 * c + j) * 64 + qo];
+        const int qsc = s_qsc[(5 * c + j) * 64 + qo];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const v4i qop = s_qop[(10 * c + 2 * j + hh) * 64 + qo];
-#pragma unroll
-          for (int tau = 0; tau < 4; ++tau) {
-            const uint4 w = d.kw[tau][c];
-            const uint32_t pl = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : j == 3 ? (w.x ^ w.y ^ w.z) : w.w;
-            v4i op;
-            op.x = (int)(pl & (0x01010101u << (4 * hh)));
-            op.y = (int)(pl & (0x02020202u << (4 * hh)));
-            op.z = (int)(pl & (0x04040404u << (4 * hh)));
-            op.w = (int)(pl & (0x08080808u << (4 * hh)));
-            if (j < 4)
-              c1[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, qop, c1[tau], 0, 0, 0);
-            else
-              c2[tau] = __builtin_amdgcn_mfma_i32_16x16x64_i8(op, qop, c2[tau], 0, 0, 0);
-          }
+        for (int tau = 0; tau < 4; ++tau) {
+          const uint4 w = d.kw[tau][c];
+          const uint32_t pl = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : j == 3 ? (w.x ^ w.y ^ w.z) : w.w;
+          const v8i op = {(int)(pl & 0x11111111u), (int)(pl & 0x22222222u), (int)(pl & 0x44444444u),
+                          (int)((pl >> 1) & 0x44444444u), 0, 0, 0, 0};
+          if (j < 4)
+            c1[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(op, qop, c1[tau], 4, 0, 0, 127, 0, qsc);
+          else
+            c2[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(op, qop, c2[tau], 4, 0, 0, 127, 0, qsc);
         }
       }
     }
@@ -247,7 +256,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float Gr = f16_bits_to_f32((uint16_t)(gw[2 * r + (tau >> 1)] >> (16 * (tau & 1))));
-        t[r] = fmaf((float)c2[tau][r] * lsc2, Gr, (float)c1[tau][r] * lsc1);
+        t[r] = fmaf(c2[tau][r], Gr, c1[tau][r]);
       }
       // transpose-reduce over the quad: lane lam keeps token lam
       const bool o1 = lam & 1, o2 = lam & 2;
@@ -351,7 +360,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     MfmaBlock<D> d0, d1;
     if (pg0 < pg1) load_block(d0, pg0);
     // the packed query operand is shared by the four waves: keep it in LDS
-    for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
+    stage_query<NMU>(grp, s_qop, s_qsc, tid);
     __syncthreads();
     for (int pg = pg0; pg < pg1; pg += 2) {
       if (pg + 1 < pg1) load_block(d1, pg + 1);
@@ -362,7 +371,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
   } else {
     // d = 256: one register set (two would cost the second wave per SIMD)
-    for (int e = tid; e < NMU * 64; e += 256) s_qop[e] = reinterpret_cast<const v4i *>(grp)[e];
+    stage_query<NMU>(grp, s_qop, s_qsc, tid);
     __syncthreads();
     for (int pg = pg0; pg < pg1; ++pg) {
       MfmaBlock<D> d0;

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
 template <int D, int DT>
 __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   constexpr int R = D / 64;
-  constexpr int NMU = 10 * (D / 128);
+  constexpr int NMU = 5 * (D / 128);   // scoring MFMAs per 16-token tile
   constexpr int RPW = D / 4;         // rows of S per wave
   constexpr int LPR = 64 / RPW;      // lanes per row of S: 2 (d = 128) or 1 (d = 256)
   constexpr int EPL = D / LPR;       // elements of a row per lane
@@ -345,65 +345,75 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   if (a.packed == nullptr) return;
   __syncthreads();
 
-  // scales of this row (every wave computes them): |value / delta| < 2^30, so
-  // four balanced base-256 limbs hold each scaled value
+  // Scoring operand of this row for the fp4 x fp8 block-scaled MFMA
+  // (16x16x128): MFMA mu = 5 c + pl scores coordinate chunk c (coordinates
+  // 128 c .. 128 c + 127) against key plane pl (code bits 0..2, their xor, then
+  // the QJL sign). Key side (fp4): in lane group kq (coordinate group
+  // s = kq + 4 c) nibble slot n = 8 v + m holds bit 4 m + v of the plane word,
+  // i.e. coordinate 32 s + 4 m + v, with value 0.5, 1, 2, 2 for v = 0..3 (v = 3
+  // is shifted down one bit). Query side (fp8 e4m3): the value paired with that
+  // slot is y / value, y = w_pl * q~_i (code planes; c[idx] = sum_pl w_pl b_pl - c7)
+  // or 2 kappa p_i (sign plane, sigma = 2 b - 1), as four limbs on the columns
+  // 4 q + limb, each limb with an E8M0 scale per 32-slot block, so the MFMA sums
+  // of the four limb columns add up to the full product. Pairing (measured): key
+  // lane group kq, slot n <-> query lane group 2 (kq & 1) + n / 16, byte
+  // 16 (kq / 2) + n % 16; the query scale of slot block kq sits in lane 16 kq + column.
   float w[4];
   plane_weights(a.cb, w);
-  const float wmax = fmaxf(fmaxf(fabsf(w[0]), fabsf(w[1])), fmaxf(fabsf(w[2]), fabsf(w[3])));
-  float mq = 0.f, mp = 0.f, sq = 0.f, sp = 0.f;
+  float sq = 0.f, sp = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float x = s_q[lane + 64 * r], y = s_p[lane + 64 * r];
-    mq = fmaxf(mq, fabsf(x));
-    mp = fmaxf(mp, fabsf(y));
-    sq += x;
-    sp += y;
+    sq += s_q[lane + 64 * r];
+    sp += s_p[lane + 64 * r];
   }
-  mq = wave_max(mq);
-  mp = wave_max(mp);
   sq = wave_sum(sq);
   sp = wave_sum(sp);
-  const float d1 = mq > 0.f ? wmax * mq * 0x1p-30f : 1.f;
-  const float d2 = mp > 0.f ? 2.f * mp * 0x1p-30f : 1.f;
-  const float i1 = 1.0f / d1, i2 = 1.0f / d2;
-
-  // Operand byte (mu, lane = 16 kg + n, 4 r' + bb): column n = 4 q + limb, MFMA mu of a
-  // 16-token tile: group s = kg + 4 (mu / 10); mu % 10 < 8 -> code plane j = (mu%10)/2,
-  // else the sign plane; half h = mu % 2; coordinate 32 s + 8 bb + 4 h + r' with
-  // key-side byte value 2^(4h + r') (-128 for bit 7). This row writes columns 4 qq .. 4 qq + 3;
-  // row 0 also clears the columns of rows G .. 3.
   // query group rho = qq / 4 has its own operand; this row is its column group qloc
   const int QG = query_groups(G), rho = qq / kMfmaMaxGroup, qloc = qq % kMfmaMaxGroup;
   const int Gr = min(kMfmaMaxGroup, G - kMfmaMaxGroup * rho);   // rows of the group
   uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * packed_group_bytes(D);
-  const int ncol = (qloc == 0) ? 4 * (kMfmaMaxGroup - Gr) + 4 : 4;
-  for (int e = threadIdx.x; e < NMU * 4 * 4 * ncol; e += 256) {
-    const int rr = e & 3, kg = (e >> 2) & 3, c = (e >> 4) % ncol, mu = (e >> 4) / ncol;
-    const int n = c < 4 ? 4 * qloc + c : 4 * Gr + (c - 4);   // column; c >= 4: an unused row
-    const int limb = n & 3;
-    const int s = kg + 4 * (mu / 10), m10 = mu % 10, h = m10 & 1;
-    uint32_t word = 0;
-    if (c < 4) {
-      // value / (delta * key byte value) as an integer X; limb bytes of X + 0x80808080
-      // are the digits of X in base 256 offset by 128 (X = sum (byte_l - 128) 256^l)
-      const int kb = 4 * h + rr;
-      const float vkey = kb == 7 ? -128.f : (float)(1 << kb);
-      const float f = (m10 < 8 ? w[m10 >> 1] * i1 : 2.f * i2) / vkey;
-      const float *src = m10 < 8 ? s_q : s_p;
-      uint32_t bytes = 0;
+  uint8_t *opb = grp;                                                  // [mu][lane][32] bytes
+  uint32_t *scl = reinterpret_cast<uint32_t *>(grp + (size_t)NMU * 2048);   // [mu][lane]
+  const float kap2 = 2.f * qjl_kappa<D>();
+  const int half = threadIdx.x >> 5, e = threadIdx.x & 31;   // half-wave = one (mu, block)
+  for (int blkid = half; blkid < NMU * 4; blkid += 8) {
+    const int mu = blkid >> 2, kb = blkid & 3;
+    const int c = mu / 5, pl = mu % 5;
+    const int v = e >> 3, mm = e & 7;
+    const int i = 32 * (kb + 4 * c) + 4 * mm + v;
+    const float val = v == 0 ? 0.5f : v == 1 ? 1.f : 2.f;
+    float r = (pl < 4 ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
+    const int lg = 2 * (kb & 1) + (e >> 4), byte = 16 * (kb >> 1) + (e & 15);
 #pragma unroll
-      for (int bb = 0; bb < 4; ++bb) {
-        const int X = (int)rintf(src[32 * s + 8 * bb + 4 * h + rr] * f);
-        const uint32_t byte = (((uint32_t)X + 0x80808080u) >> (8 * limb)) & 0xFFu;
-        bytes |= byte << (8 * bb);
-      }
-      word = bytes ^ 0x80808080u;
+    for (int limb = 0; limb < 4; ++limb) {
+      float mx = fabsf(r);
+      mx = fmaxf(mx, xor_lane<1>(mx));
+      mx = fmaxf(mx, xor_lane<2>(mx));
+      mx = fmaxf(mx, xor_lane<4>(mx));
+      mx = fmaxf(mx, xor_lane<8>(mx));
+      mx = fmaxf(mx, xor_lane<16>(mx));
+      // block scale 2^ex puts the largest value in [128, 256)
+      const int ex = mx > 0.f ? max(-127, min(127, __builtin_amdgcn_frexp_expf(mx) - 8)) : 0;
+      const uint32_t code = fp8_e4m3_rne(ldexpf(r, -ex));
+      r -= ldexpf(fp8_e4m3_value(code), ex);
+      const int col = 4 * qloc + limb;
+      opb[((size_t)mu * 64 + 16 * lg + col) * 32 + byte] = (uint8_t)code;
+      if (e == 0) scl[mu * 64 + 16 * kb + col] = (uint32_t)(ex + 127);
     }
-    reinterpret_cast<uint32_t *>(grp)[(size_t)mu * 256 + (16 * kg + n) * 4 + rr] = word;
   }
-  float *rc = reinterpret_cast<float *>(grp + (size_t)NMU * 1024);
+  // columns of rows Gr .. 3 of the group (no query): zero bytes, unit scales
+  if (qloc == 0 && Gr < kMfmaMaxGroup) {
+    const int ncol = 4 * (kMfmaMaxGroup - Gr);
+    for (int t = threadIdx.x; t < NMU * 4 * ncol * 32; t += 256) {
+      const int byte = t & 31, rest = t >> 5;
+      const int col = 4 * Gr + rest % ncol, lg = (rest / ncol) & 3, mu = rest / ncol / 4;
+      opb[((size_t)mu * 64 + 16 * lg + col) * 32 + byte] = 0;
+      if (byte == 0) scl[mu * 64 + 16 * lg + col] = 127u;
+    }
+  }
+  float *rc = reinterpret_cast<float *>(grp + (size_t)NMU * (2048 + 256));
   if (threadIdx.x < 4) {
-    const float cv[4] = {d1, d2, sq, sp};
+    const float cv[4] = {0.f, 0.f, sq, sp};
     rc[4 * qloc + threadIdx.x] = cv[threadIdx.x];
   } else if (qloc == 0 && threadIdx.x < 4 * kMfmaMaxGroup && threadIdx.x >= 4 * Gr) {
     rc[threadIdx.x] = 0.f;

@@ -53,11 +53,14 @@ struct PrepArgs {
   Codebook cb;
 };
 
-// Bytes of the packed scoring operand of one (sequence, KV head): per 16-token
-// tile a wave issues mfma_per_tile int8 MFMAs whose query operand (16 B per
-// lane) is stored lane-major, then 4 rows x {delta1, delta2, sum q~, sum p}.
-__host__ __device__ inline int mfma_per_tile(int d) { return 10 * (d / 128); }
-__host__ __device__ inline size_t packed_group_bytes(int d) { return (size_t)mfma_per_tile(d) * 64 * 16 + 64; }
+// Bytes of the packed scoring operand of one query group of a (sequence, KV
+// head): per 16-token tile a wave issues mfma_per_tile scaled fp4 x fp8 MFMAs
+// whose query operand (32 B per lane) is stored lane-major, then their scale
+// words (4 B per lane), then 4 rows x {0, 0, sum q~, sum p}.
+__host__ __device__ inline int mfma_per_tile(int d) { return 5 * (d / 128); }
+__host__ __device__ inline size_t packed_group_bytes(int d) {
+  return (size_t)mfma_per_tile(d) * (64 * 32 + 64 * 4) + 64;
+}
 constexpr int kMfmaMaxGroup = 4;   // query rows per MFMA query group (4 rows x 4 limbs)
 __host__ __device__ inline int query_groups(int group) { return (group + kMfmaMaxGroup - 1) / kMfmaMaxGroup; }
 // The MFMA decode kernel covers head_dim 128 and 256 with up to TQ_MAX_GROUP

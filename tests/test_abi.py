@@ -96,8 +96,11 @@ def test_dequant_and_prepare_validation(L):
     sz = C.c_size_t(0)
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, None, C.byref(sz), None) == tq.TQ_OK
     need = sz.value
-    # rows of (Pi q, S Pi q) plus the packed operands of the 2 x 2 (sequence, KV head) groups
-    assert need >= 2 * 8 * 2 * 128 * 4 + 4 * (10 * 1024 + 64)
+    # rows of (Pi q, S Pi q) plus the packed operands of the 2 x 2 (sequence, KV head)
+    # groups: 5 scoring MFMAs per 128 coordinates, each with 32 query bytes and a
+    # scale word per lane, then 4 x 4 row constants
+    grp = 5 * (64 * 32 + 64 * 4) + 64
+    assert need >= 2 * 8 * 2 * 128 * 4 + 4 * grp
     sz = C.c_size_t(need - 1)
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE, C.byref(sz), None) == tq.TQ_EWORKSPACE
     assert sz.value == need
@@ -110,7 +113,7 @@ def test_dequant_and_prepare_validation(L):
     # 16 rows per KV head: four query groups of 4 rows, each with its own operand
     sz16 = C.c_size_t(0)
     assert L.tq_query_prepare(r, FAKE, 0, 2, 2, 16, None, C.byref(sz16), None) == tq.TQ_OK
-    assert sz16.value == 2 * 2 * 16 * 2 * 128 * 4 + 2 * 2 * 4 * (10 * 1024 + 64)
+    assert sz16.value == 2 * 2 * 16 * 2 * 128 * 4 + 2 * 2 * 4 * grp
 
 
 def _decode(L, dsc, ws=None, size=None, B=2, nq=1, Hq=8, maxp=16, causal=0, q=FAKE):
