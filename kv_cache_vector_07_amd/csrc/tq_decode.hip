@@ -45,22 +45,25 @@ constexpr int kPartHead = 4;   // partial record: m, l, mU (log2 units), pad, th
 // ------------------------------------------------------------------ MFMA kernel
 __device__ inline int dpp_swap1(int x) { return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true); }
 __device__ inline int dpp_swap2(int x) { return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true); }
-__device__ inline float dpp_swap1f(float x) { return __builtin_bit_cast(float, dpp_swap1(__builtin_bit_cast(int, x))); }
-__device__ inline float dpp_swap2f(float x) { return __builtin_bit_cast(float, dpp_swap2(__builtin_bit_cast(int, x))); }
+template <int CTRL>
+__device__ inline float dppf(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
 
-// Reductions over the 16 lanes of one query row: the quad (lanes 4q..4q+3 of a
-// 16-lane row) and the four rows l, l^16, l^32, l^48.
+// Reductions over the 16 lanes of one DPP row (one query row of the score
+// layout): row mirror (i <-> 15 - i), half-row mirror (i <-> 7 - i), then the
+// quad swaps i ^ 2 and i ^ 1 leave every lane with all 16 values combined.
 __device__ inline float rowmax16(float x) {
-  x = fmaxf(x, dpp_swap1f(x));
-  x = fmaxf(x, dpp_swap2f(x));
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  return fmaxf(x, __shfl_xor(x, 32, 64));
+  x = fmaxf(x, dppf<0x140>(x));
+  x = fmaxf(x, dppf<0x141>(x));
+  x = fmaxf(x, dppf<0x4E>(x));
+  return fmaxf(x, dppf<0xB1>(x));
 }
 __device__ inline float rowsum16(float x) {
-  x += dpp_swap1f(x);
-  x += dpp_swap2f(x);
-  x += __shfl_xor(x, 16, 64);
-  return x + __shfl_xor(x, 32, 64);
+  x += dppf<0x140>(x);
+  x += dppf<0x141>(x);
+  x += dppf<0x4E>(x);
+  return x + dppf<0xB1>(x);
 }
 
 // 4x4 byte transpose inside a quad: lane L holds the four bytes of token L; on
@@ -76,15 +79,19 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // loads to the V accumulation, with its own online softmax; the four waves of
 // the workgroup combine once at the end into one partial per query row.
 //
-// Scores: scaled MFMA over the key bit planes (A: key nibbles, 16 tokens x 128
-// coordinates; B: query limbs, 16 columns = 4 query rows x 4 limbs). The limb partials of a
-// token sit in the four lanes of a quad; a transpose-reduce leaves lane L of the
-// quad with the full score of token L, so every later per-score step runs once.
+// Scores: scaled MFMA with the query limbs as A (16 rows = 4 query rows x 4
+// limbs, fp8) and the key bit planes as B (16 token columns x 128 coordinates,
+// fp4). Lane (n, kg) receives rows 4 kg .. 4 kg + 3 of column n: the four limbs
+// of query row kg for token 16 tau + n, summed in the lane, so each score, its
+// sidecars and its softmax step live in exactly one lane, and the 16 lanes of a
+// DPP row hold one query row. The softmax weights then move to the V operand
+// layout with one ds_bpermute per 16-token tile.
 // V: int8 MFMA with the softmax weight (times each plane weight) as 4 int8 limbs
 // on the 16 rows and the V bit planes on the columns: lane (n, k) reads its 16
 // tokens x 2 coordinates per u32 word, and a shift plus one AND per 4 tokens
-// makes the B operand. Per 64-token block the int32 sums are folded into a
-// float accumulator.
+// makes the B operand. The int32 sums stay in the MFMA accumulators across
+// blocks and are folded into a float accumulator only when the softmax
+// reference moves, and once at the end.
 //
 // Up to 16 query rows per KV head run as query groups of 4 rows (4 rows x 4
 // limbs fill the 16 MFMA columns); each group is its own workgroup, and the
@@ -110,9 +117,8 @@ __device__ inline void stage_query(const uint8_t *grp, v8i *s_qop, int *s_qsc, i
 template <int D>
 struct MfmaBlock {
   static constexpr bool kPrefetchV = D == 128;
-  uint4 kw[4][D / 128];            // key record chunks k, k + 4 of tokens 16 tau + n
-  uint4 g[2];                      // G of side entries 16 k + 0..15 (r = 0..3, tau = 0..3)
-  uint2 nk, nv;                    // N^K, N^V of side entries 16 k + 4 lam + 0..3 (tau = 0..3)
+  uint4 kw[4][D / 128];            // key record chunks kg, kg + 4 of tokens 16 tau + n
+  uint2 g, nk, nv;                 // G, N^K, N^V of side entries 4 n + tau (tokens 16 tau + n)
   uint4 v[kPrefetchV ? 3 : 1][D / 128];   // V words of plane j: coordinate pairs kp
 };
 
@@ -135,17 +141,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   const int QG = a.plan.qgroups;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / QG, rho = blockIdx.z % QG;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int n = lane & 15, kg = lane >> 4;
-  const int q = n >> 2, lam = n & 3;   // query row (in the group) of this lane's 16-lane row slot, limb / token
+  const int n = lane & 15, kg = lane >> 4;   // scores: token 16 tau + n of query row kg
+  const int lam = n & 3;                     // V weight operand: limb row / token of the quad
   const int H = a.n_kv_heads, g = a.n_q_heads / H;
   const int qbase = kMfmaMaxGroup * rho;                   // first query row of the group
   const int G = min(kMfmaMaxGroup, a.plan.group - qbase);  // rows in this group
   const int L = a.seq_lens[b];
 
   const uint8_t *grp = a.packed + (((size_t)b * H + kvh) * QG + rho) * packed_group_bytes(D);
-  const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * (2048 + 256))[q];
+  const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * (2048 + 256))[kg];
   const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w * qjl_kappa<D>();
-  const int vis = q < G ? (a.causal_tail ? L - (a.n_q - 1 - (qbase + q) / g) : L) : 0;
+  const int vis = kg < G ? (a.causal_tail ? L - (a.n_q - 1 - (qbase + kg) / g) : L) : 0;
+  // V weight operand: lane 16 kg + 4 q + lam takes the weight of query q, token
+  // 16 tau + 4 kg + lam, which the score layout holds in lane 16 q + 4 kg + lam
+  const int perm_addr = 4 * (16 * (n >> 2) + 4 * kg + lam);
   const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
   float wpl[4];
   plane_weights(a.cb, wpl);
@@ -163,9 +172,31 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
   // running maxima start finite, so exp2 of a masked (-inf) score is 0 and no
   // per-token guard is needed; a row with no visible token keeps l = 0
   float m_run = -kFltMax, mu_run = -kFltMax, l_lane = 0.f, us_lane = 0.f;
+  // V sums: int32 MFMA accumulators folded into a float accumulator. At
+  // d = 256 they are folded only when the softmax reference moves and at the
+  // end (per 64-token block a limb row gains at most 4 planes x 64 tokens x 128
+  // x 8 = 2^18, so up to 2^13 blocks, far more than one split holds, fit in
+  // int32); at d = 128 the registers for that are not free next to the
+  // prefetched block, so they are folded after every block.
+  constexpr bool kLazyV = D == 256;
   float facc[NB];
+  v4i vacc[NB];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) facc[k] = 0.f;
+  for (int k = 0; k < NB; ++k) {
+    facc[k] = 0.f;
+    vacc[k] = v4i{0, 0, 0, 0};
+  }
+  // rows 4 kg + r of a V accumulator are (query kg, limb r): limb r weighs 256^r
+  auto fold_one = [&](int k) {
+    const float v = (float)vacc[k][0] + 256.f * (float)vacc[k][1] + 65536.f * (float)vacc[k][2] +
+                    16777216.f * (float)vacc[k][3];
+    facc[k] = fmaf(delta_u, v, facc[k]);
+    vacc[k] = v4i{0, 0, 0, 0};
+  };
+  auto fold_v = [&]() {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) fold_one(k);
+  };
 
   const int n_pages_seq = min((L + kPage - 1) / kPage, a.max_pages);
   const int pg0 = split * a.plan.pages_per_split;
@@ -183,11 +214,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
         d.kw[tau][c] = reinterpret_cast<const uint4 *>(ks + (size_t)(blk0 + 16 * tau + n) * KREC)[kg + 4 * c];
-    const int se = blk0 + 16 * kg;   // first side entry of this lane's tokens
-    d.g[0] = reinterpret_cast<const uint4 *>(ks + KCODES + 2 * kPage + 2 * se)[0];
-    d.g[1] = reinterpret_cast<const uint4 *>(ks + KCODES + 2 * kPage + 2 * se)[1];
-    d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * (se + 4 * lam));
-    d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * (se + 4 * lam));
+    const int se = blk0 + 4 * n;   // side entries of tokens 16 tau + n, tau = 0..3
+    d.g = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * kPage + 2 * se);
+    d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * se);
+    d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * se);
     if constexpr (MfmaBlock<D>::kPrefetchV) {
       const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
 #pragma unroll
@@ -219,13 +249,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
-    // ---- scores: lane (n, kg) ends with the score of token blk0 + 16 tau + 4 kg + lam
-    const uint32_t gw[8] = {d.g[0].x, d.g[0].y, d.g[0].z, d.g[0].w, d.g[1].x, d.g[1].y, d.g[1].z, d.g[1].w};
+    // ---- scores: lane (n, kg) ends with query row kg, token blk0 + 16 tau + n
     float sc[4], sv[4];
     // the four 16-token tiles' MFMAs are interleaved (consecutive MFMAs are
     // independent); the query operand of each step is shared by the four.
-    // Key operand (fp4 e2m1): nibble m of dword v holds plane bit 4 m + v, as
-    // 0.5, 1, 2, 2 (bit 3 shifted down one place); the query side carries 1 / value.
+    // Key operand (B, fp4 e2m1): nibble m of dword v holds plane bit 4 m + v, as
+    // 0.5, 1, 2, 2 (bit 3 shifted down one place); the query side (A, fp8)
+    // carries 1 / value.
     v4f c1[4], c2[4];
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) c1[tau] = c2[tau] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -242,36 +272,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           const v8i op = {(int)(pl & 0x11111111u), (int)(pl & 0x22222222u), (int)(pl & 0x44444444u),
                           (int)((pl >> 1) & 0x44444444u), 0, 0, 0, 0};
           if (j < 4)
-            c1[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(op, qop, c1[tau], 4, 0, 0, 127, 0, qsc);
+            c1[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c1[tau], 0, 4, 0, qsc, 0, 127);
           else
-            c2[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(op, qop, c2[tau], 4, 0, 0, 127, 0, qsc);
+            c2[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c2[tau], 0, 4, 0, qsc, 0, 127);
         }
       }
     }
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      // this lane's limb of (S1 + kappa G S2) for the 4 tokens r of the column group;
-      // G of (tau, r) is side entry 4 r + tau of the lane's 16
-      float t[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float Gr = f16_bits_to_f32((uint16_t)(gw[2 * r + (tau >> 1)] >> (16 * (tau & 1))));
-        t[r] = fmaf(c2[tau][r], Gr, c1[tau][r]);
-      }
-      // transpose-reduce over the quad: lane lam keeps token lam
-      const bool o1 = lam & 1, o2 = lam & 2;
-      const float u0 = (o1 ? t[1] : t[0]) + dpp_swap1f(o1 ? t[0] : t[1]);
-      const float u1 = (o1 ? t[3] : t[2]) + dpp_swap1f(o1 ? t[2] : t[3]);
-      const float T = (o2 ? u1 : u0) + dpp_swap2f(o2 ? u0 : u1);
-      const uint32_t gsel = (lam & 2) ? ((lam & 1) ? gw[6 + (tau >> 1)] : gw[4 + (tau >> 1)])
-                                      : ((lam & 1) ? gw[2 + (tau >> 1)] : gw[tau >> 1]);
-      const float Gm = f16_bits_to_f32((uint16_t)(gsel >> (16 * (tau & 1))));
-      const uint32_t nkw = (tau >> 1) ? d.nk.y : d.nk.x, nvw = (tau >> 1) ? d.nv.y : d.nv.x;
-      const float N = f16_bits_to_f32((uint16_t)(nkw >> (16 * (tau & 1))));
-      const float NV = f16_bits_to_f32((uint16_t)(nvw >> (16 * (tau & 1))));
-      const int tok = blk0 + 16 * tau + 4 * kg + lam;
-      const bool valid = q < G && tok < ntok && tok0 + tok < vis;
-      const float sco = scale2 * N * (T - off1 - Gm * off2);
+      // the four limbs of (S1, S2) for query row kg, token 16 tau + n
+      const float T1 = (c1[tau][0] + c1[tau][1]) + (c1[tau][2] + c1[tau][3]);
+      const float T2 = (c2[tau][0] + c2[tau][1]) + (c2[tau][2] + c2[tau][3]);
+      const int sh = 16 * (tau & 1);
+      const float Gt = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.g.y : d.g.x) >> sh));
+      const float N = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nk.y : d.nk.x) >> sh));
+      const float NV = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nv.y : d.nv.x) >> sh));
+      const int tok = blk0 + 16 * tau + n;
+      const bool valid = tok < ntok && tok0 + tok < vis;   // vis = 0 for rows past the group
+      const float sco = scale2 * N * fmaf(Gt, T2 - off2, T1 - off1);
       sc[tau] = valid ? sco : kNegInf;
       sv[tau] = valid ? sco + __builtin_amdgcn_logf(NV) : kNegInf;   // + log2 N^V
     }
@@ -289,10 +307,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
         const float mu_new = fmaxf(mu_run, rowmax16(vmax));
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         const float alphaU = __builtin_amdgcn_exp2f(mu_run - mu_new);
-        // the accumulator row of this lane's column lane is query row kg
-        const float aU_row = __shfl(alphaU, 4 * (kg & 3), 64);
+        // the V accumulator rows of this lane are query row kg, as its scores
+        if constexpr (kLazyV) fold_v();
 #pragma unroll
-        for (int k = 0; k < NB; ++k) facc[k] *= aU_row;
+        for (int k = 0; k < NB; ++k) facc[k] *= alphaU;
         l_lane *= alpha;
         us_lane *= alphaU;
         m_run = m_new;
@@ -306,7 +324,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
       ps += __builtin_amdgcn_exp2f(sc[tau] - m_run);
       const float U = __builtin_amdgcn_exp2f(sv[tau] - mu_run);
       us += U;
-      const float Ut = __builtin_amdgcn_ldexpf(U, -tau);
+      const float Uv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_addr, __builtin_bit_cast(int, U)));
+      const float Ut = __builtin_amdgcn_ldexpf(Uv, -tau);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int X = (int)fmaf(Ut, cx[j], half[j]);
@@ -331,7 +350,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int kp = 0; kp < D / 32; ++kp) {
       const uint32_t wj[4] = {vword(0, kp), vword(1, kp), vword(2, kp), xw[kp]};
-      v4i c[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -342,14 +360,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           bop.y = (int)(w & 0x02020202u);
           bop.z = (int)(w & 0x04040404u);
           bop.w = (int)(w & 0x08080808u);
-          c[h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bop, c[h], 0, 0, 0);
+          vacc[2 * kp + h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bop, vacc[2 * kp + h], 0, 0, 0);
         }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        // rows 4 kg + r are (query kg, limb r)
-        const float v = (float)c[h][0] + 256.f * (float)c[h][1] + 65536.f * (float)c[h][2] +
-                        16777216.f * (float)c[h][3];
-        facc[2 * kp + h] = fmaf(delta_u, v, facc[2 * kp + h]);
+      if constexpr (!kLazyV) {
+        fold_one(2 * kp);
+        fold_one(2 * kp + 1);
       }
     }
   };
@@ -380,13 +395,14 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
+  if constexpr (kLazyV) fold_v();
   // ---- combine the four waves into one partial per query row
   const float l_row = rowsum16(l_lane), us_row = rowsum16(us_lane);
-  if (kg == 0 && lam == 0) {
-    s_wm[wave][0][q] = m_run;
-    s_wm[wave][1][q] = l_row;
-    s_wm[wave][2][q] = mu_run;
-    s_wm[wave][3][q] = us_row;
+  if (n == 0) {
+    s_wm[wave][0][kg] = m_run;
+    s_wm[wave][1][kg] = l_row;
+    s_wm[wave][2][kg] = mu_run;
+    s_wm[wave][3][kg] = us_row;
   }
   __syncthreads();
   {
