@@ -138,7 +138,7 @@ int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype,
  * aligned, *prep_bytes bytes):
  *   [rows][2][d] float32 with rows in (b, t, h) order: Pi q, then S Pi q;
  *   then, when Hq/Hkv * n_q <= TQ_MAX_GROUP, the packed scoring operand
- *   (fp8 query limbs with block scales) of each (sequence, KV head, group of
+ *   (fp6 query limbs with block scales) of each (sequence, KV head, group of
  *   4 query rows) used by the MFMA decode kernel (internal layout).
  * prep == NULL returns the size in *prep_bytes and launches nothing; a short
  * buffer returns TQ_EWORKSPACE with the size written back.

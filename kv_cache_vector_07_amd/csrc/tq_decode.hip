@@ -16,13 +16,13 @@
 // release per workgroup, which on this GPU writes back and invalidates the whole
 // L2 of the XCD every time.)
 //
-// Scores are a block-scaled fp4 x fp8 MFMA contraction. The codebook is odd
+// Scores are a block-scaled fp6 x fp4 MFMA contraction. The codebook is odd
 // (c[7-k] = -c[k]), so the 3-bit code splits over four binary planes,
 // c[idx] = 2 (a0 b0 + a1 b1 + a2 b2 + a3 (b0^b1^b2)) - c7, and each key bit plane
 // becomes an fp4 operand (one AND per eight coordinates, the bit's position
-// folded into the fp4 value); the query side is four fp8 limbs with a power-of-two
-// scale per 32 coordinates on the MFMA columns (4 query rows x 4 limbs per query
-// group), about 2^-16 of the largest term per block. V is accumulated with the
+// folded into the fp4 value); the query side is four fp6 (e2m3) limbs with a
+// power-of-two scale per 32 coordinates on the MFMA rows (4 query rows x 4 limbs
+// per query group), about 2^-16 of the largest term per block. V is accumulated with the
 // same planes on int8 MFMA: the softmax weight times each plane weight, as four
 // int8 limbs, against the V bit planes; every product there is exact in int32.
 #include "tq_device.h"
@@ -80,7 +80,7 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // the workgroup combine once at the end into one partial per query row.
 //
 // Scores: scaled MFMA with the query limbs as A (16 rows = 4 query rows x 4
-// limbs, fp8) and the key bit planes as B (16 token columns x 128 coordinates,
+// limbs, fp6) and the key bit planes as B (16 token columns x 128 coordinates,
 // fp4). Lane (n, kg) receives rows 4 kg .. 4 kg + 3 of column n: the four limbs
 // of query row kg for token 16 tau + n, summed in the lane, so each score, its
 // sidecars and its softmax step live in exactly one lane, and the 16 lanes of a
@@ -123,7 +123,7 @@ struct MfmaBlock {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NMU = 5 * (D / 128);        // scaled MFMAs per 16-token scoring tile
   constexpr int NCH = D / 128;              // 16-byte key chunks per lane and token
   constexpr int KREC = D / 2;
@@ -254,7 +254,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
     // the four 16-token tiles' MFMAs are interleaved (consecutive MFMAs are
     // independent); the query operand of each step is shared by the four.
     // Key operand (B, fp4 e2m1): nibble m of dword v holds plane bit 4 m + v, as
-    // 0.5, 1, 2, 2 (bit 3 shifted down one place); the query side (A, fp8)
+    // 0.5, 1, 2, 2 (bit 3 shifted down one place); the query side (A, fp6)
     // carries 1 / value.
     v4f c1[4], c2[4];
 #pragma unroll
@@ -272,9 +272,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a) {
           const v8i op = {(int)(pl & 0x11111111u), (int)(pl & 0x22222222u), (int)(pl & 0x44444444u),
                           (int)((pl >> 1) & 0x44444444u), 0, 0, 0, 0};
           if (j < 4)
-            c1[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c1[tau], 0, 4, 0, qsc, 0, 127);
+            c1[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c1[tau], 2, 4, 0, qsc, 0, 127);
           else
-            c2[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c2[tau], 0, 4, 0, qsc, 0, 127);
+            c2[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c2[tau], 2, 4, 0, qsc, 0, 127);
         }
       }
     }

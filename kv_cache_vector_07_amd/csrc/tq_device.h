@@ -158,14 +158,15 @@ __device__ inline void plane_weights(const Codebook &cb, float (&w)[4]) {
   w[3] = 2.f * (0.5f * (c4 + c7) - a2);
 }
 
-// OCP fp8 e4m3 (bias 7, no infinities; 0x7f = NaN): round to nearest even of
-// |x| <= 448, and the value of a code.
-__device__ inline uint32_t fp8_e4m3_rne(float x) {
-  const uint32_t sign = x < 0.f ? 0x80u : 0u;
+// fp6 e2m3 (OCP MX format: sign, 2 exponent bits with bias 1, 3 mantissa
+// bits; no infinities or NaN, largest magnitude 7.5): round to nearest even,
+// saturating at 7.5, and the value of a code.
+__device__ inline uint32_t fp6_e2m3_rne(float x) {
+  const uint32_t sign = x < 0.f ? 0x20u : 0u;
   const float ax = fabsf(x);
   uint32_t code;
-  if (ax < 0x1p-6f) {
-    code = (uint32_t)__builtin_rintf(ax * 512.f);   // subnormal steps of 2^-9 (8 -> 0x08, the min normal)
+  if (ax < 1.f) {
+    code = (uint32_t)__builtin_rintf(ax * 8.f);   // steps of 1/8; 8 is the code of 1.0
   } else {
     int e = __builtin_amdgcn_frexp_expf(ax) - 1;   // ax in [2^e, 2^(e+1))
     uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(ax, -e) * 8.f) - 8u;
@@ -173,15 +174,15 @@ __device__ inline uint32_t fp8_e4m3_rne(float x) {
       m = 0u;
       ++e;
     }
-    code = ((uint32_t)(e + 7) << 3) | m;
+    code = e > 2 ? 0x1Fu : (((uint32_t)(e + 1) << 3) | m);
   }
   return code | sign;
 }
 
-__device__ inline float fp8_e4m3_value(uint32_t code) {
-  const uint32_t e = (code >> 3) & 15u, m = code & 7u;
-  const float v = e == 0u ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf((float)(8u + m), (int)e - 10);
-  return (code & 0x80u) ? -v : v;
+__device__ inline float fp6_e2m3_value(uint32_t code) {
+  const uint32_t e = (code >> 3) & 3u, m = code & 7u;
+  const float v = e == 0u ? 0.125f * (float)m : __builtin_ldexpf((float)(8u + m), (int)e - 4);
+  return (code & 0x20u) ? -v : v;
 }
 
 __device__ inline uint16_t f32_to_f16_bits(float x) {

@@ -345,19 +345,19 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   if (a.packed == nullptr) return;
   __syncthreads();
 
-  // Scoring operand of this row for the fp4 x fp8 block-scaled MFMA
+  // Scoring operand of this row for the fp6 x fp4 block-scaled MFMA
   // (16x16x128): MFMA mu = 5 c + pl scores coordinate chunk c (coordinates
   // 128 c .. 128 c + 127) against key plane pl (code bits 0..2, their xor, then
-  // the QJL sign). Key side (fp4): in lane group kq (coordinate group
-  // s = kq + 4 c) nibble slot n = 8 v + m holds bit 4 m + v of the plane word,
+  // the QJL sign). Both operands hold K = 32 kq + f in lane group kq, slot f (a
+  // nibble of the key side, a 6-bit field of the query side, fields packed
+  // contiguously from bit 0). Key side (B, fp4): slot f = 8 v + m of lane group
+  // kq holds bit 4 m + v of the plane word of coordinate group s = kq + 4 c,
   // i.e. coordinate 32 s + 4 m + v, with value 0.5, 1, 2, 2 for v = 0..3 (v = 3
-  // is shifted down one bit). Query side (fp8 e4m3): the value paired with that
-  // slot is y / value, y = w_pl * q~_i (code planes; c[idx] = sum_pl w_pl b_pl - c7)
-  // or 2 kappa p_i (sign plane, sigma = 2 b - 1), as four limbs on the columns
-  // 4 q + limb, each limb with an E8M0 scale per 32-slot block, so the MFMA sums
-  // of the four limb columns add up to the full product. Pairing (measured): key
-  // lane group kq, slot n <-> query lane group 2 (kq & 1) + n / 16, byte
-  // 16 (kq / 2) + n % 16; the query scale of slot block kq sits in lane 16 kq + column.
+  // is shifted down one bit). Query side (A, fp6 e2m3): the paired slot holds
+  // y / value, y = w_pl * q~_i (code planes; c[idx] = sum_pl w_pl b_pl - c7) or
+  // 2 kappa p_i (sign plane, sigma = 2 b - 1), as four limbs on the rows
+  // 4 q + limb, each limb with an E8M0 scale per 32-slot block (in lane
+  // 16 kq + row), so the MFMA sums of the four limb rows add up to the product.
   float w[4];
   plane_weights(a.cb, w);
   float sq = 0.f, sp = 0.f;
@@ -368,13 +368,14 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   }
   sq = wave_sum(sq);
   sp = wave_sum(sp);
-  // query group rho = qq / 4 has its own operand; this row is its column group qloc
+  // query group rho = qq / 4 has its own operand; this row is its row group qloc
   const int QG = query_groups(G), rho = qq / kMfmaMaxGroup, qloc = qq % kMfmaMaxGroup;
   const int Gr = min(kMfmaMaxGroup, G - kMfmaMaxGroup * rho);   // rows of the group
   uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * packed_group_bytes(D);
   uint8_t *opb = grp;                                                  // [mu][lane][32] bytes
   uint32_t *scl = reinterpret_cast<uint32_t *>(grp + (size_t)NMU * 2048);   // [mu][lane]
   const float kap2 = 2.f * qjl_kappa<D>();
+  __shared__ uint8_t s_f6[8][4][32];                          // per half-wave: limb, slot
   const int half = threadIdx.x >> 5, e = threadIdx.x & 31;   // half-wave = one (mu, block)
   for (int blkid = half; blkid < NMU * 4; blkid += 8) {
     const int mu = blkid >> 2, kb = blkid & 3;
@@ -383,7 +384,6 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
     const int i = 32 * (kb + 4 * c) + 4 * mm + v;
     const float val = v == 0 ? 0.5f : v == 1 ? 1.f : 2.f;
     float r = (pl < 4 ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
-    const int lg = 2 * (kb & 1) + (e >> 4), byte = 16 * (kb >> 1) + (e & 15);
 #pragma unroll
     for (int limb = 0; limb < 4; ++limb) {
       float mx = fabsf(r);
@@ -392,23 +392,43 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
       mx = fmaxf(mx, xor_lane<4>(mx));
       mx = fmaxf(mx, xor_lane<8>(mx));
       mx = fmaxf(mx, xor_lane<16>(mx));
-      // block scale 2^ex puts the largest value in [128, 256)
-      const int ex = mx > 0.f ? max(-127, min(127, __builtin_amdgcn_frexp_expf(mx) - 8)) : 0;
-      const uint32_t code = fp8_e4m3_rne(ldexpf(r, -ex));
-      r -= ldexpf(fp8_e4m3_value(code), ex);
-      const int col = 4 * qloc + limb;
-      opb[((size_t)mu * 64 + 16 * lg + col) * 32 + byte] = (uint8_t)code;
-      if (e == 0) scl[mu * 64 + 16 * kb + col] = (uint32_t)(ex + 127);
+      // block scale 2^ex puts the largest value in [4, 8)
+      const int ex = mx > 0.f ? max(-127, min(127, __builtin_amdgcn_frexp_expf(mx) - 3)) : 0;
+      const uint32_t code = fp6_e2m3_rne(ldexpf(r, -ex));
+      r -= ldexpf(fp6_e2m3_value(code), ex);
+      s_f6[half][limb][e] = (uint8_t)code;
+      if (e == 0) scl[mu * 64 + 16 * kb + 4 * qloc + limb] = (uint32_t)(ex + 127);
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // thread e < 24 packs dword t = e % 6 of limb e / 6 (bits 32 t .. 32 t + 31 of
+    // the 32 fields); the rest clear dwords 6 and 7
+    const int limb = e < 24 ? e / 6 : (e - 24) >> 1;
+    uint32_t word = 0, dw;
+    if (e < 24) {
+      dw = e % 6;
+      for (int f = (32 * dw) / 6; f < 32 && 6 * f < 32 * (int)dw + 32; ++f) {
+        const int sh = 6 * f - 32 * (int)dw;
+        const uint32_t cf = s_f6[half][limb][f];
+        word |= sh >= 0 ? (cf << sh) : (cf >> -sh);
+      }
+    } else {
+      dw = 6 + ((e - 24) & 1);
+    }
+    reinterpret_cast<uint32_t *>(opb)[((size_t)mu * 64 + 16 * kb + 4 * qloc + limb) * 8 + dw] = word;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
-  // columns of rows Gr .. 3 of the group (no query): zero bytes, unit scales
+  // limb rows of rows Gr .. 3 of the group (no query): zero fields, unit scales
   if (qloc == 0 && Gr < kMfmaMaxGroup) {
-    const int ncol = 4 * (kMfmaMaxGroup - Gr);
-    for (int t = threadIdx.x; t < NMU * 4 * ncol * 32; t += 256) {
+    const int nrow = 4 * (kMfmaMaxGroup - Gr);
+    for (int t = threadIdx.x; t < NMU * 4 * nrow * 32; t += 256) {
       const int byte = t & 31, rest = t >> 5;
-      const int col = 4 * Gr + rest % ncol, lg = (rest / ncol) & 3, mu = rest / ncol / 4;
-      opb[((size_t)mu * 64 + 16 * lg + col) * 32 + byte] = 0;
-      if (byte == 0) scl[mu * 64 + 16 * lg + col] = 127u;
+      const int row = 4 * Gr + rest % nrow, lg = (rest / nrow) & 3, mu = rest / nrow / 4;
+      opb[((size_t)mu * 64 + 16 * lg + row) * 32 + byte] = 0;
+      if (byte == 0) scl[mu * 64 + 16 * lg + row] = 127u;
     }
   }
   float *rc = reinterpret_cast<float *>(grp + (size_t)NMU * (2048 + 256));

@@ -54,7 +54,7 @@ struct PrepArgs {
 };
 
 // Bytes of the packed scoring operand of one query group of a (sequence, KV
-// head): per 16-token tile a wave issues mfma_per_tile scaled fp4 x fp8 MFMAs
+// head): per 16-token tile a wave issues mfma_per_tile scaled fp6 x fp4 MFMAs
 // whose query operand (32 B per lane) is stored lane-major, then their scale
 // words (4 B per lane), then 4 rows x {0, 0, sum q~, sum p}.
 __host__ __device__ inline int mfma_per_tile(int d) { return 5 * (d / 128); }
