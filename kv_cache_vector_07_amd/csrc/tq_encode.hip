@@ -384,16 +384,24 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
     const int i = 32 * (kb + 4 * c) + 4 * mm + v;
     const float val = v == 0 ? 0.5f : v == 1 ? 1.f : 2.f;
     float r = (pl < 4 ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
+    // limb 0: the block scale 2^ex puts the block's largest value in [4, 8).
+    // Later limbs take their scale from the rounding bound of the previous one
+    // (no reduction): limb 0 leaves |r| <= 0.5 * 2^ex (0.25 from rounding in
+    // [4, 8), 0.5 where 7.75 .. 8 saturates to 7.5), so limb 1 uses ex - 3;
+    // a limb whose values stay below 4 leaves |r| <= 0.125 * 2^ex, so limbs 2
+    // and 3 use ex - 5. Every later limb value is then at most 4, no later limb
+    // saturates, and after four limbs |r| <= 2^(ex0 - 16), under 2^-18 of the
+    // block's largest value.
+    float mx = fabsf(r);
+    mx = fmaxf(mx, xor_lane<1>(mx));
+    mx = fmaxf(mx, xor_lane<2>(mx));
+    mx = fmaxf(mx, xor_lane<4>(mx));
+    mx = fmaxf(mx, xor_lane<8>(mx));
+    mx = fmaxf(mx, xor_lane<16>(mx));
+    const int ex0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 3 : 0;
 #pragma unroll
     for (int limb = 0; limb < 4; ++limb) {
-      float mx = fabsf(r);
-      mx = fmaxf(mx, xor_lane<1>(mx));
-      mx = fmaxf(mx, xor_lane<2>(mx));
-      mx = fmaxf(mx, xor_lane<4>(mx));
-      mx = fmaxf(mx, xor_lane<8>(mx));
-      mx = fmaxf(mx, xor_lane<16>(mx));
-      // block scale 2^ex puts the largest value in [4, 8)
-      const int ex = mx > 0.f ? max(-127, min(127, __builtin_amdgcn_frexp_expf(mx) - 3)) : 0;
+      const int ex = max(-127, min(127, ex0 - (limb == 0 ? 0 : limb == 1 ? 3 : 3 + 5 * (limb - 1))));
       const uint32_t code = fp6_e2m3_rne(ldexpf(r, -ex));
       r -= ldexpf(fp6_e2m3_value(code), ex);
       s_f6[half][limb][e] = (uint8_t)code;
