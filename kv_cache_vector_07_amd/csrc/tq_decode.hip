@@ -448,13 +448,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 }
 
 // One workgroup per (query row, KV head, sequence). Wave w takes splits
-// w, w + 4, ...: it issues the loads of up to 8 of them at once (the headers are
+// w, w + 4, ...: it issues the loads of up to 16 of them at once (the headers are
 // wave-uniform) and folds them with a running log-sum-exp; the four waves then
 // combine in LDS, and wave 0 applies the inverse rotation and writes the row.
 template <int D, bool kRotate>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int R = D / 64;
-  constexpr int CH = 8;   // splits per wave in flight
+  constexpr int CH = 16;   // splits per wave in flight
   __shared__ float s_st[4][3];
   __shared__ float s_x[4][D];
   const int qq = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
