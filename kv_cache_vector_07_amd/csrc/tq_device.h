@@ -159,30 +159,20 @@ __device__ inline void plane_weights(const Codebook &cb, float (&w)[4]) {
 }
 
 // fp6 e2m3 (OCP MX format: sign, 2 exponent bits with bias 1, 3 mantissa
-// bits; no infinities or NaN, largest magnitude 7.5): round to nearest even,
-// saturating at 7.5, and the value of a code.
-__device__ inline uint32_t fp6_e2m3_rne(float x) {
-  const uint32_t sign = x < 0.f ? 0x20u : 0u;
-  const float ax = fabsf(x);
-  uint32_t code;
-  if (ax < 1.f) {
-    code = (uint32_t)__builtin_rintf(ax * 8.f);   // steps of 1/8; 8 is the code of 1.0
-  } else {
-    int e = __builtin_amdgcn_frexp_expf(ax) - 1;   // ax in [2^e, 2^(e+1))
-    uint32_t m = (uint32_t)__builtin_rintf(__builtin_ldexpf(ax, -e) * 8.f) - 8u;
-    if (m == 8u) {
-      m = 0u;
-      ++e;
-    }
-    code = e > 2 ? 0x1Fu : (((uint32_t)(e + 1) << 3) | m);
-  }
-  return code | sign;
-}
-
-__device__ inline float fp6_e2m3_value(uint32_t code) {
-  const uint32_t e = (code >> 3) & 3u, m = code & 7u;
-  const float v = e == 0u ? 0.125f * (float)m : __builtin_ldexpf((float)(8u + m), (int)e - 4);
-  return (code & 0x20u) ? -v : v;
+// bits; no infinities or NaN, largest magnitude 7.5) rounding of |x| < 8:
+// round to nearest even, 7.75 and above saturating to 7.5. Returns the rounded
+// value; `code` gets its 6-bit code. The step is 1/8 below 2, 1/4 in [2, 4) and
+// 1/2 in [4, 8): adding 1.5 * 2^(20 + e) rounds to a multiple of 2^(e - 3) in
+// fp32, and subtracting it back is exact.
+__device__ inline float fp6_e2m3_round(float x, uint32_t &code) {
+  const float a = fabsf(x);
+  const int e = min(2, max(0, __builtin_amdgcn_frexp_expf(a) - 1));
+  const float k = __builtin_ldexpf(1.5f, 20 + e);
+  const float q = fminf((a + k) - k, 7.5f);
+  // codes: 8 q below 2 (subnormals and the first binade alike), then 4 q + 8, 2 q + 16
+  const float cf = q < 2.f ? 8.f * q : (q < 4.f ? fmaf(4.f, q, 8.f) : fmaf(2.f, q, 16.f));
+  code = (uint32_t)cf | (x < 0.f ? 0x20u : 0u);
+  return x < 0.f ? -q : q;
 }
 
 __device__ inline uint16_t f32_to_f16_bits(float x) {

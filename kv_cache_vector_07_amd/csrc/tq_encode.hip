@@ -375,59 +375,69 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   uint8_t *opb = grp;                                                  // [mu][lane][32] bytes
   uint32_t *scl = reinterpret_cast<uint32_t *>(grp + (size_t)NMU * 2048);   // [mu][lane]
   const float kap2 = 2.f * qjl_kappa<D>();
-  __shared__ uint8_t s_f6[8][4][32];                          // per half-wave: limb, slot
-  const int half = threadIdx.x >> 5, e = threadIdx.x & 31;   // half-wave = one (mu, block)
-  for (int blkid = half; blkid < NMU * 4; blkid += 8) {
-    const int mu = blkid >> 2, kb = blkid & 3;
-    const int c = mu / 5, pl = mu % 5;
-    const int v = e >> 3, mm = e & 7;
-    const int i = 32 * (kb + 4 * c) + 4 * mm + v;
-    const float val = v == 0 ? 0.5f : v == 1 ? 1.f : 2.f;
-    float r = (pl < 4 ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
-    // limb 0: the block scale 2^ex puts the block's largest value in [4, 8).
-    // Later limbs take their scale from the rounding bound of the previous one
-    // (no reduction): limb 0 leaves |r| <= 0.5 * 2^ex (0.25 from rounding in
-    // [4, 8), 0.5 where 7.75 .. 8 saturates to 7.5), so limb 1 uses ex - 3;
-    // a limb whose values stay below 4 leaves |r| <= 0.125 * 2^ex, so limbs 2
-    // and 3 use ex - 5. Every later limb value is then at most 4, no later limb
-    // saturates, and after four limbs |r| <= 2^(ex0 - 16), under 2^-18 of the
-    // block's largest value.
-    float mx = fabsf(r);
-    mx = fmaxf(mx, xor_lane<1>(mx));
-    mx = fmaxf(mx, xor_lane<2>(mx));
-    mx = fmaxf(mx, xor_lane<4>(mx));
-    mx = fmaxf(mx, xor_lane<8>(mx));
-    mx = fmaxf(mx, xor_lane<16>(mx));
-    const int ex0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 3 : 0;
+  // Half-wave h takes the (mu, block) tasks h, h + 8, ...: all of them in one
+  // pass, so their limb chains interleave. Fields are ORed into LDS dwords
+  // (field f of a lane's 32 sits at bits 6 f .. 6 f + 5 of its 192), then each
+  // packed dword is stored once.
+  constexpr int NTASK = NMU * 4, NT = (NTASK + 7) / 8;
+  __shared__ uint32_t s_pk[8][NT][4][6];                      // per half-wave: task, limb, dword
+  const int half = threadIdx.x >> 5, e = threadIdx.x & 31;
+  for (int z = e; z < NT * 4 * 6; z += 32) (&s_pk[half][0][0][0])[z] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int fv = e >> 3, fm = e & 7;   // field e: bit 4 fm + fv of its plane word
+  const float val = fv == 0 ? 0.5f : fv == 1 ? 1.f : 2.f;
+  const int sh0 = (6 * e) & 31, dw0 = (6 * e) >> 5;   // where field e starts
 #pragma unroll
-    for (int limb = 0; limb < 4; ++limb) {
-      const int ex = max(-127, min(127, ex0 - (limb == 0 ? 0 : limb == 1 ? 3 : 3 + 5 * (limb - 1))));
-      const uint32_t code = fp6_e2m3_rne(ldexpf(r, -ex));
-      r -= ldexpf(fp6_e2m3_value(code), ex);
-      s_f6[half][limb][e] = (uint8_t)code;
-      if (e == 0) scl[mu * 64 + 16 * kb + 4 * qloc + limb] = (uint32_t)(ex + 127);
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // thread e < 24 packs dword t = e % 6 of limb e / 6 (bits 32 t .. 32 t + 31 of
-    // the 32 fields); the rest clear dwords 6 and 7
-    const int limb = e < 24 ? e / 6 : (e - 24) >> 1;
-    uint32_t word = 0, dw;
-    if (e < 24) {
-      dw = e % 6;
-      for (int f = (32 * dw) / 6; f < 32 && 6 * f < 32 * (int)dw + 32; ++f) {
-        const int sh = 6 * f - 32 * (int)dw;
-        const uint32_t cf = s_f6[half][limb][f];
-        word |= sh >= 0 ? (cf << sh) : (cf >> -sh);
+  for (int t = 0; t < NT; ++t) {
+    const int blkid = half + 8 * t;   // the same for both halves of a wave
+    if (blkid < NTASK) {
+      const int mu = blkid >> 2, kb = blkid & 3;
+      const int c = mu / 5, pl = mu % 5;
+      const int i = 32 * (kb + 4 * c) + 4 * fm + fv;
+      float r = (pl < 4 ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
+      // limb 0: the block scale 2^ex puts the block's largest value in [4, 8).
+      // Later limbs take their scale from the rounding bound of the previous one
+      // (no reduction): limb 0 leaves |r| <= 0.5 * 2^ex (0.25 from rounding in
+      // [4, 8), 0.5 where 7.75 .. 8 saturates to 7.5), so limb 1 uses ex - 3;
+      // a limb whose values stay below 4 leaves |r| <= 0.125 * 2^ex, so limbs 2
+      // and 3 use ex - 5. Every later limb value is then at most 4, no later limb
+      // saturates, and after four limbs |r| <= 2^(ex0 - 16), under 2^-18 of the
+      // block's largest value.
+      float mx = fabsf(r);
+      mx = fmaxf(mx, xor_lane<1>(mx));
+      mx = fmaxf(mx, xor_lane<2>(mx));
+      mx = fmaxf(mx, xor_lane<4>(mx));
+      mx = fmaxf(mx, xor_lane<8>(mx));
+      mx = fmaxf(mx, xor_lane<16>(mx));
+      const int ex0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 3 : 0;
+#pragma unroll
+      for (int limb = 0; limb < 4; ++limb) {
+        const int ex = max(-127, min(127, ex0 - (limb == 0 ? 0 : limb == 1 ? 3 : 3 + 5 * (limb - 1))));
+        uint32_t code;
+        const float qv = fp6_e2m3_round(__builtin_ldexpf(r, -ex), code);
+        r = fmaf(-qv, __builtin_ldexpf(1.f, ex), r);
+        atomicOr(&s_pk[half][t][limb][dw0], code << sh0);
+        if (sh0 > 26) atomicOr(&s_pk[half][t][limb][dw0 + 1], code >> (32 - sh0));
+        if (e == 0) scl[mu * 64 + 16 * kb + 4 * qloc + limb] = (uint32_t)(ex + 127);
       }
-    } else {
-      dw = 6 + ((e - 24) & 1);
     }
-    reinterpret_cast<uint32_t *>(opb)[((size_t)mu * 64 + 16 * kb + 4 * qloc + limb) * 8 + dw] = word;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // lane e < 24 stores dword e % 6 of limb e / 6; lanes 24..31 clear dwords 6 and 7
+  const int plimb = e < 24 ? e / 6 : (e - 24) >> 1;
+  const int pdw = e < 24 ? e % 6 : 6 + ((e - 24) & 1);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int blkid = half + 8 * t;
+    if (blkid < NTASK) {
+      const int mu = blkid >> 2, kb = blkid & 3;
+      const uint32_t word = e < 24 ? s_pk[half][t][plimb][pdw] : 0u;
+      reinterpret_cast<uint32_t *>(opb)[((size_t)mu * 64 + 16 * kb + 4 * qloc + plimb) * 8 + pdw] = word;
+    }
   }
   // limb rows of rows Gr .. 3 of the group (no query): zero fields, unit scales
   if (qloc == 0 && Gr < kMfmaMaxGroup) {
