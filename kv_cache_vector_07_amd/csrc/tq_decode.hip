@@ -318,14 +318,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       }
     }
     float ps = 0.f, us = 0.f;
-    v4i A[4];   // per plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
+    // the four weights go to the V operand layout first, so the four
+    // ds_bpermutes are in flight together
+    float Uv[4];
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       ps += __builtin_amdgcn_exp2f(sc[tau] - m_run);
       const float U = __builtin_amdgcn_exp2f(sv[tau] - mu_run);
       us += U;
-      const float Uv = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_addr, __builtin_bit_cast(int, U)));
-      const float Ut = __builtin_amdgcn_ldexpf(Uv, -tau);
+      Uv[tau] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_addr, __builtin_bit_cast(int, U)));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    v4i A[4];   // per plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      const float Ut = __builtin_amdgcn_ldexpf(Uv[tau], -tau);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int X = (int)fmaf(Ut, cx[j], half[j]);
