@@ -100,10 +100,14 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
   p.group = n_q_heads / n_kv_heads * n_q;
   p.mfma = mfma_path(d, p.group);
   p.qgroups = p.mfma ? query_groups(p.group) : 1;
+  // Several query groups of a (sequence, KV head) share a workgroup, so the key
+  // and V operands of a block are built once for all of them.
+  p.groups_per_wg = p.qgroups > 1 ? max_groups_per_wg(d) : 1;
+  p.wg_per_seq = (p.qgroups + p.groups_per_wg - 1) / p.groups_per_wg;
   // About 512 workgroups (two per CU, one occupancy round) so that every
   // workgroup streams several pages with its loads overlapped; whole pages per
   // split; at most 256 pages (65536 tokens) per split.
-  long work = (long)batch * n_kv_heads * max_pages * p.qgroups;
+  long work = (long)batch * n_kv_heads * max_pages * p.wg_per_seq;
   int pps = (int)((work + 511) / 512);
   if (pps < 1) pps = 1;
   if (pps > 256) pps = 256;
@@ -520,6 +524,8 @@ int tq_dense_attn_decode(const void *k, const void *v, int32_t head_dim, int32_t
   ma.plan.group = group;
   ma.plan.n_split = n_split;
   ma.plan.qgroups = 1;
+  ma.plan.groups_per_wg = 1;
+  ma.plan.wg_per_seq = 1;
   return hip_status(tq::launch_decode_merge(ma, head_dim, s, false));
 }
 

@@ -122,8 +122,11 @@ struct MfmaBlock {
   uint4 v[kPrefetchV ? 3 : 1][D / 128];   // V words of plane j: coordinate pairs kp
 };
 
-template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(DecodeArgs a) {
+// NG query groups (4 rows each) share a workgroup: the key and V operands of a
+// block are built once and each MFMA operand of the keys or V bits meets the NG
+// query operands in turn. NG = 1 gives each group its own workgroup.
+template <int D, int NG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2 : 1))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NMU = 5 * (D / 128);        // scaled MFMAs per 16-token scoring tile
   constexpr int NCH = D / 128;              // 16-byte key chunks per lane and token
   constexpr int KREC = D / 2;
@@ -132,26 +135,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
   constexpr size_t VSEC = VCODES + 2 * kPage;
   constexpr int NB = D / 16;                // 16-coordinate V column blocks
+  constexpr int NR = NG * kMfmaMaxGroup;    // query rows of the workgroup
 
-  __shared__ float s_wm[4][4][kMfmaMaxGroup];     // per wave: m, l, mU, sum U of each row
-  __shared__ float s_wacc[4][kMfmaMaxGroup][D];   // per wave V numerators
-  __shared__ v8i s_qop[NMU * 64];                  // packed query operand, [mfma][lane]
-  __shared__ int s_qsc[NMU * 64];                  // its block scales (E8M0), [mfma][lane]
+  // the query operands live in LDS during the page loop; the same bytes then
+  // hold the per-wave V numerators for the final combine
+  constexpr size_t QOP_BYTES = (size_t)NG * NMU * 64 * 32, QSC_BYTES = (size_t)NG * NMU * 64 * 4;
+  constexpr size_t WACC_BYTES = (size_t)4 * NR * D * 4;
+  constexpr size_t RAW = QOP_BYTES + QSC_BYTES > WACC_BYTES ? QOP_BYTES + QSC_BYTES : WACC_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[RAW];
+  __shared__ float s_wm[4][4][NR];                  // per wave: m, l, mU, sum U of each row
+  v8i *s_qop = reinterpret_cast<v8i *>(s_raw);      // [group][mfma][lane]
+  int *s_qsc = reinterpret_cast<int *>(s_raw + QOP_BYTES);
+  auto s_wacc = reinterpret_cast<float (*)[NR][D]>(s_raw);   // [wave][row][d]
 
-  const int QG = a.plan.qgroups;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / QG, rho = blockIdx.z % QG;
+  const int QG = a.plan.qgroups, WZ = a.plan.wg_per_seq;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / WZ;
+  const int rho0 = (blockIdx.z % WZ) * NG;           // first query group of the workgroup
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;   // scores: token 16 tau + n of query row kg
   const int lam = n & 3;                     // V weight operand: limb row / token of the quad
   const int H = a.n_kv_heads, g = a.n_q_heads / H;
-  const int qbase = kMfmaMaxGroup * rho;                   // first query row of the group
-  const int G = min(kMfmaMaxGroup, a.plan.group - qbase);  // rows in this group
   const int L = a.seq_lens[b];
 
-  const uint8_t *grp = a.packed + (((size_t)b * H + kvh) * QG + rho) * packed_group_bytes(D);
-  const float4 rc = reinterpret_cast<const float4 *>(grp + (size_t)NMU * (2048 + 256))[kg];
-  const float off1 = a.cb.levels[7] * rc.z, off2 = rc.w * qjl_kappa<D>();
-  const int vis = kg < G ? (a.causal_tail ? L - (a.n_q - 1 - (qbase + kg) / g) : L) : 0;
+  const uint8_t *grp0 = a.packed + (((size_t)b * H + kvh) * QG + rho0) * packed_group_bytes(D);
+  float off1[NG], off2[NG];
+  int vis[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int row = kMfmaMaxGroup * (rho0 + gi) + kg;   // query row of this lane in group gi
+    off1[gi] = off2[gi] = 0.f;
+    vis[gi] = 0;
+    if (row < a.plan.group) {
+      const float4 rc = reinterpret_cast<const float4 *>(grp0 + (size_t)gi * packed_group_bytes(D) +
+                                                         (size_t)NMU * (2048 + 256))[kg];
+      off1[gi] = a.cb.levels[7] * rc.z;
+      off2[gi] = rc.w * qjl_kappa<D>();
+      vis[gi] = a.causal_tail ? L - (a.n_q - 1 - row / g) : L;
+    }
+  }
   // V weight operand: lane 16 kg + 4 q + lam takes the weight of query q, token
   // 16 tau + 4 kg + lam, which the score layout holds in lane 16 q + 4 kg + lam
   const int perm_addr = 4 * (16 * (n >> 2) + 4 * kg + lam);
@@ -171,31 +192,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 
   // running maxima start finite, so exp2 of a masked (-inf) score is 0 and no
   // per-token guard is needed; a row with no visible token keeps l = 0
-  float m_run = -kFltMax, mu_run = -kFltMax, l_lane = 0.f, us_lane = 0.f;
-  // V sums: int32 MFMA accumulators folded into a float accumulator. At
-  // d = 256 they are folded only when the softmax reference moves and at the
-  // end (per 64-token block a limb row gains at most 4 planes x 64 tokens x 128
-  // x 8 = 2^18, so up to 2^13 blocks, far more than one split holds, fit in
-  // int32); at d = 128 the registers for that are not free next to the
-  // prefetched block, so they are folded after every block.
-  constexpr bool kLazyV = D == 256;
-  float facc[NB];
-  v4i vacc[NB];
+  float m_run[NG], mu_run[NG], l_lane[NG], us_lane[NG];
 #pragma unroll
-  for (int k = 0; k < NB; ++k) {
-    facc[k] = 0.f;
-    vacc[k] = v4i{0, 0, 0, 0};
+  for (int gi = 0; gi < NG; ++gi) {
+    m_run[gi] = mu_run[gi] = -kFltMax;
+    l_lane[gi] = us_lane[gi] = 0.f;
   }
-  // rows 4 kg + r of a V accumulator are (query kg, limb r): limb r weighs 256^r
-  auto fold_one = [&](int k) {
-    const float v = (float)vacc[k][0] + 256.f * (float)vacc[k][1] + 65536.f * (float)vacc[k][2] +
-                    16777216.f * (float)vacc[k][3];
-    facc[k] = fmaf(delta_u, v, facc[k]);
-    vacc[k] = v4i{0, 0, 0, 0};
-  };
-  auto fold_v = [&]() {
+  // V sums: int32 MFMA accumulators folded into a float accumulator. With one
+  // group at d = 256 they are folded only when the softmax reference moves and
+  // at the end (per 64-token block a limb row gains at most 4 planes x 64
+  // tokens x 128 x 8 = 2^18, so up to 2^13 blocks, far more than one split
+  // holds, fit in int32); otherwise the registers for that are not free, so
+  // they are folded after every block.
+  constexpr bool kLazyV = D == 256 && NG == 1;
+  float facc[NG][NB];
+  v4i vacc[NG][NB];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) fold_one(k);
+  for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      facc[gi][k] = 0.f;
+      vacc[gi][k] = v4i{0, 0, 0, 0};
+    }
+  // rows 4 kg + r of a V accumulator are (query kg, limb r): limb r weighs 256^r
+  auto fold_one = [&](int gi, int k) {
+    const float v = (float)vacc[gi][k][0] + 256.f * (float)vacc[gi][k][1] + 65536.f * (float)vacc[gi][k][2] +
+                    16777216.f * (float)vacc[gi][k][3];
+    facc[gi][k] = fmaf(delta_u, v, facc[gi][k]);
+    vacc[gi][k] = v4i{0, 0, 0, 0};
+  };
+  auto fold_v = [&](int gi) {
+#pragma unroll
+    for (int k = 0; k < NB; ++k) fold_one(gi, k);
   };
 
   const int n_pages_seq = min((L + kPage - 1) / kPage, a.max_pages);
@@ -204,6 +232,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   const int blk0 = 64 * wave;
   // pages whose block of this wave holds no token are skipped (only the last can)
   if (pg1 > pg0 && blk0 >= L - (pg1 - 1) * kPage) --pg1;
+
+  // the query operands of the workgroup's groups (a group past the last one
+  // gets zero operands; its rows are masked)
+  auto stage = [&]() {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      if (rho0 + gi < QG) {
+        stage_query<NMU>(grp0 + (size_t)gi * packed_group_bytes(D), s_qop + gi * NMU * 64,
+                         s_qsc + gi * NMU * 64, tid);
+      } else {
+        uint4 *dst = reinterpret_cast<uint4 *>(s_qop + gi * NMU * 64);
+        for (int e = tid; e < NMU * 128; e += 256) dst[e] = make_uint4(0u, 0u, 0u, 0u);
+        for (int e = tid; e < NMU * 64; e += 256) s_qsc[gi * NMU * 64 + e] = 127;
+      }
+    }
+  };
 
   auto load_block = [&](MfmaBlock<D> &d, int pg) {
     const int phys = a.block_table[(size_t)b * a.max_pages + pg];
@@ -231,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // at d = 256 the query operand (20 MFMA operands, 80 registers) is read from
     // LDS where it is used: an opaque lane offset keeps it from being hoisted
     int qo = lane;
-    if constexpr (D == 256) asm volatile("" : "+v"(qo));
+    if constexpr (D == 256 || NG > 1) asm volatile("" : "+v"(qo));
     uint4 vcur[3][NCH];
     if constexpr (MfmaBlock<D>::kPrefetchV) {
 #pragma unroll
@@ -249,49 +293,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
-    // ---- scores: lane (n, kg) ends with query row kg, token blk0 + 16 tau + n
-    float sc[4], sv[4];
+    // ---- scores: lane (n, kg) ends with query row kg of each group, token blk0 + 16 tau + n
+    float sc[NG][4], sv[NG][4];
     // the four 16-token tiles' MFMAs are interleaved (consecutive MFMAs are
-    // independent); the query operand of each step is shared by the four.
+    // independent); the query operand of each step is shared by the four, and
+    // each tile's key operand by the NG groups.
     // Key operand (B, fp4 e2m1): nibble m of dword v holds plane bit 4 m + v, as
     // 0.5, 1, 2, 2 (bit 3 shifted down one place); the query side (A, fp6)
     // carries 1 / value.
-    v4f c1[4], c2[4];
+    v4f c1[NG][4], c2[NG][4];
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) c1[tau] = c2[tau] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) c1[gi][tau] = c2[gi][tau] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
       for (int j = 0; j < 5; ++j) {   // code planes b0, b1, b2, b0^b1^b2, then the sign plane
-        const v8i qop = s_qop[(5 * c + j) * 64 + qo];
-        const int qsc = s_qsc[(5 * c + j) * 64 + qo];
+        v8i op[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           const uint4 w = d.kw[tau][c];
           const uint32_t pl = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : j == 3 ? (w.x ^ w.y ^ w.z) : w.w;
-          const v8i op = {(int)(pl & 0x11111111u), (int)(pl & 0x22222222u), (int)(pl & 0x44444444u),
-                          (int)((pl >> 1) & 0x44444444u), 0, 0, 0, 0};
-          if (j < 4)
-            c1[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c1[tau], 2, 4, 0, qsc, 0, 127);
-          else
-            c2[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op, c2[tau], 2, 4, 0, qsc, 0, 127);
+          op[tau] = v8i{(int)(pl & 0x11111111u), (int)(pl & 0x22222222u), (int)(pl & 0x44444444u),
+                        (int)((pl >> 1) & 0x44444444u), 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          const v8i qop = s_qop[(gi * NMU + 5 * c + j) * 64 + qo];
+          const int qsc = s_qsc[(gi * NMU + 5 * c + j) * 64 + qo];
+#pragma unroll
+          for (int tau = 0; tau < 4; ++tau) {
+            if (j < 4)
+              c1[gi][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op[tau], c1[gi][tau], 2, 4, 0, qsc, 0, 127);
+            else
+              c2[gi][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op[tau], c2[gi][tau], 2, 4, 0, qsc, 0, 127);
+          }
         }
       }
     }
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
-      // the four limbs of (S1, S2) for query row kg, token 16 tau + n
-      const float T1 = (c1[tau][0] + c1[tau][1]) + (c1[tau][2] + c1[tau][3]);
-      const float T2 = (c2[tau][0] + c2[tau][1]) + (c2[tau][2] + c2[tau][3]);
       const int sh = 16 * (tau & 1);
       const float Gt = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.g.y : d.g.x) >> sh));
       const float N = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nk.y : d.nk.x) >> sh));
-      const float NV = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nv.y : d.nv.x) >> sh));
+      const float lnv = __builtin_amdgcn_logf(f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nv.y : d.nv.x) >> sh)));
       const int tok = blk0 + 16 * tau + n;
-      const bool valid = tok < ntok && tok0 + tok < vis;   // vis = 0 for rows past the group
-      const float sco = scale2 * N * fmaf(Gt, T2 - off2, T1 - off1);
-      sc[tau] = valid ? sco : kNegInf;
-      sv[tau] = valid ? sco + __builtin_amdgcn_logf(NV) : kNegInf;   // + log2 N^V
+      const bool in_page = tok < ntok;
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        // the four limbs of (S1, S2) for query row kg, token 16 tau + n
+        const float T1 = (c1[gi][tau][0] + c1[gi][tau][1]) + (c1[gi][tau][2] + c1[gi][tau][3]);
+        const float T2 = (c2[gi][tau][0] + c2[gi][tau][1]) + (c2[gi][tau][2] + c2[gi][tau][3]);
+        const bool valid = in_page && tok0 + tok < vis[gi];   // vis = 0 for rows past the group
+        const float sco = scale2 * N * fmaf(Gt, T2 - off2[gi], T1 - off1[gi]);
+        sc[gi][tau] = valid ? sco : kNegInf;
+        sv[gi][tau] = valid ? sco + lnv : kNegInf;   // + log2 N^V
+      }
     }
 
     // ---- online softmax of this wave (log2 units; scores, and scores + log2 N^V for V).
@@ -299,49 +357,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // score exceeds them by more than kSlack (log2 units), so every V weight
     // stays below 2^kSlack (its int32 limbs cannot overflow) and most blocks
     // skip the cross-lane maximum and the rescale.
-    {
-      const float smax = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-      const float vmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      if (__any(smax > m_run + kSlack || vmax > mu_run + kSlack)) {
-        const float m_new = fmaxf(m_run, rowmax16(smax));
-        const float mu_new = fmaxf(mu_run, rowmax16(vmax));
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        const float alphaU = __builtin_amdgcn_exp2f(mu_run - mu_new);
-        // the V accumulator rows of this lane are query row kg, as its scores
-        if constexpr (kLazyV) fold_v();
 #pragma unroll
-        for (int k = 0; k < NB; ++k) facc[k] *= alphaU;
-        l_lane *= alpha;
-        us_lane *= alphaU;
-        m_run = m_new;
-        mu_run = mu_new;
+    for (int gi = 0; gi < NG; ++gi) {
+      const float smax = fmaxf(fmaxf(sc[gi][0], sc[gi][1]), fmaxf(sc[gi][2], sc[gi][3]));
+      const float vmax = fmaxf(fmaxf(sv[gi][0], sv[gi][1]), fmaxf(sv[gi][2], sv[gi][3]));
+      if (__any(smax > m_run[gi] + kSlack || vmax > mu_run[gi] + kSlack)) {
+        const float m_new = fmaxf(m_run[gi], rowmax16(smax));
+        const float mu_new = fmaxf(mu_run[gi], rowmax16(vmax));
+        const float alpha = __builtin_amdgcn_exp2f(m_run[gi] - m_new);
+        const float alphaU = __builtin_amdgcn_exp2f(mu_run[gi] - mu_new);
+        // the V accumulator rows of this lane are query row kg, as its scores
+        if constexpr (kLazyV) fold_v(gi);
+#pragma unroll
+        for (int k = 0; k < NB; ++k) facc[gi][k] *= alphaU;
+        l_lane[gi] *= alpha;
+        us_lane[gi] *= alphaU;
+        m_run[gi] = m_new;
+        mu_run[gi] = mu_new;
       }
     }
-    float ps = 0.f, us = 0.f;
-    // the four weights go to the V operand layout first, so the four
-    // ds_bpermutes are in flight together
-    float Uv[4];
+    // the weights go to the V operand layout first, so the ds_bpermutes are in
+    // flight together
+    float Uv[NG][4];
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      ps += __builtin_amdgcn_exp2f(sc[tau] - m_run);
-      const float U = __builtin_amdgcn_exp2f(sv[tau] - mu_run);
-      us += U;
-      Uv[tau] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_addr, __builtin_bit_cast(int, U)));
+    for (int gi = 0; gi < NG; ++gi) {
+      float ps = 0.f, us = 0.f;
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        ps += __builtin_amdgcn_exp2f(sc[gi][tau] - m_run[gi]);
+        const float U = __builtin_amdgcn_exp2f(sv[gi][tau] - mu_run[gi]);
+        us += U;
+        Uv[gi][tau] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(perm_addr, __builtin_bit_cast(int, U)));
+      }
+      l_lane[gi] += ps;
+      us_lane[gi] += us;
     }
     __builtin_amdgcn_sched_barrier(0);
-    v4i A[4];   // per plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
+    v4i A[NG][4];   // per group and plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) {
-      const float Ut = __builtin_amdgcn_ldexpf(Uv[tau], -tau);
+    for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int X = (int)fmaf(Ut, cx[j], half[j]);
-        const uint32_t t4 = quad_byte_transpose((uint32_t)X + 0x80808080u, lam) ^ 0x80808080u;
-        A[j][tau] = (int)t4;
+      for (int tau = 0; tau < 4; ++tau) {
+        const float Ut = __builtin_amdgcn_ldexpf(Uv[gi][tau], -tau);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int X = (int)fmaf(Ut, cx[j], half[j]);
+          const uint32_t t4 = quad_byte_transpose((uint32_t)X + 0x80808080u, lam) ^ 0x80808080u;
+          A[gi][j][tau] = (int)t4;
+        }
       }
-    }
-    l_lane += ps;
-    us_lane += us;
 
     // ---- V: one 64-token K block, D/16 column blocks x 4 planes
     auto vword = [&](int j, int kp) -> uint32_t {
@@ -353,7 +417,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
     for (int kp = 0; kp < D / 32; ++kp) xw[kp] = vword(0, kp) ^ vword(1, kp) ^ vword(2, kp);
     // column blocks 2 kp and 2 kp + 1 come from the low and high nibbles of the
-    // same words; their two accumulation chains are interleaved
+    // same words; their accumulation chains (and those of the groups) are
+    // interleaved
 #pragma unroll
     for (int kp = 0; kp < D / 32; ++kp) {
       const uint32_t wj[4] = {vword(0, kp), vword(1, kp), vword(2, kp), xw[kp]};
@@ -367,22 +432,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
           bop.y = (int)(w & 0x02020202u);
           bop.z = (int)(w & 0x04040404u);
           bop.w = (int)(w & 0x08080808u);
-          vacc[2 * kp + h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[j], bop, vacc[2 * kp + h], 0, 0, 0);
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi)
+            vacc[gi][2 * kp + h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[gi][j], bop, vacc[gi][2 * kp + h], 0, 0, 0);
         }
       if constexpr (!kLazyV) {
-        fold_one(2 * kp);
-        fold_one(2 * kp + 1);
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          fold_one(gi, 2 * kp);
+          fold_one(gi, 2 * kp + 1);
+        }
       }
     }
   };
 
   // the first block's loads go out before the query operand is staged, so the
   // two fetches overlap
-  if constexpr (D == 128) {
+  if constexpr (D == 128 && NG == 1) {
     MfmaBlock<D> d0, d1;
     if (pg0 < pg1) load_block(d0, pg0);
     // the packed query operand is shared by the four waves: keep it in LDS
-    stage_query<NMU>(grp, s_qop, s_qsc, tid);
+    stage();
     __syncthreads();
     for (int pg = pg0; pg < pg1; pg += 2) {
       if (pg + 1 < pg1) load_block(d1, pg + 1);
@@ -392,8 +462,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       process(d1, pg + 1);
     }
   } else {
-    // d = 256: one register set (two would cost the second wave per SIMD)
-    stage_query<NMU>(grp, s_qop, s_qsc, tid);
+    // one register set (at d = 256 two would cost the second wave per SIMD)
+    stage();
     __syncthreads();
     for (int pg = pg0; pg < pg1; ++pg) {
       MfmaBlock<D> d0;
@@ -402,26 +472,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
   }
 
-  if constexpr (kLazyV) fold_v();
+  if constexpr (kLazyV) fold_v(0);
   // ---- combine the four waves into one partial per query row
-  const float l_row = rowsum16(l_lane), us_row = rowsum16(us_lane);
-  if (n == 0) {
-    s_wm[wave][0][kg] = m_run;
-    s_wm[wave][1][kg] = l_row;
-    s_wm[wave][2][kg] = mu_run;
-    s_wm[wave][3][kg] = us_row;
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const float l_row = rowsum16(l_lane[gi]), us_row = rowsum16(us_lane[gi]);
+    if (n == 0) {
+      s_wm[wave][0][4 * gi + kg] = m_run[gi];
+      s_wm[wave][1][4 * gi + kg] = l_row;
+      s_wm[wave][2][4 * gi + kg] = mu_run[gi];
+      s_wm[wave][3][4 * gi + kg] = us_row;
+    }
   }
-  __syncthreads();
+  __syncthreads();   // every wave is past the page loop: the query operands are dead
   {
     const float c7 = a.cb.levels[7];
-    const float usq = s_wm[wave][3][kg & 3];
 #pragma unroll
-    for (int k = 0; k < NB; ++k) s_wacc[wave][kg & 3][16 * k + n] = facc[k] - c7 * usq;
+    for (int gi = 0; gi < NG; ++gi) {
+      const float usq = s_wm[wave][3][4 * gi + kg];
+#pragma unroll
+      for (int k = 0; k < NB; ++k) s_wacc[wave][4 * gi + kg][16 * k + n] = facc[gi][k] - c7 * usq;
+    }
   }
   __syncthreads();
   const int nsplit = a.plan.n_split;
-  const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * a.plan.group + qbase;
-  for (int qq = wave; qq < G; qq += 4) {
+  const int rbase = kMfmaMaxGroup * rho0;   // first query row of the workgroup
+  const int nrow = min(NR, a.plan.group - rbase);
+  const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * a.plan.group + rbase;
+  for (int qq = wave; qq < nrow; qq += 4) {
     float M = kNegInf, MU = kNegInf;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
@@ -548,8 +626,17 @@ template <int D>
 hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
   const int G = a.plan.group;
   if (!a.plan.mfma || G > TQ_MAX_GROUP) return hipErrorInvalidValue;
-  const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.qgroups);
-  hipLaunchKernelGGL((decode_mfma_kernel<D>), grid, dim3(256), 0, s, a);
+  const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.wg_per_seq);
+  switch (a.plan.groups_per_wg) {
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
+    case 2:
+      if constexpr (D == 128) {
+        hipLaunchKernelGGL((decode_mfma_kernel<D, 2>), grid, dim3(256), 0, s, a);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

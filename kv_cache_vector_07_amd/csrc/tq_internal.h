@@ -63,6 +63,11 @@ __host__ __device__ inline size_t packed_group_bytes(int d) {
 }
 constexpr int kMfmaMaxGroup = 4;   // query rows per MFMA query group (4 rows x 4 limbs)
 __host__ __device__ inline int query_groups(int group) { return (group + kMfmaMaxGroup - 1) / kMfmaMaxGroup; }
+// Most query groups one decode workgroup serves (1 or 2), by head_dim. At
+// d = 128 two groups per workgroup keep two waves per SIMD (242 VGPRs) and
+// share the key and V operands; at d = 256 two groups need more than 256
+// registers (one wave per SIMD) and are slower than one group per workgroup.
+__host__ __device__ inline int max_groups_per_wg(int d) { return d == 128 ? 2 : 1; }
 // The MFMA decode kernel covers head_dim 128 and 256 with up to TQ_MAX_GROUP
 // query rows per KV head, as query groups of 4 rows.
 __host__ __device__ inline bool mfma_path(int d, int group) {
@@ -73,6 +78,8 @@ __host__ __device__ inline bool mfma_path(int d, int group) {
 struct DecodePlan {
   int group;              // query rows per (sequence, KV head) = Hq/Hkv * n_q
   int qgroups;            // MFMA query groups of 4 rows (MFMA path)
+  int groups_per_wg;      // query groups one decode workgroup serves: 1 or 2
+  int wg_per_seq;         // decode workgroups per (split, KV head, sequence)
   int pages_per_split;
   int n_split;
   size_t counter_bytes;   // reserved (0)

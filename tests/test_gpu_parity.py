@@ -145,6 +145,9 @@ DEC_CASES = [
     (256, 4, 16, 1, [700, 256], "bf16", "outlier", 0, 8),             # d=256, one query group
     (128, 4, 8, 2, [400, 2, 257], "bf16", "outlier", 1, 9),           # n_q=2 causal, MFMA path
     (128, 2, 16, 1, [300], "bf16", "normal", 0, 10),                  # 8 rows: two query groups
+    (128, 2, 12, 1, [700, 300], "bf16", "outlier", 0, 11),            # 6 rows: two groups, one partial
+    (128, 2, 24, 1, [600, 5], "bf16", "normal", 0, 12),               # 12 rows: three groups, the second workgroup half empty
+    (128, 1, 16, 1, [900], "bf16", "outlier", 0, 13),                 # 16 rows at d=128: two workgroups of two groups
 ]
 
 
