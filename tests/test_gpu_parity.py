@@ -151,6 +151,40 @@ DEC_CASES = [
 ]
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_decode_query_extremes(tq, d):
+    """The query operand is four fp6 limbs with power-of-two block scales (about
+    2^-18 of each 32-coordinate block's largest term), so the score error grows
+    with the logits: a zero query, a query scaled by 1e-4 or by 1e3 (logits near
+    1e4, softmax near one-hot) and queries with one large coordinate before or
+    after the rotation all stay within tolerance. (At 1e4 times the workloads'
+    query norm the error passes 2e-3.)"""
+    H, Hq, lens = 2, 8, [700, 300]
+    table, n_pages, kp, vp, cb, S = _oracle_cache(d, H, lens, "f32", "outlier", 21)
+    cache = tq.Cache(d, H, n_pages)
+    cache.k_pool.copy_(torch.from_numpy(kp))
+    cache.v_pool.copy_(torch.from_numpy(vp))
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(21)
+    base = rng.standard_normal((len(lens), 1, Hq, d)).astype(np.float32)
+    spike = np.full_like(base, 1e-6)
+    spike[..., 5] = 3.0
+    # a spike after the rotation: row 5 of the Sylvester Hadamard matrix, so the
+    # rotated query has one large coordinate in one 32-coordinate block
+    hrow = np.array([(-1) ** bin(5 & j).count("1") for j in range(d)], np.float32) / math.sqrt(d)
+    rot_spike = (base * 1e-6 + 3.0 * hrow).astype(np.float32)
+    for name, q in [("zero", np.zeros_like(base)), ("small", base * 1e-4), ("large", base * 1e3),
+                    ("spike", spike), ("rotated spike", rot_spike)]:
+        print(f"[query extremes] d={d} {name}", flush=True)
+        ref = O.attn_decode(kp, vp, cb, S, q.astype(np.float64), table, lens, H, 256, Hn.scale_of(d))
+        out = tq.tq_attn_decode(cache, Hn.torch_input(q, "f32"), bt, sl)
+        torch.cuda.synchronize()
+        err = Hn.attn_rel_err(out.cpu().numpy(), ref)
+        print(f"  max rel err {err:.3e}")
+        assert err <= Hn.ATTN_TOL, name
+
+
 @pytest.mark.parametrize("case", DEC_CASES, ids=lambda c: f"d{c[0]}-H{c[1]}-Hq{c[2]}-nq{c[3]}-L{len(c[4])}-c{c[7]}")
 def test_decode_parity(tq, case):
     d, H, Hq, nq, lens, dtype, dist, causal, seed = case
