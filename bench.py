@@ -63,6 +63,22 @@ def read_traffic(workload: str):
     return float(kv["hbm_bytes_per_launch"])
 
 
+def platform_info():
+    """ROCm/HIP version, GPU name and the current clocks (best effort)."""
+    import subprocess
+    import torch
+    info = {"hip": torch.version.hip, "torch": torch.__version__,
+            "gpu": torch.cuda.get_device_name(0)}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        clk = [ln.split(":", 1)[-1].strip() for ln in r.stdout.splitlines()
+               if ("sclk" in ln or "mclk" in ln) and "level" in ln]
+        info["clocks"] = clk[:4]
+    except Exception as e:  # the clocks are context only
+        info["clocks"] = f"unavailable ({type(e).__name__})"
+    return info
+
+
 def dense_baseline(dense, qs, seq, scale, tq_dec_ms, sh, log):
     """The uncompressed bf16 decode kernel on the same K, V and queries, over
     rotating device copies (>= 1 GiB), against the compressed split kernel."""
@@ -327,6 +343,20 @@ def main():
     merge_ms = timed(merge, 64)
     dec_kernel = "decode_mfma_kernel"
 
+    # the same split kernel on one copy only: its data can stay in the 256 MB
+    # Infinity Cache, so this is the "warm" figure, not the HBM-bound one
+    def dec_warm(i):
+        dec(0)
+    dec_warm_ms = timed(dec_warm, 64)
+
+    # the append encode of one step alone (one K and one V vector per sequence
+    # and KV head), as separate tq_encode_k / tq_encode_v calls
+    def append(i):
+        c = copies[i % R]
+        tq.tq_encode_k(c, new_k, app_slots, stream=sh)
+        tq.tq_encode_v(c, new_v, app_slots, stream=sh)
+    append_ms = timed(append, 64)
+
     ctx_tokens = int(lens.sum())
     kv_bytes = ctx_tokens * H * kv_bytes_per_token_head(d)
     app_bytes = B * H * (2 * d * (2 if w.dtype == "bf16" else 4) + kv_bytes_per_token_head(d))
@@ -357,7 +387,10 @@ def main():
         "encode_k_vec_per_s": round(n_vec / (enc_k_ms / 1e3), 1),
         "encode_v_vec_per_s": round(n_vec / (enc_v_ms / 1e3), 1),
         "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "decode_kernel_us_warm_single_copy": round(dec_warm_ms * 1e3, 3),
         "merge_kernel_us": round(merge_ms * 1e3, 3),
+        "append_encode_us": round(append_ms * 1e3, 3),
+        "platform": platform_info(),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": dec_kernel,
