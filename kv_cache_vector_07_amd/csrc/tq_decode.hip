@@ -8,11 +8,11 @@
 // and projected once per step; scores and the V sum live in the rotated domain
 // and one inverse rotation is applied per output row.
 //
-// Grid (split, KV head, sequence). A workgroup streams whole 256-token pages of
-// one (sequence, KV head) for every query row of that KV head, keeps an online
-// softmax, and writes (max, sum, V numerator) partials; a second, small kernel
-// merges the partials of each (sequence, KV head) by log-sum-exp and writes
-// float32 rows. (Merging in the last-arriving workgroup would need a device-scope
+// Grid (split, KV head, sequence x query-group workgroup). A workgroup streams
+// whole 256-token pages of one (sequence, KV head) for the query rows of one or
+// two query groups (4 rows each), keeps an online softmax, and writes (max, sum,
+// V numerator) partials; a second, small kernel merges the partials of each
+// query row by log-sum-exp and writes float32 rows. (Merging in the last-arriving workgroup would need a device-scope
 // release per workgroup, which on this GPU writes back and invalidates the whole
 // L2 of the XCD every time.)
 //
@@ -22,9 +22,10 @@
 // becomes an fp4 operand (one AND per eight coordinates, the bit's position
 // folded into the fp4 value); the query side is four fp6 (e2m3) limbs with a
 // power-of-two scale per 32 coordinates on the MFMA rows (4 query rows x 4 limbs
-// per query group), about 2^-16 of the largest term per block. V is accumulated with the
-// same planes on int8 MFMA: the softmax weight times each plane weight, as four
-// int8 limbs, against the V bit planes; every product there is exact in int32.
+// per query group), exact to under 2^-18 of the largest term of each block. V is
+// accumulated with the same planes on int8 MFMA: the softmax weight times each
+// plane weight, as four int8 limbs, against the V bit planes; every product there
+// is exact in int32.
 #include "tq_device.h"
 
 namespace tq {
@@ -89,20 +90,20 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // V: int8 MFMA with the softmax weight (times each plane weight) as 4 int8 limbs
 // on the 16 rows and the V bit planes on the columns: lane (n, k) reads its 16
 // tokens x 2 coordinates per u32 word, and a shift plus one AND per 4 tokens
-// makes the B operand. The int32 sums stay in the MFMA accumulators across
-// blocks and are folded into a float accumulator only when the softmax
+// makes the B operand. The int32 sums are folded into a float accumulator
+// after every block, or (one query group at d = 256) only when the softmax
 // reference moves, and once at the end.
 //
 // Up to 16 query rows per KV head run as query groups of 4 rows (4 rows x 4
-// limbs fill the 16 MFMA columns); each group is its own workgroup, and the
-// groups of one split sit in blockIdx.z next to each other, so with n_split * Hkv
-// a multiple of 8 they land on the same XCD and share its L2.
+// limbs fill the 16 MFMA rows). At d = 128 two groups share a workgroup; the
+// workgroups of one split sit in blockIdx.z, n_split * Hkv apart, so with
+// n_split * Hkv a multiple of 8 they land on the same XCD and share its L2.
 //
-// Everything one block needs (key records, sidecars, V words) is loaded one
-// block ahead; two register sets alternate between even and odd pages so that
-// no copy is needed.
-// (At d = 256 the V words are loaded at the start of the block instead, to keep
-// two waves per SIMD.)
+// At d = 128 with one group, everything one block needs (key records, sidecars,
+// V words) is loaded one block ahead; two register sets alternate between even
+// and odd pages so that no copy is needed. Otherwise the block's loads are
+// issued at its start, to keep two waves per SIMD.
+
 // Copies the packed scoring operand of a query group (NMU x 64 lanes x 32 bytes,
 // then NMU x 64 scale words) into LDS.
 template <int NMU>

@@ -132,7 +132,8 @@ __device__ inline int quantize_code(const Codebook &cb, float y) {
 
 // Page offsets are split as t = 64 b + 16 tau + 4 k + r (b: 64-token block;
 // tau, k, r = 0..3). The per-page N / G arrays hold token t at entry
-// 64 b + 16 k + 4 r + tau, so the 16 tokens with one (b, k) are adjacent.
+// 64 b + 16 k + 4 r + tau = 64 b + 4 n + tau (n = 4 k + r), so the four tokens
+// 16 tau + n of one (b, n) are adjacent.
 __host__ __device__ inline int side_entry(int t) {
   return (t & ~63) | ((t & 12) << 2) | ((t & 3) << 2) | ((t >> 4) & 3);
 }

@@ -281,8 +281,8 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
 // ------------------------------------------------------------------ prepare
 // One workgroup per query row qq of a (sequence, KV head) group: rotate the
 // row, project it with S, write q~ and p, and on the MFMA path pack this row's
-// four limb columns of the int8 scoring operand. The four waves split the m
-// rows of S, and every S load of a chunk is issued before the row is rotated.
+// four limb rows of the fp6 scoring operand. The four waves split the m rows
+// of S, and every S load of a chunk is issued before the row is rotated.
 template <int D, int DT>
 __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   constexpr int R = D / 64;

@@ -42,14 +42,15 @@ struct DequantArgs {
 };
 
 // Query preparation for one decode call: rotation, QJL projection and, for
-// the MFMA decode path, the packed int8 scoring operand of each (sequence, KV head).
+// the MFMA decode path, the packed scoring operand (fp6 query limbs with block
+// scales) of each (sequence, KV head, query group).
 struct PrepArgs {
   const void *q;          // [batch][n_q][Hq][d]
   int dtype;
   int batch, n_q, n_q_heads, n_kv_heads;
   const float *qjl;
   float *prep;            // [rows][2][d]: Pi q, then S Pi q
-  uint8_t *packed;        // per (sequence, KV head): int8 operand + row constants (or null)
+  uint8_t *packed;        // per (sequence, KV head, query group): operand + row constants (or null)
   Codebook cb;
 };
 
