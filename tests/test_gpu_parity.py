@@ -330,6 +330,55 @@ def test_append_decode_matches_separate_calls_and_reference(tq, d, Hq, nq):
     assert err <= Hn.ATTN_TOL
 
 
+def test_speculative_verify_and_rollback(tq):
+    """Speculative verify: append n_q = 4 draft tokens per sequence, score the four
+    draft queries against the cache with the causal tail (query t sees
+    L - (n_q - 1 - t) tokens) and check them against the reference; then roll back
+    by rewinding seq_lens. Earlier slots are never rewritten, so decoding after the
+    rollback gives the same bits as before the drafts were appended."""
+    d, H, Hq, nq = 128, 4, 8, 4
+    lens0 = np.array([600, 255, 256])
+    print("[verify rollback]", flush=True)
+    w = I.Workload("spec", len(lens0), Hq, H, d, "bf16", "outlier", 41, n_q=nq, fixed_len=1)
+    table, n_pages = I.page_table(w, lens0, extra_tokens=nq, shuffle=True)
+    cache = tq.Cache(d, H, n_pages)
+    bt = torch.from_numpy(table).cuda()
+    for b, L in enumerate(lens0):
+        t = torch.arange(0, int(L), device="cuda")
+        sl = (bt[b, t // 256] * 256 + t % 256).to(torch.int32)
+        tq.tq_encode_k(cache, torch.from_numpy(I.kv_tokens(w, "k", b, 0, int(L))).to("cuda", torch.bfloat16), sl)
+        tq.tq_encode_v(cache, torch.from_numpy(I.kv_tokens(w, "v", b, 0, int(L))).to("cuda", torch.bfloat16), sl)
+    # one decode step (a single query token per sequence) before the drafts
+    w1 = I.Workload("spec1", len(lens0), Hq, H, d, "bf16", "outlier", 41, n_q=1, fixed_len=1)
+    q1 = torch.from_numpy(I.queries(w1, 0)).to("cuda", torch.bfloat16)
+    sl0 = torch.from_numpy(lens0.astype(np.int32)).cuda()
+    before = tq.tq_attn_decode(cache, q1, bt, sl0).clone()
+    # append the drafts and verify them in one call
+    pos = np.concatenate([np.arange(L, L + nq) for L in lens0])
+    bidx = np.repeat(np.arange(len(lens0)), nq)
+    slots = torch.from_numpy((table[bidx, pos // 256].astype(np.int64) * 256 + pos % 256).astype(np.int32)).cuda()
+    dk = np.concatenate([I.kv_tokens(w, "k", b, int(L), int(L) + nq) for b, L in enumerate(lens0)])
+    dv = np.concatenate([I.kv_tokens(w, "v", b, int(L), int(L) + nq) for b, L in enumerate(lens0)])
+    q = I.queries(w, 0)
+    lens = lens0 + nq
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    out = tq.tq_append_decode(cache, torch.from_numpy(dk).to("cuda", torch.bfloat16),
+                              torch.from_numpy(dv).to("cuda", torch.bfloat16), slots,
+                              torch.from_numpy(q).to("cuda", torch.bfloat16), bt, sl, causal_tail=1)
+    torch.cuda.synchronize()
+    kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+    cb = Hn.codebook_from_cache(cache)
+    ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens, H, 256,
+                        Hn.scale_of(d), causal_tail=True)
+    err = Hn.attn_rel_err(out.cpu().numpy(), ref)
+    print(f"  verify max rel err {err:.3e}", flush=True)
+    assert err <= Hn.ATTN_TOL
+    # rollback: the drafts are rejected, seq_lens go back; the same step again
+    after = tq.tq_attn_decode(cache, q1, bt, sl0)
+    torch.cuda.synchronize()
+    assert torch.equal(before, after)
+
+
 @pytest.mark.parametrize("d,Hq,nq,lens", [(128, 16, 1, [700, 257]), (128, 32, 1, [1000, 1]),
                                           (256, 16, 2, [300, 64]), (128, 8, 2, [513, 0])])
 def test_dense_baseline_parity(tq, d, Hq, nq, lens):
