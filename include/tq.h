@@ -174,6 +174,26 @@ int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype,
                    float *out, void *workspace, size_t *workspace_bytes, void *stream);
 
 /*
+ * tq_attn_decode with a window: in sequence b only tokens
+ * seq_starts[b] <= j < (the tq_attn_decode bound) are visible, so a sliding-
+ * window layer attends to its last W tokens with seq_starts[b] = max(0, L_b - W).
+ * Pages wholly before seq_starts[b] are never read: their block-table entries
+ * may name pages that were recycled for newer tokens (a ring of pages). A row
+ * with no visible token is all zero. seq_starts: device int32 [batch], not null
+ * (TQ_EINVAL), 4-byte aligned (TQ_EALIGN); a negative start counts as 0.
+ * Everything else, including the workspace, is as tq_attn_decode.
+ * Source: the agentlenshq SharpAI/SwiftLM project page (Japanese), section
+ * それは何か, names sliding-window layers (a window-boundary bug) but defines no
+ * mechanics; the per-sequence first visible token is this library's reading.
+ */
+int tq_attn_decode_window(const tq_cache *c, const void *q, int32_t dtype,
+                          int32_t batch, int32_t n_q, int32_t n_q_heads,
+                          const int32_t *block_table, int32_t max_pages,
+                          const int32_t *seq_lens, const int32_t *seq_starts,
+                          int32_t causal_tail, float scale, float *out,
+                          void *workspace, size_t *workspace_bytes, void *stream);
+
+/*
  * One decode step with an append: encode n_new new K and V vectors
  * ([n_new][Hkv][d], kv_dtype) into `slots` exactly as tq_encode_k and
  * tq_encode_v do, then run tq_attn_decode over the updated cache (seq_lens

@@ -280,6 +280,7 @@ static tq::DecodeArgs decode_args(const tq_cache *c, const uint8_t *prep, int32_
   a.block_table = block_table;
   a.max_pages = max_pages;
   a.seq_lens = seq_lens;
+  a.seq_starts = nullptr;
   a.out = out;
   a.counters = nullptr;
   a.partials = (float *)(ws + plan.counter_bytes);
@@ -297,20 +298,24 @@ static tq::DecodeArgs decode_args(const tq_cache *c, const uint8_t *prep, int32_
 static int decode_run(const tq_cache *c, const uint8_t *prep, int32_t batch, int32_t n_q,
                       int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
                       const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
-                      uint8_t *ws, const tq::DecodePlan &plan, hipStream_t s) {
+                      uint8_t *ws, const tq::DecodePlan &plan, hipStream_t s,
+                      const int32_t *seq_starts = nullptr) {
   tq::DecodeArgs a = decode_args(c, prep, batch, n_q, n_q_heads, block_table, max_pages,
                                  seq_lens, causal_tail, scale, out, ws, plan);
+  a.seq_starts = seq_starts;
   if (tq::launch_decode_split(a, c->head_dim, s) != hipSuccess) return TQ_EHIP;
   return hip_status(tq::launch_decode_merge(a, c->head_dim, s));
 }
 
-int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype, int32_t batch, int32_t n_q,
-                   int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
-                   const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
-                   void *workspace, size_t *workspace_bytes, void *stream) {
+static int attn_decode_impl(const tq_cache *c, const void *q, int32_t dtype, int32_t batch,
+                            int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
+                            int32_t max_pages, const int32_t *seq_lens, const int32_t *seq_starts,
+                            int32_t causal_tail, float scale, float *out, void *workspace,
+                            size_t *workspace_bytes, void *stream) {
   int st = decode_checks(c, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
                          out, workspace_bytes);
   if (st) return st;
+  if (seq_starts && !aligned(seq_starts, 4)) return TQ_EALIGN;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
@@ -330,7 +335,25 @@ int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype, int32_t batc
   hipStream_t s = (hipStream_t)stream;
   if (run_prepare(c, q, dtype, batch, n_q, n_q_heads, prep, s) != hipSuccess) return TQ_EHIP;
   return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
-                    scale, out, ws, plan, s);
+                    scale, out, ws, plan, s, seq_starts);
+}
+
+int tq_attn_decode(const tq_cache *c, const void *q, int32_t dtype, int32_t batch, int32_t n_q,
+                   int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,
+                   const int32_t *seq_lens, int32_t causal_tail, float scale, float *out,
+                   void *workspace, size_t *workspace_bytes, void *stream) {
+  return attn_decode_impl(c, q, dtype, batch, n_q, n_q_heads, block_table, max_pages, seq_lens,
+                          nullptr, causal_tail, scale, out, workspace, workspace_bytes, stream);
+}
+
+int tq_attn_decode_window(const tq_cache *c, const void *q, int32_t dtype, int32_t batch,
+                          int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
+                          int32_t max_pages, const int32_t *seq_lens, const int32_t *seq_starts,
+                          int32_t causal_tail, float scale, float *out, void *workspace,
+                          size_t *workspace_bytes, void *stream) {
+  if (!seq_starts) return TQ_EINVAL;
+  return attn_decode_impl(c, q, dtype, batch, n_q, n_q_heads, block_table, max_pages, seq_lens,
+                          seq_starts, causal_tail, scale, out, workspace, workspace_bytes, stream);
 }
 
 int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, int32_t kv_dtype,

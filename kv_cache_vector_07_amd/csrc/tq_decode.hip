@@ -228,8 +228,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   };
 
   const int n_pages_seq = min((L + kPage - 1) / kPage, a.max_pages);
-  const int pg0 = split * a.plan.pages_per_split;
-  int pg1 = min(pg0 + a.plan.pages_per_split, n_pages_seq);
+  // tokens before S0 are not visible (a window); pages wholly before it are
+  // never read, so their block-table entries may point at recycled pages
+  const int S0 = a.seq_starts ? max(0, a.seq_starts[b]) : 0;
+  const int pg0 = max(split * a.plan.pages_per_split, S0 / kPage);
+  int pg1 = min(split * a.plan.pages_per_split + a.plan.pages_per_split, n_pages_seq);
   const int blk0 = 64 * wave;
   // pages whose block of this wave holds no token are skipped (only the last can)
   if (pg1 > pg0 && blk0 >= L - (pg1 - 1) * kPage) --pg1;
@@ -340,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
       const float N = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nk.y : d.nk.x) >> sh));
       const float lnv = __builtin_amdgcn_logf(f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nv.y : d.nv.x) >> sh)));
       const int tok = blk0 + 16 * tau + n;
-      const bool in_page = tok < ntok;
+      const bool in_page = tok < ntok && tok0 + tok >= S0;
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         // the four limbs of (S1, S2) for query row kg, token 16 tau + n

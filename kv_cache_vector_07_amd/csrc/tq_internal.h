@@ -104,6 +104,7 @@ struct DecodeArgs {
   const int32_t *block_table;
   int max_pages;
   const int32_t *seq_lens;
+  const int32_t *seq_starts;  // first visible token per sequence (or null: 0)
   float *out;             // [B][n_q][Hq][d]
   float *partials;
   uint32_t *counters;

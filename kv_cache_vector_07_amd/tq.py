@@ -22,7 +22,8 @@ TQ_F32, TQ_BF16 = 0, 1
 TQ_PAGE_SIZE = 256
 TQ_MAX_GROUP = 16
 EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_encode_k",
-           "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_append_decode",
+           "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_window",
+           "tq_append_decode",
            "tq_attn_decode_prepared", "tq_attn_decode_split", "tq_attn_decode_merge",
            "tq_dense_attn_decode", "tq_dequant", "tq_status_string")
 
@@ -62,6 +63,8 @@ def lib():
     L.tq_query_prepare.argtypes = [vp, vp, i32, i32, i32, i32, vp, C.POINTER(sz), vp]
     L.tq_attn_decode.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
                                  C.POINTER(sz), vp]
+    L.tq_attn_decode_window.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp, vp, i32, f32, vp,
+                                        vp, C.POINTER(sz), vp]
     L.tq_append_decode.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, vp, i32, vp,
                                    i32, f32, vp, vp, C.POINTER(sz), vp]
     L.tq_attn_decode_prepared.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
@@ -73,7 +76,8 @@ def lib():
     L.tq_dense_attn_decode.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, f32,
                                        vp, vp, C.POINTER(sz), vp]
     for name in ("tq_build_codebook", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
-                 "tq_attn_decode", "tq_append_decode", "tq_attn_decode_prepared", "tq_attn_decode_split",
+                 "tq_attn_decode", "tq_attn_decode_window", "tq_append_decode", "tq_attn_decode_prepared",
+                 "tq_attn_decode_split",
                  "tq_attn_decode_merge", "tq_dense_attn_decode", "tq_dequant"):
         getattr(L, name).restype = i32
     _lib = L
@@ -218,6 +222,25 @@ def tq_attn_decode(cache: Cache, q, block_table, seq_lens, causal_tail: int = 0,
     size = C.c_size_t(ws.numel())
     st = L.tq_attn_decode(*args(ws.data_ptr()), C.byref(size), _stream(stream))
     _check(st, "tq_attn_decode")
+    return out
+
+
+def tq_attn_decode_window(cache: Cache, q, block_table, seq_lens, seq_starts, causal_tail: int = 0,
+                          scale=None, out=None, workspace=None, stream=None):
+    """tq_attn_decode where sequence b sees only tokens j >= seq_starts[b] (int32 [B])."""
+    import torch
+    B, n_q, Hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=q.device)
+    L = lib()
+    args = lambda ws: (cache.ref, q.data_ptr(), _dtype_code(q), B, n_q, Hq, block_table.data_ptr(),
+                       int(block_table.shape[1]), seq_lens.data_ptr(), seq_starts.data_ptr(),
+                       int(causal_tail), scale, out.data_ptr(), ws)
+    ws, size = _decode_ws(cache, L.tq_attn_decode_window, args, workspace)
+    size = C.c_size_t(ws.numel())
+    st = L.tq_attn_decode_window(*args(ws.data_ptr()), C.byref(size), _stream(stream))
+    _check(st, "tq_attn_decode_window")
     return out
 
 

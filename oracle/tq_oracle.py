@@ -447,14 +447,16 @@ def score(qt, p, idx, sign, N, G, cb: Codebook, m: int):
 
 def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
                 n_kv_heads: int, page_size: int, scale: float,
-                causal_tail: bool = False, pairs=None) -> np.ndarray:
+                causal_tail: bool = False, pairs=None, seq_starts=None) -> np.ndarray:
     """Naive two-pass softmax attention over the packed cache, float64.
 
     For query (b, t, h) with KV head h // (Hq/Hkv) (R15) and visible tokens
-    j < L_b (or L_b - (n_q-1-t) with causal_tail, R16):
+    s_b <= j < L_b (or L_b - (n_q-1-t) with causal_tail, R16), s_b = seq_starts[b]
+    (0 without a window):
       w = softmax_j(scale * score_j),  a = sum_j w_j N^V_j c[idxV_j],  o = Pi a.
-    `pairs` restricts the work to the listed (b, kv_head) pairs; other rows
-    stay zero. Returns out [B][n_q][Hq][d].
+    A row with no visible token is zero. Records of tokens before s_b are not
+    read. `pairs` restricts the work to the listed (b, kv_head) pairs; other
+    rows stay zero. Returns out [B][n_q][Hq][d].
     """
     q = np.asarray(q, dtype=np.float64)
     B, n_q, Hq, d = q.shape
@@ -466,25 +468,30 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
         pairs = [(b, h) for b in range(B) for h in range(n_kv_heads)]
     for b, kvh in pairs:
         L = int(seq_lens[b])
-        if L <= 0:
+        s0 = max(0, int(seq_starts[b])) if seq_starts is not None else 0
+        if L <= s0:
             continue
-        idx, sign, N, G = gather_k(k_pool, block_table[b], L, kvh, n_kv_heads, d, page_size)
-        vidx, NV = gather_v(v_pool, block_table[b], L, kvh, n_kv_heads, d, page_size)
-        vals = NV[:, None] * cb.levels[vidx]                               # [L][d]
-        ckey = cb.levels[idx]                                              # [L][d]
+        # the visible range starts on page s0 // P: earlier pages are not read
+        p0 = s0 // page_size
+        base = p0 * page_size
+        idx, sign, N, G = gather_k(k_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size)
+        vidx, NV = gather_v(v_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size)
+        vals = NV[:, None] * cb.levels[vidx]                               # [L - base][d]
+        ckey = cb.levels[idx]                                              # [L - base][d]
         sig = np.where(sign, 1.0, -1.0)
+        lo = s0 - base
         for t in range(n_q):
-            vis = L - (n_q - 1 - t) if causal_tail else L
-            if vis <= 0:
+            vis = (L - (n_q - 1 - t) if causal_tail else L) - base
+            if vis <= lo:
                 continue
             for h in range(kvh * g, (kvh + 1) * g):
                 qt, p = rotate_query(q[b, t, h], S64)
                 # the estimate of score() with c[idx] and sigma evaluated once per head
-                est = N[:vis] * (ckey[:vis] @ qt + (QJL_KAPPA_NUM / m) * G[:vis] * (sig[:vis] @ p))
+                est = N[lo:vis] * (ckey[lo:vis] @ qt + (QJL_KAPPA_NUM / m) * G[lo:vis] * (sig[lo:vis] @ p))
                 logits = scale * est
                 w = np.exp(logits - logits.max())
                 w /= w.sum()
-                out[b, t, h] = fwht(w @ vals[:vis])
+                out[b, t, h] = fwht(w @ vals[lo:vis])
     return out
 
 

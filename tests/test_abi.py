@@ -187,3 +187,18 @@ def test_append_decode_validation(L):
     assert L.tq_append_decode(*args(FAKE, q=None), C.byref(ok), None) == tq.TQ_EINVAL
     assert L.tq_append_decode(*args(FAKE, k=FAKE + 4), C.byref(ok), None) == tq.TQ_EALIGN
     assert L.tq_append_decode(*args(FAKE + 16), C.byref(ok), None) == tq.TQ_EALIGN
+
+
+def test_window_decode_validation(L):
+    dsc = _desc(H=2)
+    _, need = _decode(L, dsc)
+    sz = C.c_size_t(0)
+    # the window variant needs the same workspace as the plain call
+    assert L.tq_attn_decode_window(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, FAKE, 0, 0.1,
+                                   FAKE, None, C.byref(sz), None) == tq.TQ_OK
+    assert sz.value == need
+    assert L.tq_attn_decode_window(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, None, 0, 0.1,
+                                   FAKE, None, C.byref(sz), None) == tq.TQ_EINVAL
+    sz = C.c_size_t(need)
+    assert L.tq_attn_decode_window(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, FAKE + 2, 0,
+                                   0.1, FAKE, FAKE, C.byref(sz), None) == tq.TQ_EALIGN

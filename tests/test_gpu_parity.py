@@ -379,6 +379,55 @@ def test_speculative_verify_and_rollback(tq):
     assert torch.equal(before, after)
 
 
+WIN_CASES = [
+    # (d, Hkv, Hq, n_q, lens, starts, causal, seed)
+    # mid-page, page-aligned, the last token only, a start past the length (zero rows)
+    (128, 2, 8, 1, [1000, 700, 300, 5], [300, 256, 299, 10], 0, 31),
+    # d = 256, causal tail: the second sequence's first row sees no token
+    (256, 2, 8, 4, [600, 300], [520, 297], 1, 32),
+    # 16 rows at d = 128 (two workgroups per KV head), a long window
+    (128, 1, 16, 1, [2100, 900], [1300, 1], 0, 33),
+]
+
+
+@pytest.mark.parametrize("case", WIN_CASES, ids=lambda c: f"d{c[0]}-Hq{c[2]}-nq{c[3]}-c{c[6]}")
+def test_window_decode_parity(tq, case):
+    """A per-sequence first visible token (a sliding window): pages wholly before
+    it are not read, so their block-table entries name recycled pages here."""
+    d, H, Hq, nq, lens, starts, causal, seed = case
+    print(f"[window parity] {case}", flush=True)
+    table, n_pages, kp, vp, cb, S = _oracle_cache(d, H, lens, "bf16", "outlier", seed)
+    w = I.Workload(f"w{seed}", len(lens), Hq, H, d, "bf16", "outlier", seed, n_q=nq, fixed_len=1)
+    q = I.queries(w, 0)
+    recycled = table.copy()
+    for b, s0 in enumerate(starts):
+        # in-range pages of other sequences stand in for pages handed to them
+        recycled[b, :s0 // 256] = table[(b + 1) % len(lens), 0]
+    ref = O.attn_decode(kp, vp, cb, S, q.astype(np.float64), table, lens, H, 256, Hn.scale_of(d),
+                        causal_tail=bool(causal), seq_starts=np.asarray(starts))
+    cache = tq.Cache(d, H, n_pages)
+    cache.k_pool.copy_(torch.from_numpy(kp))
+    cache.v_pool.copy_(torch.from_numpy(vp))
+    bt = torch.from_numpy(recycled).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    st = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    qt = Hn.torch_input(q, "bf16")
+    out = tq.tq_attn_decode_window(cache, qt, bt, sl, st, causal_tail=causal)
+    # a window starting at token 0 is the plain call, bit for bit
+    z = torch.zeros_like(st)
+    bt0 = torch.from_numpy(table).cuda()
+    outz = tq.tq_attn_decode_window(cache, qt, bt0, sl, z, causal_tail=causal)
+    plain = tq.tq_attn_decode(cache, qt, bt0, sl, causal_tail=causal)
+    torch.cuda.synchronize()
+    o = out.cpu().numpy()
+    err = Hn.attn_rel_err(o, ref)
+    print(f"max rel err {err:.3e}")
+    assert err <= Hn.ATTN_TOL
+    empty = np.all(ref == 0, axis=-1)           # rows with no visible token
+    assert np.all(o[empty] == 0) and not np.any(np.all(o[~empty] == 0, axis=-1))
+    assert torch.equal(outz, plain)
+
+
 @pytest.mark.parametrize("d,Hq,nq,lens", [(128, 16, 1, [700, 257]), (128, 32, 1, [1000, 1]),
                                           (256, 16, 2, [300, 64]), (128, 8, 2, [513, 0])])
 def test_dense_baseline_parity(tq, d, Hq, nq, lens):

@@ -417,3 +417,44 @@ def test_dense_attention_special_cases():
     assert np.allclose(out[0, 0, 3], v[0, 0, 1])
     out = O.dense_attn_decode(k, v, np.zeros_like(q), [5], 0.3)
     assert np.allclose(out[0, 0, 0], v[0, :, 0].mean(0))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_equals_dense_softmax_over_the_visible_tokens(causal):
+    """A per-sequence first visible token s_b: the result is softmax attention
+    over the dequantised tokens s_b <= j < vis only, and pages wholly before s_b
+    are never read (their block-table entries may name any page)."""
+    c = _small_cache(L=150, P=64)
+    scale = 1 / math.sqrt(c["d"])
+    B, nq, Hq, d = c["q"].shape
+    for starts in ([0, 0], [70, 3], [149, 64], [128, 40]):
+        starts = np.array(starts)
+        table = c["table"].copy()
+        for b in range(B):
+            # recycled pages: entries before the window's first page name another page
+            table[b, :starts[b] // c["P"]] = table[1 - b, 0]
+        out = O.attn_decode(c["kp"], c["vp"], c["cb"], c["S"], c["q"], table, c["lens"],
+                            c["H"], c["P"], scale, causal_tail=causal, seq_starts=starts)
+        for b in range(B):
+            Kt, Vt = c["dense"][b]
+            for t in range(nq):
+                vis = int(c["lens"][b]) - (nq - 1 - t) if causal else int(c["lens"][b])
+                s0 = int(starts[b])
+                for h in range(Hq):
+                    if vis <= s0:
+                        assert np.all(out[b, t, h] == 0)
+                        continue
+                    kv = h // c["g"]
+                    lg = scale * (Kt[s0:vis, kv] @ c["q"][b, t, h])
+                    w = np.exp(lg - lg.max())
+                    w /= w.sum()
+                    assert np.max(np.abs(out[b, t, h] - w @ Vt[s0:vis, kv])) < 1e-12
+    # a start of 0 is the plain call; a start at or past the length gives zero rows
+    plain = O.attn_decode(c["kp"], c["vp"], c["cb"], c["S"], c["q"], c["table"], c["lens"],
+                          c["H"], c["P"], scale)
+    zero = O.attn_decode(c["kp"], c["vp"], c["cb"], c["S"], c["q"], c["table"], c["lens"],
+                         c["H"], c["P"], scale, seq_starts=np.array([0, 0]))
+    assert np.array_equal(plain, zero)
+    past = O.attn_decode(c["kp"], c["vp"], c["cb"], c["S"], c["q"], c["table"], c["lens"],
+                         c["H"], c["P"], scale, seq_starts=c["lens"].copy())
+    assert np.all(past == 0)
