@@ -158,6 +158,87 @@ def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0):
             "encode_vec_per_s": round(2 * x.shape[0] * H / enc_dt, 1)}
 
 
+def prefill_attention(copies, table, lens, w, chunk, tdt, scale, sh, log):
+    """Chunked-prefill attention: the last `chunk` tokens of each sequence are
+    appended again (encoding is idempotent) and their chunk x Hq/Hkv query rows
+    attend causally over the whole compressed cache, in one tq_append_decode.
+    Reported against the time its MFMA instructions need at the published
+    rates (16 clocks per 16x16x128 fp6 x fp4 and per 16x16x64 int8 MFMA on
+    1024 SIMDs at 2.4 GHz), counted over the 64-token blocks each workgroup's
+    rows can see."""
+    import torch
+    from kv_cache_vector_07_amd import inputs as I
+    from kv_cache_vector_07_amd import tq
+    dev = table.device
+    d, H, Hq, B = w.head_dim, w.n_kv_heads, w.n_q_heads, w.batch
+    g = Hq // H
+    rows = chunk * g
+    R = len(copies)
+    pos = np.concatenate([np.arange(int(L) - chunk, int(L)) for L in lens])
+    seq_np = np.repeat(np.arange(B), chunk)
+    tbl = table.cpu().numpy()
+    slots = torch.from_numpy((tbl[seq_np, pos // 256].astype(np.int64) * 256 + pos % 256)
+                             .astype(np.int32)).to(dev)
+    k = torch.from_numpy(np.concatenate([I.kv_tokens(w, "k", b, int(L) - chunk, int(L))
+                                         for b, L in enumerate(lens)])).to(dev, tdt)
+    v = torch.from_numpy(np.concatenate([I.kv_tokens(w, "v", b, int(L) - chunk, int(L))
+                                         for b, L in enumerate(lens)])).to(dev, tdt)
+    rng = np.random.default_rng([w.data_seed, 7, chunk])
+    q = torch.from_numpy(rng.standard_normal((B, chunk, Hq, d)).astype(np.float32)).to(dev, tdt)
+    seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    out = torch.empty(B, chunk, Hq, d, dtype=torch.float32, device=dev)
+    size = C.c_size_t(0)
+    L_ = tq.lib()
+    qdt = tq._dtype_code(q)
+    args = lambda i, wsp: (copies[i % R].ref, k.data_ptr(), v.data_ptr(), qdt, slots.data_ptr(),
+                           B * chunk, q.data_ptr(), qdt, B, chunk, Hq, table.data_ptr(),
+                           table.shape[1], seq.data_ptr(), 1, scale, out.data_ptr(), wsp)
+    st = L_.tq_append_decode(*args(0, None), C.byref(size), None)
+    if st:
+        log(f"[bench] prefill attention: chunk {chunk} not supported (status {st})")
+        return None
+    ws = torch.empty(size.value, dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def run(i):
+        sz = C.c_size_t(ws.numel())
+        r = L_.tq_append_decode(*args(i, ws.data_ptr()), C.byref(sz), sh)
+        if r:
+            raise RuntimeError(f"prefill attention launch failed with status {r}")
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    n = 8
+    e0.record()
+    for i in range(n):
+        run(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    # MFMA instructions: per visible 64-token block and query group of 4 rows,
+    # 4 tiles x 5 d/128 fp6 x fp4 MFMAs and 4 planes x d/16 int8 MFMAs
+    per_blk = 4 * 5 * (d // 128) + 4 * (d // 16)
+    groups = (rows + 3) // 4
+    blocks = 0
+    useful = 0
+    for L in lens:
+        for gi in range(groups):
+            t_last = min(4 * gi + 3, rows - 1) // g
+            vis = int(L) - (chunk - 1 - t_last)
+            blocks += (vis + 63) // 64
+        t = np.arange(chunk)
+        useful += g * int(np.sum(int(L) - (chunk - 1 - t)))
+    blocks *= H
+    mfma_us = blocks * per_blk * 16 / (1024 * 2.4e9) * 1e6
+    flops = 4.0 * d * useful * H
+    log(f"[bench] prefill attention: chunk {chunk}, {rows} rows per KV head: {ms * 1e3:.1f} us "
+        f"(MFMA issue bound {mfma_us:.1f} us)")
+    return {"entry": "tq_append_decode (causal tail)", "chunk": chunk, "rows_per_kv_head": rows,
+            "us": round(ms * 1e3, 2), "query_tokens_per_s": round(B * chunk / (ms / 1e3), 1),
+            "dense_equiv_tflops": round(flops / (ms / 1e3) / 1e12, 2),
+            "mfma_issue_bound_us": round(mfma_us, 2), "frac_of_mfma_bound": round(mfma_us / (ms * 1e3), 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +247,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-launches", type=int, default=512)
+    ap.add_argument("--prefill-chunk", type=int, default=512,
+                    help="chunk length of the chunked-prefill attention measurement (0: skip)")
     ap.add_argument("--no-dense-baseline", action="store_true",
                     help="skip the uncompressed bf16 decode baseline")
     args = ap.parse_args()
@@ -396,6 +479,10 @@ def main():
                      "traffic": traffic, "kernel": dec_kernel,
                      "bytes_per_launch": kv_bytes},
     }
+    if args.prefill_chunk > 0 and int(lens.min()) >= args.prefill_chunk:
+        pa = prefill_attention(copies, table, lens, w, args.prefill_chunk, tdt, scale, sh, log)
+        if pa is not None:
+            result["prefill_attention"] = pa
     if dense is not None:
         result["dense_bf16_baseline"] = dense_baseline(dense, qs, seq, scale, dec_ms, sh, log)
     if not args.no_cpu_baseline:

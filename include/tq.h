@@ -72,7 +72,7 @@ typedef enum {
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
 #define TQ_PAGE_SIZE 256   /* the only page size the kernels implement */
-#define TQ_MAX_GROUP 16    /* max query rows per KV head per sequence (Hq/Hkv * n_q) */
+#define TQ_MAX_GROUP 4096  /* max query rows per KV head per sequence (Hq/Hkv * n_q) */
 
 /* Cache descriptor: plain data, owned by the caller, read by every call. */
 typedef struct {

@@ -204,6 +204,17 @@ int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype, const int32_t *
   return encode_common(c, v, dtype, slots, n_tokens, stream, false);
 }
 
+// The decode grids are (splits, Hkv, batch x workgroups per sequence) and the
+// merge grid (rows, Hkv, batch); the second and third dimensions stay within
+// 65535.
+static bool grid_fits(const tq_cache *c, int32_t batch, int32_t n_q, int32_t n_q_heads) {
+  const int group = n_q_heads / c->n_kv_heads * n_q;
+  const int qg = tq::query_groups(group);
+  const int per_wg = qg > 1 ? tq::max_groups_per_wg(c->head_dim) : 1;
+  const long wz = (qg + per_wg - 1) / per_wg;
+  return c->n_kv_heads <= 65535 && (long)batch * wz <= 65535;
+}
+
 static int prepare_checks(const tq_cache *c, int32_t dtype, int32_t batch, int32_t n_q,
                           int32_t n_q_heads) {
   if (!c) return TQ_EINVAL;
@@ -212,6 +223,7 @@ static int prepare_checks(const tq_cache *c, int32_t dtype, int32_t batch, int32
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   if (batch <= 0 || n_q <= 0 || n_q_heads <= 0 || n_q_heads % c->n_kv_heads) return TQ_EINVAL;
   if (n_q_heads / c->n_kv_heads * n_q > TQ_MAX_GROUP) return TQ_EUNSUPPORTED;
+  if (!grid_fits(c, batch, n_q, n_q_heads)) return TQ_EUNSUPPORTED;
   return TQ_OK;
 }
 
@@ -262,6 +274,7 @@ static int decode_checks(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   if (n_q_heads % c->n_kv_heads) return TQ_EINVAL;
   if (causal_tail != 0 && causal_tail != 1) return TQ_EINVAL;
   if (n_q_heads / c->n_kv_heads * n_q > TQ_MAX_GROUP) return TQ_EUNSUPPORTED;
+  if (!grid_fits(c, batch, n_q, n_q_heads)) return TQ_EUNSUPPORTED;
   if (!block_table || !seq_lens || !out || !c->qjl) return TQ_EINVAL;
   if (!aligned(out, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4)) return TQ_EALIGN;
   return TQ_OK;
@@ -481,6 +494,7 @@ int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   if (batch <= 0 || n_q <= 0 || n_q_heads <= 0 || max_pages <= 0) return TQ_EINVAL;
   if (n_q_heads % c->n_kv_heads) return TQ_EINVAL;
   if (n_q_heads / c->n_kv_heads * n_q > TQ_MAX_GROUP) return TQ_EUNSUPPORTED;
+  if (!grid_fits(c, batch, n_q, n_q_heads)) return TQ_EUNSUPPORTED;
   if (!out || !workspace) return TQ_EINVAL;
   if (!aligned(out, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
   tq::DecodePlan plan =

@@ -227,15 +227,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     for (int k = 0; k < NB; ++k) fold_one(gi, k);
   };
 
-  const int n_pages_seq = min((L + kPage - 1) / kPage, a.max_pages);
+  // Lv: one past the last token any row of the workgroup sees (with a causal
+  // tail the last row sees the most); pages from Lv on are not read
+  const int row_last = min(kMfmaMaxGroup * (rho0 + NG), a.plan.group) - 1;
+  const int Lv = a.causal_tail ? L - (a.n_q - 1 - row_last / g) : L;
+  const int n_pages_seq = min((Lv + kPage - 1) / kPage, a.max_pages);
   // tokens before S0 are not visible (a window); pages wholly before it are
   // never read, so their block-table entries may point at recycled pages
   const int S0 = a.seq_starts ? max(0, a.seq_starts[b]) : 0;
   const int pg0 = max(split * a.plan.pages_per_split, S0 / kPage);
   int pg1 = min(split * a.plan.pages_per_split + a.plan.pages_per_split, n_pages_seq);
   const int blk0 = 64 * wave;
-  // pages whose block of this wave holds no token are skipped (only the last can)
-  if (pg1 > pg0 && blk0 >= L - (pg1 - 1) * kPage) --pg1;
+  // pages whose block of this wave holds no visible token are skipped (only the last can)
+  if (pg1 > pg0 && blk0 >= Lv - (pg1 - 1) * kPage) --pg1;
 
   // the query operands of the workgroup's groups (a group past the last one
   // gets zero operands; its rows are masked)

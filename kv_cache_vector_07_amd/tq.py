@@ -20,7 +20,7 @@ _lib = None
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2, -3, -4, -5
 TQ_F32, TQ_BF16 = 0, 1
 TQ_PAGE_SIZE = 256
-TQ_MAX_GROUP = 16
+TQ_MAX_GROUP = 4096
 EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_encode_k",
            "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_window",
            "tq_append_decode",

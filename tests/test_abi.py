@@ -135,7 +135,10 @@ def test_decode_validation_and_workspace(L):
                                      None, C.byref(sz), None) == tq.TQ_OK
     assert 0 < sz.value < need
     assert _decode(L, dsc, Hq=7)[0] == tq.TQ_EINVAL                # Hq not a multiple of Hkv
-    assert _decode(L, dsc, Hq=8, nq=5)[0] == tq.TQ_EUNSUPPORTED   # 4 * 5 rows > 16
+    assert _decode(L, dsc, Hq=8, nq=1025)[0] == tq.TQ_EUNSUPPORTED   # 4 * 1025 rows > 4096
+    assert _decode(L, dsc, Hq=8, nq=1024)[0] == tq.TQ_OK
+    # batch x workgroups per sequence must fit the third grid dimension (65535)
+    assert _decode(L, dsc, B=128, Hq=8, nq=1024)[0] == tq.TQ_EUNSUPPORTED
     assert _decode(L, dsc, causal=2)[0] == tq.TQ_EINVAL
     assert _decode(L, dsc, B=0)[0] == tq.TQ_EINVAL
     assert _decode(L, dsc, maxp=0)[0] == tq.TQ_EINVAL

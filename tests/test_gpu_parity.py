@@ -148,6 +148,9 @@ DEC_CASES = [
     (128, 2, 12, 1, [700, 300], "bf16", "outlier", 0, 11),            # 6 rows: two groups, one partial
     (128, 2, 24, 1, [600, 5], "bf16", "normal", 0, 12),               # 12 rows: three groups, the second workgroup half empty
     (128, 1, 16, 1, [900], "bf16", "outlier", 0, 13),                 # 16 rows at d=128: two workgroups of two groups
+    (128, 2, 8, 40, [700, 300], "bf16", "normal", 0, 14),             # 160 rows per KV head
+    (128, 1, 4, 64, [30, 600], "bf16", "outlier", 1, 15),             # 256 causal rows, L < n_q: zero rows
+    (256, 2, 4, 48, [520, 47], "bf16", "outlier", 1, 16),             # d=256, 96 causal rows
 ]
 
 
@@ -377,6 +380,60 @@ def test_speculative_verify_and_rollback(tq):
     after = tq.tq_attn_decode(cache, q1, bt, sl0)
     torch.cuda.synchronize()
     assert torch.equal(before, after)
+
+
+@pytest.mark.parametrize("d,H,Hq,C", [(128, 2, 8, 128), (256, 8, 8, 200)],
+                         ids=["d128-512rows-fused-prologue", "d256-200rows-separate-encode"])
+def test_chunked_prefill_attention(tq, d, H, Hq, C):
+    """Chunked prefill: C new tokens per sequence are appended (encoded) and their
+    C x Hq/Hkv query rows attend causally over the compressed history and the
+    chunk (causal tail: chunk token t sees the history and chunk tokens <= t).
+    One sequence starts empty, so its first chunk attends to itself only. Checked
+    bit for bit against separate encode + decode calls on a twin cache, and
+    against the reference over the updated cache."""
+    lens0 = np.array([900, 0, 37])
+    print(f"[chunked prefill] d={d} Hkv={H} Hq={Hq} chunk={C}", flush=True)
+    w = I.Workload(f"pre{d}", len(lens0), Hq, H, d, "bf16", "outlier", 41, n_q=C, fixed_len=1)
+    table, n_pages = I.page_table(w, lens0, extra_tokens=C, shuffle=True)
+    caches = [tq.Cache(d, H, n_pages) for _ in range(2)]
+    bt = torch.from_numpy(table).cuda()
+    for c in caches:
+        for b, L in enumerate(lens0):
+            if L == 0:
+                continue
+            t = torch.arange(0, int(L), device="cuda")
+            sl = (bt[b, t // 256] * 256 + t % 256).to(torch.int32)
+            tq.tq_encode_k(c, torch.from_numpy(I.kv_tokens(w, "k", b, 0, int(L))).to("cuda", torch.bfloat16), sl)
+            tq.tq_encode_v(c, torch.from_numpy(I.kv_tokens(w, "v", b, 0, int(L))).to("cuda", torch.bfloat16), sl)
+    pos = np.concatenate([np.arange(L, L + C) for L in lens0])
+    seq = np.repeat(np.arange(len(lens0)), C)
+    slots = torch.from_numpy((table[seq, pos // 256].astype(np.int64) * 256 + pos % 256).astype(np.int32)).cuda()
+    nk = np.concatenate([I.kv_tokens(w, "k", b, int(L), int(L) + C) for b, L in enumerate(lens0)])
+    nv = np.concatenate([I.kv_tokens(w, "v", b, int(L), int(L) + C) for b, L in enumerate(lens0)])
+    nk_t = torch.from_numpy(nk).to("cuda", torch.bfloat16)
+    nv_t = torch.from_numpy(nv).to("cuda", torch.bfloat16)
+    lens = lens0 + C
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    q = I.queries(w, 0)
+    qt = torch.from_numpy(q).to("cuda", torch.bfloat16)
+    out_a = tq.tq_append_decode(caches[0], nk_t, nv_t, slots, qt, bt, sl, causal_tail=1)
+    tq.tq_encode_k(caches[1], nk_t, slots)
+    tq.tq_encode_v(caches[1], nv_t, slots)
+    out_b = tq.tq_attn_decode(caches[1], qt, bt, sl, causal_tail=1)
+    torch.cuda.synchronize()
+    assert torch.equal(caches[0].k_pool, caches[1].k_pool)
+    assert torch.equal(caches[0].v_pool, caches[1].v_pool)
+    assert torch.equal(out_a, out_b)
+    kp, vp = caches[0].k_pool.cpu().numpy(), caches[0].v_pool.cpu().numpy()
+    cb = Hn.codebook_from_cache(caches[0])
+    s_np = slots.cpu().numpy()
+    Hn.compare_encode_k(O.unpack_k(kp, s_np, H, d, 256), nk.astype(np.float64), cb, caches[0].qjl_host)
+    Hn.compare_encode_v(O.unpack_v(vp, s_np, H, d, 256), nv.astype(np.float64), cb)
+    ref = O.attn_decode(kp, vp, cb, caches[0].qjl_host, q.astype(np.float64), table, lens, H, 256,
+                        Hn.scale_of(d), causal_tail=True)
+    err = Hn.attn_rel_err(out_a.cpu().numpy(), ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= Hn.ATTN_TOL
 
 
 WIN_CASES = [
