@@ -82,11 +82,21 @@ typedef struct {
   int32_t n_pages;      /* pool capacity in pages                                */
   void *k_pool;         /* device, n_pages * Hkv * k_page_bytes, 256-B aligned    */
   void *v_pool;         /* device, n_pages * Hkv * v_page_bytes, 256-B aligned    */
-  const float *qjl;     /* device, S as m x d float32 row-major (m = d)           */
+  const float *qjl;     /* device, S as m x d float32 row-major (m = d); may be
+                           NULL when k_mse_only = 1                               */
   float levels[8];      /* c[0..7], strictly ascending and odd, c[7-k] = -c[k]
                            (from tq_build_codebook); otherwise calls return
                            TQ_EINVAL                                              */
   float thresholds[7];  /* t[0..6], midpoints, thresholds[3] == 0                 */
+  int32_t k_mse_only;   /* 0: K keeps the QJL stage ("K-Cache圧縮" steps 4-5, the
+                           pages' K path). 1: keys without it, the ablation of
+                           the pages' reason for QJL (inner-product scoring):
+                           the encoder skips z = S r and writes a zero sign
+                           plane (codes, N and G as usual; same record size),
+                           the decode score keeps only <Pi q, c[code]>, and
+                           tq_dequant rejects with_qjl = 1 (TQ_EINVAL). Must
+                           match how the records were written. Other values:
+                           TQ_EINVAL.                                           */
 } tq_cache;
 
 /* Bytes of one (page, KV head) section; 0 for unsupported d or P. */
@@ -109,6 +119,23 @@ size_t tq_v_page_bytes(int32_t head_dim, int32_t page_size);
  */
 int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed,
                       float *levels, float *thresholds, float *qjl_host);
+
+/*
+ * tq_build_codebook with the codebook fitted to the exact law of one coordinate
+ * of a uniform unit vector in R^d, density proportional to (1 - x^2)^((d-3)/2)
+ * on (-1, 1), instead of its large-d limit N(0, 1/d). The pages' "V3" line
+ * ("TurboQuant KVキャッシュ圧縮アーキテクチャ") carries a Lloyd-Max codebook over the
+ * rotated unit vector's coordinates without naming the density; this is the
+ * density that the normalise-then-rotate steps produce for isotropic inputs.
+ * Lloyd iteration in float64 from the N(0, 1/d) levels until no level moves by
+ * 1e-14 of the largest, cell masses by Gauss-Legendre quadrature in u = asin x,
+ * first moments in closed form; symmetrised, midpoint thresholds, rounded to
+ * float32. The codebook is odd, as the kernels require. qjl_host as above.
+ * Errors: TQ_EINVAL (null levels/thresholds, head_dim < 4 or not a power of
+ * two), TQ_EUNSUPPORTED (bits != 3).
+ */
+int tq_build_codebook_sphere(int32_t head_dim, int32_t bits, uint64_t qjl_seed,
+                             float *levels, float *thresholds, float *qjl_host);
 
 /*
  * K encode ("K-Cache圧縮" flow steps 1-5): for each token i and KV head h,

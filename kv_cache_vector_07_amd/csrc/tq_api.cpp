@@ -21,6 +21,7 @@ int check_cache(const tq_cache *c) {
   if (!supported_dim(c->head_dim) || c->page_size != TQ_PAGE_SIZE) return TQ_EUNSUPPORTED;
   if (!c->k_pool || !c->v_pool) return TQ_EINVAL;
   if (!aligned(c->k_pool, 256) || !aligned(c->v_pool, 256)) return TQ_EALIGN;
+  if (c->k_mse_only != 0 && c->k_mse_only != 1) return TQ_EINVAL;
   // the decode kernels split each level into odd bit-plane weights: the
   // codebook must be strictly increasing and odd (c[7-k] = -c[k])
   for (int k = 0; k < 8; ++k) {
@@ -38,6 +39,11 @@ Codebook codebook_of(const tq_cache *c) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+// The QJL matrix as the key-side kernels see it: NULL for MSE-only keys, which
+// makes the encoder skip z = S r and the query prologue write p = 0.
+const float *qjl_of(const tq_cache *c) { return c->k_mse_only ? nullptr : c->qjl; }
+bool qjl_missing(const tq_cache *c) { return !c->k_mse_only && !c->qjl; }
 
 // ---- Lloyd-Max for N(0, sigma^2), float64 -------------------------------------
 double std_pdf(double u) { return isinf(u) ? 0.0 : exp(-0.5 * u * u) / sqrt(2.0 * M_PI); }
@@ -74,6 +80,65 @@ void lloyd_max(double sigma, double *c, double *t) {
       c[k] = nc;
     }
     if (delta < 1e-14 * sigma) break;
+  }
+  double s[8];
+  for (int k = 0; k < n; ++k) s[k] = 0.5 * (c[k] - c[n - 1 - k]);
+  for (int k = 0; k < n; ++k) c[k] = s[k];
+  for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+  t[n / 2 - 1] = 0.0;
+}
+
+// ---- Lloyd-Max for one coordinate of a uniform unit vector in R^d, float64 ----
+// The density is proportional to (1 - x^2)^((d-3)/2) on (-1, 1). With x = sin u
+// the mass of a cell (a, b) is proportional to the integral of cos^(d-2) u over
+// (asin a, asin b), a smooth integrand, taken here by composite 8-point
+// Gauss-Legendre; the first moment has the closed form
+// ((1 - a^2)^((d-1)/2) - (1 - b^2)^((d-1)/2)) / (d - 1) in the same units, so
+// the normalising constant cancels in the centroid.
+double sphere_mass(int d, double a, double b) {
+  static const double xg[4] = {0.1834346424956498, 0.5255324099163290, 0.7966664774136267,
+                               0.9602898564975363};
+  static const double wg[4] = {0.3626837833783620, 0.3137066458778873, 0.2223810344533745,
+                               0.1012285362903763};
+  const int panels = 128;
+  const double u0 = asin(fmax(-1.0, fmin(1.0, a))), u1 = asin(fmax(-1.0, fmin(1.0, b)));
+  const double h = (u1 - u0) / panels;
+  double sum = 0.0;
+  for (int p = 0; p < panels; ++p) {
+    const double mid = u0 + (p + 0.5) * h;
+    for (int k = 0; k < 4; ++k) {
+      sum += wg[k] * pow(cos(mid - 0.5 * h * xg[k]), d - 2);
+      sum += wg[k] * pow(cos(mid + 0.5 * h * xg[k]), d - 2);
+    }
+  }
+  return 0.5 * h * sum;
+}
+
+double sphere_moment(int d, double a, double b) {
+  auto F = [d](double x) {
+    x = fmax(-1.0, fmin(1.0, x));
+    return pow(1.0 - x * x, 0.5 * (d - 1)) / (d - 1);
+  };
+  return F(a) - F(b);
+}
+
+void lloyd_max_sphere(int d, double *c, double *t) {
+  const int n = 8;
+  lloyd_max(1.0 / sqrt((double)d), c, t);
+  for (int k = 0; k < n; ++k) c[k] = fmax(-0.999, fmin(0.999, c[k]));
+  double scale = 0.0;
+  for (int k = 0; k < n; ++k) scale = fmax(scale, fabs(c[k]));
+  for (int it = 0; it < 20000; ++it) {
+    for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+    double delta = 0.0;
+    for (int k = 0; k < n; ++k) {
+      const double a = k == 0 ? -1.0 : t[k - 1];
+      const double b = k == n - 1 ? 1.0 : t[k];
+      const double nc = sphere_moment(d, a, b) / sphere_mass(d, a, b);
+      delta = fmax(delta, fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (delta < 1e-14 * scale) break;
   }
   double s[8];
   for (int k = 0; k < n; ++k) s[k] = 0.5 * (c[k] - c[n - 1 - k]);
@@ -146,6 +211,20 @@ const char *tq_status_string(int32_t s) {
   }
 }
 
+static void build_qjl(int32_t head_dim, uint64_t qjl_seed, float *qjl_host) {
+  uint64_t state = qjl_seed;
+  const size_t n = (size_t)head_dim * head_dim;
+  for (size_t i = 0; i < n; i += 2) {
+    uint64_t x1 = splitmix64_next(state), x2 = splitmix64_next(state);
+    double u1 = (double)((x1 >> 11) + 1) * 0x1.0p-53;
+    double u2 = (double)((x2 >> 11) + 1) * 0x1.0p-53;
+    double rad = sqrt(-2.0 * log(u1));
+    double ang = 2.0 * M_PI * u2;
+    qjl_host[i] = (float)(rad * cos(ang));
+    if (i + 1 < n) qjl_host[i + 1] = (float)(rad * sin(ang));
+  }
+}
+
 int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed, float *levels,
                       float *thresholds, float *qjl_host) {
   if (!levels || !thresholds) return TQ_EINVAL;
@@ -155,19 +234,20 @@ int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed, float *
   lloyd_max(1.0 / sqrt((double)head_dim), c, t);
   for (int k = 0; k < 8; ++k) levels[k] = (float)c[k];
   for (int k = 0; k < 7; ++k) thresholds[k] = (float)t[k];
-  if (qjl_host) {
-    uint64_t state = qjl_seed;
-    const size_t n = (size_t)head_dim * head_dim;
-    for (size_t i = 0; i < n; i += 2) {
-      uint64_t x1 = splitmix64_next(state), x2 = splitmix64_next(state);
-      double u1 = (double)((x1 >> 11) + 1) * 0x1.0p-53;
-      double u2 = (double)((x2 >> 11) + 1) * 0x1.0p-53;
-      double rad = sqrt(-2.0 * log(u1));
-      double ang = 2.0 * M_PI * u2;
-      qjl_host[i] = (float)(rad * cos(ang));
-      if (i + 1 < n) qjl_host[i + 1] = (float)(rad * sin(ang));
-    }
-  }
+  if (qjl_host) build_qjl(head_dim, qjl_seed, qjl_host);
+  return TQ_OK;
+}
+
+int tq_build_codebook_sphere(int32_t head_dim, int32_t bits, uint64_t qjl_seed, float *levels,
+                             float *thresholds, float *qjl_host) {
+  if (!levels || !thresholds) return TQ_EINVAL;
+  if (head_dim < 4 || (head_dim & (head_dim - 1))) return TQ_EINVAL;
+  if (bits != 3) return TQ_EUNSUPPORTED;
+  double c[8], t[7];
+  lloyd_max_sphere(head_dim, c, t);
+  for (int k = 0; k < 8; ++k) levels[k] = (float)c[k];
+  for (int k = 0; k < 7; ++k) thresholds[k] = (float)t[k];
+  if (qjl_host) build_qjl(head_dim, qjl_seed, qjl_host);
   return TQ_OK;
 }
 
@@ -178,8 +258,8 @@ static int encode_common(const tq_cache *c, const void *x, int32_t dtype, const 
   if (n_tokens < 0) return TQ_EINVAL;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   if (n_tokens == 0) return TQ_OK;
-  if (!x || !slots || (is_k && !c->qjl)) return TQ_EINVAL;
-  if (!aligned(x, 16) || !aligned(slots, 4) || (is_k && !aligned(c->qjl, 16))) return TQ_EALIGN;
+  if (!x || !slots || (is_k && qjl_missing(c))) return TQ_EINVAL;
+  if (!aligned(x, 16) || !aligned(slots, 4) || (is_k && !aligned(qjl_of(c), 16))) return TQ_EALIGN;
   tq::EncodeArgs a;
   a.x = x;
   a.dtype = dtype;
@@ -187,7 +267,7 @@ static int encode_common(const tq_cache *c, const void *x, int32_t dtype, const 
   a.n_tokens = n_tokens;
   a.n_heads = c->n_kv_heads;
   a.pool = (uint8_t *)(is_k ? c->k_pool : c->v_pool);
-  a.qjl = c->qjl;
+  a.qjl = qjl_of(c);
   a.cb = codebook_of(c);
   hipStream_t s = (hipStream_t)stream;
   return hip_status(is_k ? tq::launch_encode_k(a, c->head_dim, s)
@@ -219,6 +299,7 @@ static int prepare_checks(const tq_cache *c, int32_t dtype, int32_t batch, int32
                           int32_t n_q_heads) {
   if (!c) return TQ_EINVAL;
   if (c->head_dim <= 0 || c->n_kv_heads <= 0) return TQ_EINVAL;
+  if (c->k_mse_only != 0 && c->k_mse_only != 1) return TQ_EINVAL;
   if (!supported_dim(c->head_dim)) return TQ_EUNSUPPORTED;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   if (batch <= 0 || n_q <= 0 || n_q_heads <= 0 || n_q_heads % c->n_kv_heads) return TQ_EINVAL;
@@ -236,7 +317,7 @@ static hipError_t run_prepare(const tq_cache *c, const void *q, int32_t dtype, i
   a.n_q = n_q;
   a.n_q_heads = n_q_heads;
   a.n_kv_heads = c->n_kv_heads;
-  a.qjl = c->qjl;
+  a.qjl = qjl_of(c);
   a.prep = (float *)prep;
   const bool mfma = tq::mfma_path(c->head_dim, n_q_heads / c->n_kv_heads * n_q);
   a.packed = mfma ? prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads) : nullptr;
@@ -258,8 +339,8 @@ int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t ba
     *prep_bytes = need;
     return TQ_EWORKSPACE;
   }
-  if (!q || !c->qjl) return TQ_EINVAL;
-  if (!aligned(q, 16) || !aligned(prep, 256) || !aligned(c->qjl, 16)) return TQ_EALIGN;
+  if (!q || qjl_missing(c)) return TQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(prep, 256) || !aligned(qjl_of(c), 16)) return TQ_EALIGN;
   return hip_status(run_prepare(c, q, dtype, batch, n_q, n_q_heads, (uint8_t *)prep,
                                 (hipStream_t)stream));
 }
@@ -275,7 +356,7 @@ static int decode_checks(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   if (causal_tail != 0 && causal_tail != 1) return TQ_EINVAL;
   if (n_q_heads / c->n_kv_heads * n_q > TQ_MAX_GROUP) return TQ_EUNSUPPORTED;
   if (!grid_fits(c, batch, n_q, n_q_heads)) return TQ_EUNSUPPORTED;
-  if (!block_table || !seq_lens || !out || !c->qjl) return TQ_EINVAL;
+  if (!block_table || !seq_lens || !out || qjl_missing(c)) return TQ_EINVAL;
   if (!aligned(out, 16) || !aligned(block_table, 4) || !aligned(seq_lens, 4)) return TQ_EALIGN;
   return TQ_OK;
 }
@@ -391,9 +472,9 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
     *workspace_bytes = need;
     return TQ_EWORKSPACE;
   }
-  if (!q || !c->qjl) return TQ_EINVAL;
+  if (!q || qjl_missing(c)) return TQ_EINVAL;
   if (n_new > 0 && (!k_new || !v_new || !slots)) return TQ_EINVAL;
-  if (!aligned(q, 16) || !aligned(workspace, 256) || !aligned(c->qjl, 16)) return TQ_EALIGN;
+  if (!aligned(q, 16) || !aligned(workspace, 256) || !aligned(qjl_of(c), 16)) return TQ_EALIGN;
   if (n_new > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slots, 4)))
     return TQ_EALIGN;
   uint8_t *ws = (uint8_t *)workspace;
@@ -407,7 +488,7 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   ek.n_tokens = n_new;
   ek.n_heads = c->n_kv_heads;
   ek.pool = (uint8_t *)c->k_pool;
-  ek.qjl = c->qjl;
+  ek.qjl = qjl_of(c);
   ek.cb = codebook_of(c);
   ev = ek;
   ev.x = v_new;
@@ -419,7 +500,7 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   pa.n_q = n_q;
   pa.n_q_heads = n_q_heads;
   pa.n_kv_heads = c->n_kv_heads;
-  pa.qjl = c->qjl;
+  pa.qjl = qjl_of(c);
   pa.prep = (float *)prep;
   pa.packed = prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads);
   pa.cb = codebook_of(c);
@@ -573,7 +654,7 @@ int tq_dequant(const tq_cache *c, int32_t which, int32_t with_qjl, const int32_t
   if ((which != 0 && which != 1) || (with_qjl != 0 && with_qjl != 1) || n_tokens < 0)
     return TQ_EINVAL;
   if (n_tokens == 0) return TQ_OK;
-  if (!slots || !out || (which == 0 && with_qjl && !c->qjl)) return TQ_EINVAL;
+  if (!slots || !out || (which == 0 && with_qjl && (c->k_mse_only || !c->qjl))) return TQ_EINVAL;
   if (!aligned(out, 16) || !aligned(slots, 4)) return TQ_EALIGN;
   tq::DequantArgs a;
   a.pool = (const uint8_t *)(which == 0 ? c->k_pool : c->v_pool);

@@ -70,9 +70,10 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
   // S rows of this wave's tiles: the loads do not depend on the data, so for
   // d = 128 they are all issued before the encode starts
   const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
+  const bool qjl = a.qjl != nullptr;   // MSE-only keys (no S) skip z = S r
   constexpr bool kHoist = D == 128;
   float4 sreg[kHoist ? RT * (D / 16) : 1];
-  if constexpr (kHoist) {
+  if (kHoist && qjl) {
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -111,43 +112,45 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
 
   // Z tile (vector tile vt, row tile rt) = sum over i of R[16 vt + .][i] S[16 rt + .][i].
   // MFMA m of a 16-wide i step uses i = i0 + 4 kq + m in lane group kq, for A and B alike.
-  v4f acc[VT][RT];
+  if (qjl) {
+    v4f acc[VT][RT];
 #pragma unroll
-  for (int vt = 0; vt < VT; ++vt)
+    for (int vt = 0; vt < VT; ++vt)
 #pragma unroll
-    for (int t = 0; t < RT; ++t) acc[vt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < RT; ++t) acc[vt][t] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int c = 0; c < D / 16; ++c) {
-    float4 bv[RT], av[VT];
+    for (int c = 0; c < D / 16; ++c) {
+      float4 bv[RT], av[VT];
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      if constexpr (kHoist)
-        bv[t] = sreg[t * (D / 16) + c];
-      else
-        bv[t] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
-    }
-#pragma unroll
-    for (int vt = 0; vt < VT; ++vt) av[vt] = s_r[16 * vt + l16][4 * c + kq];
-    // independent tiles between the dependent steps of one accumulator
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-        for (int t = 0; t < RT; ++t)
-          acc[vt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[vt][m], bv[t][m], acc[vt][t], 0, 0, 0);
-  }
-  // lane (l16, kq), register r of a tile: vector 16 vt + 4 kq + r, row 16 rt + l16
-#pragma unroll
-  for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-    for (int t = 0; t < RT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint64_t m = __ballot(acc[vt][t][r] >= 0.f);
-        const int u = 16 * vt + 4 * kq + r;
-        if (l16 == 0 && u < VB) s_sign[u][wave * RT + t] = (uint16_t)(m >> (16 * kq));
+      for (int t = 0; t < RT; ++t) {
+        if constexpr (kHoist)
+          bv[t] = sreg[t * (D / 16) + c];
+        else
+          bv[t] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
       }
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) av[vt] = s_r[16 * vt + l16][4 * c + kq];
+      // independent tiles between the dependent steps of one accumulator
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            acc[vt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[vt][m], bv[t][m], acc[vt][t], 0, 0, 0);
+    }
+    // lane (l16, kq), register r of a tile: vector 16 vt + 4 kq + r, row 16 rt + l16
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint64_t m = __ballot(acc[vt][t][r] >= 0.f);
+          const int u = 16 * vt + 4 * kq + r;
+          if (l16 == 0 && u < VB) s_sign[u][wave * RT + t] = (uint16_t)(m >> (16 * kq));
+        }
+  }
   __syncthreads();
 
   // records: wave w writes vectors w, w + 4, ...
@@ -165,7 +168,7 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
         const uint64_t m = s_code[u][j][s >> 1];
         w = (s & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
       } else {
-        w = (uint32_t)s_sign[u][2 * s] | ((uint32_t)s_sign[u][2 * s + 1] << 16);
+        w = qjl ? (uint32_t)s_sign[u][2 * s] | ((uint32_t)s_sign[u][2 * s + 1] << 16) : 0u;
       }
       reinterpret_cast<uint32_t *>(sec + (size_t)off * (D / 2))[lane] = w;
     }
@@ -298,10 +301,14 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   const int t = qq / g, hh = qq % g;
   const size_t row = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
   const int srow = wave * RPW + lane / LPR, part = lane % LPR;
-  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl) + (size_t)srow * (D / 4) + part * (EPL / 4);
+  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
+  const size_t s_off = (size_t)srow * (D / 4) + part * (EPL / 4);   // this lane's part of its S row
+  const bool qjl = a.qjl != nullptr;   // MSE-only keys: p = 0, S is not read
   float4 sv[CH];
+  if (qjl) {
 #pragma unroll
-  for (int k = 0; k < CH; ++k) sv[k] = S4[k];
+    for (int k = 0; k < CH; ++k) sv[k] = S4[s_off + k];
+  }
 
   float v[R];
 #pragma unroll
@@ -322,19 +329,21 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   // p_l = sum_i S[l][i] q~_i
   const float4 *q4 = reinterpret_cast<const float4 *>(s_q) + part * (EPL / 4);
   float acc = 0.f;
+  if (qjl) {
 #pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    if (c > 0) {
+    for (int c = 0; c < NCH; ++c) {
+      if (c > 0) {
 #pragma unroll
-      for (int k = 0; k < CH; ++k) sv[k] = S4[c * CH + k];
-    }
+        for (int k = 0; k < CH; ++k) sv[k] = S4[s_off + c * CH + k];
+      }
 #pragma unroll
-    for (int k = 0; k < CH; ++k) {
-      const float4 qv = q4[c * CH + k];
-      acc = fmaf(sv[k].x, qv.x, acc);
-      acc = fmaf(sv[k].y, qv.y, acc);
-      acc = fmaf(sv[k].z, qv.z, acc);
-      acc = fmaf(sv[k].w, qv.w, acc);
+      for (int k = 0; k < CH; ++k) {
+        const float4 qv = q4[c * CH + k];
+        acc = fmaf(sv[k].x, qv.x, acc);
+        acc = fmaf(sv[k].y, qv.y, acc);
+        acc = fmaf(sv[k].z, qv.z, acc);
+        acc = fmaf(sv[k].w, qv.w, acc);
+      }
     }
   }
   if (LPR == 2) acc += __shfl_xor(acc, 1, 64);

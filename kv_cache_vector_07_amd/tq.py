@@ -21,7 +21,8 @@ TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2
 TQ_F32, TQ_BF16 = 0, 1
 TQ_PAGE_SIZE = 256
 TQ_MAX_GROUP = 4096
-EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_encode_k",
+EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_build_codebook_sphere",
+           "tq_encode_k",
            "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_window",
            "tq_append_decode",
            "tq_attn_decode_prepared", "tq_attn_decode_split", "tq_attn_decode_merge",
@@ -38,7 +39,8 @@ class TqCacheDesc(C.Structure):
     """Mirror of struct tq_cache."""
     _fields_ = [("head_dim", C.c_int32), ("n_kv_heads", C.c_int32), ("page_size", C.c_int32),
                 ("n_pages", C.c_int32), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
-                ("qjl", C.c_void_p), ("levels", C.c_float * 8), ("thresholds", C.c_float * 7)]
+                ("qjl", C.c_void_p), ("levels", C.c_float * 8), ("thresholds", C.c_float * 7),
+                ("k_mse_only", C.c_int32)]
 
 
 def lib():
@@ -58,6 +60,7 @@ def lib():
     L.tq_status_string.argtypes = [i32]
     L.tq_status_string.restype = C.c_char_p
     L.tq_build_codebook.argtypes = [i32, i32, C.c_uint64, vp, vp, vp]
+    L.tq_build_codebook_sphere.argtypes = [i32, i32, C.c_uint64, vp, vp, vp]
     L.tq_encode_k.argtypes = [vp, vp, i32, vp, i32, vp]
     L.tq_encode_v.argtypes = [vp, vp, i32, vp, i32, vp]
     L.tq_query_prepare.argtypes = [vp, vp, i32, i32, i32, i32, vp, C.POINTER(sz), vp]
@@ -75,7 +78,7 @@ def lib():
     L.tq_dequant.argtypes = [vp, i32, i32, vp, i32, vp, vp]
     L.tq_dense_attn_decode.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, f32,
                                        vp, vp, C.POINTER(sz), vp]
-    for name in ("tq_build_codebook", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
+    for name in ("tq_build_codebook", "tq_build_codebook_sphere", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
                  "tq_attn_decode", "tq_attn_decode_window", "tq_append_decode", "tq_attn_decode_prepared",
                  "tq_attn_decode_split",
                  "tq_attn_decode_merge", "tq_dense_attn_decode", "tq_dequant"):
@@ -117,14 +120,18 @@ def tq_v_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE) -> int:
     return int(lib().tq_v_page_bytes(head_dim, page_size))
 
 
-def tq_build_codebook(head_dim: int, bits: int = 3, qjl_seed: int = 12345, with_qjl: bool = True):
-    """Host-only: (levels float32[8], thresholds float32[7], S float32[d][d] or None)."""
+def tq_build_codebook(head_dim: int, bits: int = 3, qjl_seed: int = 12345, with_qjl: bool = True,
+                      density: str = "gaussian"):
+    """Host-only: (levels float32[8], thresholds float32[7], S float32[d][d] or None).
+    density "gaussian" fits N(0, 1/d); "sphere" the exact law of a coordinate of
+    a uniform unit vector (tq_build_codebook_sphere)."""
     levels = np.zeros(8, np.float32)
     thr = np.zeros(7, np.float32)
     S = np.zeros((head_dim, head_dim), np.float32) if with_qjl and head_dim > 0 else None
-    st = lib().tq_build_codebook(head_dim, bits, qjl_seed, levels.ctypes.data, thr.ctypes.data,
-                                 S.ctypes.data if S is not None else None)
-    _check(st, "tq_build_codebook")
+    fn = {"gaussian": "tq_build_codebook", "sphere": "tq_build_codebook_sphere"}[density]
+    st = getattr(lib(), fn)(head_dim, bits, qjl_seed, levels.ctypes.data, thr.ctypes.data,
+                            S.ctypes.data if S is not None else None)
+    _check(st, fn)
     return levels, thr, S
 
 
@@ -133,7 +140,7 @@ class Cache:
     the descriptor passed to every call. Pools are allocated with torch."""
 
     def __init__(self, head_dim: int, n_kv_heads: int, n_pages: int, qjl_seed: int = 12345,
-                 device="cuda", codebook=None, zero: bool = True):
+                 device="cuda", codebook=None, zero: bool = True, k_mse_only: bool = False):
         import torch
         self.head_dim, self.n_kv_heads, self.n_pages = head_dim, n_kv_heads, n_pages
         self.page_size = TQ_PAGE_SIZE
@@ -146,7 +153,9 @@ class Cache:
         self.qjl = torch.from_numpy(S).to(device)
         self.desc = TqCacheDesc(head_dim, n_kv_heads, self.page_size, n_pages,
                                 self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.qjl.data_ptr(),
-                                (C.c_float * 8)(*levels.tolist()), (C.c_float * 7)(*thr.tolist()))
+                                (C.c_float * 8)(*levels.tolist()), (C.c_float * 7)(*thr.tolist()),
+                                int(k_mse_only))
+        self.k_mse_only = bool(k_mse_only)
         self._ws = None
 
     @property

@@ -36,6 +36,10 @@ notes; the ones that shape arithmetic are restated where they are used:
   R16 by default every query of a step sees all L cached tokens; with
       causal_tail query t sees the first L - (n_q - 1 - t).
   R22 an empty visible range yields an all-zero output row.
+  R25 (variant) the codebook may instead be fitted to the exact law of one
+      coordinate of a uniform unit vector in R^d, whose large-d limit is R4's.
+  R26 (variant) keys may skip the QJL stage: the record keeps codes, N and G,
+      its sign plane is zero, and the score keeps only the codebook term.
 """
 
 from __future__ import annotations
@@ -45,14 +49,15 @@ import math
 from dataclasses import dataclass
 
 import numpy as np
-from scipy.special import ndtr, ndtri
+from scipy.special import betaincc, gammaln, ndtr, ndtri
 
 __all__ = [
-    "QJL_KAPPA_NUM", "bits_per_dim", "fwht", "lloyd_max_gaussian", "Codebook",
+    "QJL_KAPPA_NUM", "bits_per_dim", "fwht", "lloyd_max_gaussian", "lloyd_max_sphere",
+    "sphere_coordinate_pdf", "Codebook",
     "codebook", "splitmix64", "qjl_matrix", "fp16_rne", "quantize", "encode",
     "k_page_bytes", "v_page_bytes", "pack_k", "pack_v", "unpack_k", "unpack_v",
     "gather_k", "gather_v", "rotate_query", "score", "attn_decode", "dequant_k",
-    "dequant_v", "bf16_to_f64", "dense_attn_decode",
+    "dequant_v", "bf16_to_f64", "dense_attn_decode", "encode_k_mse_only",
 ]
 
 # sqrt(pi/2): the QJL estimator constant numerator (R9); divided by m at use.
@@ -160,12 +165,85 @@ class Codebook:
     iterations: int
 
 
-def codebook(head_dim: int, bits: int = 3) -> Codebook:
-    """8-level Lloyd-Max codebook for N(0, 1/d) (R4); stored values are float32."""
+def sphere_coordinate_pdf(x, d: int):
+    """Density of one coordinate of a point drawn uniformly from the unit sphere
+    in R^d (d >= 2): Gamma(d/2) / (sqrt(pi) Gamma((d-1)/2)) (1 - x^2)^((d-3)/2)
+    on (-1, 1). N(0, 1/d) is its large-d limit. A unit vector x_hat that the
+    rotation leaves in general position has coordinates of this law when x is
+    isotropic, which is the setting the Lloyd-Max codebook is fitted for."""
+    x = np.asarray(x, dtype=np.float64)
+    lc = gammaln(d / 2.0) - 0.5 * math.log(math.pi) - gammaln((d - 1) / 2.0)
+    inside = np.abs(x) < 1.0
+    out = np.zeros_like(x)
+    out[inside] = np.exp(lc + 0.5 * (d - 3) * np.log1p(-x[inside] ** 2))
+    return out
+
+
+def _sphere_tail(u, d: int):
+    """P(X > u) for one sphere coordinate X: by symmetry and X^2 ~ Beta(1/2, (d-1)/2),
+    P(X > u) = (1 - I_{u^2}(1/2, (d-1)/2)) / 2 for u >= 0."""
+    u = np.asarray(u, dtype=np.float64)
+    uc = np.clip(np.abs(u), 0.0, 1.0)
+    half = 0.5 * betaincc(0.5, 0.5 * (d - 1), uc ** 2)
+    return np.where(u >= 0, half, 1.0 - half)
+
+
+def _sphere_first_moment(a, b, d: int):
+    """Integral of x f(x) over (a, b): the antiderivative of x (1 - x^2)^m is
+    -(1 - x^2)^(m+1) / (2 (m + 1)) with m = (d - 3)/2."""
+    m1 = 0.5 * (d - 1)
+    k = math.exp(gammaln(d / 2.0) - 0.5 * math.log(math.pi) - gammaln((d - 1) / 2.0)) / (2.0 * m1)
+
+    def F(x):
+        x = np.clip(np.asarray(x, dtype=np.float64), -1.0, 1.0)
+        return -k * np.power(1.0 - x * x, m1)
+    return F(b) - F(a)
+
+
+def lloyd_max_sphere(d: int, n_levels: int = 8, init=None, tol: float = 1e-14,
+                     max_iter: int = 20000):
+    """Lloyd iteration for the n-level MSE quantiser of one coordinate of a
+    uniform point on the unit sphere in R^d (density sphere_coordinate_pdf).
+    The same two conditions as lloyd_max_gaussian: thresholds at midpoints,
+    levels at the conditional mean of their cell, the mean taken from the
+    closed-form first moment and the cell mass from the incomplete beta
+    function. Starts from the N(0, 1/d) levels unless `init` is given;
+    symmetrises at the end. Returns (levels, thresholds, iterations), float64."""
+    if init is None:
+        c = lloyd_max_gaussian(1.0 / math.sqrt(d), n_levels)[0]
+        c = np.clip(c, -0.999, 0.999)
+    else:
+        c = np.array(init, np.float64)
+    scale = float(np.max(np.abs(c)))
+    it = 0
+    for it in range(1, max_iter + 1):
+        t = 0.5 * (c[:-1] + c[1:])
+        a = np.concatenate([[-1.0], t])
+        b = np.concatenate([t, [1.0]])
+        mass = _sphere_tail(a, d) - _sphere_tail(b, d)
+        c_new = _sphere_first_moment(a, b, d) / mass
+        delta = np.max(np.abs(c_new - c))
+        c = c_new
+        if delta < tol * scale:
+            break
+    c = 0.5 * (c - c[::-1])
+    t = 0.5 * (c[:-1] + c[1:])
+    t[n_levels // 2 - 1] = 0.0
+    return c, t, it
+
+
+def codebook(head_dim: int, bits: int = 3, density: str = "gaussian") -> Codebook:
+    """8-level Lloyd-Max codebook (R4); stored values are float32. density
+    "gaussian" fits N(0, 1/d) (the default, R4); "sphere" fits the exact
+    marginal of a coordinate of a uniform unit vector in R^d (R25)."""
     if bits != 3:
         raise ValueError("the pages describe 3-bit codes only")
-    sigma = 1.0 / math.sqrt(head_dim)
-    c, t, it = lloyd_max_gaussian(sigma, 1 << bits)
+    if density == "gaussian":
+        c, t, it = lloyd_max_gaussian(1.0 / math.sqrt(head_dim), 1 << bits)
+    elif density == "sphere":
+        c, t, it = lloyd_max_sphere(head_dim, 1 << bits)
+    else:
+        raise ValueError(f"unknown density {density!r}")
     return Codebook(head_dim, c, t,
                     c.astype(np.float32).astype(np.float64),
                     t.astype(np.float32).astype(np.float64), it)
@@ -255,6 +333,16 @@ def encode(x, cb: Codebook, S=None) -> dict:
         gamma = np.sqrt(np.sum(r * r, axis=-1))
         z = r @ S.T
         out.update(r=r, gamma=gamma, G=fp16_rne(gamma), z=z, sign=(z >= 0))
+    return out
+
+
+def encode_k_mse_only(x, cb: Codebook) -> dict:
+    """K without the QJL stage (R26): steps 1-4 of encode(); the record keeps
+    G = fp16(||r||) and its sign plane is all zero."""
+    out = encode(x, cb)
+    r = out["y"] - cb.levels[out["idx"]]
+    gamma = np.sqrt(np.sum(r * r, axis=-1))
+    out.update(r=r, gamma=gamma, G=fp16_rne(gamma), sign=np.zeros(r.shape, dtype=bool))
     return out
 
 
@@ -461,8 +549,10 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
     q = np.asarray(q, dtype=np.float64)
     B, n_q, Hq, d = q.shape
     g = Hq // n_kv_heads
-    S64 = np.asarray(S, dtype=np.float64)
+    # S None: MSE-only keys (R26), the score keeps only the codebook term
+    S64 = np.asarray(S, dtype=np.float64) if S is not None else np.zeros((d, d))
     m = S64.shape[0]
+    qjl_w = QJL_KAPPA_NUM / m if S is not None else 0.0
     out = np.zeros((B, n_q, Hq, d))
     if pairs is None:
         pairs = [(b, h) for b in range(B) for h in range(n_kv_heads)]
@@ -487,7 +577,7 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
             for h in range(kvh * g, (kvh + 1) * g):
                 qt, p = rotate_query(q[b, t, h], S64)
                 # the estimate of score() with c[idx] and sigma evaluated once per head
-                est = N[lo:vis] * (ckey[lo:vis] @ qt + (QJL_KAPPA_NUM / m) * G[lo:vis] * (sig[lo:vis] @ p))
+                est = N[lo:vis] * (ckey[lo:vis] @ qt + qjl_w * G[lo:vis] * (sig[lo:vis] @ p))
                 logits = scale * est
                 w = np.exp(logits - logits.max())
                 w /= w.sum()

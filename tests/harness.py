@@ -86,6 +86,26 @@ def compare_encode_k(gpu: dict, x64: np.ndarray, cb, S) -> dict:
             "sidecar_midpoint": int(exN.sum() + exG.sum()), "values": n_coded}
 
 
+def compare_encode_k_mse_only(gpu: dict, x64: np.ndarray, cb) -> dict:
+    """K records written without the QJL stage: codes and N as compare_encode_v,
+    G from the residual of the GPU's own codes (the cascade rule), and an all-zero
+    sign plane."""
+    e = O.encode_k_mse_only(x64, cb)
+    code_diff = check_codes(gpu["idx"], e, cb)
+    r = e["y"] - cb.levels[gpu["idx"]]
+    gamma = np.sqrt((r * r).sum(-1))
+    assert not gpu["sign"].any(), "sign plane of MSE-only keys is not zero"
+    okN, exN = _fp16_match(gpu["N"], e["norm"])
+    okG, exG = _fp16_match(gpu["G"], gamma)
+    assert okN.all(), "N sidecar mismatch"
+    assert okG.all(), "G sidecar mismatch"
+    n_coded = gpu["idx"].size + 2 * gpu["N"].size
+    exc = int(code_diff.sum() + exN.sum() + exG.sum())
+    assert exc / n_coded < MAX_EXCEPTION_RATE, f"boundary exceptions {exc}/{n_coded}"
+    return {"code_boundary": int(code_diff.sum()), "sidecar_midpoint": int(exN.sum() + exG.sum()),
+            "values": n_coded}
+
+
 def compare_encode_v(gpu: dict, x64: np.ndarray, cb) -> dict:
     e = O.encode(x64, cb)
     code_diff = check_codes(gpu["idx"], e, cb)
@@ -110,9 +130,10 @@ def attn_rel_err(gpu_out: np.ndarray, ref_out: np.ndarray) -> float:
     return float(np.max(num[~zero] / den[~zero])) if (~zero).any() else 0.0
 
 
-def codebook_from_cache(cache):
-    """The reference's view of the codebook the cache descriptor carries."""
-    cb = O.codebook(cache.head_dim)
+def codebook_from_cache(cache, density: str = "gaussian"):
+    """The reference's view of the codebook the cache descriptor carries (the
+    reference fits it itself and checks that the descriptor holds the same bits)."""
+    cb = O.codebook(cache.head_dim, density=density)
     assert np.array_equal(cache.levels.astype(np.float64), cb.levels)
     assert np.array_equal(cache.thresholds.astype(np.float64), cb.thresholds)
     return cb

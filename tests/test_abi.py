@@ -205,3 +205,35 @@ def test_window_decode_validation(L):
     sz = C.c_size_t(need)
     assert L.tq_attn_decode_window(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, FAKE + 2, 0,
                                    0.1, FAKE, FAKE, C.byref(sz), None) == tq.TQ_EALIGN
+
+
+@pytest.mark.parametrize("d", [4, 8, 128, 256])
+def test_host_sphere_codebook_matches_reference_bitwise(L, d):
+    levels, thr, S = tq.tq_build_codebook(d, 3, 777, density="sphere")
+    cb = O.codebook(d, density="sphere")
+    assert np.array_equal(levels.astype(np.float64), cb.levels)
+    assert np.array_equal(thr.astype(np.float64), cb.thresholds)
+    assert np.array_equal(S, O.qjl_matrix(d, 777))
+    lv, th = np.zeros(8, np.float32), np.zeros(7, np.float32)
+    assert L.tq_build_codebook_sphere(2, 3, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EINVAL
+    assert L.tq_build_codebook_sphere(128, 2, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_build_codebook_sphere(96, 3, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EINVAL
+
+
+def test_mse_only_keys_validation(L):
+    """k_mse_only = 1 needs no QJL matrix; other values are rejected; tq_dequant
+    refuses the QJL term on such a cache."""
+    dsc = _desc(H=2)
+    dsc.qjl = None
+    sz = C.c_size_t(0)
+    decode = lambda: L.tq_attn_decode(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE,
+                                      None, C.byref(sz), None)
+    assert decode() == tq.TQ_EINVAL                                      # S needed
+    assert L.tq_encode_k(C.byref(dsc), FAKE, 1, FAKE, 4, None) == tq.TQ_EINVAL
+    dsc.k_mse_only = 1
+    assert decode() == tq.TQ_OK                                          # workspace query
+    assert L.tq_dequant(C.byref(dsc), 0, 1, FAKE, 4, FAKE, None) == tq.TQ_EINVAL
+    dsc.k_mse_only = 2
+    assert L.tq_encode_v(C.byref(dsc), FAKE, 1, FAKE, 4, None) == tq.TQ_EINVAL
+    prep = C.c_size_t(0)
+    assert L.tq_query_prepare(C.byref(dsc), FAKE, 0, 2, 1, 8, None, C.byref(prep), None) == tq.TQ_EINVAL

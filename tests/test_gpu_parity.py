@@ -436,6 +436,89 @@ def test_chunked_prefill_attention(tq, d, H, Hq, C):
     assert err <= Hn.ATTN_TOL
 
 
+@pytest.mark.parametrize("d", [128, 256])
+def test_sphere_codebook_encode_and_decode(tq, d):
+    """The kernels take the codebook by value: a cache built with the exact
+    sphere-coordinate codebook encodes and decodes to the reference fitted on
+    that density (codes bit-exact up to boundary cases, attention within
+    tolerance)."""
+    H, Hq, lens = 2, 8, [700, 300]
+    print(f"[sphere codebook] d={d}", flush=True)
+    w = I.Workload(f"sph{d}", len(lens), Hq, H, d, "bf16", "outlier", 51, fixed_len=1)
+    table, n_pages = I.page_table(w, np.asarray(lens), shuffle=True)
+    cache = tq.Cache(d, H, n_pages, codebook=tq.tq_build_codebook(d, 3, 12345, density="sphere"))
+    cb = Hn.codebook_from_cache(cache, density="sphere")
+    bt = torch.from_numpy(table).cuda()
+    for b, L in enumerate(lens):
+        k = I.kv_tokens(w, "k", b, 0, L)
+        v = I.kv_tokens(w, "v", b, 0, L)
+        t = np.arange(L)
+        slots = (table[b][t // 256].astype(np.int64) * 256 + t % 256).astype(np.int32)
+        ts = torch.from_numpy(slots).cuda()
+        tq.tq_encode_k(cache, Hn.torch_input(k, "bf16"), ts)
+        tq.tq_encode_v(cache, Hn.torch_input(v, "bf16"), ts)
+        torch.cuda.synchronize()
+        kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+        rk = Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k.astype(np.float64), cb, cache.qjl_host)
+        rv = Hn.compare_encode_v(O.unpack_v(vp, slots, H, d, 256), v.astype(np.float64), cb)
+        print("  K", rk, "V", rv)
+    q = I.queries(w, 0)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = tq.tq_attn_decode(cache, Hn.torch_input(q, "bf16"), bt, sl)
+    torch.cuda.synchronize()
+    ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens, H, 256,
+                        Hn.scale_of(d))
+    err = Hn.attn_rel_err(out.cpu().numpy(), ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= Hn.ATTN_TOL
+
+
+@pytest.mark.parametrize("d", [128, 256])
+def test_mse_only_keys_encode_and_decode(tq, d):
+    """Keys without the QJL stage (k_mse_only = 1, no S on the device): codes, N
+    and G as the reference, a zero sign plane, and attention that keeps only
+    the codebook term. The fused append step takes the same path."""
+    H, Hq, lens = 2, 8, [700, 300]
+    print(f"[mse-only keys] d={d}", flush=True)
+    w = I.Workload(f"mse{d}", len(lens), Hq, H, d, "bf16", "outlier", 61, fixed_len=1)
+    table, n_pages = I.page_table(w, np.asarray(lens), extra_tokens=1, shuffle=True)
+    # S stays on the device: were it read, the signs or the scores would show it
+    cache = tq.Cache(d, H, n_pages, k_mse_only=True)
+    cb = Hn.codebook_from_cache(cache)
+    bt = torch.from_numpy(table).cuda()
+    for b, L in enumerate(lens):
+        k = I.kv_tokens(w, "k", b, 0, L - 1)
+        v = I.kv_tokens(w, "v", b, 0, L - 1)
+        t = np.arange(L - 1)
+        slots = (table[b][t // 256].astype(np.int64) * 256 + t % 256).astype(np.int32)
+        ts = torch.from_numpy(slots).cuda()
+        tq.tq_encode_k(cache, Hn.torch_input(k, "bf16"), ts)
+        tq.tq_encode_v(cache, Hn.torch_input(v, "bf16"), ts)
+        torch.cuda.synchronize()
+        rk = Hn.compare_encode_k_mse_only(O.unpack_k(cache.k_pool.cpu().numpy(), slots, H, d, 256),
+                                          k.astype(np.float64), cb)
+        print("  K", rk)
+    # one appended token per sequence through the fused step, then the reference
+    pos = np.asarray(lens) - 1
+    slots = torch.from_numpy((table[np.arange(len(lens)), pos // 256].astype(np.int64) * 256
+                              + pos % 256).astype(np.int32)).cuda()
+    nk = np.concatenate([I.kv_tokens(w, "k", b, L - 1, L) for b, L in enumerate(lens)])
+    nv = np.concatenate([I.kv_tokens(w, "v", b, L - 1, L) for b, L in enumerate(lens)])
+    q = I.queries(w, 0)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = tq.tq_append_decode(cache, Hn.torch_input(nk, "bf16"), Hn.torch_input(nv, "bf16"), slots,
+                              Hn.torch_input(q, "bf16"), bt, sl)
+    out2 = tq.tq_attn_decode(cache, Hn.torch_input(q, "bf16"), bt, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+    Hn.compare_encode_k_mse_only(O.unpack_k(kp, slots.cpu().numpy(), H, d, 256), nk.astype(np.float64), cb)
+    ref = O.attn_decode(kp, vp, cb, None, q.astype(np.float64), table, lens, H, 256, Hn.scale_of(d))
+    err = Hn.attn_rel_err(out.cpu().numpy(), ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= Hn.ATTN_TOL
+
+
 WIN_CASES = [
     # (d, Hkv, Hq, n_q, lens, starts, causal, seed)
     # mid-page, page-aligned, the last token only, a start past the length (zero rows)

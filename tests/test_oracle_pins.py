@@ -458,3 +458,110 @@ def test_window_equals_dense_softmax_over_the_visible_tokens(causal):
     past = O.attn_decode(c["kp"], c["vp"], c["cb"], c["S"], c["q"], c["table"], c["lens"],
                          c["H"], c["P"], scale, seq_starts=c["lens"].copy())
     assert np.all(past == 0)
+
+
+# ---- the codebook of the exact sphere-coordinate law --------------------------
+
+def test_sphere_codebook_d3_is_the_uniform_quantiser():
+    """At d = 3 a coordinate of a uniform point on the sphere is uniform on
+    (-1, 1) (Archimedes), whose 8-level Lloyd-Max quantiser is the uniform one:
+    levels (2k - 7)/8 and thresholds at multiples of 1/4."""
+    c, t, _ = O.lloyd_max_sphere(3)
+    assert np.allclose(c, (2 * np.arange(8) - 7) / 8, atol=1e-13)
+    assert np.allclose(t, (np.arange(7) - 3) / 4, atol=1e-13)
+
+
+@pytest.mark.parametrize("d", [4, 16, 128, 256])
+def test_sphere_density_normalised_with_second_moment_one_over_d(d):
+    from scipy.integrate import quad
+    f = lambda x: float(O.sphere_coordinate_pdf(np.array([x]), d)[0])
+    assert abs(quad(f, -1, 1, limit=200)[0] - 1) < 1e-10
+    # the d coordinates of a unit vector have squares summing to one
+    assert abs(quad(lambda x: x * x * f(x), -1, 1, limit=200)[0] - 1 / d) < 1e-12
+
+
+@pytest.mark.parametrize("d", [8, 128])
+def test_sphere_codebook_centroid_and_midpoint_conditions(d):
+    from scipy.integrate import quad
+    cb = O.codebook(d, density="sphere")
+    c, t = cb.levels64, cb.thresholds64
+    f = lambda x: float(O.sphere_coordinate_pdf(np.array([x]), d)[0])
+    edges = np.concatenate([[-1.0], t, [1.0]])
+    for k in range(8):
+        m0 = quad(f, edges[k], edges[k + 1], limit=200, epsabs=1e-15)[0]
+        m1 = quad(lambda x: x * f(x), edges[k], edges[k + 1], limit=200, epsabs=1e-15)[0]
+        assert abs(m1 / m0 - c[k]) < 1e-9 * np.max(np.abs(c))
+    assert np.allclose(t, 0.5 * (c[:-1] + c[1:]), atol=1e-15)
+    assert np.array_equal(c, -c[::-1]) and t[3] == 0.0
+
+
+def test_sphere_codebook_tends_to_the_gaussian_one():
+    """N(0, 1/d) is the large-d limit; the gap in units of 1/sqrt(d) shrinks like 1/d."""
+    gap = {}
+    for d in (256, 1024, 4096):
+        s = O.codebook(d, density="sphere").levels64
+        g = O.codebook(d).levels64
+        gap[d] = np.max(np.abs(s - g)) * math.sqrt(d)
+    assert gap[4096] < 1e-3
+    assert 3.0 < gap[256] / gap[1024] < 5.0 and 3.0 < gap[1024] / gap[4096] < 5.0
+
+
+def test_sphere_codebook_against_sampled_unit_vectors():
+    """Monte Carlo from the definition: coordinates of normalised Gaussian
+    vectors in R^8. Each level is the mean of the samples in its cell (within
+    sampling error), and the sphere codebook's MSE is below the Gaussian one's."""
+    d = 8
+    rng = np.random.default_rng(5)
+    z = rng.standard_normal((400_000, d))
+    x = (z / np.linalg.norm(z, axis=1, keepdims=True)).ravel()
+    sph = O.codebook(d, density="sphere")
+    gau = O.codebook(d)
+    idx = np.searchsorted(sph.thresholds64, x, side="right")
+    for k in range(8):
+        sel = x[idx == k]
+        se = sel.std() / math.sqrt(len(sel))
+        assert abs(sel.mean() - sph.levels64[k]) < 5 * se
+    mse_s = np.mean((x - sph.levels64[idx]) ** 2)
+    ig = np.searchsorted(gau.thresholds64, x, side="right")
+    mse_g = np.mean((x - gau.levels64[ig]) ** 2)
+    assert mse_s < 0.99 * mse_g
+
+
+# ---- keys without the QJL stage ----------------------------------------------
+
+def test_mse_only_keys_drop_only_the_qjl_stage_and_term():
+    """encode_k_mse_only keeps codes, N and G of the full K encode with a zero
+    sign plane, and attention over such records with no S is dense softmax over
+    the MSE-only dequantised keys."""
+    d, H, P, L, g = 32, 2, 64, 150, 2
+    rng = np.random.default_rng(8)
+    cb = O.codebook(d)
+    S = O.qjl_matrix(d, 9).astype(np.float64)
+    k = rng.standard_normal((L, H, d)) * 2
+    v = rng.standard_normal((L, H, d))
+    full = O.encode(k, cb, S)
+    mse = O.encode_k_mse_only(k, cb)
+    assert np.array_equal(full["idx"], mse["idx"]) and not mse["sign"].any()
+    assert np.array_equal(full["N"], mse["N"]) and np.array_equal(full["G"], mse["G"])
+    npg = (L + P - 1) // P
+    table = np.arange(npg, dtype=np.int32)[::-1].copy()[None, :]
+    t = np.arange(L)
+    slots = table[0][t // P] * P + t % P
+    kp = np.zeros(npg * H * O.k_page_bytes(d, P), np.uint8)
+    vp = np.zeros(npg * H * O.v_page_bytes(d, P), np.uint8)
+    O.pack_k(kp, slots, mse["idx"], mse["sign"], mse["N"], mse["G"], P)
+    ev = O.encode(v, cb)
+    O.pack_v(vp, slots, ev["idx"], ev["N"], P)
+    q = rng.standard_normal((1, 1, H * g, d))
+    scale = 0.4
+    out = O.attn_decode(kp, vp, cb, None, q, table, [L], H, P, scale)
+    Kt = O.dequant_k(mse["idx"], mse["sign"], mse["N"], mse["G"], cb, S, with_qjl=False)
+    Vt = O.dequant_v(ev["idx"], ev["N"], cb)
+    for h in range(H * g):
+        lg = scale * (Kt[:, h // g] @ q[0, 0, h])
+        w = np.exp(lg - lg.max())
+        w /= w.sum()
+        assert np.max(np.abs(out[0, 0, h] - w @ Vt[:, h // g])) < 1e-12
+    # with S the same records score differently (the zero plane reads as sigma = -1)
+    out_q = O.attn_decode(kp, vp, cb, S, q, table, [L], H, P, scale)
+    assert np.max(np.abs(out_q - out)) > 1e-6
