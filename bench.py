@@ -447,6 +447,7 @@ def main():
     value = (kv_bytes + app_bytes) / step_s / 1e9
     dec_gbs = kv_bytes / (dec_ms / 1e3) / 1e9
     traffic = read_traffic(w.name)
+    in_bytes = 2 if w.dtype == "bf16" else 4
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -469,6 +470,11 @@ def main():
         "ctx_tokens_per_s": round(ctx_tokens / step_s, 1),
         "encode_k_vec_per_s": round(n_vec / (enc_k_ms / 1e3), 1),
         "encode_v_vec_per_s": round(n_vec / (enc_v_ms / 1e3), 1),
+        # input + record bytes per vector; S r is m x d = d^2 multiply-adds per K vector
+        "encode_k_GBps": round(n_vec * (d * in_bytes + d // 2 + 4) / (enc_k_ms / 1e3) / 1e9, 2),
+        "encode_v_GBps": round(n_vec * (d * in_bytes + 3 * d // 8 + 2) / (enc_v_ms / 1e3) / 1e9, 2),
+        "encode_k_sr_tflops": round(n_vec * 2 * d * d / (enc_k_ms / 1e3) / 1e12, 2),
+        "encode_k_sr_frac_fp32_peak": round(n_vec * 2 * d * d / (enc_k_ms / 1e3) / 157.3e12, 4),
         "decode_kernel_us": round(dec_ms * 1e3, 3),
         "decode_kernel_us_warm_single_copy": round(dec_warm_ms * 1e3, 3),
         "merge_kernel_us": round(merge_ms * 1e3, 3),
