@@ -94,10 +94,12 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // after every block, or (one query group at d = 256) only when the softmax
 // reference moves, and once at the end.
 //
-// Up to 16 query rows per KV head run as query groups of 4 rows (4 rows x 4
+// Up to TQ_MAX_GROUP query rows per KV head (a few for decode and verify, a
+// whole chunk's for chunked prefill) run as query groups of 4 rows (4 rows x 4
 // limbs fill the 16 MFMA rows). At d = 128 two groups share a workgroup; the
 // workgroups of one split sit in blockIdx.z, n_split * Hkv apart, so with
 // n_split * Hkv a multiple of 8 they land on the same XCD and share its L2.
+// With a causal tail a workgroup stops at the last token its rows can see.
 //
 // At d = 128 with one group, everything one block needs (key records, sidecars,
 // V words) is loaded one block ahead; two register sets alternate between even
