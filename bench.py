@@ -64,18 +64,23 @@ def read_traffic(workload: str):
 
 
 def platform_info():
-    """ROCm/HIP version, GPU name and the current clocks (best effort)."""
-    import subprocess
+    """ROCm/HIP version, GPU name and the current clock levels (best effort). The
+    clocks are read from the amdgpu sysfs files (the level marked '*'), so no
+    helper program is started from this GPU process."""
+    import glob
     import torch
     info = {"hip": torch.version.hip, "torch": torch.__version__,
             "gpu": torch.cuda.get_device_name(0)}
-    try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        clk = [ln.split(":", 1)[-1].strip() for ln in r.stdout.splitlines()
-               if ("sclk" in ln or "mclk" in ln) and "level" in ln]
-        info["clocks"] = clk[:4]
-    except Exception as e:  # the clocks are context only
-        info["clocks"] = f"unavailable ({type(e).__name__})"
+    clk = []
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_[sm]clk")):
+        try:
+            with open(path) as f:
+                cur = [ln.strip() for ln in f if ln.strip().endswith("*")]
+            if cur:
+                clk.append(f"{os.path.basename(path)[7:]} {cur[0]}")
+        except OSError:
+            pass
+    info["clocks"] = clk[:4] if clk else "unavailable"
     return info
 
 
