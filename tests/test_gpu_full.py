@@ -140,3 +140,26 @@ def test_full_size_prefill_chunks_and_verify(tq):
     sl = torch.from_numpy(lens.astype(np.int32)).cuda()
     out = tq.tq_attn_decode(cache, torch.from_numpy(q).to("cuda", torch.bfloat16), bt, sl).cpu().numpy()
     _check_decode(cache, w, q, out, kp, vp, cb, table, lens, [(0, 0), (3, 5)])
+
+
+def test_full_size_chunked_prefill(tq):
+    """Chunked prefill in the benchmark's configuration: on the full GQA 32K cache
+    the last 512 tokens are appended again and their 512 x 4 query rows per KV
+    head attend with the causal tail (2048 rows per KV head); one (sequence, KV
+    head) pair is checked row by row against the reference."""
+    w = I.workload(2)
+    C = 512
+    print(f"[full chunked prefill] {w.note}, chunk {C}", flush=True)
+    cache, table, lens, bt = _build(tq, w)
+    L = int(lens[0])
+    t = torch.arange(L - C, L, device="cuda")
+    slots = (bt[0, t // 256] * 256 + t % 256).to(torch.int32)
+    k = torch.from_numpy(I.kv_tokens(w, "k", 0, L - C, L)).to("cuda", torch.bfloat16)
+    v = torch.from_numpy(I.kv_tokens(w, "v", 0, L - C, L)).to("cuda", torch.bfloat16)
+    q = np.random.default_rng([w.data_seed, 7, C]).standard_normal((1, C, w.n_q_heads, w.head_dim))
+    q = I.round_to_dtype(q.astype(np.float32), "bf16")
+    sl = torch.from_numpy(lens.astype(np.int32)).cuda()
+    out = tq.tq_append_decode(cache, k, v, slots, torch.from_numpy(q).to("cuda", torch.bfloat16),
+                              bt, sl, causal_tail=1).cpu().numpy()
+    kp, vp, cb = _check_encode_ranges(cache, w, table, lens, 0, [(L - C, L - C + 256)])
+    _check_decode(cache, w, q, out, kp, vp, cb, table, lens, [(0, 5)], causal=True)
