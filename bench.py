@@ -127,40 +127,71 @@ def dense_baseline(dense, qs, seq, scale, tq_dec_ms, sh, log):
             "ideal_byte_ratio": round(nbytes / (Lm * B * H * kv_bytes_per_token_head(d)), 3)}
 
 
-def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0):
+def _host_cpu():
+    """CPU model, logical CPUs and the ones this process may run on (no helper
+    program is started)."""
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "cpu_count": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+
+
+def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0, budget_1t_s=6.0):
     """The CPU reference (numpy float64, as it stands) timed on this host on a
-    bounded sample: whole decode steps over every KV head of sequence 0, and
-    an encode of a slice of the K/V inputs."""
+    bounded sample: whole decode steps over every KV head of sequence 0 with the
+    BLAS thread pool as it is, then again on one BLAS thread, and an encode of a
+    slice of the K/V inputs."""
     import oracle as O
     from kv_cache_vector_07_amd import inputs as I
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
+        threadpool_limits = None
         threads = 1
     cb = O.codebook(w.head_dim)
     S = O.qjl_matrix(w.head_dim, w.qjl_seed)
     d, H = w.head_dim, w.n_kv_heads
     L = int(lens[0])
-    t0 = time.perf_counter()
-    heads_done = 0
-    while time.perf_counter() - t0 < budget_s and heads_done < 64 * H:
-        O.attn_decode(kp, vp, cb, S, q[:1].astype(np.float64), table[:1], lens[:1], H,
-                      w.page_size, 1 / math.sqrt(d), pairs=[(0, heads_done % H)])
-        heads_done += 1
-    dt = time.perf_counter() - t0
-    gbs = heads_done * L * kv_bytes_per_token_head(d) / dt / 1e9
+
+    def decode_rate(budget):
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < budget and done < 64 * H:
+            O.attn_decode(kp, vp, cb, S, q[:1].astype(np.float64), table[:1], lens[:1], H,
+                          w.page_size, 1 / math.sqrt(d), pairs=[(0, done % H)])
+            done += 1
+        dt = time.perf_counter() - t0
+        return done, dt, done * L * kv_bytes_per_token_head(d) / dt / 1e9
+
+    heads_done, dt, gbs = decode_rate(budget_s)
+    one = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            one = decode_rate(budget_1t_s)
     n_enc = 2048
     x = I.kv_tokens(w, "k", 0, 0, n_enc // H + 1)[: n_enc // H].astype(np.float64)
     t1 = time.perf_counter()
     O.encode(x, cb, S)
     O.encode(x, cb)
     enc_dt = time.perf_counter() - t1
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads_done} (sequence, KV head) decode passes over L={L} "
-                      f"({heads_done * w.group} query rows) in {dt:.1f} s; "
-                      f"encode of {x.shape[0] * H} K and V vectors",
-            "encode_vec_per_s": round(2 * x.shape[0] * H / enc_dt, 1)}
+    out = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{heads_done} (sequence, KV head) decode passes over L={L} "
+                     f"({heads_done * w.group} query rows) in {dt:.1f} s; "
+                     f"encode of {x.shape[0] * H} K and V vectors",
+           "encode_vec_per_s": round(2 * x.shape[0] * H / enc_dt, 1),
+           "host": _host_cpu()}
+    if one is not None:
+        out["value_1_thread"] = round(one[2], 4)
+        out["sample_1_thread"] = f"{one[0]} decode passes in {one[1]:.1f} s on one BLAS thread"
+    return out
 
 
 def prefill_attention(copies, table, lens, w, chunk, tdt, scale, sh, log):
