@@ -184,8 +184,13 @@ int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t ba
  *   score_j = scale * N_j * (<Pi q, c[code_j]> + sqrt(pi/2)/m * G_j * <S Pi q, sigma_j>)
  *   w = softmax(score),  out = Pi( sum_j w_j N^V_j c[codeV_j] )   (float32)
  * Token j of sequence b lives at slot block_table[b][j / P] * P + j % P
- * (block_table: device int32 [batch][max_pages]). An empty visible range gives
- * a zero row. Hq / Hkv * n_q must not exceed TQ_MAX_GROUP.
+ * (block_table: device int32 [batch][max_pages]). The entries of the first
+ * ceil(L_b / P) pages must lie in [0, n_pages) (device data, not checked);
+ * later entries are never read, and tokens past max_pages * P are not seen.
+ * L_b <= 0 or an empty visible range gives a zero row. Hq / Hkv * n_q must not
+ * exceed TQ_MAX_GROUP, and batch * ceil(ceil(rows / 4) / k) must not exceed
+ * 65535, with rows = Hq / Hkv * n_q and k = 2 at d = 128 when rows > 4, else 1
+ * (TQ_EUNSUPPORTED).
  * Workspace: call with workspace == NULL to get the size in *workspace_bytes
  * (nothing is launched). It holds split partials and the prepared queries; its
  * contents need no initialisation and are scratch after the call. Calls that
