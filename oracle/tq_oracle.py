@@ -40,6 +40,8 @@ notes; the ones that shape arithmetic are restated where they are used:
       coordinate of a uniform unit vector in R^d, whose large-d limit is R4's.
   R26 (variant) keys may skip the QJL stage: the record keeps codes, N and G,
       its sign plane is zero, and the score keeps only the codebook term.
+  R27 (variant) V codes may have 2 or 4 bits (4 or 16 Lloyd-Max levels of the
+      same density), stored as that many bit planes.
 """
 
 from __future__ import annotations
@@ -236,8 +238,8 @@ def codebook(head_dim: int, bits: int = 3, density: str = "gaussian") -> Codeboo
     """8-level Lloyd-Max codebook (R4); stored values are float32. density
     "gaussian" fits N(0, 1/d) (the default, R4); "sphere" fits the exact
     marginal of a coordinate of a uniform unit vector in R^d (R25)."""
-    if bits != 3:
-        raise ValueError("the pages describe 3-bit codes only")
+    if bits not in (2, 3, 4):
+        raise ValueError("codes of 2, 3 or 4 bits (3 for K, R27 for V)")
     if density == "gaussian":
         c, t, it = lloyd_max_gaussian(1.0 / math.sqrt(head_dim), 1 << bits)
     elif density == "sphere":
@@ -374,15 +376,16 @@ def side_entry(t):
 
 
 @functools.lru_cache(maxsize=None)
-def _v_bit_table(d: int, P: int) -> np.ndarray:
-    """[3][d][P] -> index of that bit in the section's code bits (as a flat
-    little-endian bit string, bit 32 w + p = bit p of word w)."""
-    j = np.arange(3)[:, None, None]
+def _v_bit_table(d: int, P: int, vb: int = 3) -> np.ndarray:
+    """[vb][d][P] -> index of that bit in the section's code bits (as a flat
+    little-endian bit string, bit 32 w + p = bit p of word w). A 64-token block
+    holds vb planes of 2 d words each."""
+    j = np.arange(vb)[:, None, None]
     i = np.arange(d)[None, :, None]
     b, tau, k, r = _split_offset(np.arange(P)[None, None, :])
     kk, n = i // 16, i % 16
     kp, h = kk // 2, kk % 2
-    word = b * (6 * d) + j * (2 * d) + (16 * k + n) * (d // 32) + kp
+    word = b * (2 * vb * d) + j * (2 * d) + (16 * k + n) * (d // 32) + kp
     bit = 8 * r + 4 * h + tau
     return (32 * word + bit).astype(np.int64)
 
@@ -391,8 +394,9 @@ def k_page_bytes(d: int, P: int) -> int:
     return P * d // 2 + 4 * P
 
 
-def v_page_bytes(d: int, P: int) -> int:
-    return 3 * d * P // 8 + 2 * P
+def v_page_bytes(d: int, P: int, vb: int = 3) -> int:
+    """V section of one (page, KV head) with vb-bit codes."""
+    return vb * d * P // 8 + 2 * P
 
 
 def pack_k(pool: np.ndarray, slots, idx, sign, N, G, P: int) -> None:
@@ -415,14 +419,14 @@ def pack_k(pool: np.ndarray, slots, idx, sign, N, G, P: int) -> None:
     pool[(side + 2 * P)[..., None] + np.arange(2)] = gb
 
 
-def pack_v(pool: np.ndarray, slots, idx, N, P: int) -> None:
-    """Write V records of tokens [n][H][d] into a uint8 pool at `slots`
+def pack_v(pool: np.ndarray, slots, idx, N, P: int, vb: int = 3) -> None:
+    """Write vb-bit V records of tokens [n][H][d] into a uint8 pool at `slots`
     (only the addressed tokens' bits change)."""
     idx = np.asarray(idx, dtype=np.uint8)
     n, H, d = idx.shape
-    vpb = v_page_bytes(d, P)
-    cbytes = 3 * d * P // 8
-    tab = _v_bit_table(d, P)
+    vpb = v_page_bytes(d, P, vb)
+    cbytes = vb * d * P // 8
+    tab = _v_bit_table(d, P, vb)
     slots = np.asarray(slots, dtype=np.int64)
     page, off = slots // P, slots % P
     for pg in np.unique(page):
@@ -430,7 +434,7 @@ def pack_v(pool: np.ndarray, slots, idx, N, P: int) -> None:
         for h in range(H):
             base = (int(pg) * H + h) * vpb
             bits = np.unpackbits(pool[base:base + cbytes], bitorder="little")
-            for j in range(3):
+            for j in range(vb):
                 bits[tab[j][:, off[sel]]] = ((idx[sel, h, :] >> j) & 1).T
             pool[base:base + cbytes] = np.packbits(bits, bitorder="little")
             nb = np.asarray(N, dtype=np.float16)[sel, h].view(np.uint8).reshape(-1, 2)
@@ -455,11 +459,11 @@ def unpack_k(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
     return {"idx": idx.astype(np.uint8), "sign": bits[:, :, 3].astype(bool), "N": N, "G": G}
 
 
-def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
-    """Read V records of `slots` for all heads: idx [n][H][d], N [n][H]."""
-    vpb = v_page_bytes(d, P)
-    cbytes = 3 * d * P // 8
-    tab = _v_bit_table(d, P)
+def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int, vb: int = 3) -> dict:
+    """Read vb-bit V records of `slots` for all heads: idx [n][H][d], N [n][H]."""
+    vpb = v_page_bytes(d, P, vb)
+    cbytes = vb * d * P // 8
+    tab = _v_bit_table(d, P, vb)
     slots = np.asarray(slots, dtype=np.int64)
     page, off = slots // P, slots % P
     n = len(slots)
@@ -470,8 +474,8 @@ def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
         for h in range(H):
             base = (int(pg) * H + h) * vpb
             bits = np.unpackbits(pool[base:base + cbytes], bitorder="little")
-            sub = bits[tab[:, :, off[sel]]]                                # [3][d][k]
-            idx[sel, h, :] = (sub[0] | (sub[1] << 1) | (sub[2] << 2)).T
+            sub = bits[tab[:, :, off[sel]]]                                # [vb][d][k]
+            idx[sel, h, :] = sum(sub[j].astype(np.uint8) << j for j in range(vb)).T
             pos = base + cbytes + 2 * side_entry(off[sel])
             N[sel, h] = pool[pos[:, None] + np.arange(2)].copy().view(np.float16)[:, 0]
     return {"idx": idx, "N": N}
@@ -499,16 +503,16 @@ def gather_k(pool, block_table_row, L, kv_head, H, d, P):
     return idx, bits[:, 3].astype(bool), N.astype(np.float64), G.astype(np.float64)
 
 
-def gather_v(pool, block_table_row, L, kv_head, H, d, P):
-    """V records of tokens 0..L-1 of one sequence and one KV head."""
-    vpb = v_page_bytes(d, P)
-    cbytes = 3 * d * P // 8
+def gather_v(pool, block_table_row, L, kv_head, H, d, P, vb: int = 3):
+    """vb-bit V records of tokens 0..L-1 of one sequence and one KV head."""
+    vpb = v_page_bytes(d, P, vb)
+    cbytes = vb * d * P // 8
     npg = (L + P - 1) // P
     pages = np.asarray(block_table_row, dtype=np.int64)[:npg]
     base = (pages * H + kv_head) * vpb
     codes = pool[base[:, None] + np.arange(cbytes)]                     # [pg][cbytes]
-    bits = np.unpackbits(codes, axis=-1, bitorder="little")[:, _v_bit_table(d, P)]  # [pg][3][d][P]
-    idx = bits[:, 0] | (bits[:, 1] << 1) | (bits[:, 2] << 2)               # [pg][d][P]
+    bits = np.unpackbits(codes, axis=-1, bitorder="little")[:, _v_bit_table(d, P, vb)]  # [pg][vb][d][P]
+    idx = sum(bits[:, j].astype(np.uint8) << j for j in range(vb))          # [pg][d][P]
     idx = idx.transpose(0, 2, 1).reshape(npg * P, d)[:L]
     t = np.arange(L, dtype=np.int64)
     side = base[t // P] + cbytes + 2 * side_entry(t % P)
@@ -535,7 +539,8 @@ def score(qt, p, idx, sign, N, G, cb: Codebook, m: int):
 
 def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
                 n_kv_heads: int, page_size: int, scale: float,
-                causal_tail: bool = False, pairs=None, seq_starts=None) -> np.ndarray:
+                causal_tail: bool = False, pairs=None, seq_starts=None,
+                cb_v: Codebook | None = None, v_bits: int = 3) -> np.ndarray:
     """Naive two-pass softmax attention over the packed cache, float64.
 
     For query (b, t, h) with KV head h // (Hq/Hkv) (R15) and visible tokens
@@ -544,7 +549,8 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
       w = softmax_j(scale * score_j),  a = sum_j w_j N^V_j c[idxV_j],  o = Pi a.
     A row with no visible token is zero. Records of tokens before s_b are not
     read. `pairs` restricts the work to the listed (b, kv_head) pairs; other
-    rows stay zero. Returns out [B][n_q][Hq][d].
+    rows stay zero. V records hold v_bits-bit codes of the codebook cb_v (cb
+    when None; R27). Returns out [B][n_q][Hq][d].
     """
     q = np.asarray(q, dtype=np.float64)
     B, n_q, Hq, d = q.shape
@@ -565,8 +571,9 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
         p0 = s0 // page_size
         base = p0 * page_size
         idx, sign, N, G = gather_k(k_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size)
-        vidx, NV = gather_v(v_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size)
-        vals = NV[:, None] * cb.levels[vidx]                               # [L - base][d]
+        vidx, NV = gather_v(v_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size,
+                            v_bits)
+        vals = NV[:, None] * (cb_v or cb).levels[vidx]                     # [L - base][d]
         ckey = cb.levels[idx]                                              # [L - base][d]
         sig = np.where(sign, 1.0, -1.0)
         lo = s0 - base
