@@ -97,25 +97,39 @@ typedef struct {
                            tq_dequant rejects with_qjl = 1 (TQ_EINVAL). Must
                            match how the records were written. Other values:
                            TQ_EINVAL.                                           */
+  int32_t v_bits;       /* V code width. 0 or 3: 3-bit V with levels and
+                           thresholds above (the pages' 3.125 bits/dim). 2 or
+                           4: V codes of that width with v_levels and
+                           v_thresholds, the bit-width variant (2.125 or 4.125
+                           bits/dim at d = 128); v_pool sections are then
+                           tq_v_page_bytes_bits(d, P, v_bits). Other values:
+                           TQ_EINVAL. K is always 3-bit.                        */
+  float v_levels[16];   /* with v_bits 2 or 4: the first 2^v_bits entries,
+                           strictly ascending and odd (else TQ_EINVAL)          */
+  float v_thresholds[15]; /* with v_bits 2 or 4: the first 2^v_bits - 1         */
 } tq_cache;
 
 /* Bytes of one (page, KV head) section; 0 for unsupported d or P. */
 size_t tq_k_page_bytes(int32_t head_dim, int32_t page_size);
 size_t tq_v_page_bytes(int32_t head_dim, int32_t page_size);
+/* V section for codes of `bits` bits (2, 3 or 4; 0 otherwise): bits planes of
+ * d x P bits, then the fp16 norms. */
+size_t tq_v_page_bytes_bits(int32_t head_dim, int32_t page_size, int32_t bits);
 
 /*
  * Lloyd-Max codebook and QJL matrix ("TurboQuant KVキャッシュ圧縮アーキテクチャ",
  * item 1; "K-Cache圧縮" steps 3 and 5). Host only, no GPU needed.
- *   levels[8], thresholds[7] (host out): the 8-level MSE quantiser of N(0, 1/d),
- *     found by Lloyd iteration in float64 from the Gaussian quantiles
- *     sigma*Phi^-1((k+1/2)/8) until no level moves by 1e-14*sigma, symmetrised,
- *     thresholds at midpoints, then rounded to float32.
+ *   levels[n], thresholds[n-1] (host out), n = 2^bits: the n-level MSE quantiser
+ *     of N(0, 1/d), found by Lloyd iteration in float64 from the Gaussian
+ *     quantiles sigma*Phi^-1((k+1/2)/n) until no level moves by 1e-14*sigma,
+ *     symmetrised, thresholds at midpoints, then rounded to float32. bits = 3
+ *     is the pages' codebook (K and V); 2 and 4 serve the V bit-width variant.
  *   qjl_host (host out, d*d floats, may be NULL): S[l][i] row-major; SplitMix64
  *     seeded with qjl_seed gives pairs (x1, x2) -> u = ((x>>11)+1)*2^-53, Box-Muller
  *     sqrt(-2 ln u1) cos(2 pi u2) then sin(...), filled in order, rounded to float32.
  *     The caller uploads it and points tq_cache.qjl at the device copy.
  * Errors: TQ_EINVAL (null levels/thresholds, head_dim < 2 or not a power of two),
- * TQ_EUNSUPPORTED (bits != 3).
+ * TQ_EUNSUPPORTED (bits not 2, 3 or 4).
  */
 int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed,
                       float *levels, float *thresholds, float *qjl_host);
@@ -132,7 +146,7 @@ int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed,
  * first moments in closed form; symmetrised, midpoint thresholds, rounded to
  * float32. The codebook is odd, as the kernels require. qjl_host as above.
  * Errors: TQ_EINVAL (null levels/thresholds, head_dim < 4 or not a power of
- * two), TQ_EUNSUPPORTED (bits != 3).
+ * two), TQ_EUNSUPPORTED (bits not 2, 3 or 4).
  */
 int tq_build_codebook_sphere(int32_t head_dim, int32_t bits, uint64_t qjl_seed,
                              float *levels, float *thresholds, float *qjl_host);

@@ -23,18 +23,36 @@ int check_cache(const tq_cache *c) {
   if (!aligned(c->k_pool, 256) || !aligned(c->v_pool, 256)) return TQ_EALIGN;
   if (c->k_mse_only != 0 && c->k_mse_only != 1) return TQ_EINVAL;
   // the decode kernels split each level into odd bit-plane weights: the
-  // codebook must be strictly increasing and odd (c[7-k] = -c[k])
-  for (int k = 0; k < 8; ++k) {
-    if (!isfinite(c->levels[k]) || c->levels[7 - k] != -c->levels[k]) return TQ_EINVAL;
-    if (k > 0 && !(c->levels[k] > c->levels[k - 1])) return TQ_EINVAL;
-  }
+  // codebooks must be strictly increasing and odd (c[n-1-k] = -c[k])
+  auto odd_increasing = [](const float *lv, int n) {
+    for (int k = 0; k < n; ++k) {
+      if (!isfinite(lv[k]) || lv[n - 1 - k] != -lv[k]) return false;
+      if (k > 0 && !(lv[k] > lv[k - 1])) return false;
+    }
+    return true;
+  };
+  if (!odd_increasing(c->levels, 8)) return TQ_EINVAL;
+  if (c->v_bits != 0 && c->v_bits != 2 && c->v_bits != 3 && c->v_bits != 4) return TQ_EINVAL;
+  if ((c->v_bits == 2 || c->v_bits == 4) && !odd_increasing(c->v_levels, 1 << c->v_bits))
+    return TQ_EINVAL;
   return TQ_OK;
 }
 
 Codebook codebook_of(const tq_cache *c) {
-  Codebook cb;
-  memcpy(cb.levels, c->levels, sizeof cb.levels);
-  memcpy(cb.thresholds, c->thresholds, sizeof cb.thresholds);
+  Codebook cb = {};
+  memcpy(cb.levels, c->levels, sizeof c->levels);
+  memcpy(cb.thresholds, c->thresholds, sizeof c->thresholds);
+  return cb;
+}
+
+// V code width and codebook: 3-bit V shares the K codebook
+int v_bits_of(const tq_cache *c) { return (c->v_bits == 2 || c->v_bits == 4) ? c->v_bits : 3; }
+Codebook v_codebook_of(const tq_cache *c) {
+  if (v_bits_of(c) == 3) return codebook_of(c);
+  Codebook cb = {};
+  const int n = 1 << c->v_bits;
+  memcpy(cb.levels, c->v_levels, sizeof(float) * n);
+  memcpy(cb.thresholds, c->v_thresholds, sizeof(float) * (n - 1));
   return cb;
 }
 
@@ -66,8 +84,8 @@ double std_quantile(double p) {
   return 0.5 * (lo + hi);
 }
 
-void lloyd_max(double sigma, double *c, double *t) {
-  const int n = 8;
+// n levels (n <= 16) of N(0, sigma^2); c[n], t[n - 1]
+void lloyd_max(double sigma, int n, double *c, double *t) {
   for (int k = 0; k < n; ++k) c[k] = sigma * std_quantile((k + 0.5) / n);
   for (int it = 0; it < 10000; ++it) {
     for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
@@ -81,7 +99,7 @@ void lloyd_max(double sigma, double *c, double *t) {
     }
     if (delta < 1e-14 * sigma) break;
   }
-  double s[8];
+  double s[16];
   for (int k = 0; k < n; ++k) s[k] = 0.5 * (c[k] - c[n - 1 - k]);
   for (int k = 0; k < n; ++k) c[k] = s[k];
   for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
@@ -122,9 +140,8 @@ double sphere_moment(int d, double a, double b) {
   return F(a) - F(b);
 }
 
-void lloyd_max_sphere(int d, double *c, double *t) {
-  const int n = 8;
-  lloyd_max(1.0 / sqrt((double)d), c, t);
+void lloyd_max_sphere(int d, int n, double *c, double *t) {
+  lloyd_max(1.0 / sqrt((double)d), n, c, t);
   for (int k = 0; k < n; ++k) c[k] = fmax(-0.999, fmin(0.999, c[k]));
   double scale = 0.0;
   for (int k = 0; k < n; ++k) scale = fmax(scale, fabs(c[k]));
@@ -140,7 +157,7 @@ void lloyd_max_sphere(int d, double *c, double *t) {
     }
     if (delta < 1e-14 * scale) break;
   }
-  double s[8];
+  double s[16];
   for (int k = 0; k < n; ++k) s[k] = 0.5 * (c[k] - c[n - 1 - k]);
   for (int k = 0; k < n; ++k) c[k] = s[k];
   for (int k = 0; k + 1 < n; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
@@ -195,8 +212,13 @@ size_t tq_k_page_bytes(int32_t head_dim, int32_t page_size) {
 }
 
 size_t tq_v_page_bytes(int32_t head_dim, int32_t page_size) {
+  return tq_v_page_bytes_bits(head_dim, page_size, 3);
+}
+
+size_t tq_v_page_bytes_bits(int32_t head_dim, int32_t page_size, int32_t bits) {
   if (head_dim <= 0 || head_dim % 32 || page_size <= 0 || page_size % 32) return 0;
-  return (size_t)3 * head_dim * page_size / 8 + 2u * page_size;
+  if (bits < 2 || bits > 4) return 0;
+  return (size_t)bits * head_dim * page_size / 8 + 2u * page_size;
 }
 
 const char *tq_status_string(int32_t s) {
@@ -229,11 +251,12 @@ int tq_build_codebook(int32_t head_dim, int32_t bits, uint64_t qjl_seed, float *
                       float *thresholds, float *qjl_host) {
   if (!levels || !thresholds) return TQ_EINVAL;
   if (head_dim < 2 || (head_dim & (head_dim - 1))) return TQ_EINVAL;
-  if (bits != 3) return TQ_EUNSUPPORTED;
-  double c[8], t[7];
-  lloyd_max(1.0 / sqrt((double)head_dim), c, t);
-  for (int k = 0; k < 8; ++k) levels[k] = (float)c[k];
-  for (int k = 0; k < 7; ++k) thresholds[k] = (float)t[k];
+  if (bits < 2 || bits > 4) return TQ_EUNSUPPORTED;
+  const int n = 1 << bits;
+  double c[16], t[15];
+  lloyd_max(1.0 / sqrt((double)head_dim), n, c, t);
+  for (int k = 0; k < n; ++k) levels[k] = (float)c[k];
+  for (int k = 0; k + 1 < n; ++k) thresholds[k] = (float)t[k];
   if (qjl_host) build_qjl(head_dim, qjl_seed, qjl_host);
   return TQ_OK;
 }
@@ -242,11 +265,12 @@ int tq_build_codebook_sphere(int32_t head_dim, int32_t bits, uint64_t qjl_seed, 
                              float *thresholds, float *qjl_host) {
   if (!levels || !thresholds) return TQ_EINVAL;
   if (head_dim < 4 || (head_dim & (head_dim - 1))) return TQ_EINVAL;
-  if (bits != 3) return TQ_EUNSUPPORTED;
-  double c[8], t[7];
-  lloyd_max_sphere(head_dim, c, t);
-  for (int k = 0; k < 8; ++k) levels[k] = (float)c[k];
-  for (int k = 0; k < 7; ++k) thresholds[k] = (float)t[k];
+  if (bits < 2 || bits > 4) return TQ_EUNSUPPORTED;
+  const int n = 1 << bits;
+  double c[16], t[15];
+  lloyd_max_sphere(head_dim, n, c, t);
+  for (int k = 0; k < n; ++k) levels[k] = (float)c[k];
+  for (int k = 0; k + 1 < n; ++k) thresholds[k] = (float)t[k];
   if (qjl_host) build_qjl(head_dim, qjl_seed, qjl_host);
   return TQ_OK;
 }
@@ -268,7 +292,8 @@ static int encode_common(const tq_cache *c, const void *x, int32_t dtype, const 
   a.n_heads = c->n_kv_heads;
   a.pool = (uint8_t *)(is_k ? c->k_pool : c->v_pool);
   a.qjl = qjl_of(c);
-  a.cb = codebook_of(c);
+  a.cb = is_k ? codebook_of(c) : v_codebook_of(c);
+  a.bits = is_k ? 3 : v_bits_of(c);
   hipStream_t s = (hipStream_t)stream;
   return hip_status(is_k ? tq::launch_encode_k(a, c->head_dim, s)
                          : tq::launch_encode_v(a, c->head_dim, s));
@@ -386,6 +411,8 @@ static tq::DecodeArgs decode_args(const tq_cache *c, const uint8_t *prep, int32_
   a.scale = scale;
   a.plan = plan;
   a.cb = codebook_of(c);
+  a.vcb = v_codebook_of(c);
+  a.v_bits = v_bits_of(c);
   return a;
 }
 
@@ -490,9 +517,12 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   ek.pool = (uint8_t *)c->k_pool;
   ek.qjl = qjl_of(c);
   ek.cb = codebook_of(c);
+  ek.bits = 3;
   ev = ek;
   ev.x = v_new;
   ev.pool = (uint8_t *)c->v_pool;
+  ev.cb = v_codebook_of(c);
+  ev.bits = v_bits_of(c);
   tq::PrepArgs pa;
   pa.q = q;
   pa.dtype = q_dtype;
@@ -664,7 +694,8 @@ int tq_dequant(const tq_cache *c, int32_t which, int32_t with_qjl, const int32_t
   a.with_qjl = which == 0 ? with_qjl : 0;
   a.qjl = c->qjl;
   a.out = out;
-  a.cb = codebook_of(c);
+  a.cb = which == 0 ? codebook_of(c) : v_codebook_of(c);
+  a.bits = which == 0 ? 3 : v_bits_of(c);
   return hip_status(tq::launch_dequant(a, c->head_dim, which, (hipStream_t)stream));
 }
 

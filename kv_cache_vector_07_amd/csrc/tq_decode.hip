@@ -117,26 +117,27 @@ __device__ inline void stage_query(const uint8_t *grp, v8i *s_qop, int *s_qsc, i
   for (int e = tid; e < NMU * 64; e += 256) s_qsc[e] = ssrc[e];
 }
 
-template <int D>
+template <int D, int VBITS>
 struct MfmaBlock {
   static constexpr bool kPrefetchV = D == 128;
   uint4 kw[4][D / 128];            // key record chunks kg, kg + 4 of tokens 16 tau + n
   uint2 g, nk, nv;                 // G, N^K, N^V of side entries 4 n + tau (tokens 16 tau + n)
-  uint4 v[kPrefetchV ? 3 : 1][D / 128];   // V words of plane j: coordinate pairs kp
+  uint4 v[kPrefetchV ? VBITS : 1][D / 128];   // V words of plane j: coordinate pairs kp
 };
 
 // NG query groups (4 rows each) share a workgroup: the key and V operands of a
 // block are built once and each MFMA operand of the keys or V bits meets the NG
 // query operands in turn. NG = 1 gives each group its own workgroup.
-template <int D, int NG>
+template <int D, int NG, int VBITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2 : 1))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NMU = 5 * (D / 128);        // scaled MFMAs per 16-token scoring tile
   constexpr int NCH = D / 128;              // 16-byte key chunks per lane and token
   constexpr int KREC = D / 2;
   constexpr size_t KCODES = (size_t)kPage * KREC;
   constexpr size_t KSEC = KCODES + 4 * kPage;
-  constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
+  constexpr size_t VCODES = (size_t)VBITS * D * kPage / 8;   // VBITS-bit V codes
   constexpr size_t VSEC = VCODES + 2 * kPage;
+  constexpr int NP = VPlanes<VBITS>::n;     // V bit planes (odd Walsh functions of the code bits)
   constexpr int NB = D / 16;                // 16-coordinate V column blocks
   constexpr int NR = NG * kMfmaMaxGroup;    // query rows of the workgroup
 
@@ -180,14 +181,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   // 16 tau + 4 kg + lam, which the score layout holds in lane 16 q + 4 kg + lam
   const int perm_addr = 4 * (16 * (n >> 2) + 4 * kg + lam);
   const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
-  float wpl[4];
-  plane_weights(a.cb, wpl);
-  const float wmax = fmaxf(fmaxf(fabsf(wpl[0]), fabsf(wpl[1])), fmaxf(fabsf(wpl[2]), fabsf(wpl[3])));
+  float wpl[NP];
+  if constexpr (VBITS == 3)
+    plane_weights(a.vcb, wpl);
+  else
+    v_plane_weights<VBITS>(a.vcb, wpl);
+  float wmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) wmax = fmaxf(wmax, fabsf(wpl[j]));
   // weight limbs: X = U * 2^-tau * (w_j / wmax) * 2^30, where 2^tau is the value
   // the V bit of token 16 tau + 4 k + r takes in byte r of the B operand
-  float cx[4], half[4];
+  float cx[NP], half[NP];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NP; ++j) {
     half[j] = wpl[j] < 0.f ? -0.5f : 0.5f;   // round to nearest with a truncating convert
     cx[j] = wpl[j] / wmax * 1073741824.f;
   }
@@ -259,7 +265,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     }
   };
 
-  auto load_block = [&](MfmaBlock<D> &d, int pg) {
+  auto load_block = [&](MfmaBlock<D, VBITS> &d, int pg) {
     const int phys = a.block_table[(size_t)b * a.max_pages + pg];
     const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
     const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
@@ -272,32 +278,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     d.g = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * kPage + 2 * se);
     d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * se);
     d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * se);
-    if constexpr (MfmaBlock<D>::kPrefetchV) {
-      const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
+    if constexpr (MfmaBlock<D, VBITS>::kPrefetchV) {
+      const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 2 * VBITS * D) + 4 * (D / 32) * lane);
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < VBITS; ++j)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) d.v[j][c] = vw[j * 2 * D * 4 / 16 + c];
     }
   };
 
-  auto process = [&](const MfmaBlock<D> &d, int pg) {
+  auto process = [&](const MfmaBlock<D, VBITS> &d, int pg) {
     // at d = 256 the query operand (20 MFMA operands, 80 registers) is read from
     // LDS where it is used: an opaque lane offset keeps it from being hoisted
     int qo = lane;
     if constexpr (D == 256 || NG > 1) asm volatile("" : "+v"(qo));
-    uint4 vcur[3][NCH];
-    if constexpr (MfmaBlock<D>::kPrefetchV) {
+    uint4 vcur[VBITS][NCH];
+    if constexpr (MfmaBlock<D, VBITS>::kPrefetchV) {
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < VBITS; ++j)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) vcur[j][c] = d.v[j][c];
     } else {
       const int phys = a.block_table[(size_t)b * a.max_pages + pg];
       const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
-      const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 6 * D) + 4 * (D / 32) * lane);
+      const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 2 * VBITS * D) + 4 * (D / 32) * lane);
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < VBITS; ++j)
 #pragma unroll
         for (int c = 0; c < NCH; ++c) vcur[j][c] = vw[j * 2 * D * 4 / 16 + c];
     }
@@ -403,6 +409,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
       us_lane[gi] += us;
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (VBITS == 3) {
     v4i A[NG][4];   // per group and plane: weight limbs, VGPR tau, byte r = token 16 tau + 4 kg + r
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi)
@@ -454,12 +461,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
         }
       }
     }
+    } else {
+    // other code widths: the NP planes in turn, each with its own weight limbs
+    float Ut[NG][4];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) Ut[gi][tau] = __builtin_amdgcn_ldexpf(Uv[gi][tau], -tau);
+    auto vword = [&](int j, int kp) -> uint32_t {
+      const uint4 &u = vcur[j][kp >> 2];
+      const int e = kp & 3;
+      return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
+    };
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      v4i Ap[NG];
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          const int X = (int)fmaf(Ut[gi][tau], cx[p], half[p]);
+          Ap[gi][tau] = (int)(quad_byte_transpose((uint32_t)X + 0x80808080u, lam) ^ 0x80808080u);
+        }
+#pragma unroll
+      for (int kp = 0; kp < D / 32; ++kp) {
+        // the plane word: parity of the code bits in the plane's mask
+        uint32_t wp = 0u;
+#pragma unroll
+        for (int j = 0; j < VBITS; ++j)
+          if ((VPlanes<VBITS>::mask[p] >> j) & 1) wp ^= vword(j, kp);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint32_t w = wp >> (4 * h);
+          v4i bop;   // VGPR tau, byte r: token 16 tau + 4 kg + r, bit value 2^tau
+          bop.x = (int)(w & 0x01010101u);
+          bop.y = (int)(w & 0x02020202u);
+          bop.z = (int)(w & 0x04040404u);
+          bop.w = (int)(w & 0x08080808u);
+#pragma unroll
+          for (int gi = 0; gi < NG; ++gi)
+            vacc[gi][2 * kp + h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(Ap[gi], bop, vacc[gi][2 * kp + h], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (!kLazyV) {
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) fold_v(gi);
+    }
+    }
   };
 
   // the first block's loads go out before the query operand is staged, so the
   // two fetches overlap
   if constexpr (D == 128 && NG == 1) {
-    MfmaBlock<D> d0, d1;
+    MfmaBlock<D, VBITS> d0, d1;
     if (pg0 < pg1) load_block(d0, pg0);
     // the packed query operand is shared by the four waves: keep it in LDS
     stage();
@@ -476,7 +531,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     stage();
     __syncthreads();
     for (int pg = pg0; pg < pg1; ++pg) {
-      MfmaBlock<D> d0;
+      MfmaBlock<D, VBITS> d0;
       load_block(d0, pg);
       process(d0, pg);
     }
@@ -496,7 +551,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   }
   __syncthreads();   // every wave is past the page loop: the query operands are dead
   {
-    const float c7 = a.cb.levels[7];
+    const float c7 = a.vcb.levels[(1 << VBITS) - 1];   // the V codebook's largest level
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       const float usq = s_wm[wave][3][4 * gi + kg];
@@ -632,22 +687,32 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   for (int r = 0; r < R; ++r) o[lane + 64 * r] = x[r];
 }
 
-template <int D>
-hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
-  const int G = a.plan.group;
-  if (!a.plan.mfma || G > TQ_MAX_GROUP) return hipErrorInvalidValue;
+template <int D, int VBITS>
+hipError_t launch_split_bits(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.wg_per_seq);
   switch (a.plan.groups_per_wg) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS>), grid, dim3(256), 0, s, a); break;
     case 2:
       if constexpr (D == 128) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, 2>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, 2, VBITS>), grid, dim3(256), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
+  const int G = a.plan.group;
+  if (!a.plan.mfma || G > TQ_MAX_GROUP) return hipErrorInvalidValue;
+  switch (a.v_bits) {
+    case 2: return launch_split_bits<D, 2>(a, s);
+    case 3: return launch_split_bits<D, 3>(a, s);
+    case 4: return launch_split_bits<D, 4>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace

@@ -122,12 +122,22 @@ __device__ inline float level_of(const Codebook &cb, int idx) {
   return b2 ? l47 : l03;
 }
 
-// Code = number of thresholds t_k <= y (a tie goes to the upper cell).
+// Code = number of thresholds t_k <= y (a tie goes to the upper cell); NT
+// thresholds (7 for 3-bit codes).
+template <int NT = 7>
 __device__ inline int quantize_code(const Codebook &cb, float y) {
   int idx = 0;
 #pragma unroll
-  for (int k = 0; k < 7; ++k) idx += (y >= cb.thresholds[k]) ? 1 : 0;
+  for (int k = 0; k < NT; ++k) idx += (y >= cb.thresholds[k]) ? 1 : 0;
   return idx;
+}
+
+// c[idx] for a code of up to 4 bits (not on a hot path).
+__device__ inline float level_any(const Codebook &cb, int idx) {
+  float r = cb.levels[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) r = idx == k ? cb.levels[k] : r;
+  return r;
 }
 
 // Page offsets are split as t = 64 b + 16 tau + 4 k + r (b: 64-token block;
@@ -138,15 +148,49 @@ __host__ __device__ inline int side_entry(int t) {
   return (t & ~63) | ((t & 12) << 2) | ((t & 3) << 2) | ((t >> 4) & 3);
 }
 
-// V code bits: bit j of the code of coordinate i = 16 (2 kp + h) + n of token
-// t is bit 8 r + 4 h + tau of u32 word b*6D + j*2D + (16 k + n)*(D/32) + kp.
-// One lane of the decode kernel (k, n) reads its D/32 words of a plane as one
-// contiguous run, and the words of one plane and block are contiguous.
-template <int D>
+// V code bits (VB-bit codes): bit j of the code of coordinate i = 16 (2 kp + h)
+// + n of token t is bit 8 r + 4 h + tau of u32 word
+// b*2*VB*D + j*2D + (16 k + n)*(D/32) + kp. One lane of the decode kernel
+// (k, n) reads its D/32 words of a plane as one contiguous run, and the words
+// of one plane and block are contiguous.
+template <int D, int VB = 3>
 __device__ inline int v_word(int t, int i, int j) {
-  return (t >> 6) * 6 * D + j * 2 * D + (16 * ((t >> 2) & 3) + (i & 15)) * (D / 32) + (i >> 5);
+  return (t >> 6) * 2 * VB * D + j * 2 * D + (16 * ((t >> 2) & 3) + (i & 15)) * (D / 32) + (i >> 5);
+}
+__device__ inline int v_word_rt(int t, int i, int j, int d, int vb) {
+  return (t >> 6) * 2 * vb * d + j * 2 * d + (16 * ((t >> 2) & 3) + (i & 15)) * (d / 32) + (i >> 5);
 }
 __device__ inline int v_bit(int t, int i) { return 8 * (t & 3) + 4 * ((i >> 4) & 1) + ((t >> 4) & 3); }
+
+// Bit planes of VB-bit codes for an odd codebook (c[n-1-k] = -c[k]): the odd
+// Walsh functions of the code bits, i.e. the parities of the bit subsets of odd
+// size, as masks. c[idx] = sum_p w_p parity(idx & mask_p) - c[n-1], with
+// w_p = -2 a_p and a_p the Walsh coefficient 2^-VB sum_idx c[idx] (-1)^popc(idx & mask_p).
+template <int VB> struct VPlanes;
+template <> struct VPlanes<2> {
+  static constexpr int n = 2;
+  static constexpr int mask[2] = {1, 2};
+};
+template <> struct VPlanes<3> {
+  static constexpr int n = 4;
+  static constexpr int mask[4] = {1, 2, 4, 7};
+};
+template <> struct VPlanes<4> {
+  static constexpr int n = 8;
+  static constexpr int mask[8] = {1, 2, 4, 8, 7, 11, 13, 14};
+};
+
+template <int VB>
+__device__ inline void v_plane_weights(const Codebook &cb, float (&w)[VPlanes<VB>::n]) {
+#pragma unroll
+  for (int p = 0; p < VPlanes<VB>::n; ++p) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < (1 << VB); ++i)
+      a += (__builtin_popcount(i & VPlanes<VB>::mask[p]) & 1) ? -cb.levels[i] : cb.levels[i];
+    w[p] = -2.f * a / (float)(1 << VB);
+  }
+}
 
 // Weights of the odd-codebook bit planes: c[idx] = sum_j 2 a_j plane_j - c7 with
 // planes (b0, b1, b2, b0^b1^b2).

@@ -12,9 +12,9 @@ namespace {
 
 constexpr int kWaves = 4;      // waves per workgroup
 
-// Steps 1-3 for one vector: norm, rotation, codes. Returns y (rotated, unit
-// norm) in y[], the codes in idx[] and the norm.
-template <int D, int DT>
+// Steps 1-3 for one vector: norm, rotation, codes (NT thresholds). Returns y
+// (rotated, unit norm) in y[], the codes in idx[] and the norm.
+template <int D, int DT, int NT = 7>
 __device__ inline float encode_front(const void *x, size_t base, const Codebook &cb,
                                      float (&y)[D / 64], int (&idx)[D / 64]) {
   constexpr int R = D / 64;
@@ -34,7 +34,7 @@ __device__ inline float encode_front(const void *x, size_t base, const Codebook 
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     y[r] *= rsqrt_dim<D>();
-    idx[r] = quantize_code(cb, y[r]);
+    idx[r] = quantize_code<NT>(cb, y[r]);
   }
   return n;
 }
@@ -184,13 +184,13 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
 // words are assembled and stored whole (coalesced, no atomics). Otherwise each
 // token's bits are set one by one with atomics, which leaves the neighbours in
 // the same words intact.
-template <int D, int DT, int VPW>
+template <int D, int DT, int VPW, int VBITS>
 __device__ void encode_v_block(const EncodeArgs &a, int bx, int head) {
   constexpr int R = D / 64;
   constexpr int VB = kWaves * VPW;   // tokens per workgroup: 64 (whole blocks possible) or 4
-  constexpr size_t VSEC = (size_t)3 * D * kPage / 8 + 2 * kPage;
-  constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
-  __shared__ uint64_t s_code[VB][3][R];
+  constexpr size_t VCODES = (size_t)VBITS * D * kPage / 8;
+  constexpr size_t VSEC = VCODES + 2 * kPage;
+  __shared__ uint64_t s_code[VB][VBITS][R];
   __shared__ float s_n[VB];
   __shared__ int s_whole;
 
@@ -208,11 +208,12 @@ __device__ void encode_v_block(const EncodeArgs &a, int bx, int head) {
   for (int u = wave; u < nt; u += kWaves) {
     float y[R];
     int idx[R];
-    const float n = encode_front<D, DT>(a.x, ((size_t)(t0 + u) * a.n_heads + head) * D, a.cb, y, idx);
+    const float n = encode_front<D, DT, (1 << VBITS) - 1>(a.x, ((size_t)(t0 + u) * a.n_heads + head) * D,
+                                                          a.cb, y, idx);
 #pragma unroll
     for (int k = 0; k < R; ++k)
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
+      for (int j = 0; j < VBITS; ++j) {
         const uint64_t m = __ballot((idx[k] >> j) & 1);
         if (lane == 0) s_code[u][j][k] = m;
       }
@@ -224,10 +225,10 @@ __device__ void encode_v_block(const EncodeArgs &a, int bx, int head) {
     const int s0 = a.slots[t0];
     uint8_t *sec = a.pool + ((size_t)(s0 / kPage) * a.n_heads + head) * VSEC;
     const int bofs = s0 % kPage;   // offset of the block in the page (a multiple of 64)
-    uint32_t *words = reinterpret_cast<uint32_t *>(sec) + (bofs >> 6) * 6 * D;
+    uint32_t *words = reinterpret_cast<uint32_t *>(sec) + (bofs >> 6) * 2 * VBITS * D;
     // word e = j*2D + (16 k + n)*(D/32) + kp; bit 8 r + 4 h + tau <- token 16 tau + 4 k + r,
     // coordinate 32 kp + 16 h + n (both coordinates in the same 64-bit ballot)
-    for (int e = threadIdx.x; e < 6 * D; e += 256) {
+    for (int e = threadIdx.x; e < 2 * VBITS * D; e += 256) {
       const int j = e / (2 * D), rem = e % (2 * D);
       const int c = rem / (D / 32), kp = rem % (D / 32);
       const int k = c >> 4, n = c & 15;
@@ -259,8 +260,8 @@ __device__ void encode_v_block(const EncodeArgs &a, int bx, int head) {
       const int i = lane + 64 * k;
       const uint32_t bit = 1u << v_bit(off, i);
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
-        uint32_t *w = rows + v_word<D>(off, i, j);
+      for (int j = 0; j < VBITS; ++j) {
+        uint32_t *w = rows + v_word<D, VBITS>(off, i, j);
         if ((s_code[u][j][k] >> lane) & 1)
           atomicOr(w, bit);
         else
@@ -276,9 +277,9 @@ __global__ __launch_bounds__(256) void encode_k_kernel(EncodeArgs a) {
   encode_k_block<D, DT, VPW>(a, blockIdx.x);
 }
 
-template <int D, int DT, int VPW>
+template <int D, int DT, int VPW, int VBITS>
 __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
-  encode_v_block<D, DT, VPW>(a, blockIdx.x, blockIdx.y);
+  encode_v_block<D, DT, VPW, VBITS>(a, blockIdx.x, blockIdx.y);
 }
 
 // ------------------------------------------------------------------ prepare
@@ -491,7 +492,13 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(StepArgs s) {
   }
   id -= s.nk;
   if (id < s.nv) {
-    encode_v_block<D, DT, 1>(s.v, id % s.nvx, id / s.nvx);
+    // the V code width is uniform over the launch
+    if (s.v.bits == 2)
+      encode_v_block<D, DT, 1, 2>(s.v, id % s.nvx, id / s.nvx);
+    else if (s.v.bits == 4)
+      encode_v_block<D, DT, 1, 4>(s.v, id % s.nvx, id / s.nvx);
+    else
+      encode_v_block<D, DT, 1, 3>(s.v, id % s.nvx, id / s.nvx);
     return;
   }
   id -= s.nv;
@@ -504,8 +511,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
   constexpr int R = D / 64;
   constexpr size_t KSEC = (size_t)kPage * D / 2 + 4 * kPage;
   constexpr size_t KCODES = (size_t)kPage * D / 2;
-  constexpr size_t VSEC = (size_t)3 * D * kPage / 8 + 2 * kPage;
-  constexpr size_t VCODES = (size_t)3 * D * kPage / 8;
+  const size_t VCODES = (size_t)a.bits * D * kPage / 8;   // V: a.bits-bit codes
+  const size_t VSEC = VCODES + 2 * kPage;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const long vec = (long)blockIdx.x * kWaves + wave;
   if (vec >= (long)a.n_tokens * a.n_heads) return;
@@ -550,9 +557,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
     for (int r = 0; r < R; ++r) {
       const int i = lane + 64 * r, bit = v_bit(off, i);
       int idx = 0;
-#pragma unroll
-      for (int j = 0; j < 3; ++j) idx |= ((rows[v_word<D>(off, i, j)] >> bit) & 1) << j;
-      v[r] = level_of(a.cb, idx);
+      for (int j = 0; j < a.bits; ++j) idx |= ((rows[v_word_rt(off, i, j, D, a.bits)] >> bit) & 1) << j;
+      v[r] = level_any(a.cb, idx);
     }
     scale = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + VCODES)[side_entry(off)]);
   }
@@ -594,13 +600,21 @@ hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
 hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s) {
   const long total = (long)a.n_tokens * a.n_heads;
   return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
-    if (total < 4096) {
-      const dim3 grid((unsigned)((a.n_tokens + kWaves - 1) / kWaves), (unsigned)a.n_heads);
-      hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 1>), grid, dim3(256), 0, s, a);
-    } else {
-      const dim3 grid((unsigned)((a.n_tokens + 63) / 64), (unsigned)a.n_heads);
-      hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 16>), grid, dim3(256), 0, s, a);
-    }
+    auto go = [&](auto VBITS) {
+      if (total < 4096) {
+        const dim3 grid((unsigned)((a.n_tokens + kWaves - 1) / kWaves), (unsigned)a.n_heads);
+        hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 1, VBITS.value>), grid, dim3(256), 0, s, a);
+      } else {
+        const dim3 grid((unsigned)((a.n_tokens + 63) / 64), (unsigned)a.n_heads);
+        hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 16, VBITS.value>), grid, dim3(256), 0, s, a);
+      }
+    };
+    if (a.bits == 2)
+      go(std::integral_constant<int, 2>{});
+    else if (a.bits == 4)
+      go(std::integral_constant<int, 4>{});
+    else
+      go(std::integral_constant<int, 3>{});
     return hipGetLastError();
   });
 }

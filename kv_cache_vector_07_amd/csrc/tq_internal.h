@@ -11,13 +11,17 @@ namespace tq {
 
 constexpr int kPage = TQ_PAGE_SIZE;
 
+// Levels and thresholds of one codebook: 2^bits and 2^bits - 1 entries used
+// (K: 3 bits; V: 2, 3 or 4).
 struct Codebook {
-  float levels[8];
-  float thresholds[7];
+  float levels[16];
+  float thresholds[15];
 };
 
 inline size_t k_section_bytes(int d) { return (size_t)kPage * d / 2 + 4u * kPage; }
-inline size_t v_section_bytes(int d) { return (size_t)3 * d * kPage / 8 + 2u * kPage; }
+inline size_t v_section_bytes(int d, int vbits = 3) {
+  return (size_t)vbits * d * kPage / 8 + 2u * kPage;
+}
 
 struct EncodeArgs {
   const void *x;          // [n_tokens][H][d], float32 or bfloat16
@@ -27,7 +31,8 @@ struct EncodeArgs {
   int n_heads;
   uint8_t *pool;          // K or V pool
   const float *qjl;       // S [d][d] (K only)
-  Codebook cb;
+  Codebook cb;            // the codebook of what is encoded
+  int bits;               // V code width (2, 3 or 4); K codes are 3-bit
 };
 
 struct DequantArgs {
@@ -38,7 +43,8 @@ struct DequantArgs {
   int with_qjl;
   const float *qjl;
   float *out;             // [n_tokens][H][d]
-  Codebook cb;
+  Codebook cb;            // K or V codebook
+  int bits;               // V code width (V only)
 };
 
 // Query preparation for one decode call: rotation, QJL projection and, for
@@ -112,7 +118,9 @@ struct DecodeArgs {
   int causal_tail;
   float scale;
   DecodePlan plan;
-  Codebook cb;
+  Codebook cb;            // K
+  Codebook vcb;           // V, v_bits wide
+  int v_bits;
 };
 
 DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages);

@@ -21,7 +21,8 @@ TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2
 TQ_F32, TQ_BF16 = 0, 1
 TQ_PAGE_SIZE = 256
 TQ_MAX_GROUP = 4096
-EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_build_codebook", "tq_build_codebook_sphere",
+EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_v_page_bytes_bits", "tq_build_codebook",
+           "tq_build_codebook_sphere",
            "tq_encode_k",
            "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_window",
            "tq_append_decode",
@@ -40,7 +41,8 @@ class TqCacheDesc(C.Structure):
     _fields_ = [("head_dim", C.c_int32), ("n_kv_heads", C.c_int32), ("page_size", C.c_int32),
                 ("n_pages", C.c_int32), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
                 ("qjl", C.c_void_p), ("levels", C.c_float * 8), ("thresholds", C.c_float * 7),
-                ("k_mse_only", C.c_int32)]
+                ("k_mse_only", C.c_int32), ("v_bits", C.c_int32), ("v_levels", C.c_float * 16),
+                ("v_thresholds", C.c_float * 15)]
 
 
 def lib():
@@ -57,6 +59,8 @@ def lib():
     L.tq_k_page_bytes.restype = sz
     L.tq_v_page_bytes.argtypes = [i32, i32]
     L.tq_v_page_bytes.restype = sz
+    L.tq_v_page_bytes_bits.argtypes = [i32, i32, i32]
+    L.tq_v_page_bytes_bits.restype = sz
     L.tq_status_string.argtypes = [i32]
     L.tq_status_string.restype = C.c_char_p
     L.tq_build_codebook.argtypes = [i32, i32, C.c_uint64, vp, vp, vp]
@@ -116,17 +120,18 @@ def tq_k_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE) -> int:
     return int(lib().tq_k_page_bytes(head_dim, page_size))
 
 
-def tq_v_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE) -> int:
-    return int(lib().tq_v_page_bytes(head_dim, page_size))
+def tq_v_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE, bits: int = 3) -> int:
+    return int(lib().tq_v_page_bytes_bits(head_dim, page_size, bits))
 
 
 def tq_build_codebook(head_dim: int, bits: int = 3, qjl_seed: int = 12345, with_qjl: bool = True,
                       density: str = "gaussian"):
-    """Host-only: (levels float32[8], thresholds float32[7], S float32[d][d] or None).
-    density "gaussian" fits N(0, 1/d); "sphere" the exact law of a coordinate of
-    a uniform unit vector (tq_build_codebook_sphere)."""
-    levels = np.zeros(8, np.float32)
-    thr = np.zeros(7, np.float32)
+    """Host-only: (levels float32[2^bits], thresholds float32[2^bits - 1], S float32[d][d]
+    or None). density "gaussian" fits N(0, 1/d); "sphere" the exact law of a
+    coordinate of a uniform unit vector (tq_build_codebook_sphere)."""
+    n = 1 << bits if 2 <= bits <= 4 else 16
+    levels = np.zeros(n, np.float32)
+    thr = np.zeros(n - 1, np.float32)
     S = np.zeros((head_dim, head_dim), np.float32) if with_qjl and head_dim > 0 else None
     fn = {"gaussian": "tq_build_codebook", "sphere": "tq_build_codebook_sphere"}[density]
     st = getattr(lib(), fn)(head_dim, bits, qjl_seed, levels.ctypes.data, thr.ctypes.data,
@@ -140,21 +145,35 @@ class Cache:
     the descriptor passed to every call. Pools are allocated with torch."""
 
     def __init__(self, head_dim: int, n_kv_heads: int, n_pages: int, qjl_seed: int = 12345,
-                 device="cuda", codebook=None, zero: bool = True, k_mse_only: bool = False):
+                 device="cuda", codebook=None, zero: bool = True, k_mse_only: bool = False,
+                 v_bits: int = 3, v_codebook=None):
         import torch
         self.head_dim, self.n_kv_heads, self.n_pages = head_dim, n_kv_heads, n_pages
         self.page_size = TQ_PAGE_SIZE
         levels, thr, S = codebook if codebook is not None else tq_build_codebook(head_dim, 3, qjl_seed)
         self.levels, self.thresholds, self.qjl_host = levels, thr, S
-        kpb, vpb = tq_k_page_bytes(head_dim), tq_v_page_bytes(head_dim)
+        # V codes of v_bits bits: 3 shares the K codebook; 2 and 4 bring their own
+        self.v_bits = int(v_bits)
+        if self.v_bits == 3:
+            vlev, vthr = levels, thr
+        else:
+            vlev, vthr = (v_codebook if v_codebook is not None
+                          else tq_build_codebook(head_dim, self.v_bits, qjl_seed, with_qjl=False)[:2])
+        self.v_levels, self.v_thresholds = vlev, vthr
+        kpb, vpb = tq_k_page_bytes(head_dim), tq_v_page_bytes(head_dim, bits=self.v_bits)
         alloc = torch.zeros if zero else torch.empty
         self.k_pool = alloc(n_pages * n_kv_heads * kpb, dtype=torch.uint8, device=device)
         self.v_pool = alloc(n_pages * n_kv_heads * vpb, dtype=torch.uint8, device=device)
         self.qjl = torch.from_numpy(S).to(device)
+        vl = np.zeros(16, np.float32)
+        vt = np.zeros(15, np.float32)
+        vl[:len(vlev)] = vlev
+        vt[:len(vthr)] = vthr
         self.desc = TqCacheDesc(head_dim, n_kv_heads, self.page_size, n_pages,
                                 self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.qjl.data_ptr(),
                                 (C.c_float * 8)(*levels.tolist()), (C.c_float * 7)(*thr.tolist()),
-                                int(k_mse_only))
+                                int(k_mse_only), self.v_bits, (C.c_float * 16)(*vl.tolist()),
+                                (C.c_float * 15)(*vt.tolist()))
         self.k_mse_only = bool(k_mse_only)
         self._ws = None
 

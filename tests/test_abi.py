@@ -54,8 +54,9 @@ def test_host_codebook_matches_reference_bitwise(L, d):
 
 
 def test_codebook_errors(L):
-    lv, th = np.zeros(8, np.float32), np.zeros(7, np.float32)
-    assert L.tq_build_codebook(128, 4, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EUNSUPPORTED
+    lv, th = np.zeros(16, np.float32), np.zeros(15, np.float32)
+    assert L.tq_build_codebook(128, 5, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_build_codebook(128, 1, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EUNSUPPORTED
     assert L.tq_build_codebook(100, 3, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EINVAL
     assert L.tq_build_codebook(128, 3, 1, None, th.ctypes.data, None) == tq.TQ_EINVAL
     assert L.tq_status_string(tq.TQ_EWORKSPACE) == b"workspace too small"
@@ -214,9 +215,9 @@ def test_host_sphere_codebook_matches_reference_bitwise(L, d):
     assert np.array_equal(levels.astype(np.float64), cb.levels)
     assert np.array_equal(thr.astype(np.float64), cb.thresholds)
     assert np.array_equal(S, O.qjl_matrix(d, 777))
-    lv, th = np.zeros(8, np.float32), np.zeros(7, np.float32)
+    lv, th = np.zeros(16, np.float32), np.zeros(15, np.float32)
     assert L.tq_build_codebook_sphere(2, 3, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EINVAL
-    assert L.tq_build_codebook_sphere(128, 2, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EUNSUPPORTED
+    assert L.tq_build_codebook_sphere(128, 5, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EUNSUPPORTED
     assert L.tq_build_codebook_sphere(96, 3, 1, lv.ctypes.data, th.ctypes.data, None) == tq.TQ_EINVAL
 
 
@@ -237,3 +238,37 @@ def test_mse_only_keys_validation(L):
     assert L.tq_encode_v(C.byref(dsc), FAKE, 1, FAKE, 4, None) == tq.TQ_EINVAL
     prep = C.c_size_t(0)
     assert L.tq_query_prepare(C.byref(dsc), FAKE, 0, 2, 1, 8, None, C.byref(prep), None) == tq.TQ_EINVAL
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("density", ["gaussian", "sphere"])
+def test_host_codebooks_of_other_widths_match_reference(L, bits, density):
+    for d in (128, 256):
+        levels, thr, _ = tq.tq_build_codebook(d, bits, 1, with_qjl=False, density=density)
+        cb = O.codebook(d, bits, density=density)
+        assert len(levels) == 1 << bits
+        assert np.array_equal(levels.astype(np.float64), cb.levels)
+        assert np.array_equal(thr.astype(np.float64), cb.thresholds)
+
+
+def test_v_widths_page_bytes_and_validation(L):
+    for d in (128, 256):
+        for b in (2, 3, 4):
+            assert tq.tq_v_page_bytes(d, bits=b) == O.v_page_bytes(d, 256, b)
+        assert L.tq_v_page_bytes_bits(d, 256, 5) == 0 and L.tq_v_page_bytes_bits(d, 256, 1) == 0
+    assert tq.tq_v_page_bytes(128) == L.tq_v_page_bytes(128, 256)
+    dsc = _desc(H=2)
+    sz = C.c_size_t(0)
+    decode = lambda: L.tq_attn_decode(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE,
+                                      None, C.byref(sz), None)
+    assert decode() == tq.TQ_OK
+    dsc.v_bits = 5
+    assert decode() == tq.TQ_EINVAL
+    dsc.v_bits = 2                                   # v_levels still zero: not increasing
+    assert decode() == tq.TQ_EINVAL
+    lv, _, _ = tq.tq_build_codebook(128, 2, 1, with_qjl=False)
+    for k in range(4):
+        dsc.v_levels[k] = float(lv[k])
+    assert decode() == tq.TQ_OK
+    dsc.v_levels[0] = float(lv[0]) * 1.01           # no longer odd
+    assert decode() == tq.TQ_EINVAL

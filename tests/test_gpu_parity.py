@@ -519,6 +519,62 @@ def test_mse_only_keys_encode_and_decode(tq, d):
     assert err <= Hn.ATTN_TOL
 
 
+@pytest.mark.parametrize("d,vb", [(128, 2), (128, 4), (256, 2), (256, 4)])
+def test_v_code_widths(tq, d, vb):
+    """V codes of 2 and 4 bits (v_bits): the encode's codes and norms against the
+    reference with the 4- or 16-level codebook (whole 64-token blocks and single
+    tokens), dequant, the fused append step, and attention for one query row
+    group, for two groups per workgroup (16 rows) and with the causal tail."""
+    H, lens = 8, np.array([700, 300])
+    print(f"[v bits] d={d} vb={vb}", flush=True)
+    w = I.Workload(f"vb{d}{vb}", len(lens), 32, H, d, "bf16", "outlier", 70 + vb, n_q=4, fixed_len=1)
+    table, n_pages = I.page_table(w, lens, extra_tokens=1, shuffle=True)
+    cache = tq.Cache(d, H, n_pages, v_bits=vb)
+    cb = Hn.codebook_from_cache(cache)
+    cbv = O.codebook(d, vb)
+    assert np.array_equal(cache.v_levels.astype(np.float64), cbv.levels)
+    bt = torch.from_numpy(table).cuda()
+    for b, L in enumerate(lens):
+        t = np.arange(L)
+        slots = (table[b][t // 256].astype(np.int64) * 256 + t % 256).astype(np.int32)
+        ts = torch.from_numpy(slots).cuda()
+        k = I.kv_tokens(w, "k", b, 0, L)
+        v = I.kv_tokens(w, "v", b, 0, L)
+        tq.tq_encode_k(cache, Hn.torch_input(k, "bf16"), ts)
+        tq.tq_encode_v(cache, Hn.torch_input(v, "bf16"), ts)   # 700 x 8 vectors: whole blocks
+        torch.cuda.synchronize()
+        vp = cache.v_pool.cpu().numpy()
+        rv = Hn.compare_encode_v(O.unpack_v(vp, slots, H, d, 256, vb), v.astype(np.float64), cbv)
+        print(f"  seq {b}: V {rv}", flush=True)
+        if b == 0:
+            uv = O.unpack_v(vp, slots, H, d, 256, vb)
+            got = tq.tq_dequant(cache, 1, 0, ts).cpu().numpy()
+            ref = O.dequant_v(uv["idx"], uv["N"], cbv)
+            assert np.max(np.abs(got - ref) / np.max(np.abs(ref), axis=-1, keepdims=True)) < 1e-5
+    # one appended token per sequence through the fused step (single-token V encode)
+    pos = lens.copy()
+    aslots = torch.from_numpy((table[np.arange(2), pos // 256].astype(np.int64) * 256 + pos % 256)
+                              .astype(np.int32)).cuda()
+    nk = np.concatenate([I.kv_tokens(w, "k", b, int(L), int(L) + 1) for b, L in enumerate(lens)])
+    nv = np.concatenate([I.kv_tokens(w, "v", b, int(L), int(L) + 1) for b, L in enumerate(lens)])
+    lens1 = lens + 1
+    sl = torch.from_numpy(lens1.astype(np.int32)).cuda()
+    q1 = I.queries(w, 0)[:, :1].copy()                     # 4 rows per KV head
+    out1 = tq.tq_append_decode(cache, Hn.torch_input(nk, "bf16"), Hn.torch_input(nv, "bf16"), aslots,
+                               Hn.torch_input(q1, "bf16"), bt, sl)
+    q4 = I.queries(w, 1)                                     # 16 rows, causal tail
+    out4 = tq.tq_attn_decode(cache, Hn.torch_input(q4, "bf16"), bt, sl, causal_tail=1)
+    torch.cuda.synchronize()
+    kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+    Hn.compare_encode_v(O.unpack_v(vp, aslots.cpu().numpy(), H, d, 256, vb), nv.astype(np.float64), cbv)
+    for q, out, causal in ((q1, out1, False), (q4, out4, True)):
+        ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens1, H, 256,
+                            Hn.scale_of(d), causal_tail=causal, cb_v=cbv, v_bits=vb)
+        err = Hn.attn_rel_err(out.cpu().numpy(), ref)
+        print(f"  rows {q.shape[1] * 4} causal {causal}: max rel err {err:.3e}", flush=True)
+        assert err <= Hn.ATTN_TOL
+
+
 WIN_CASES = [
     # (d, Hkv, Hq, n_q, lens, starts, causal, seed)
     # mid-page, page-aligned, the last token only, a start past the length (zero rows)
