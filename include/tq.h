@@ -165,8 +165,10 @@ int tq_encode_k(const tq_cache *c, const void *k, int32_t dtype,
 
 /*
  * V encode ("V-Cache圧縮"): steps 1-3 of the K flow, then the V record and
- * N = fp16(n). Bits of other tokens sharing the same V rows are preserved
- * (the rows are updated with per-bit atomics). Same arguments and errors as
+ * N = fp16(n). The codes have tq_cache.v_bits bits (3 by default, with the K
+ * codebook; 2 or 4 with v_levels / v_thresholds). Bits of other tokens sharing
+ * the same V rows are preserved (whole aligned 64-token blocks are written
+ * whole, other tokens bit by bit with atomics). Same arguments and errors as
  * tq_encode_k.
  */
 int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype,
@@ -309,7 +311,7 @@ int tq_dense_attn_decode(const void *k, const void *v, int32_t head_dim, int32_t
  * Dequantise records back to the original domain (float32 [n_tokens][Hkv][d]):
  *   which = 0 (K): N * Pi(c[code] + sqrt(pi/2)/m * G * S^T sigma)  (with_qjl = 1)
  *                  N * Pi c[code]                                    (with_qjl = 0)
- *   which = 1 (V): N * Pi c[code]
+ *   which = 1 (V): N * Pi c_V[code]   (the V codebook and code width)
  * so that <q, K_tilde_j> equals the attention score estimate of token j.
  * Errors: TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EHIP.
  */

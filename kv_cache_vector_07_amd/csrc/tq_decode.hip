@@ -12,9 +12,9 @@
 // whole 256-token pages of one (sequence, KV head) for the query rows of one or
 // two query groups (4 rows each), keeps an online softmax, and writes (max, sum,
 // V numerator) partials; a second, small kernel merges the partials of each
-// query row by log-sum-exp and writes float32 rows. (Merging in the last-arriving workgroup would need a device-scope
-// release per workgroup, which on this GPU writes back and invalidates the whole
-// L2 of the XCD every time.)
+// query row by log-sum-exp and writes float32 rows. (Merging in the
+// last-arriving workgroup would need a device-scope release per workgroup, which
+// on this GPU writes back and invalidates the whole L2 of the XCD every time.)
 //
 // Scores are a block-scaled fp6 x fp4 MFMA contraction. The codebook is odd
 // (c[7-k] = -c[k]), so the 3-bit code splits over four binary planes,
@@ -25,7 +25,9 @@
 // per query group), exact to under 2^-18 of the largest term of each block. V is
 // accumulated with the same planes on int8 MFMA: the softmax weight times each
 // plane weight, as four int8 limbs, against the V bit planes; every product there
-// is exact in int32.
+// is exact in int32. V codes may also have 2 or 4 bits (a bit-width variant):
+// their planes are the odd Walsh functions of the code bits (b0, b1; or the four
+// bits and their four 3-bit parities), taken one plane at a time.
 #include "tq_device.h"
 
 namespace tq {
@@ -92,7 +94,8 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // tokens x 2 coordinates per u32 word, and a shift plus one AND per 4 tokens
 // makes the B operand. The int32 sums are folded into a float accumulator
 // after every block, or (one query group at d = 256) only when the softmax
-// reference moves, and once at the end.
+// reference moves, and once at the end. (Folding only at a rescale also fits at
+// d = 128 but measured slower there.)
 //
 // Up to TQ_MAX_GROUP query rows per KV head (a few for decode and verify, a
 // whole chunk's for chunked prefill) run as query groups of 4 rows (4 rows x 4
@@ -209,10 +212,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   }
   // V sums: int32 MFMA accumulators folded into a float accumulator. With one
   // group at d = 256 they are folded only when the softmax reference moves and
-  // at the end (per 64-token block a limb row gains at most 4 planes x 64
-  // tokens x 128 x 8 = 2^18, so up to 2^13 blocks, far more than one split
-  // holds, fit in int32); otherwise the registers for that are not free, so
-  // they are folded after every block.
+  // at the end (per 64-token block a limb row gains at most NP <= 8 planes x 64
+  // tokens x 128 x 8 = 2^19, so up to 2^12 blocks, far more than the 256 blocks
+  // a wave sees in one split, fit in int32); otherwise they are folded after
+  // every block.
   constexpr bool kLazyV = D == 256 && NG == 1;
   float facc[NG][NB];
   v4i vacc[NG][NB];
