@@ -40,8 +40,9 @@ notes; the ones that shape arithmetic are restated where they are used:
       coordinate of a uniform unit vector in R^d, whose large-d limit is R4's.
   R26 (variant) keys may skip the QJL stage: the record keeps codes, N and G,
       its sign plane is zero, and the score keeps only the codebook term.
-  R27 (variant) V codes may have 2 or 4 bits (4 or 16 Lloyd-Max levels of the
-      same density), stored as that many bit planes.
+  R27 (variant) K and V codes may have 2 or 4 bits (4 or 16 Lloyd-Max levels of
+      the same density), stored as that many bit planes (K: kb + 1 words per 32
+      coordinates, the signs last).
 """
 
 from __future__ import annotations
@@ -352,11 +353,11 @@ def encode_k_mse_only(x, cb: Codebook) -> dict:
 # Packed page layout (frozen format of this library; not given by the pages)
 #   Offsets t within a page are split as t = 64 b + 16 tau + 4 k + r
 #   (b = 64-token block, tau, k, r = 0..3).
-#   K section of one (page, kv-head), P tokens:
-#     token t record (d/2 bytes) at t*d/2: for group s = 0..d/32-1 four
-#     little-endian u32 words [code bit0, code bit1, code bit2, QJL sign];
+#   K section of one (page, kv-head), P tokens, kb-bit codes (kb = 3 by default):
+#     token t record ((kb+1) d/8 bytes) at t*(kb+1)*d/8: for group s = 0..d/32-1,
+#     kb + 1 little-endian u32 words [code bit0, ..., code bit kb-1, QJL sign];
 #     bit e of a word belongs to coordinate 32 s + e;
-#     then N[P] fp16 at P*d/2, then G[P] fp16 at P*d/2 + 2P, each array in
+#     then N[P] fp16 at P*(kb+1)*d/8, then G[P] fp16 2P bytes later, each array in
 #     side order: token t at entry 64 b + 16 k + 4 r + tau.
 #   V section of one (page, kv-head): code bits, then N[P] fp16 at 3*d*P/8 in
 #     side order. Code bits are little-endian u32 words; bit j of the code of
@@ -390,8 +391,9 @@ def _v_bit_table(d: int, P: int, vb: int = 3) -> np.ndarray:
     return (32 * word + bit).astype(np.int64)
 
 
-def k_page_bytes(d: int, P: int) -> int:
-    return P * d // 2 + 4 * P
+def k_page_bytes(d: int, P: int, kb: int = 3) -> int:
+    """K section of one (page, KV head) with kb-bit codes."""
+    return P * (kb + 1) * d // 8 + 4 * P
 
 
 def v_page_bytes(d: int, P: int, vb: int = 3) -> int:
@@ -399,22 +401,23 @@ def v_page_bytes(d: int, P: int, vb: int = 3) -> int:
     return vb * d * P // 8 + 2 * P
 
 
-def pack_k(pool: np.ndarray, slots, idx, sign, N, G, P: int) -> None:
-    """Write K records of tokens [n][H][d] into a uint8 pool at `slots`."""
+def pack_k(pool: np.ndarray, slots, idx, sign, N, G, P: int, kb: int = 3) -> None:
+    """Write kb-bit K records of tokens [n][H][d] into a uint8 pool at `slots`."""
     idx = np.asarray(idx, dtype=np.uint8)
     n, H, d = idx.shape
-    kpb = k_page_bytes(d, P)
+    kpb = k_page_bytes(d, P, kb)
+    rb = (kb + 1) * d // 8                                               # record bytes
     slots = np.asarray(slots, dtype=np.int64)
-    planes = np.stack([(idx >> 0) & 1, (idx >> 1) & 1, (idx >> 2) & 1,
-                       np.asarray(sign, dtype=np.uint8)], axis=2)      # [n][H][4][d]
-    planes = planes.reshape(n, H, 4, d // 32, 32).transpose(0, 1, 3, 2, 4)
-    rec = np.packbits(planes, axis=-1, bitorder="little").reshape(n, H, d // 2)
+    planes = np.stack([(idx >> j) & 1 for j in range(kb)] + [np.asarray(sign, dtype=np.uint8)],
+                      axis=2)                                            # [n][H][kb+1][d]
+    planes = planes.reshape(n, H, kb + 1, d // 32, 32).transpose(0, 1, 3, 2, 4)
+    rec = np.packbits(planes, axis=-1, bitorder="little").reshape(n, H, rb)
     page, off = slots // P, slots % P
     base = (page[:, None] * H + np.arange(H)[None, :]) * kpb             # [n][H]
-    pool[(base + off[:, None] * (d // 2))[..., None] + np.arange(d // 2)] = rec
+    pool[(base + off[:, None] * rb)[..., None] + np.arange(rb)] = rec
     nb = np.asarray(N, dtype=np.float16).reshape(n, H, 1).view(np.uint8)
     gb = np.asarray(G, dtype=np.float16).reshape(n, H, 1).view(np.uint8)
-    side = base + P * d // 2 + 2 * side_entry(off)[:, None]
+    side = base + P * rb + 2 * side_entry(off)[:, None]
     pool[side[..., None] + np.arange(2)] = nb
     pool[(side + 2 * P)[..., None] + np.arange(2)] = gb
 
@@ -442,21 +445,22 @@ def pack_v(pool: np.ndarray, slots, idx, N, P: int, vb: int = 3) -> None:
             pool[pos[:, None] + np.arange(2)] = nb
 
 
-def unpack_k(pool: np.ndarray, slots, H: int, d: int, P: int) -> dict:
-    """Read K records of `slots` for all heads: idx [n][H][d], sign, N, G."""
-    kpb = k_page_bytes(d, P)
+def unpack_k(pool: np.ndarray, slots, H: int, d: int, P: int, kb: int = 3) -> dict:
+    """Read kb-bit K records of `slots` for all heads: idx [n][H][d], sign, N, G."""
+    kpb = k_page_bytes(d, P, kb)
+    rb = (kb + 1) * d // 8
     slots = np.asarray(slots, dtype=np.int64)
     page, off = slots // P, slots % P
     base = (page[:, None] * H + np.arange(H)[None, :]) * kpb
-    rec = pool[(base + off[:, None] * (d // 2))[..., None] + np.arange(d // 2)]
-    bits = np.unpackbits(rec.reshape(len(slots), H, d // 32, 4, 4), axis=-1,
-                         bitorder="little")                                # [n][H][S][4][32]
-    bits = bits.transpose(0, 1, 3, 2, 4).reshape(len(slots), H, 4, d)
-    idx = bits[:, :, 0] | (bits[:, :, 1] << 1) | (bits[:, :, 2] << 2)
-    side = base + P * d // 2 + 2 * side_entry(off)[:, None]
+    rec = pool[(base + off[:, None] * rb)[..., None] + np.arange(rb)]
+    bits = np.unpackbits(rec.reshape(len(slots), H, d // 32, kb + 1, 4), axis=-1,
+                         bitorder="little")                                # [n][H][S][kb+1][32]
+    bits = bits.transpose(0, 1, 3, 2, 4).reshape(len(slots), H, kb + 1, d)
+    idx = sum(bits[:, :, j].astype(np.uint8) << j for j in range(kb))
+    side = base + P * rb + 2 * side_entry(off)[:, None]
     N = pool[side[..., None] + np.arange(2)].copy().view(np.float16)[..., 0]
     G = pool[(side + 2 * P)[..., None] + np.arange(2)].copy().view(np.float16)[..., 0]
-    return {"idx": idx.astype(np.uint8), "sign": bits[:, :, 3].astype(bool), "N": N, "G": G}
+    return {"idx": idx.astype(np.uint8), "sign": bits[:, :, kb].astype(bool), "N": N, "G": G}
 
 
 def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int, vb: int = 3) -> dict:
@@ -486,21 +490,22 @@ def _seq_slots(block_table_row, L: int, P: int) -> np.ndarray:
     return np.asarray(block_table_row, dtype=np.int64)[t // P] * P + t % P
 
 
-def gather_k(pool, block_table_row, L, kv_head, H, d, P):
-    """K records of tokens 0..L-1 of one sequence and one KV head."""
-    kpb = k_page_bytes(d, P)
+def gather_k(pool, block_table_row, L, kv_head, H, d, P, kb: int = 3):
+    """kb-bit K records of tokens 0..L-1 of one sequence and one KV head."""
+    kpb = k_page_bytes(d, P, kb)
+    rb = (kb + 1) * d // 8
     t = np.arange(L, dtype=np.int64)
     page = np.asarray(block_table_row, dtype=np.int64)[t // P]
     off = t % P
     base = (page * H + kv_head) * kpb
-    rec = pool[(base + off * (d // 2))[:, None] + np.arange(d // 2)]
-    bits = np.unpackbits(rec.reshape(L, d // 32, 4, 4), axis=-1, bitorder="little")
-    bits = bits.transpose(0, 2, 1, 3).reshape(L, 4, d)
-    idx = bits[:, 0] | (bits[:, 1] << 1) | (bits[:, 2] << 2)
-    side = base + P * d // 2 + 2 * side_entry(off)
+    rec = pool[(base + off * rb)[:, None] + np.arange(rb)]
+    bits = np.unpackbits(rec.reshape(L, d // 32, kb + 1, 4), axis=-1, bitorder="little")
+    bits = bits.transpose(0, 2, 1, 3).reshape(L, kb + 1, d)
+    idx = sum(bits[:, j].astype(np.uint8) << j for j in range(kb))
+    side = base + P * rb + 2 * side_entry(off)
     N = pool[side[:, None] + np.arange(2)].copy().view(np.float16)[:, 0]
     G = pool[(side + 2 * P)[:, None] + np.arange(2)].copy().view(np.float16)[:, 0]
-    return idx, bits[:, 3].astype(bool), N.astype(np.float64), G.astype(np.float64)
+    return idx, bits[:, kb].astype(bool), N.astype(np.float64), G.astype(np.float64)
 
 
 def gather_v(pool, block_table_row, L, kv_head, H, d, P, vb: int = 3):
@@ -540,7 +545,7 @@ def score(qt, p, idx, sign, N, G, cb: Codebook, m: int):
 def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
                 n_kv_heads: int, page_size: int, scale: float,
                 causal_tail: bool = False, pairs=None, seq_starts=None,
-                cb_v: Codebook | None = None, v_bits: int = 3) -> np.ndarray:
+                cb_v: Codebook | None = None, v_bits: int = 3, k_bits: int = 3) -> np.ndarray:
     """Naive two-pass softmax attention over the packed cache, float64.
 
     For query (b, t, h) with KV head h // (Hq/Hkv) (R15) and visible tokens
@@ -549,8 +554,9 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
       w = softmax_j(scale * score_j),  a = sum_j w_j N^V_j c[idxV_j],  o = Pi a.
     A row with no visible token is zero. Records of tokens before s_b are not
     read. `pairs` restricts the work to the listed (b, kv_head) pairs; other
-    rows stay zero. V records hold v_bits-bit codes of the codebook cb_v (cb
-    when None; R27). Returns out [B][n_q][Hq][d].
+    rows stay zero. K records hold k_bits-bit codes of cb; V records hold
+    v_bits-bit codes of the codebook cb_v (cb when None; R27). Returns
+    out [B][n_q][Hq][d].
     """
     q = np.asarray(q, dtype=np.float64)
     B, n_q, Hq, d = q.shape
@@ -570,7 +576,8 @@ def attn_decode(k_pool, v_pool, cb: Codebook, S, q, block_table, seq_lens,
         # the visible range starts on page s0 // P: earlier pages are not read
         p0 = s0 // page_size
         base = p0 * page_size
-        idx, sign, N, G = gather_k(k_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size)
+        idx, sign, N, G = gather_k(k_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size,
+                                   k_bits)
         vidx, NV = gather_v(v_pool, block_table[b][p0:], L - base, kvh, n_kv_heads, d, page_size,
                             v_bits)
         vals = NV[:, None] * (cb_v or cb).levels[vidx]                     # [L - base][d]

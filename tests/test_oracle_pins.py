@@ -362,6 +362,76 @@ def test_attention_with_other_v_widths_equals_dense_softmax(vb):
             assert np.max(np.abs(out[0, tq_, h] - w @ Vt[:vis, h // g])) < 1e-12
 
 
+@pytest.mark.parametrize("kb", [2, 4])
+def test_k_pack_unpack_other_widths(kb):
+    """kb-bit K records: round trip, untouched neighbours, the section size, and
+    the word order (kb code planes, then the signs, per 32 coordinates)."""
+    d, P, H = 128, 256, 2
+    rng = np.random.default_rng(30 + kb)
+    n = 200
+    slots = rng.choice(3 * P, size=n, replace=False)
+    idx = rng.integers(0, 1 << kb, (n, H, d)).astype(np.uint8)
+    sign = rng.integers(0, 2, (n, H, d)).astype(bool)
+    N = rng.standard_normal((n, H)).astype(np.float16)
+    G = rng.standard_normal((n, H)).astype(np.float16)
+    assert O.k_page_bytes(d, P, kb) == (kb + 1) * d * P // 8 + 4 * P
+    kp = rng.integers(0, 256, 3 * H * O.k_page_bytes(d, P, kb)).astype(np.uint8)
+    kp0 = kp.copy()
+    O.pack_k(kp, slots, idx, sign, N, G, P, kb)
+    u = O.unpack_k(kp, slots, H, d, P, kb)
+    assert np.array_equal(u["idx"], idx) and np.array_equal(u["sign"], sign)
+    assert np.array_equal(u["N"].view(np.uint16), N.view(np.uint16))
+    assert np.array_equal(u["G"].view(np.uint16), G.view(np.uint16))
+    others = np.setdiff1d(np.arange(3 * P), slots)[:50]
+    a, b = O.unpack_k(kp, others, H, d, P, kb), O.unpack_k(kp0, others, H, d, P, kb)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["sign"], b["sign"])
+    # one set bit: code bit j (or the sign) of coordinate 33 of token 1, head 0
+    for j in range(kb + 1):
+        z = np.zeros(3 * H * O.k_page_bytes(d, P, kb), np.uint8)
+        one = np.zeros((1, H, d), np.uint8)
+        sg = np.zeros((1, H, d), bool)
+        if j < kb:
+            one[0, 0, 33] = 1 << j
+        else:
+            sg[0, 0, 33] = True
+        O.pack_k(z, [1], one, sg, np.zeros((1, H), np.float16), np.zeros((1, H), np.float16), P, kb)
+        words = z[:(kb + 1) * d * P // 8].view("<u4")
+        rec_words = (kb + 1) * d // 32
+        assert np.flatnonzero(words).tolist() == [rec_words + (kb + 1) * 1 + j]
+        assert words[rec_words + (kb + 1) + j] == 2
+
+
+@pytest.mark.parametrize("kb", [2, 4])
+def test_attention_with_other_k_widths_equals_dense_softmax(kb):
+    """Attention over kb-bit K records with QJL (R27) is softmax attention over
+    the keys dequantised with the kb-bit codebook and the QJL term."""
+    d, H, P, L, g = 32, 2, 64, 150, 2
+    rng = np.random.default_rng(40 + kb)
+    cbk, cb = O.codebook(d, kb), O.codebook(d)
+    S = O.qjl_matrix(d, 4).astype(np.float64)
+    k = rng.standard_normal((L, H, d)) * 2
+    v = rng.standard_normal((L, H, d))
+    ek, ev = O.encode(k, cbk, S), O.encode(v, cb)
+    assert ek["idx"].max() == (1 << kb) - 1
+    npg = (L + P - 1) // P
+    table = np.arange(npg, dtype=np.int32)[::-1].copy()[None, :]
+    t = np.arange(L)
+    slots = table[0][t // P] * P + t % P
+    kp = np.zeros(npg * H * O.k_page_bytes(d, P, kb), np.uint8)
+    vp = np.zeros(npg * H * O.v_page_bytes(d, P), np.uint8)
+    O.pack_k(kp, slots, ek["idx"], ek["sign"], ek["N"], ek["G"], P, kb)
+    O.pack_v(vp, slots, ev["idx"], ev["N"], P)
+    q = rng.standard_normal((1, 1, H * g, d))
+    out = O.attn_decode(kp, vp, cbk, S, q, table, [L], H, P, 0.3, cb_v=cb, k_bits=kb)
+    Kt = O.dequant_k(ek["idx"], ek["sign"], ek["N"], ek["G"], cbk, S)
+    Vt = O.dequant_v(ev["idx"], ev["N"], cb)
+    for h in range(H * g):
+        lg = 0.3 * (Kt[:, h // g] @ q[0, 0, h])
+        w = np.exp(lg - lg.max())
+        w /= w.sum()
+        assert np.max(np.abs(out[0, 0, h] - w @ Vt[:, h // g])) < 1e-12
+
+
 # ---------------------------------------------------------------- attention
 def _small_cache(d=32, L=150, H=2, P=64, seed=0, nq=3, g=2, B=2):
     rng = np.random.default_rng(seed)
