@@ -49,6 +49,10 @@
  *     N (fp16) at byte 3*d*P/8 + 2*e(t).
  *   At d = 128 that is 544 bits per K vector (4.25 bits/dim) and 400 bits per V
  *   vector (3.125 bits/dim); at d = 256, 4.125 and 3.0625 bits/dim.
+ *   With kb-bit K codes (k_bits 2 or 4) a record has kb + 1 words per group
+ *   (kb code planes, then the signs), (kb + 1)*d/8 bytes, and N, G follow at
+ *   P*(kb + 1)*d/8; with vb-bit V codes a block holds vb planes, word
+ *   b*2*vb*d + j*2d + ..., and N at vb*d*P/8.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -107,6 +111,16 @@ typedef struct {
   float v_levels[16];   /* with v_bits 2 or 4: the first 2^v_bits entries,
                            strictly ascending and odd (else TQ_EINVAL)          */
   float v_thresholds[15]; /* with v_bits 2 or 4: the first 2^v_bits - 1         */
+  int32_t k_bits;       /* K code width. 0 or 3: 3-bit K with levels and
+                           thresholds above (the pages' 4.25 bits/dim). 2 or 4:
+                           K codes of that width with k_levels and k_thresholds
+                           (3.25 or 5.25 bits/dim at d = 128, the QJL signs
+                           kept); k_pool sections are then
+                           tq_k_page_bytes_bits(d, P, k_bits). Other values:
+                           TQ_EINVAL.                                           */
+  float k_levels[16];   /* with k_bits 2 or 4: the first 2^k_bits entries,
+                           strictly ascending and odd (else TQ_EINVAL)          */
+  float k_thresholds[15]; /* with k_bits 2 or 4: the first 2^k_bits - 1         */
 } tq_cache;
 
 /* Bytes of one (page, KV head) section; 0 for unsupported d or P. */
@@ -115,6 +129,10 @@ size_t tq_v_page_bytes(int32_t head_dim, int32_t page_size);
 /* V section for codes of `bits` bits (2, 3 or 4; 0 otherwise): bits planes of
  * d x P bits, then the fp16 norms. */
 size_t tq_v_page_bytes_bits(int32_t head_dim, int32_t page_size, int32_t bits);
+/* K section for codes of `bits` bits (2, 3 or 4; 0 otherwise): per token
+ * (bits + 1) * d / 8 bytes (bits code planes and the sign plane per 32
+ * coordinates), then the fp16 N and G arrays. */
+size_t tq_k_page_bytes_bits(int32_t head_dim, int32_t page_size, int32_t bits);
 
 /*
  * Lloyd-Max codebook and QJL matrix ("TurboQuant KVキャッシュ圧縮アーキテクチャ",

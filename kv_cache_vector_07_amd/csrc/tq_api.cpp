@@ -35,10 +35,29 @@ int check_cache(const tq_cache *c) {
   if (c->v_bits != 0 && c->v_bits != 2 && c->v_bits != 3 && c->v_bits != 4) return TQ_EINVAL;
   if ((c->v_bits == 2 || c->v_bits == 4) && !odd_increasing(c->v_levels, 1 << c->v_bits))
     return TQ_EINVAL;
+  if (c->k_bits != 0 && c->k_bits != 2 && c->k_bits != 3 && c->k_bits != 4) return TQ_EINVAL;
+  if ((c->k_bits == 2 || c->k_bits == 4) && !odd_increasing(c->k_levels, 1 << c->k_bits))
+    return TQ_EINVAL;
   return TQ_OK;
 }
 
+// K code width and codebook: 3-bit K uses levels / thresholds
+int k_bits_of(const tq_cache *c) { return (c->k_bits == 2 || c->k_bits == 4) ? c->k_bits : 3; }
 Codebook codebook_of(const tq_cache *c) {
+  Codebook cb = {};
+  if (k_bits_of(c) == 3) {
+    memcpy(cb.levels, c->levels, sizeof c->levels);
+    memcpy(cb.thresholds, c->thresholds, sizeof c->thresholds);
+  } else {
+    const int n = 1 << c->k_bits;
+    memcpy(cb.levels, c->k_levels, sizeof(float) * n);
+    memcpy(cb.thresholds, c->k_thresholds, sizeof(float) * (n - 1));
+  }
+  return cb;
+}
+
+// The 3-bit codebook in levels / thresholds (V at 3 bits uses it)
+Codebook codebook3_of(const tq_cache *c) {
   Codebook cb = {};
   memcpy(cb.levels, c->levels, sizeof c->levels);
   memcpy(cb.thresholds, c->thresholds, sizeof c->thresholds);
@@ -48,7 +67,7 @@ Codebook codebook_of(const tq_cache *c) {
 // V code width and codebook: 3-bit V shares the K codebook
 int v_bits_of(const tq_cache *c) { return (c->v_bits == 2 || c->v_bits == 4) ? c->v_bits : 3; }
 Codebook v_codebook_of(const tq_cache *c) {
-  if (v_bits_of(c) == 3) return codebook_of(c);
+  if (v_bits_of(c) == 3) return codebook3_of(c);
   Codebook cb = {};
   const int n = 1 << c->v_bits;
   memcpy(cb.levels, c->v_levels, sizeof(float) * n);
@@ -177,7 +196,8 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 namespace tq {
 
-DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages) {
+DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages,
+                       int kb) {
   DecodePlan p;
   p.group = n_q_heads / n_kv_heads * n_q;
   p.mfma = mfma_path(d, p.group);
@@ -198,7 +218,7 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
   p.counter_bytes = 0;
   p.partial_bytes =
       round_up((size_t)batch * n_kv_heads * p.n_split * p.group * (d + 4) * sizeof(float), 256);
-  p.prep_bytes = prep_region_bytes(d, batch, n_q, n_q_heads, n_kv_heads);
+  p.prep_bytes = prep_region_bytes(d, batch, n_q, n_q_heads, n_kv_heads, kb);
   return p;
 }
 
@@ -207,8 +227,13 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
 extern "C" {
 
 size_t tq_k_page_bytes(int32_t head_dim, int32_t page_size) {
+  return tq_k_page_bytes_bits(head_dim, page_size, 3);
+}
+
+size_t tq_k_page_bytes_bits(int32_t head_dim, int32_t page_size, int32_t bits) {
   if (head_dim <= 0 || head_dim % 32 || page_size <= 0 || page_size % 32) return 0;
-  return (size_t)page_size * head_dim / 2 + 4u * page_size;
+  if (bits < 2 || bits > 4) return 0;
+  return (size_t)page_size * (bits + 1) * head_dim / 8 + 4u * page_size;
 }
 
 size_t tq_v_page_bytes(int32_t head_dim, int32_t page_size) {
@@ -293,7 +318,7 @@ static int encode_common(const tq_cache *c, const void *x, int32_t dtype, const 
   a.pool = (uint8_t *)(is_k ? c->k_pool : c->v_pool);
   a.qjl = qjl_of(c);
   a.cb = is_k ? codebook_of(c) : v_codebook_of(c);
-  a.bits = is_k ? 3 : v_bits_of(c);
+  a.bits = is_k ? k_bits_of(c) : v_bits_of(c);
   hipStream_t s = (hipStream_t)stream;
   return hip_status(is_k ? tq::launch_encode_k(a, c->head_dim, s)
                          : tq::launch_encode_v(a, c->head_dim, s));
@@ -347,6 +372,7 @@ static hipError_t run_prepare(const tq_cache *c, const void *q, int32_t dtype, i
   const bool mfma = tq::mfma_path(c->head_dim, n_q_heads / c->n_kv_heads * n_q);
   a.packed = mfma ? prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads) : nullptr;
   a.cb = codebook_of(c);
+  a.k_bits = k_bits_of(c);
   return tq::launch_prepare(a, c->head_dim, s);
 }
 
@@ -355,7 +381,8 @@ int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t ba
   int st = prepare_checks(c, dtype, batch, n_q, n_q_heads);
   if (st) return st;
   if (!prep_bytes) return TQ_EINVAL;
-  const size_t need = tq::prep_region_bytes(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads);
+  const size_t need =
+      tq::prep_region_bytes(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, k_bits_of(c));
   if (!prep) {
     *prep_bytes = need;
     return TQ_OK;
@@ -412,6 +439,7 @@ static tq::DecodeArgs decode_args(const tq_cache *c, const uint8_t *prep, int32_
   a.plan = plan;
   a.cb = codebook_of(c);
   a.vcb = v_codebook_of(c);
+  a.k_bits = k_bits_of(c);
   a.v_bits = v_bits_of(c);
   return a;
 }
@@ -439,7 +467,8 @@ static int attn_decode_impl(const tq_cache *c, const void *q, int32_t dtype, int
   if (seq_starts && !aligned(seq_starts, 4)) return TQ_EALIGN;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   tq::DecodePlan plan =
-      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
+                      k_bits_of(c));
   size_t need = plan.counter_bytes + plan.partial_bytes + plan.prep_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -489,7 +518,8 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   if (n_new < 0) return TQ_EINVAL;
   tq::DecodePlan plan =
-      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
+                      k_bits_of(c));
   size_t need = plan.counter_bytes + plan.partial_bytes + plan.prep_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -517,7 +547,7 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   ek.pool = (uint8_t *)c->k_pool;
   ek.qjl = qjl_of(c);
   ek.cb = codebook_of(c);
-  ek.bits = 3;
+  ek.bits = k_bits_of(c);
   ev = ek;
   ev.x = v_new;
   ev.pool = (uint8_t *)c->v_pool;
@@ -534,6 +564,7 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   pa.prep = (float *)prep;
   pa.packed = prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads);
   pa.cb = codebook_of(c);
+  pa.k_bits = k_bits_of(c);
   if (n_new > 0 && tq::step_prologue_fits(ek, pa)) {
     if (tq::launch_step_prologue(ek, ev, pa, c->head_dim, s) != hipSuccess) return TQ_EHIP;
   } else {
@@ -554,7 +585,8 @@ int tq_attn_decode_prepared(const tq_cache *c, const void *prep, int32_t batch, 
                          out, workspace_bytes);
   if (st) return st;
   tq::DecodePlan plan =
-      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
+                      k_bits_of(c));
   size_t need = plan.counter_bytes + plan.partial_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -579,7 +611,8 @@ int tq_attn_decode_split(const tq_cache *c, const void *prep, int32_t batch, int
                          dummy_out, workspace_bytes);
   if (st) return st;
   tq::DecodePlan plan =
-      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
+                      k_bits_of(c));
   size_t need = plan.counter_bytes + plan.partial_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -609,7 +642,8 @@ int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   if (!out || !workspace) return TQ_EINVAL;
   if (!aligned(out, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
   tq::DecodePlan plan =
-      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages);
+      tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
+                      k_bits_of(c));
   if (workspace_bytes < plan.counter_bytes + plan.partial_bytes) return TQ_EWORKSPACE;
   tq::DecodeArgs a = decode_args(c, nullptr, batch, n_q, n_q_heads, nullptr, max_pages, nullptr, 0,
                                  0.f, out, (uint8_t *)workspace, plan);
@@ -695,7 +729,7 @@ int tq_dequant(const tq_cache *c, int32_t which, int32_t with_qjl, const int32_t
   a.qjl = c->qjl;
   a.out = out;
   a.cb = which == 0 ? codebook_of(c) : v_codebook_of(c);
-  a.bits = which == 0 ? 3 : v_bits_of(c);
+  a.bits = which == 0 ? k_bits_of(c) : v_bits_of(c);
   return hip_status(tq::launch_dequant(a, c->head_dim, which, (hipStream_t)stream));
 }
 

@@ -120,10 +120,12 @@ __device__ inline void stage_query(const uint8_t *grp, v8i *s_qop, int *s_qsc, i
   for (int e = tid; e < NMU * 64; e += 256) s_qsc[e] = ssrc[e];
 }
 
-template <int D, int VBITS>
+template <int D, int VBITS, int KBITS>
 struct MfmaBlock {
   static constexpr bool kPrefetchV = D == 128;
-  uint4 kw[4][D / 128];            // key record chunks kg, kg + 4 of tokens 16 tau + n
+  // key record words (KBITS code planes, then the signs) of coordinate groups
+  // kg + 4 c of tokens 16 tau + n
+  uint32_t kw[4][D / 128][KBITS + 1];
   uint2 g, nk, nv;                 // G, N^K, N^V of side entries 4 n + tau (tokens 16 tau + n)
   uint4 v[kPrefetchV ? VBITS : 1][D / 128];   // V words of plane j: coordinate pairs kp
 };
@@ -131,11 +133,12 @@ struct MfmaBlock {
 // NG query groups (4 rows each) share a workgroup: the key and V operands of a
 // block are built once and each MFMA operand of the keys or V bits meets the NG
 // query operands in turn. NG = 1 gives each group its own workgroup.
-template <int D, int NG, int VBITS>
+template <int D, int NG, int VBITS, int KBITS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2 : 1))) void decode_mfma_kernel(DecodeArgs a) {
-  constexpr int NMU = 5 * (D / 128);        // scaled MFMAs per 16-token scoring tile
-  constexpr int NCH = D / 128;              // 16-byte key chunks per lane and token
-  constexpr int KREC = D / 2;
+  constexpr int NPK = k_planes(KBITS);      // key code planes (then the sign plane)
+  constexpr int NMU = mfma_per_tile(D, KBITS);   // scaled MFMAs per 16-token scoring tile
+  constexpr int NCH = D / 128;              // 128-coordinate chunks per token
+  constexpr int KREC = (KBITS + 1) * D / 8; // K record bytes
   constexpr size_t KCODES = (size_t)kPage * KREC;
   constexpr size_t KSEC = KCODES + 4 * kPage;
   constexpr size_t VCODES = (size_t)VBITS * D * kPage / 8;   // VBITS-bit V codes
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   const int H = a.n_kv_heads, g = a.n_q_heads / H;
   const int L = a.seq_lens[b];
 
-  const uint8_t *grp0 = a.packed + (((size_t)b * H + kvh) * QG + rho0) * packed_group_bytes(D);
+  const uint8_t *grp0 = a.packed + (((size_t)b * H + kvh) * QG + rho0) * packed_group_bytes(D, KBITS);
   float off1[NG], off2[NG];
   int vis[NG];
 #pragma unroll
@@ -173,9 +176,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     off1[gi] = off2[gi] = 0.f;
     vis[gi] = 0;
     if (row < a.plan.group) {
-      const float4 rc = reinterpret_cast<const float4 *>(grp0 + (size_t)gi * packed_group_bytes(D) +
+      const float4 rc = reinterpret_cast<const float4 *>(grp0 + (size_t)gi * packed_group_bytes(D, KBITS) +
                                                          (size_t)NMU * (2048 + 256))[kg];
-      off1[gi] = a.cb.levels[7] * rc.z;
+      off1[gi] = a.cb.levels[(1 << KBITS) - 1] * rc.z;
       off2[gi] = rc.w * qjl_kappa<D>();
       vis[gi] = a.causal_tail ? L - (a.n_q - 1 - row / g) : L;
     }
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   if constexpr (VBITS == 3)
     plane_weights(a.vcb, wpl);
   else
-    v_plane_weights<VBITS>(a.vcb, wpl);
+    plane_weights_walsh<VBITS>(a.vcb, wpl);
   float wmax = 0.f;
 #pragma unroll
   for (int j = 0; j < NP; ++j) wmax = fmaxf(wmax, fabsf(wpl[j]));
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       if (rho0 + gi < QG) {
-        stage_query<NMU>(grp0 + (size_t)gi * packed_group_bytes(D), s_qop + gi * NMU * 64,
+        stage_query<NMU>(grp0 + (size_t)gi * packed_group_bytes(D, KBITS), s_qop + gi * NMU * 64,
                          s_qsc + gi * NMU * 64, tid);
       } else {
         uint4 *dst = reinterpret_cast<uint4 *>(s_qop + gi * NMU * 64);
@@ -268,20 +271,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     }
   };
 
-  auto load_block = [&](MfmaBlock<D, VBITS> &d, int pg) {
+  auto load_block = [&](MfmaBlock<D, VBITS, KBITS> &d, int pg) {
     const int phys = a.block_table[(size_t)b * a.max_pages + pg];
     const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
     const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
-        d.kw[tau][c] = reinterpret_cast<const uint4 *>(ks + (size_t)(blk0 + 16 * tau + n) * KREC)[kg + 4 * c];
+      for (int c = 0; c < NCH; ++c) {
+        const uint8_t *rec = ks + (size_t)(blk0 + 16 * tau + n) * KREC;
+        if constexpr (KBITS == 3) {   // four words: one 16-byte load
+          const uint4 u = reinterpret_cast<const uint4 *>(rec)[kg + 4 * c];
+          d.kw[tau][c][0] = u.x;
+          d.kw[tau][c][1] = u.y;
+          d.kw[tau][c][2] = u.z;
+          d.kw[tau][c][3] = u.w;
+        } else {
+          const uint32_t *r32 = reinterpret_cast<const uint32_t *>(rec) + (KBITS + 1) * (kg + 4 * c);
+#pragma unroll
+          for (int j = 0; j <= KBITS; ++j) d.kw[tau][c][j] = r32[j];
+        }
+      }
     const int se = blk0 + 4 * n;   // side entries of tokens 16 tau + n, tau = 0..3
     d.g = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * kPage + 2 * se);
     d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * se);
     d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * se);
-    if constexpr (MfmaBlock<D, VBITS>::kPrefetchV) {
+    if constexpr (MfmaBlock<D, VBITS, KBITS>::kPrefetchV) {
       const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 2 * VBITS * D) + 4 * (D / 32) * lane);
 #pragma unroll
       for (int j = 0; j < VBITS; ++j)
@@ -290,13 +305,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     }
   };
 
-  auto process = [&](const MfmaBlock<D, VBITS> &d, int pg) {
+  auto process = [&](const MfmaBlock<D, VBITS, KBITS> &d, int pg) {
     // at d = 256 the query operand (20 MFMA operands, 80 registers) is read from
     // LDS where it is used: an opaque lane offset keeps it from being hoisted
     int qo = lane;
     if constexpr (D == 256 || NG > 1) asm volatile("" : "+v"(qo));
     uint4 vcur[VBITS][NCH];
-    if constexpr (MfmaBlock<D, VBITS>::kPrefetchV) {
+    if constexpr (MfmaBlock<D, VBITS, KBITS>::kPrefetchV) {
 #pragma unroll
       for (int j = 0; j < VBITS; ++j)
 #pragma unroll
@@ -328,22 +343,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
-      for (int j = 0; j < 5; ++j) {   // code planes b0, b1, b2, b0^b1^b2, then the sign plane
+      for (int j = 0; j <= NPK; ++j) {   // code planes (b0, b1, b2, b0^b1^b2 at 3 bits), then the signs
         v8i op[4];
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
-          const uint4 w = d.kw[tau][c];
-          const uint32_t pl = j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : j == 3 ? (w.x ^ w.y ^ w.z) : w.w;
+          const uint32_t *w = d.kw[tau][c];
+          uint32_t pl;
+          if constexpr (KBITS == 3) {
+            pl = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : j == 3 ? (w[0] ^ w[1] ^ w[2]) : w[3];
+          } else if (j == NPK) {
+            pl = w[KBITS];
+          } else {
+            pl = 0u;
+#pragma unroll
+            for (int b2 = 0; b2 < KBITS; ++b2)
+              if ((VPlanes<KBITS>::mask[j] >> b2) & 1) pl ^= w[b2];
+          }
           op[tau] = v8i{(int)(pl & 0x11111111u), (int)(pl & 0x22222222u), (int)(pl & 0x44444444u),
                         (int)((pl >> 1) & 0x44444444u), 0, 0, 0, 0};
         }
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
-          const v8i qop = s_qop[(gi * NMU + 5 * c + j) * 64 + qo];
-          const int qsc = s_qsc[(gi * NMU + 5 * c + j) * 64 + qo];
+          const v8i qop = s_qop[(gi * NMU + (NPK + 1) * c + j) * 64 + qo];
+          const int qsc = s_qsc[(gi * NMU + (NPK + 1) * c + j) * 64 + qo];
 #pragma unroll
           for (int tau = 0; tau < 4; ++tau) {
-            if (j < 4)
+            if (j < NPK)
               c1[gi][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op[tau], c1[gi][tau], 2, 4, 0, qsc, 0, 127);
             else
               c2[gi][tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op[tau], c2[gi][tau], 2, 4, 0, qsc, 0, 127);
@@ -517,7 +542,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   // the first block's loads go out before the query operand is staged, so the
   // two fetches overlap
   if constexpr (D == 128 && NG == 1) {
-    MfmaBlock<D, VBITS> d0, d1;
+    MfmaBlock<D, VBITS, KBITS> d0, d1;
     if (pg0 < pg1) load_block(d0, pg0);
     // the packed query operand is shared by the four waves: keep it in LDS
     stage();
@@ -534,7 +559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     stage();
     __syncthreads();
     for (int pg = pg0; pg < pg1; ++pg) {
-      MfmaBlock<D, VBITS> d0;
+      MfmaBlock<D, VBITS, KBITS> d0;
       load_block(d0, pg);
       process(d0, pg);
     }
@@ -690,14 +715,14 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   for (int r = 0; r < R; ++r) o[lane + 64 * r] = x[r];
 }
 
-template <int D, int VBITS>
+template <int D, int VBITS, int KBITS>
 hipError_t launch_split_bits(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.wg_per_seq);
   switch (a.plan.groups_per_wg) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS>), grid, dim3(256), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS, KBITS>), grid, dim3(256), 0, s, a); break;
     case 2:
       if constexpr (D == 128) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, 2, VBITS>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, 2, VBITS, KBITS>), grid, dim3(256), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;
@@ -710,21 +735,29 @@ template <int D>
 hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
   const int G = a.plan.group;
   if (!a.plan.mfma || G > TQ_MAX_GROUP) return hipErrorInvalidValue;
+  auto by_k = [&](auto VB) -> hipError_t {
+    switch (a.k_bits) {
+      case 2: return launch_split_bits<D, VB.value, 2>(a, s);
+      case 3: return launch_split_bits<D, VB.value, 3>(a, s);
+      case 4: return launch_split_bits<D, VB.value, 4>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  };
   switch (a.v_bits) {
-    case 2: return launch_split_bits<D, 2>(a, s);
-    case 3: return launch_split_bits<D, 3>(a, s);
-    case 4: return launch_split_bits<D, 4>(a, s);
+    case 2: return by_k(std::integral_constant<int, 2>{});
+    case 3: return by_k(std::integral_constant<int, 3>{});
+    case 4: return by_k(std::integral_constant<int, 4>{});
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads) {
+size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int kb) {
   size_t bytes = prep_float_bytes(d, batch, n_q, n_q_heads);
   const int group = n_q_heads / n_kv_heads * n_q;
   if (mfma_path(d, group))
-    bytes += ((size_t)batch * n_kv_heads * query_groups(group) * packed_group_bytes(d) + 255) / 256 * 256;
+    bytes += ((size_t)batch * n_kv_heads * query_groups(group) * packed_group_bytes(d, kb) + 255) / 256 * 256;
   return bytes;
 }
 

@@ -181,7 +181,7 @@ template <> struct VPlanes<4> {
 };
 
 template <int VB>
-__device__ inline void v_plane_weights(const Codebook &cb, float (&w)[VPlanes<VB>::n]) {
+__device__ inline void plane_weights_walsh(const Codebook &cb, float (&w)[VPlanes<VB>::n]) {
 #pragma unroll
   for (int p = 0; p < VPlanes<VB>::n; ++p) {
     float a = 0.f;

@@ -47,17 +47,18 @@ __device__ inline float encode_front(const void *x, size_t base, const Codebook 
 // zero and their records are not written.
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int D, int DT, int VPW>
+template <int D, int DT, int VPW, int KB>
 __device__ void encode_k_block(const EncodeArgs &a, long blk) {
   constexpr int R = D / 64;
-  constexpr int NWORD = D / 8;              // u32 words per K record
+  constexpr int NWORD = (KB + 1) * D / 32;  // u32 words per K record: KB code planes + signs per 32
   constexpr int VB = kWaves * VPW;          // vectors per workgroup
   constexpr int VT = (VB + 15) / 16;        // 16-vector MFMA tiles
   constexpr int RT = D / 16 / kWaves;       // 16-row tiles of S per wave: 2 or 4
-  constexpr size_t KSEC = (size_t)kPage * D / 2 + 4 * kPage;
-  constexpr size_t KCODES = (size_t)kPage * D / 2;
+  constexpr size_t KREC = (size_t)(KB + 1) * D / 8;
+  constexpr size_t KCODES = (size_t)kPage * KREC;
+  constexpr size_t KSEC = KCODES + 4 * kPage;
   __shared__ float4 s_r[16 * VT][D / 4];    // residuals
-  __shared__ uint64_t s_code[VB][3][R];     // code bit planes
+  __shared__ uint64_t s_code[VB][KB][R];    // code bit planes
   __shared__ uint16_t s_sign[VB][D / 16];   // sign bits, 16 rows of S per entry
   __shared__ float s_ng[VB][2];             // N, G
 
@@ -89,15 +90,15 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
     }
     float y[R];
     int idx[R];
-    const float n = encode_front<D, DT>(a.x, (size_t)(v0 + u) * D, a.cb, y, idx);
+    const float n = encode_front<D, DT, (1 << KB) - 1>(a.x, (size_t)(v0 + u) * D, a.cb, y, idx);
     float rr = 0.f;
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-      y[k] -= level_of(a.cb, idx[k]);
+      y[k] -= KB == 3 ? level_of(a.cb, idx[k]) : level_any(a.cb, idx[k]);
       rr += y[k] * y[k];
       reinterpret_cast<float *>(rrow)[lane + 64 * k] = y[k];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
+      for (int j = 0; j < KB; ++j) {
         const uint64_t m = __ballot((idx[k] >> j) & 1);
         if (lane == 0) s_code[u][j][k] = m;
       }
@@ -162,15 +163,15 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
     uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * KSEC;
     const int off = slot % kPage;
     if (lane < NWORD) {
-      const int s = lane >> 2, j = lane & 3;
+      const int s = lane / (KB + 1), j = lane % (KB + 1);   // coordinate group, word in it
       uint32_t w;
-      if (j < 3) {
+      if (j < KB) {
         const uint64_t m = s_code[u][j][s >> 1];
         w = (s & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
       } else {
         w = qjl ? (uint32_t)s_sign[u][2 * s] | ((uint32_t)s_sign[u][2 * s + 1] << 16) : 0u;
       }
-      reinterpret_cast<uint32_t *>(sec + (size_t)off * (D / 2))[lane] = w;
+      reinterpret_cast<uint32_t *>(sec + (size_t)off * KREC)[lane] = w;
     }
     if (lane == 0) {
       reinterpret_cast<uint16_t *>(sec + KCODES)[side_entry(off)] = f32_to_f16_bits(s_ng[u][0]);
@@ -272,9 +273,9 @@ __device__ void encode_v_block(const EncodeArgs &a, int bx, int head) {
   }
 }
 
-template <int D, int DT, int VPW>
+template <int D, int DT, int VPW, int KB>
 __global__ __launch_bounds__(256) void encode_k_kernel(EncodeArgs a) {
-  encode_k_block<D, DT, VPW>(a, blockIdx.x);
+  encode_k_block<D, DT, VPW, KB>(a, blockIdx.x);
 }
 
 template <int D, int DT, int VPW, int VBITS>
@@ -287,10 +288,11 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
 // row, project it with S, write q~ and p, and on the MFMA path pack this row's
 // four limb rows of the fp6 scoring operand. The four waves split the m rows
 // of S, and every S load of a chunk is issued before the row is rotated.
-template <int D, int DT>
+template <int D, int DT, int KB>
 __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   constexpr int R = D / 64;
-  constexpr int NMU = 5 * (D / 128);   // scoring MFMAs per 16-token tile
+  constexpr int NPK = k_planes(KB);    // key code planes (KB-bit codes), then the sign plane
+  constexpr int NMU = mfma_per_tile(D, KB);   // scoring MFMAs per 16-token tile
   constexpr int RPW = D / 4;         // rows of S per wave
   constexpr int LPR = 64 / RPW;      // lanes per row of S: 2 (d = 128) or 1 (d = 256)
   constexpr int EPL = D / LPR;       // elements of a row per lane
@@ -368,8 +370,11 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   // 2 kappa p_i (sign plane, sigma = 2 b - 1), as four limbs on the rows
   // 4 q + limb, each limb with an E8M0 scale per 32-slot block (in lane
   // 16 kq + row), so the MFMA sums of the four limb rows add up to the product.
-  float w[4];
-  plane_weights(a.cb, w);
+  float w[NPK];
+  if constexpr (KB == 3)
+    plane_weights(a.cb, w);
+  else
+    plane_weights_walsh<KB>(a.cb, w);
   float sq = 0.f, sp = 0.f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -381,7 +386,7 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   // query group rho = qq / 4 has its own operand; this row is its row group qloc
   const int QG = query_groups(G), rho = qq / kMfmaMaxGroup, qloc = qq % kMfmaMaxGroup;
   const int Gr = min(kMfmaMaxGroup, G - kMfmaMaxGroup * rho);   // rows of the group
-  uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * packed_group_bytes(D);
+  uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * packed_group_bytes(D, KB);
   uint8_t *opb = grp;                                                  // [mu][lane][32] bytes
   uint32_t *scl = reinterpret_cast<uint32_t *>(grp + (size_t)NMU * 2048);   // [mu][lane]
   const float kap2 = 2.f * qjl_kappa<D>();
@@ -404,9 +409,9 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
     const int blkid = half + 8 * t;   // the same for both halves of a wave
     if (blkid < NTASK) {
       const int mu = blkid >> 2, kb = blkid & 3;
-      const int c = mu / 5, pl = mu % 5;
+      const int c = mu / (NPK + 1), pl = mu % (NPK + 1);
       const int i = 32 * (kb + 4 * c) + 4 * fm + fv;
-      float r = (pl < 4 ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
+      float r = (pl < NPK ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
       // limb 0: the block scale 2^ex puts the block's largest value in [4, 8).
       // Later limbs take their scale from the rounding bound of the previous one
       // (no reduction): limb 0 leaves |r| <= 0.5 * 2^ex (0.25 from rounding in
@@ -470,7 +475,13 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
 
 template <int D, int DT>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
-  prepare_row<D, DT>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  // the K code width is uniform over the launch
+  if (a.k_bits == 2)
+    prepare_row<D, DT, 2>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  else if (a.k_bits == 4)
+    prepare_row<D, DT, 4>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+  else
+    prepare_row<D, DT, 3>(a, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // One launch for the work of a decode step that precedes the split-K decode:
@@ -487,7 +498,13 @@ template <int D, int DT>
 __global__ __launch_bounds__(256) void step_prologue_kernel(StepArgs s) {
   int id = blockIdx.x;
   if (id < s.nk) {
-    encode_k_block<D, DT, 1>(s.k, id);
+    // the K code width is uniform over the launch
+    if (s.k.bits == 2)
+      encode_k_block<D, DT, 1, 2>(s.k, id);
+    else if (s.k.bits == 4)
+      encode_k_block<D, DT, 1, 4>(s.k, id);
+    else
+      encode_k_block<D, DT, 1, 3>(s.k, id);
     return;
   }
   id -= s.nk;
@@ -503,14 +520,22 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(StepArgs s) {
   }
   id -= s.nv;
   const int G = s.p.n_q * (s.p.n_q_heads / s.p.n_kv_heads);
-  prepare_row<D, DT>(s.p, id % G, (id / G) % s.p.n_kv_heads, id / (G * s.p.n_kv_heads));
+  const int qq = id % G, kvh = (id / G) % s.p.n_kv_heads, b = id / (G * s.p.n_kv_heads);
+  if (s.p.k_bits == 2)
+    prepare_row<D, DT, 2>(s.p, qq, kvh, b);
+  else if (s.p.k_bits == 4)
+    prepare_row<D, DT, 4>(s.p, qq, kvh, b);
+  else
+    prepare_row<D, DT, 3>(s.p, qq, kvh, b);
 }
 
 template <int D>
 __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) {
   constexpr int R = D / 64;
-  constexpr size_t KSEC = (size_t)kPage * D / 2 + 4 * kPage;
-  constexpr size_t KCODES = (size_t)kPage * D / 2;
+  const int kw = a.bits + 1;                          // K: words per 32 coordinates
+  const size_t KREC = (size_t)kw * D / 8;
+  const size_t KCODES = (size_t)kPage * KREC;
+  const size_t KSEC = KCODES + 4 * kPage;
   const size_t VCODES = (size_t)a.bits * D * kPage / 8;   // V: a.bits-bit codes
   const size_t VSEC = VCODES + 2 * kPage;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -524,13 +549,13 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
   float scale;
   if (which == 0) {
     const uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * KSEC;
-    const uint32_t *rec = reinterpret_cast<const uint32_t *>(sec + (size_t)off * (D / 2));
+    const uint32_t *rec = reinterpret_cast<const uint32_t *>(sec + (size_t)off * KREC);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int i = lane + 64 * r, s = i >> 5, e = i & 31;
-      const int idx = ((rec[4 * s] >> e) & 1) | (((rec[4 * s + 1] >> e) & 1) << 1) |
-                      (((rec[4 * s + 2] >> e) & 1) << 2);
-      v[r] = level_of(a.cb, idx);
+      int idx = 0;
+      for (int j = 0; j < a.bits; ++j) idx |= ((rec[kw * s + j] >> e) & 1) << j;
+      v[r] = level_any(a.cb, idx);
     }
     scale = f16_bits_to_f32(reinterpret_cast<const uint16_t *>(sec + KCODES)[side_entry(off)]);
     if (a.with_qjl) {
@@ -539,7 +564,7 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a, int which) 
 #pragma unroll
       for (int r = 0; r < R; ++r) t[r] = 0.f;
       for (int l = 0; l < D; ++l) {
-        const bool pos = (rec[4 * (l >> 5) + 3] >> (l & 31)) & 1;
+        const bool pos = (rec[kw * (l >> 5) + a.bits] >> (l & 31)) & 1;
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           const float s = a.qjl[(size_t)l * D + lane + 64 * r];
@@ -586,13 +611,21 @@ hipError_t by_dim_dtype(int d, int dtype, F &&f) {
 hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
   const long total = (long)a.n_tokens * a.n_heads;
   return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
-    if (total < 4096) {
-      const dim3 grid((unsigned)((total + kWaves - 1) / kWaves));
-      hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 1>), grid, dim3(256), 0, s, a);
-    } else {
-      const dim3 grid((unsigned)((total + 63) / 64));
-      hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 16>), grid, dim3(256), 0, s, a);
-    }
+    auto go = [&](auto KB) {
+      if (total < 4096) {
+        const dim3 grid((unsigned)((total + kWaves - 1) / kWaves));
+        hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 1, KB.value>), grid, dim3(256), 0, s, a);
+      } else {
+        const dim3 grid((unsigned)((total + 63) / 64));
+        hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 16, KB.value>), grid, dim3(256), 0, s, a);
+      }
+    };
+    if (a.bits == 2)
+      go(std::integral_constant<int, 2>{});
+    else if (a.bits == 4)
+      go(std::integral_constant<int, 4>{});
+    else
+      go(std::integral_constant<int, 3>{});
     return hipGetLastError();
   });
 }

@@ -18,7 +18,9 @@ struct Codebook {
   float thresholds[15];
 };
 
-inline size_t k_section_bytes(int d) { return (size_t)kPage * d / 2 + 4u * kPage; }
+inline size_t k_section_bytes(int d, int kbits = 3) {
+  return (size_t)kPage * (kbits + 1) * d / 8 + 4u * kPage;
+}
 inline size_t v_section_bytes(int d, int vbits = 3) {
   return (size_t)vbits * d * kPage / 8 + 2u * kPage;
 }
@@ -32,7 +34,7 @@ struct EncodeArgs {
   uint8_t *pool;          // K or V pool
   const float *qjl;       // S [d][d] (K only)
   Codebook cb;            // the codebook of what is encoded
-  int bits;               // V code width (2, 3 or 4); K codes are 3-bit
+  int bits;               // code width (2, 3 or 4) of what is encoded
 };
 
 struct DequantArgs {
@@ -44,7 +46,7 @@ struct DequantArgs {
   const float *qjl;
   float *out;             // [n_tokens][H][d]
   Codebook cb;            // K or V codebook
-  int bits;               // V code width (V only)
+  int bits;               // code width of the records (K or V)
 };
 
 // Query preparation for one decode call: rotation, QJL projection and, for
@@ -57,16 +59,20 @@ struct PrepArgs {
   const float *qjl;
   float *prep;            // [rows][2][d]: Pi q, then S Pi q
   uint8_t *packed;        // per (sequence, KV head, query group): operand + row constants (or null)
-  Codebook cb;
+  Codebook cb;            // K
+  int k_bits;             // K code width: the number of key bit planes follows
 };
 
 // Bytes of the packed scoring operand of one query group of a (sequence, KV
 // head): per 16-token tile a wave issues mfma_per_tile scaled fp6 x fp4 MFMAs
 // whose query operand (32 B per lane) is stored lane-major, then their scale
 // words (4 B per lane), then 4 rows x {0, 0, sum q~, sum p}.
-__host__ __device__ inline int mfma_per_tile(int d) { return 5 * (d / 128); }
-__host__ __device__ inline size_t packed_group_bytes(int d) {
-  return (size_t)mfma_per_tile(d) * (64 * 32 + 64 * 4) + 64;
+// Key bit planes of kb-bit codes (the odd Walsh functions of the code bits):
+// 2, 4 or 8; one more MFMA per 128 coordinates scores the QJL signs.
+__host__ __device__ constexpr int k_planes(int kb) { return kb == 2 ? 2 : kb == 3 ? 4 : 8; }
+__host__ __device__ constexpr int mfma_per_tile(int d, int kb = 3) { return (k_planes(kb) + 1) * (d / 128); }
+__host__ __device__ inline size_t packed_group_bytes(int d, int kb = 3) {
+  return (size_t)mfma_per_tile(d, kb) * (64 * 32 + 64 * 4) + 64;
 }
 constexpr int kMfmaMaxGroup = 4;   // query rows per MFMA query group (4 rows x 4 limbs)
 __host__ __device__ inline int query_groups(int group) { return (group + kMfmaMaxGroup - 1) / kMfmaMaxGroup; }
@@ -97,7 +103,7 @@ struct DecodePlan {
 
 // Query region of a decode call: [rows][2][d] float32, then (MFMA path) the
 // packed operands of the B*Hkv groups.
-size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads);
+size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int kb = 3);
 inline size_t prep_float_bytes(int d, int batch, int n_q, int n_q_heads) {
   return ((size_t)batch * n_q * n_q_heads * 2 * d * sizeof(float) + 255) / 256 * 256;
 }
@@ -118,12 +124,13 @@ struct DecodeArgs {
   int causal_tail;
   float scale;
   DecodePlan plan;
-  Codebook cb;            // K
+  Codebook cb;            // K, k_bits wide
   Codebook vcb;           // V, v_bits wide
-  int v_bits;
+  int k_bits, v_bits;
 };
 
-DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages);
+DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages,
+                       int kb = 3);
 
 hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s);
 hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s);

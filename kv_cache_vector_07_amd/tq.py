@@ -21,7 +21,8 @@ TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2
 TQ_F32, TQ_BF16 = 0, 1
 TQ_PAGE_SIZE = 256
 TQ_MAX_GROUP = 4096
-EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_v_page_bytes_bits", "tq_build_codebook",
+EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_k_page_bytes_bits", "tq_v_page_bytes_bits",
+           "tq_build_codebook",
            "tq_build_codebook_sphere",
            "tq_encode_k",
            "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_window",
@@ -42,7 +43,8 @@ class TqCacheDesc(C.Structure):
                 ("n_pages", C.c_int32), ("k_pool", C.c_void_p), ("v_pool", C.c_void_p),
                 ("qjl", C.c_void_p), ("levels", C.c_float * 8), ("thresholds", C.c_float * 7),
                 ("k_mse_only", C.c_int32), ("v_bits", C.c_int32), ("v_levels", C.c_float * 16),
-                ("v_thresholds", C.c_float * 15)]
+                ("v_thresholds", C.c_float * 15), ("k_bits", C.c_int32), ("k_levels", C.c_float * 16),
+                ("k_thresholds", C.c_float * 15)]
 
 
 def lib():
@@ -61,6 +63,8 @@ def lib():
     L.tq_v_page_bytes.restype = sz
     L.tq_v_page_bytes_bits.argtypes = [i32, i32, i32]
     L.tq_v_page_bytes_bits.restype = sz
+    L.tq_k_page_bytes_bits.argtypes = [i32, i32, i32]
+    L.tq_k_page_bytes_bits.restype = sz
     L.tq_status_string.argtypes = [i32]
     L.tq_status_string.restype = C.c_char_p
     L.tq_build_codebook.argtypes = [i32, i32, C.c_uint64, vp, vp, vp]
@@ -116,8 +120,8 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
-def tq_k_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE) -> int:
-    return int(lib().tq_k_page_bytes(head_dim, page_size))
+def tq_k_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE, bits: int = 3) -> int:
+    return int(lib().tq_k_page_bytes_bits(head_dim, page_size, bits))
 
 
 def tq_v_page_bytes(head_dim: int, page_size: int = TQ_PAGE_SIZE, bits: int = 3) -> int:
@@ -146,7 +150,7 @@ class Cache:
 
     def __init__(self, head_dim: int, n_kv_heads: int, n_pages: int, qjl_seed: int = 12345,
                  device="cuda", codebook=None, zero: bool = True, k_mse_only: bool = False,
-                 v_bits: int = 3, v_codebook=None):
+                 v_bits: int = 3, v_codebook=None, k_bits: int = 3, k_codebook=None):
         import torch
         self.head_dim, self.n_kv_heads, self.n_pages = head_dim, n_kv_heads, n_pages
         self.page_size = TQ_PAGE_SIZE
@@ -160,7 +164,16 @@ class Cache:
             vlev, vthr = (v_codebook if v_codebook is not None
                           else tq_build_codebook(head_dim, self.v_bits, qjl_seed, with_qjl=False)[:2])
         self.v_levels, self.v_thresholds = vlev, vthr
-        kpb, vpb = tq_k_page_bytes(head_dim), tq_v_page_bytes(head_dim, bits=self.v_bits)
+        # K codes of k_bits bits: 3 uses the codebook above; 2 and 4 bring their own
+        self.k_bits = int(k_bits)
+        if self.k_bits == 3:
+            klev, kthr = levels, thr
+        else:
+            klev, kthr = (k_codebook if k_codebook is not None
+                          else tq_build_codebook(head_dim, self.k_bits, qjl_seed, with_qjl=False)[:2])
+        self.k_levels, self.k_thresholds = klev, kthr
+        kpb = tq_k_page_bytes(head_dim, bits=self.k_bits)
+        vpb = tq_v_page_bytes(head_dim, bits=self.v_bits)
         alloc = torch.zeros if zero else torch.empty
         self.k_pool = alloc(n_pages * n_kv_heads * kpb, dtype=torch.uint8, device=device)
         self.v_pool = alloc(n_pages * n_kv_heads * vpb, dtype=torch.uint8, device=device)
@@ -169,11 +182,16 @@ class Cache:
         vt = np.zeros(15, np.float32)
         vl[:len(vlev)] = vlev
         vt[:len(vthr)] = vthr
+        kl = np.zeros(16, np.float32)
+        kt = np.zeros(15, np.float32)
+        kl[:len(klev)] = klev
+        kt[:len(kthr)] = kthr
         self.desc = TqCacheDesc(head_dim, n_kv_heads, self.page_size, n_pages,
                                 self.k_pool.data_ptr(), self.v_pool.data_ptr(), self.qjl.data_ptr(),
                                 (C.c_float * 8)(*levels.tolist()), (C.c_float * 7)(*thr.tolist()),
                                 int(k_mse_only), self.v_bits, (C.c_float * 16)(*vl.tolist()),
-                                (C.c_float * 15)(*vt.tolist()))
+                                (C.c_float * 15)(*vt.tolist()), self.k_bits,
+                                (C.c_float * 16)(*kl.tolist()), (C.c_float * 15)(*kt.tolist()))
         self.k_mse_only = bool(k_mse_only)
         self._ws = None
 

@@ -272,3 +272,29 @@ def test_v_widths_page_bytes_and_validation(L):
     assert decode() == tq.TQ_OK
     dsc.v_levels[0] = float(lv[0]) * 1.01           # no longer odd
     assert decode() == tq.TQ_EINVAL
+
+
+def test_k_widths_page_bytes_validation_and_operand_size(L):
+    for d in (128, 256):
+        for b in (2, 3, 4):
+            assert tq.tq_k_page_bytes(d, bits=b) == O.k_page_bytes(d, 256, b)
+        assert L.tq_k_page_bytes_bits(d, 256, 5) == 0
+    assert tq.tq_k_page_bytes(128) == L.tq_k_page_bytes(128, 256)
+    dsc = _desc(H=2)
+    sz = C.c_size_t(0)
+    decode = lambda: L.tq_attn_decode(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE,
+                                      None, C.byref(sz), None)
+    assert decode() == tq.TQ_OK
+    base = sz.value
+    dsc.k_bits = 1
+    assert decode() == tq.TQ_EINVAL
+    dsc.k_bits = 4                                   # k_levels still zero: not increasing
+    assert decode() == tq.TQ_EINVAL
+    lv, _, _ = tq.tq_build_codebook(128, 4, 1, with_qjl=False)
+    for k in range(16):
+        dsc.k_levels[k] = float(lv[k])
+    assert decode() == tq.TQ_OK
+    # the packed scoring operand has 9 MFMA operands per 128 coordinates instead of 5
+    grp3 = 5 * (64 * 32 + 64 * 4) + 64
+    grp4 = 9 * (64 * 32 + 64 * 4) + 64
+    assert sz.value - base == (2 * 2 * 1 * grp4 + 255) // 256 * 256 - (2 * 2 * 1 * grp3 + 255) // 256 * 256

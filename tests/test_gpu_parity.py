@@ -575,6 +575,64 @@ def test_v_code_widths(tq, d, vb):
         assert err <= Hn.ATTN_TOL
 
 
+@pytest.mark.parametrize("d,kb,vb", [(128, 2, 3), (128, 4, 3), (256, 2, 3), (256, 4, 3),
+                                     (128, 2, 2), (256, 4, 4)])
+def test_k_code_widths(tq, d, kb, vb):
+    """K codes of 2 and 4 bits with the QJL signs (k_bits; alone and with V of the
+    same width): codes, signs, N and G of whole-block and single-token encodes
+    against the reference with the 4- or 16-level codebook, dequant with and
+    without the QJL term, the fused append step, and attention for 4 rows and
+    16 causal rows."""
+    H, lens = 8, np.array([700, 300])
+    print(f"[k bits] d={d} kb={kb} vb={vb}", flush=True)
+    w = I.Workload(f"kb{d}{kb}{vb}", len(lens), 32, H, d, "bf16", "outlier", 80 + kb, n_q=4, fixed_len=1)
+    table, n_pages = I.page_table(w, lens, extra_tokens=1, shuffle=True)
+    cache = tq.Cache(d, H, n_pages, k_bits=kb, v_bits=vb)
+    cbk, cbv = O.codebook(d, kb), O.codebook(d, vb)
+    assert np.array_equal(cache.k_levels.astype(np.float64), cbk.levels)
+    S = cache.qjl_host
+    bt = torch.from_numpy(table).cuda()
+    for b, L in enumerate(lens):
+        t = np.arange(L)
+        slots = (table[b][t // 256].astype(np.int64) * 256 + t % 256).astype(np.int32)
+        ts = torch.from_numpy(slots).cuda()
+        k = I.kv_tokens(w, "k", b, 0, L)
+        v = I.kv_tokens(w, "v", b, 0, L)
+        tq.tq_encode_k(cache, Hn.torch_input(k, "bf16"), ts)   # 700 x 8 vectors: the bulk kernel
+        tq.tq_encode_v(cache, Hn.torch_input(v, "bf16"), ts)
+        torch.cuda.synchronize()
+        kp = cache.k_pool.cpu().numpy()
+        uk = O.unpack_k(kp, slots, H, d, 256, kb)
+        rk = Hn.compare_encode_k(uk, k.astype(np.float64), cbk, S)
+        print(f"  seq {b}: K {rk}", flush=True)
+        if b == 0:
+            for qjl in (1, 0):
+                got = tq.tq_dequant(cache, 0, qjl, ts).cpu().numpy()
+                ref = O.dequant_k(uk["idx"], uk["sign"], uk["N"], uk["G"], cbk, S, bool(qjl))
+                assert np.max(np.abs(got - ref) / np.max(np.abs(ref), axis=-1, keepdims=True)) < 1e-5
+    pos = lens.copy()
+    aslots = torch.from_numpy((table[np.arange(2), pos // 256].astype(np.int64) * 256 + pos % 256)
+                              .astype(np.int32)).cuda()
+    nk = np.concatenate([I.kv_tokens(w, "k", b, int(L), int(L) + 1) for b, L in enumerate(lens)])
+    nv = np.concatenate([I.kv_tokens(w, "v", b, int(L), int(L) + 1) for b, L in enumerate(lens)])
+    lens1 = lens + 1
+    sl = torch.from_numpy(lens1.astype(np.int32)).cuda()
+    q1 = I.queries(w, 0)[:, :1].copy()
+    out1 = tq.tq_append_decode(cache, Hn.torch_input(nk, "bf16"), Hn.torch_input(nv, "bf16"), aslots,
+                               Hn.torch_input(q1, "bf16"), bt, sl)
+    q4 = I.queries(w, 1)
+    out4 = tq.tq_attn_decode(cache, Hn.torch_input(q4, "bf16"), bt, sl, causal_tail=1)
+    torch.cuda.synchronize()
+    kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+    Hn.compare_encode_k(O.unpack_k(kp, aslots.cpu().numpy(), H, d, 256, kb), nk.astype(np.float64), cbk, S)
+    for q, out, causal in ((q1, out1, False), (q4, out4, True)):
+        ref = O.attn_decode(kp, vp, cbk, S, q.astype(np.float64), table, lens1, H, 256, Hn.scale_of(d),
+                            causal_tail=causal, cb_v=cbv, v_bits=vb, k_bits=kb)
+        err = Hn.attn_rel_err(out.cpu().numpy(), ref)
+        print(f"  rows {q.shape[1] * 4} causal {causal}: max rel err {err:.3e}", flush=True)
+        assert err <= Hn.ATTN_TOL
+
+
 WIN_CASES = [
     # (d, Hkv, Hq, n_q, lens, starts, causal, seed)
     # mid-page, page-aligned, the last token only, a start past the length (zero rows)
