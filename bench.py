@@ -32,10 +32,11 @@ ROTATE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.txt")
 
 
-def kv_bytes_per_token_head(d: int, v_bits: int = 3) -> int:
-    """Algorithmic compressed bytes read per (token, KV head): K record + its
-    two fp16 sidecars, V record (v_bits-bit codes) + its fp16 sidecar."""
-    return (d // 2 + 4) + (v_bits * d // 8 + 2)
+def kv_bytes_per_token_head(d: int, v_bits: int = 3, k_bits: int = 3) -> int:
+    """Algorithmic compressed bytes read per (token, KV head): K record (k_bits
+    code planes and the signs) + its two fp16 sidecars, V record (v_bits-bit
+    codes) + its fp16 sidecar."""
+    return ((k_bits + 1) * d // 8 + 4) + (v_bits * d // 8 + 2)
 
 
 def kernel_source_hash() -> str:
@@ -84,7 +85,7 @@ def platform_info():
     return info
 
 
-def dense_baseline(dense, qs, seq, scale, tq_dec_ms, sh, log, v_bits=3):
+def dense_baseline(dense, qs, seq, scale, tq_dec_ms, sh, log, v_bits=3, k_bits=3):
     """The uncompressed bf16 decode kernel on the same K, V and queries, over
     rotating device copies (>= 1 GiB), against the compressed split kernel."""
     import torch
@@ -124,7 +125,7 @@ def dense_baseline(dense, qs, seq, scale, tq_dec_ms, sh, log, v_bits=3):
             "frac": round(gbs / HBM_PEAK_GBS, 4), "rotating_copies": R,
             "speedup_compressed_split_vs_dense": round(ms / tq_dec_ms, 3),
             "speedup_vs_dense_at_hbm_peak": round(nbytes / (HBM_PEAK_GBS * 1e9) * 1e3 / tq_dec_ms, 3),
-            "ideal_byte_ratio": round(nbytes / (Lm * B * H * kv_bytes_per_token_head(d, v_bits)), 3)}
+            "ideal_byte_ratio": round(nbytes / (Lm * B * H * kv_bytes_per_token_head(d, v_bits, k_bits)), 3)}
 
 
 def _host_cpu():
@@ -144,7 +145,7 @@ def _host_cpu():
 
 
 def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0, budget_1t_s=6.0,
-                 v_bits=3):
+                 v_bits=3, k_bits=3):
     """The CPU reference (numpy float64, as it stands) timed on this host on a
     bounded sample: whole decode steps over every KV head of sequence 0 with the
     BLAS thread pool as it is, then again on one BLAS thread, and an encode of a
@@ -157,7 +158,7 @@ def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0, budget
     except Exception:
         threadpool_limits = None
         threads = 1
-    cb = O.codebook(w.head_dim)
+    cb = O.codebook(w.head_dim, k_bits)
     S = O.qjl_matrix(w.head_dim, w.qjl_seed)
     d, H = w.head_dim, w.n_kv_heads
     L = int(lens[0])
@@ -168,10 +169,10 @@ def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0, budget
         while time.perf_counter() - t0 < budget and done < 64 * H:
             O.attn_decode(kp, vp, cb, S, q[:1].astype(np.float64), table[:1], lens[:1], H,
                           w.page_size, 1 / math.sqrt(d), pairs=[(0, done % H)],
-                          cb_v=O.codebook(d, v_bits), v_bits=v_bits)
+                          cb_v=O.codebook(d, v_bits), v_bits=v_bits, k_bits=k_bits)
             done += 1
         dt = time.perf_counter() - t0
-        return done, dt, done * L * kv_bytes_per_token_head(d, v_bits) / dt / 1e9
+        return done, dt, done * L * kv_bytes_per_token_head(d, v_bits, k_bits) / dt / 1e9
 
     heads_done, dt, gbs = decode_rate(budget_s)
     one = None
@@ -180,9 +181,10 @@ def cpu_baseline(w, lens, n_pages_total, kp, vp, table, q, budget_s=12.0, budget
             one = decode_rate(budget_1t_s)
     n_enc = 2048
     x = I.kv_tokens(w, "k", 0, 0, n_enc // H + 1)[: n_enc // H].astype(np.float64)
+    cb_v = O.codebook(d, v_bits)
     t1 = time.perf_counter()
     O.encode(x, cb, S)
-    O.encode(x, cb)
+    O.encode(x, cb_v)
     enc_dt = time.perf_counter() - t1
     out = {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
            "sample": f"{heads_done} (sequence, KV head) decode passes over L={L} "
@@ -287,6 +289,8 @@ def main():
     ap.add_argument("--decode-launches", type=int, default=512)
     ap.add_argument("--v-bits", type=int, default=3, choices=(2, 3, 4),
                     help="V code width (3: the method's V path; 2 and 4: the bit-width variant)")
+    ap.add_argument("--k-bits", type=int, default=3, choices=(2, 3, 4),
+                    help="K code width (3: the method's K path; 2 and 4: the bit-width variant)")
     ap.add_argument("--prefill-chunk", type=int, default=512,
                     help="chunk length of the chunked-prefill attention measurement (0: skip)")
     ap.add_argument("--no-dense-baseline", action="store_true",
@@ -308,8 +312,8 @@ def main():
     d, H, Hq, B, nq = w.head_dim, w.n_kv_heads, w.n_q_heads, w.batch, w.n_q
     lens = I.seq_lens(w)
     table_np, n_pages = I.page_table(w, lens, shuffle=w.batch > 1)
-    vbits = args.v_bits
-    kpb, vpb = tq.tq_k_page_bytes(d), tq.tq_v_page_bytes(d, bits=vbits)
+    vbits, kbits = args.v_bits, args.k_bits
+    kpb, vpb = tq.tq_k_page_bytes(d, bits=kbits), tq.tq_v_page_bytes(d, bits=vbits)
     copy_bytes = n_pages * H * (kpb + vpb)
     R = max(1, math.ceil(ROTATE_BYTES / copy_bytes))
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -319,7 +323,7 @@ def main():
         f"{n_pages} pages, {R} rotating copies of {copy_bytes / 1e6:.1f} MB")
 
     # ---- build the compressed cache once (timed: encode vec/s), then copy it
-    base = tq.Cache(d, H, n_pages, qjl_seed=w.qjl_seed, device=dev, v_bits=vbits)
+    base = tq.Cache(d, H, n_pages, qjl_seed=w.qjl_seed, device=dev, v_bits=vbits, k_bits=kbits)
     table = torch.from_numpy(table_np).to(dev)
     seq = torch.from_numpy(lens.astype(np.int32)).to(dev)
     stream = torch.cuda.current_stream()
@@ -375,7 +379,8 @@ def main():
     for _ in range(R - 1):
         c = tq.Cache(d, H, n_pages, device=dev, zero=False,
                      codebook=(base.levels, base.thresholds, base.qjl_host), v_bits=vbits,
-                     v_codebook=(base.v_levels, base.v_thresholds))
+                     v_codebook=(base.v_levels, base.v_thresholds), k_bits=kbits,
+                     k_codebook=(base.k_levels, base.k_thresholds))
         c.k_pool.copy_(base.k_pool)
         c.v_pool.copy_(base.v_pool)
         copies.append(c)
@@ -483,12 +488,12 @@ def main():
     append_ms = timed(append, 64)
 
     ctx_tokens = int(lens.sum())
-    kv_bytes = ctx_tokens * H * kv_bytes_per_token_head(d, vbits)
-    app_bytes = B * H * (2 * d * (2 if w.dtype == "bf16" else 4) + kv_bytes_per_token_head(d, vbits))
+    kv_bytes = ctx_tokens * H * kv_bytes_per_token_head(d, vbits, kbits)
+    app_bytes = B * H * (2 * d * (2 if w.dtype == "bf16" else 4) + kv_bytes_per_token_head(d, vbits, kbits))
     step_s = step_ms / 1e3
     value = (kv_bytes + app_bytes) / step_s / 1e9
     dec_gbs = kv_bytes / (dec_ms / 1e3) / 1e9
-    traffic = read_traffic(w.name) if vbits == 3 else None
+    traffic = read_traffic(w.name) if vbits == 3 and kbits == 3 else None
     in_bytes = 2 if w.dtype == "bf16" else 4
     result = {
         "metric": METRIC,
@@ -507,7 +512,7 @@ def main():
                    "head_dim": d, "n_q": nq, "context": int(lens.max()) if B == 1 else
                    [int(lens.min()), int(lens.max())], "ctx_tokens": ctx_tokens,
                    "input_dtype": w.dtype, "page_size": 256, "rotating_copies": R,
-                   "v_bits": vbits,
+                   "v_bits": vbits, "k_bits": kbits,
                    "step": "tq_append_decode: append 1 token/seq (encode K+V) and decode (prologue, split-K, merge)"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "ctx_tokens_per_s": round(ctx_tokens / step_s, 1),
@@ -533,13 +538,13 @@ def main():
         if pa is not None:
             result["prefill_attention"] = pa
     if dense is not None:
-        result["dense_bf16_baseline"] = dense_baseline(dense, qs, seq, scale, dec_ms, sh, log, vbits)
+        result["dense_bf16_baseline"] = dense_baseline(dense, qs, seq, scale, dec_ms, sh, log, vbits, kbits)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU reference on a bounded sample")
         kp = base.k_pool.cpu().numpy()
         vp = base.v_pool.cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(w, lens, n_pages, kp, vp, table_np,
-                                              I.queries(w, 0), v_bits=vbits)
+                                              I.queries(w, 0), v_bits=vbits, k_bits=kbits)
     print(json.dumps(result), flush=True)
 
 
