@@ -141,7 +141,8 @@ size_t tq_k_page_bytes_bits(int32_t head_dim, int32_t page_size, int32_t bits);
  *     of N(0, 1/d), found by Lloyd iteration in float64 from the Gaussian
  *     quantiles sigma*Phi^-1((k+1/2)/n) until no level moves by 1e-14*sigma,
  *     symmetrised, thresholds at midpoints, then rounded to float32. bits = 3
- *     is the pages' codebook (K and V); 2 and 4 serve the V bit-width variant.
+ *     is the pages' codebook (K and V); 2 and 4 serve the K and V bit-width
+ *     variants (tq_cache.k_bits, v_bits).
  *   qjl_host (host out, d*d floats, may be NULL): S[l][i] row-major; SplitMix64
  *     seeded with qjl_seed gives pairs (x1, x2) -> u = ((x>>11)+1)*2^-53, Box-Muller
  *     sqrt(-2 ln u1) cos(2 pi u2) then sin(...), filled in order, rounded to float32.
@@ -175,7 +176,8 @@ int tq_build_codebook_sphere(int32_t head_dim, int32_t bits, uint64_t qjl_seed,
  * n = ||x||, x_hat = x/n (0 if n = 0), y = Pi x_hat, code_j = #{k: t_k <= y_j},
  * r = y - c[code], z = S r; writes the K record, N = fp16(n), G = fp16(||r||) at
  * slot slots[i] (device int32 [n_tokens]) of head h. Only the addressed records
- * change. n_tokens == 0 is a no-op.
+ * change. n_tokens == 0 is a no-op. The codes have tq_cache.k_bits bits (3 by
+ * default); with k_mse_only the QJL stage is skipped (see tq_cache).
  * Errors: TQ_EINVAL, TQ_EUNSUPPORTED (d, P, dtype), TQ_EALIGN, TQ_EHIP.
  */
 int tq_encode_k(const tq_cache *c, const void *k, int32_t dtype,
