@@ -215,7 +215,6 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
   if (pps > 256) pps = 256;
   p.pages_per_split = pps;
   p.n_split = (max_pages + pps - 1) / pps;
-  p.counter_bytes = 0;
   p.partial_bytes =
       round_up((size_t)batch * n_kv_heads * p.n_split * p.group * (d + 4) * sizeof(float), 256);
   p.prep_bytes = prep_region_bytes(d, batch, n_q, n_q_heads, n_kv_heads, kb);
@@ -428,8 +427,7 @@ static tq::DecodeArgs decode_args(const tq_cache *c, const uint8_t *prep, int32_
   a.seq_lens = seq_lens;
   a.seq_starts = nullptr;
   a.out = out;
-  a.counters = nullptr;
-  a.partials = (float *)(ws + plan.counter_bytes);
+  a.partials = (float *)ws;
   a.batch = batch;
   a.n_q = n_q;
   a.n_q_heads = n_q_heads;
@@ -469,7 +467,7 @@ static int attn_decode_impl(const tq_cache *c, const void *q, int32_t dtype, int
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
                       k_bits_of(c));
-  size_t need = plan.counter_bytes + plan.partial_bytes + plan.prep_bytes;
+  size_t need = plan.partial_bytes + plan.prep_bytes;
   if (!workspace) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -481,7 +479,7 @@ static int attn_decode_impl(const tq_cache *c, const void *q, int32_t dtype, int
   if (!q) return TQ_EINVAL;
   if (!aligned(q, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
   uint8_t *ws = (uint8_t *)workspace;
-  uint8_t *prep = ws + plan.counter_bytes + plan.partial_bytes;
+  uint8_t *prep = ws + plan.partial_bytes;
   hipStream_t s = (hipStream_t)stream;
   if (run_prepare(c, q, dtype, batch, n_q, n_q_heads, prep, s) != hipSuccess) return TQ_EHIP;
   return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
@@ -520,7 +518,7 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
                       k_bits_of(c));
-  size_t need = plan.counter_bytes + plan.partial_bytes + plan.prep_bytes;
+  size_t need = plan.partial_bytes + plan.prep_bytes;
   if (!workspace) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -535,7 +533,7 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   if (n_new > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(slots, 4)))
     return TQ_EALIGN;
   uint8_t *ws = (uint8_t *)workspace;
-  uint8_t *prep = ws + plan.counter_bytes + plan.partial_bytes;
+  uint8_t *prep = ws + plan.partial_bytes;
   hipStream_t s = (hipStream_t)stream;
 
   tq::EncodeArgs ek, ev;
@@ -587,7 +585,7 @@ int tq_attn_decode_prepared(const tq_cache *c, const void *prep, int32_t batch, 
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
                       k_bits_of(c));
-  size_t need = plan.counter_bytes + plan.partial_bytes;
+  size_t need = plan.partial_bytes;
   if (!workspace) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -613,7 +611,7 @@ int tq_attn_decode_split(const tq_cache *c, const void *prep, int32_t batch, int
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
                       k_bits_of(c));
-  size_t need = plan.counter_bytes + plan.partial_bytes;
+  size_t need = plan.partial_bytes;
   if (!workspace) {
     *workspace_bytes = need;
     return TQ_OK;
@@ -644,7 +642,7 @@ int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
                       k_bits_of(c));
-  if (workspace_bytes < plan.counter_bytes + plan.partial_bytes) return TQ_EWORKSPACE;
+  if (workspace_bytes < plan.partial_bytes) return TQ_EWORKSPACE;
   tq::DecodeArgs a = decode_args(c, nullptr, batch, n_q, n_q_heads, nullptr, max_pages, nullptr, 0,
                                  0.f, out, (uint8_t *)workspace, plan);
   return hip_status(tq::launch_decode_merge(a, c->head_dim, (hipStream_t)stream));

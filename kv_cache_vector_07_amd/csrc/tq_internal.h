@@ -95,7 +95,6 @@ struct DecodePlan {
   int wg_per_seq;         // decode workgroups per (split, KV head, sequence)
   int pages_per_split;
   int n_split;
-  size_t counter_bytes;   // reserved (0)
   size_t partial_bytes;   // [B*Hkv][n_split][group] x (d + 4) float32
   size_t prep_bytes;      // query region (tq_attn_decode only)
   bool mfma;              // the shape is one the MFMA decode kernel covers
@@ -119,7 +118,6 @@ struct DecodeArgs {
   const int32_t *seq_starts;  // first visible token per sequence (or null: 0)
   float *out;             // [B][n_q][Hq][d]
   float *partials;
-  uint32_t *counters;
   int batch, n_q, n_q_heads, n_kv_heads;
   int causal_tail;
   float scale;
