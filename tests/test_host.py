@@ -107,3 +107,25 @@ def test_split_workspace_follows_the_plan(d):
         n_split = -(-maxp // pps)
         want = -(-(B * 8 * n_split * rows * (d + 4) * 4) // 256) * 256
         assert _prepared_ws(dsc, B, nq, Hq, maxp) == want, (B, nq, Hq, maxp)
+
+
+# ---- the product path stands apart from the oracle ----------------------------
+
+def test_package_never_imports_the_oracle():
+    """The binding and the HIP sources name nothing under oracle/, and importing
+    the package (binding included) leaves the oracle unloaded."""
+    import pathlib
+    root = pathlib.Path(__file__).resolve().parent.parent
+    pkg = root / "kv_cache_vector_07_amd"
+    for f in list(pkg.glob("*.py")) + list((pkg / "csrc").glob("*")):
+        if f.is_file() and f.suffix in (".py", ".hip", ".cpp", ".h"):
+            text = f.read_text()
+            assert "import oracle" not in text and "from oracle" not in text, f
+            assert "tq_oracle" not in text, f
+    code = ("import sys; import kv_cache_vector_07_amd, kv_cache_vector_07_amd.tq, "
+            "kv_cache_vector_07_amd.inputs; "
+            "print(any(m == 'oracle' or m.startswith('oracle.') for m in sys.modules))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       timeout=120, cwd=str(root))
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "False"
