@@ -104,10 +104,13 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // n_split * Hkv a multiple of 8 they land on the same XCD and share its L2.
 // With a causal tail a workgroup stops at the last token its rows can see.
 //
-// At d = 128 with one group, everything one block needs (key records, sidecars,
-// V words) is loaded one block ahead; two register sets alternate between even
-// and odd pages so that no copy is needed. Otherwise the block's loads are
-// issued at its start, to keep two waves per SIMD.
+// With TWO_SETS (d = 128, one group, more than two pages per split),
+// everything one block needs (key records, sidecars, V words) is loaded one
+// block ahead; two register sets alternate between even and odd pages so that
+// no copy is needed. Otherwise the block's loads are issued at its start: at
+// d = 256 to keep two waves per SIMD, and at d = 128 with two pages or fewer
+// per split, where a wave sees at most two blocks and the one-set kernel
+// (about 115 VGPRs against 180) finishes sooner.
 
 // Copies the packed scoring operand of a query group (NMU x 64 lanes x 32 bytes,
 // then NMU x 64 scale words) into LDS.
@@ -133,8 +136,9 @@ struct MfmaBlock {
 // NG query groups (4 rows each) share a workgroup: the key and V operands of a
 // block are built once and each MFMA operand of the keys or V bits meets the NG
 // query operands in turn. NG = 1 gives each group its own workgroup.
-template <int D, int NG, int VBITS, int KBITS>
+template <int D, int NG, int VBITS, int KBITS, bool TWO_SETS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2 : 1))) void decode_mfma_kernel(DecodeArgs a) {
+  static_assert(!TWO_SETS || (D == 128 && NG == 1), "two register sets only at d = 128 with one group");
   constexpr int NPK = k_planes(KBITS);      // key code planes (then the sign plane)
   constexpr int NMU = mfma_per_tile(D, KBITS);   // scaled MFMAs per 16-token scoring tile
   constexpr int NCH = D / 128;              // 128-coordinate chunks per token
@@ -541,7 +545,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
 
   // the first block's loads go out before the query operand is staged, so the
   // two fetches overlap
-  if constexpr (D == 128 && NG == 1) {
+  if constexpr (TWO_SETS) {
     MfmaBlock<D, VBITS, KBITS> d0, d1;
     if (pg0 < pg1) load_block(d0, pg0);
     // the packed query operand is shared by the four waves: keep it in LDS
@@ -555,7 +559,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
       process(d1, pg + 1);
     }
   } else {
-    // one register set (at d = 256 two would cost the second wave per SIMD)
+    // one register set
     stage();
     __syncthreads();
     for (int pg = pg0; pg < pg1; ++pg) {
@@ -719,10 +723,16 @@ template <int D, int VBITS, int KBITS>
 hipError_t launch_split_bits(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.wg_per_seq);
   switch (a.plan.groups_per_wg) {
-    case 1: hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS, KBITS>), grid, dim3(256), 0, s, a); break;
+    case 1:
+      // loads one block ahead pay off once a wave sees more than two blocks
+      if (D == 128 && a.plan.pages_per_split > 2)
+        hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS, KBITS, D == 128>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS, KBITS, false>), grid, dim3(256), 0, s, a);
+      break;
     case 2:
       if constexpr (D == 128) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, 2, VBITS, KBITS>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, 2, VBITS, KBITS, false>), grid, dim3(256), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;

@@ -150,6 +150,9 @@ DEC_CASES = [
     (128, 1, 16, 1, [900], "bf16", "outlier", 0, 13),                 # 16 rows at d=128: two workgroups of two groups
     (128, 2, 8, 40, [700, 300], "bf16", "normal", 0, 14),             # 160 rows per KV head
     (128, 1, 4, 64, [30, 600], "bf16", "outlier", 1, 15),             # 256 causal rows, L < n_q: zero rows
+    # 8 x 8 x 20 pages: 3 pages per split, so d=128 takes the kernel that loads one block
+    # ahead into two register sets (odd page counts, short and empty sequences)
+    (128, 8, 32, 1, [5000, 4700, 1, 300, 5120, 4000, 0, 2500], "bf16", "outlier", 0, 30),
     (256, 2, 4, 48, [520, 47], "bf16", "outlier", 1, 16),             # d=256, 96 causal rows
 ]
 
