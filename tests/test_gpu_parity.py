@@ -522,6 +522,15 @@ def test_mse_only_keys_encode_and_decode(tq, d):
     assert err <= Hn.ATTN_TOL
 
 
+def _decode_wide_table(tq, cache, q, bt, sl):
+    """Decode with the block table padded to 72 columns (the padding is never
+    read): two sequences x 8 KV heads x 72 pages make 3 pages per split, so at
+    d = 128 the kernel that loads one block ahead into two register sets runs."""
+    wide = torch.zeros(bt.shape[0], 72, dtype=bt.dtype, device=bt.device)
+    wide[:, :bt.shape[1]] = bt
+    return tq.tq_attn_decode(cache, Hn.torch_input(q, "bf16"), wide, sl)
+
+
 @pytest.mark.parametrize("d,vb", [(128, 2), (128, 4), (256, 2), (256, 4)])
 def test_v_code_widths(tq, d, vb):
     """V codes of 2 and 4 bits (v_bits): the encode's codes and norms against the
@@ -567,10 +576,11 @@ def test_v_code_widths(tq, d, vb):
                                Hn.torch_input(q1, "bf16"), bt, sl)
     q4 = I.queries(w, 1)                                     # 16 rows, causal tail
     out4 = tq.tq_attn_decode(cache, Hn.torch_input(q4, "bf16"), bt, sl, causal_tail=1)
+    out1w = _decode_wide_table(tq, cache, q1, bt, sl)
     torch.cuda.synchronize()
     kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
     Hn.compare_encode_v(O.unpack_v(vp, aslots.cpu().numpy(), H, d, 256, vb), nv.astype(np.float64), cbv)
-    for q, out, causal in ((q1, out1, False), (q4, out4, True)):
+    for q, out, causal in ((q1, out1, False), (q4, out4, True), (q1, out1w, False)):
         ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens1, H, 256,
                             Hn.scale_of(d), causal_tail=causal, cb_v=cbv, v_bits=vb)
         err = Hn.attn_rel_err(out.cpu().numpy(), ref)
@@ -625,10 +635,11 @@ def test_k_code_widths(tq, d, kb, vb):
                                Hn.torch_input(q1, "bf16"), bt, sl)
     q4 = I.queries(w, 1)
     out4 = tq.tq_attn_decode(cache, Hn.torch_input(q4, "bf16"), bt, sl, causal_tail=1)
+    out1w = _decode_wide_table(tq, cache, q1, bt, sl)
     torch.cuda.synchronize()
     kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
     Hn.compare_encode_k(O.unpack_k(kp, aslots.cpu().numpy(), H, d, 256, kb), nk.astype(np.float64), cbk, S)
-    for q, out, causal in ((q1, out1, False), (q4, out4, True)):
+    for q, out, causal in ((q1, out1, False), (q4, out4, True), (q1, out1w, False)):
         ref = O.attn_decode(kp, vp, cbk, S, q.astype(np.float64), table, lens1, H, 256, Hn.scale_of(d),
                             causal_tail=causal, cb_v=cbv, v_bits=vb, k_bits=kb)
         err = Hn.attn_rel_err(out.cpu().numpy(), ref)
