@@ -13,6 +13,7 @@ comes from HBM. Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import ctypes as C
 import hashlib
 import json
@@ -295,6 +296,9 @@ def main():
                     help="chunk length of the chunked-prefill attention measurement (0: skip)")
     ap.add_argument("--no-dense-baseline", action="store_true",
                     help="skip the uncompressed bf16 decode baseline")
+    ap.add_argument("--context", type=int, default=0,
+                    help="override the context length of an equal-length workload (a sweep "
+                         "point, named <workload>_ctx<L>; not the headline configuration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
@@ -309,6 +313,11 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
     w = I.workload(args.workload)
+    if args.context:
+        if not w.fixed_len:
+            print(json.dumps({"error": "--context needs an equal-length workload"}))
+            sys.exit(2)
+        w = dataclasses.replace(w, name=f"{w.name}_ctx{args.context}", fixed_len=args.context)
     d, H, Hq, B, nq = w.head_dim, w.n_kv_heads, w.n_q_heads, w.batch, w.n_q
     lens = I.seq_lens(w)
     table_np, n_pages = I.page_table(w, lens, shuffle=w.batch > 1)
