@@ -107,7 +107,7 @@ typedef struct {
                            v_thresholds, the bit-width variant (2.125 or 4.125
                            bits/dim at d = 128); v_pool sections are then
                            tq_v_page_bytes_bits(d, P, v_bits). Other values:
-                           TQ_EINVAL. K is always 3-bit.                        */
+                           TQ_EINVAL. The K code width is k_bits below.         */
   float v_levels[16];   /* with v_bits 2 or 4: the first 2^v_bits entries,
                            strictly ascending and odd (else TQ_EINVAL)          */
   float v_thresholds[15]; /* with v_bits 2 or 4: the first 2^v_bits - 1         */

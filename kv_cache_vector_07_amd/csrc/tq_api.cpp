@@ -14,6 +14,8 @@ namespace {
 bool supported_dim(int d) { return d == 128 || d == 256; }
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+int check_codebooks(const tq_cache *c);
+
 int check_cache(const tq_cache *c) {
   if (!c) return TQ_EINVAL;
   if (c->head_dim <= 0 || c->n_kv_heads <= 0 || c->page_size <= 0 || c->n_pages <= 0)
@@ -21,6 +23,11 @@ int check_cache(const tq_cache *c) {
   if (!supported_dim(c->head_dim) || c->page_size != TQ_PAGE_SIZE) return TQ_EUNSUPPORTED;
   if (!c->k_pool || !c->v_pool) return TQ_EINVAL;
   if (!aligned(c->k_pool, 256) || !aligned(c->v_pool, 256)) return TQ_EALIGN;
+  return check_codebooks(c);
+}
+
+// Code widths, key mode and codebooks of a descriptor (everything but the pools)
+int check_codebooks(const tq_cache *c) {
   if (c->k_mse_only != 0 && c->k_mse_only != 1) return TQ_EINVAL;
   // the decode kernels split each level into odd bit-plane weights: the
   // codebooks must be strictly increasing and odd (c[n-1-k] = -c[k])
@@ -348,7 +355,7 @@ static int prepare_checks(const tq_cache *c, int32_t dtype, int32_t batch, int32
                           int32_t n_q_heads) {
   if (!c) return TQ_EINVAL;
   if (c->head_dim <= 0 || c->n_kv_heads <= 0) return TQ_EINVAL;
-  if (c->k_mse_only != 0 && c->k_mse_only != 1) return TQ_EINVAL;
+  if (int st = check_codebooks(c)) return st;
   if (!supported_dim(c->head_dim)) return TQ_EUNSUPPORTED;
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   if (batch <= 0 || n_q <= 0 || n_q_heads <= 0 || n_q_heads % c->n_kv_heads) return TQ_EINVAL;

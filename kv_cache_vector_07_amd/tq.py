@@ -154,6 +154,7 @@ class Cache:
         import torch
         self.head_dim, self.n_kv_heads, self.n_pages = head_dim, n_kv_heads, n_pages
         self.page_size = TQ_PAGE_SIZE
+        self.qjl_seed = qjl_seed
         levels, thr, S = codebook if codebook is not None else tq_build_codebook(head_dim, 3, qjl_seed)
         self.levels, self.thresholds, self.qjl_host = levels, thr, S
         # V codes of v_bits bits: 3 shares the K codebook; 2 and 4 bring their own

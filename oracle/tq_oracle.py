@@ -60,7 +60,7 @@ __all__ = [
     "codebook", "splitmix64", "qjl_matrix", "fp16_rne", "quantize", "encode",
     "k_page_bytes", "v_page_bytes", "pack_k", "pack_v", "unpack_k", "unpack_v",
     "gather_k", "gather_v", "rotate_query", "score", "attn_decode", "dequant_k",
-    "dequant_v", "bf16_to_f64", "dense_attn_decode", "encode_k_mse_only",
+    "dequant_v", "dense_attn_decode", "encode_k_mse_only",
 ]
 
 # sqrt(pi/2): the QJL estimator constant numerator (R9); divided by m at use.
@@ -485,11 +485,6 @@ def unpack_v(pool: np.ndarray, slots, H: int, d: int, P: int, vb: int = 3) -> di
     return {"idx": idx, "N": N}
 
 
-def _seq_slots(block_table_row, L: int, P: int) -> np.ndarray:
-    t = np.arange(L, dtype=np.int64)
-    return np.asarray(block_table_row, dtype=np.int64)[t // P] * P + t % P
-
-
 def gather_k(pool, block_table_row, L, kv_head, H, d, P, kb: int = 3):
     """kb-bit K records of tokens 0..L-1 of one sequence and one KV head."""
     kpb = k_page_bytes(d, P, kb)
@@ -612,12 +607,6 @@ def dequant_k(idx, sign, N, G, cb: Codebook, S, with_qjl: bool = True) -> np.nda
 def dequant_v(idx, N, cb: Codebook) -> np.ndarray:
     """V_tilde = N * Pi c[idx]."""
     return np.asarray(N, np.float64)[..., None] * fwht(cb.levels[np.asarray(idx)])
-
-
-def bf16_to_f64(bits) -> np.ndarray:
-    """Exact value of bfloat16 bit patterns (uint16) as float64."""
-    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)
 
 
 def dense_attn_decode(k, v, q, seq_lens, scale):

@@ -139,5 +139,15 @@ def codebook_from_cache(cache, density: str = "gaussian"):
     return cb
 
 
+def oracle_qjl(cache):
+    """The reference's own QJL matrix for the cache's seed. It must equal, bit for
+    bit, the matrix the cache descriptor points at (built by the library's host
+    code), so the reference and the GPU see the same S without the reference
+    taking it from the library."""
+    S = O.qjl_matrix(cache.head_dim, cache.qjl_seed)
+    assert np.array_equal(S, cache.qjl_host), "library S differs from the reference's S"
+    return S
+
+
 def scale_of(d: int) -> float:
     return 1.0 / math.sqrt(d)

@@ -298,3 +298,23 @@ def test_k_widths_page_bytes_validation_and_operand_size(L):
     grp3 = 5 * (64 * 32 + 64 * 4) + 64
     grp4 = 9 * (64 * 32 + 64 * 4) + 64
     assert sz.value - base == (2 * 2 * 1 * grp4 + 255) // 256 * 256 - (2 * 2 * 1 * grp3 + 255) // 256 * 256
+
+
+def test_prepare_validates_code_widths_and_codebooks(L):
+    """tq_query_prepare checks the descriptor's code widths and codebooks as every
+    decode call does: a K width or codebook the kernels cannot take is rejected
+    instead of being prepared as 3-bit."""
+    dsc = _desc(H=2)
+    prep = C.c_size_t(0)
+    prepare = lambda: L.tq_query_prepare(C.byref(dsc), FAKE, 0, 2, 1, 8, None, C.byref(prep), None)
+    assert prepare() == tq.TQ_OK
+    dsc.k_bits = 5
+    assert prepare() == tq.TQ_EINVAL
+    dsc.k_bits = 4                                   # k_levels still zero: not increasing
+    assert prepare() == tq.TQ_EINVAL
+    dsc.k_bits = 3
+    dsc.levels[0] = dsc.levels[0] * 1.01             # 3-bit codebook no longer odd
+    assert prepare() == tq.TQ_EINVAL
+    dsc = _desc(H=2)
+    dsc.v_bits = 7
+    assert prepare() == tq.TQ_EINVAL

@@ -56,14 +56,14 @@ def _check_encode_ranges(cache, w, table, lens, b, ranges):
         slots = table[b][t // 256].astype(np.int64) * 256 + t % 256
         k = I.kv_tokens(w, "k", b, t0, t1).astype(np.float64)
         v = I.kv_tokens(w, "v", b, t0, t1).astype(np.float64)
-        rk = Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k, cb, cache.qjl_host)
+        rk = Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k, cb, Hn.oracle_qjl(cache))
         rv = Hn.compare_encode_v(O.unpack_v(vp, slots, H, d, 256), v, cb)
         print(f"  encode tokens {t0}..{t1} of seq {b}: K {rk}  V {rv}", flush=True)
     return kp, vp, cb
 
 
 def _check_decode(cache, w, q, out, kp, vp, cb, table, lens, pairs, causal=False):
-    ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens,
+    ref = O.attn_decode(kp, vp, cb, Hn.oracle_qjl(cache), q.astype(np.float64), table, lens,
                         w.n_kv_heads, 256, 1 / math.sqrt(w.head_dim), causal_tail=causal,
                         pairs=pairs)
     g = w.group

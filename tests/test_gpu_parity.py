@@ -66,7 +66,7 @@ def test_encode_parity(tq, case):
     cb = Hn.codebook_from_cache(cache)
     gk = O.unpack_k(kp, slots, H, d, 256)
     gv = O.unpack_v(vp, slots, H, d, 256)
-    rk = Hn.compare_encode_k(gk, k.astype(np.float64), cb, cache.qjl_host)
+    rk = Hn.compare_encode_k(gk, k.astype(np.float64), cb, Hn.oracle_qjl(cache))
     rv = Hn.compare_encode_v(gv, v.astype(np.float64), cb)
     print("K boundary report", rk, "V boundary report", rv)
     # untouched records keep their bytes
@@ -106,7 +106,7 @@ def test_encode_deterministic_and_edge_vectors(tq):
     finite = np.ones((n, H), bool)
     finite[5, 1] = False
     sub = lambda dct: {kk: vv[finite][:, None] for kk, vv in dct.items()}
-    Hn.compare_encode_k(sub(gk), k.astype(np.float64)[finite][:, None], cb, cache.qjl_host)
+    Hn.compare_encode_k(sub(gk), k.astype(np.float64)[finite][:, None], cb, Hn.oracle_qjl(cache))
     Hn.compare_encode_v(sub(gv), k.astype(np.float64)[finite][:, None], cb)
 
 
@@ -231,7 +231,7 @@ def test_query_prepare_parity(tq, d):
     q = np.random.default_rng(3).standard_normal((3, 2, 4, d)).astype(np.float32)
     prep = tq.tq_query_prepare(cache, torch.from_numpy(q).cuda())
     rows = tq.prepared_rows(prep, q.shape).cpu().numpy()
-    qt, p = O.rotate_query(q.astype(np.float64), cache.qjl_host)
+    qt, p = O.rotate_query(q.astype(np.float64), Hn.oracle_qjl(cache))
     assert np.max(np.abs(rows[..., 0, :] - qt)) < 1e-5 * np.max(np.abs(qt))
     assert np.max(np.abs(rows[..., 1, :] - p)) < 1e-5 * np.max(np.abs(p))
 
@@ -279,7 +279,7 @@ def test_encode_whole_blocks_and_unaligned(tq, start):
     torch.cuda.synchronize()
     kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
     cb = Hn.codebook_from_cache(cache)
-    Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k.astype(np.float64), cb, cache.qjl_host)
+    Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k.astype(np.float64), cb, Hn.oracle_qjl(cache))
     Hn.compare_encode_v(O.unpack_v(vp, slots, H, d, 256), v.astype(np.float64), cb)
     # slots outside the written range stay zero
     rest = np.setdiff1d(np.arange(5 * 256), slots).astype(np.int64)
@@ -327,9 +327,9 @@ def test_append_decode_matches_separate_calls_and_reference(tq, d, Hq, nq):
     kp, vp = caches[0].k_pool.cpu().numpy(), caches[0].v_pool.cpu().numpy()
     cb = Hn.codebook_from_cache(caches[0])
     s_np = slots.cpu().numpy()
-    Hn.compare_encode_k(O.unpack_k(kp, s_np, H, d, 256), nk.astype(np.float64), cb, caches[0].qjl_host)
+    Hn.compare_encode_k(O.unpack_k(kp, s_np, H, d, 256), nk.astype(np.float64), cb, Hn.oracle_qjl(caches[0]))
     Hn.compare_encode_v(O.unpack_v(vp, s_np, H, d, 256), nv.astype(np.float64), cb)
-    ref = O.attn_decode(kp, vp, cb, caches[0].qjl_host, q.astype(np.float64), table, lens, H, 256,
+    ref = O.attn_decode(kp, vp, cb, Hn.oracle_qjl(caches[0]), q.astype(np.float64), table, lens, H, 256,
                         Hn.scale_of(d))
     err = Hn.attn_rel_err(out_a.cpu().numpy(), ref)
     print(f"  max rel err {err:.3e}", flush=True)
@@ -374,7 +374,7 @@ def test_speculative_verify_and_rollback(tq):
     torch.cuda.synchronize()
     kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
     cb = Hn.codebook_from_cache(cache)
-    ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens, H, 256,
+    ref = O.attn_decode(kp, vp, cb, Hn.oracle_qjl(cache), q.astype(np.float64), table, lens, H, 256,
                         Hn.scale_of(d), causal_tail=True)
     err = Hn.attn_rel_err(out.cpu().numpy(), ref)
     print(f"  verify max rel err {err:.3e}", flush=True)
@@ -430,9 +430,9 @@ def test_chunked_prefill_attention(tq, d, H, Hq, C):
     kp, vp = caches[0].k_pool.cpu().numpy(), caches[0].v_pool.cpu().numpy()
     cb = Hn.codebook_from_cache(caches[0])
     s_np = slots.cpu().numpy()
-    Hn.compare_encode_k(O.unpack_k(kp, s_np, H, d, 256), nk.astype(np.float64), cb, caches[0].qjl_host)
+    Hn.compare_encode_k(O.unpack_k(kp, s_np, H, d, 256), nk.astype(np.float64), cb, Hn.oracle_qjl(caches[0]))
     Hn.compare_encode_v(O.unpack_v(vp, s_np, H, d, 256), nv.astype(np.float64), cb)
-    ref = O.attn_decode(kp, vp, cb, caches[0].qjl_host, q.astype(np.float64), table, lens, H, 256,
+    ref = O.attn_decode(kp, vp, cb, Hn.oracle_qjl(caches[0]), q.astype(np.float64), table, lens, H, 256,
                         Hn.scale_of(d), causal_tail=True)
     err = Hn.attn_rel_err(out_a.cpu().numpy(), ref)
     print(f"  max rel err {err:.3e}", flush=True)
@@ -462,14 +462,14 @@ def test_sphere_codebook_encode_and_decode(tq, d):
         tq.tq_encode_v(cache, Hn.torch_input(v, "bf16"), ts)
         torch.cuda.synchronize()
         kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
-        rk = Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k.astype(np.float64), cb, cache.qjl_host)
+        rk = Hn.compare_encode_k(O.unpack_k(kp, slots, H, d, 256), k.astype(np.float64), cb, Hn.oracle_qjl(cache))
         rv = Hn.compare_encode_v(O.unpack_v(vp, slots, H, d, 256), v.astype(np.float64), cb)
         print("  K", rk, "V", rv)
     q = I.queries(w, 0)
     sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     out = tq.tq_attn_decode(cache, Hn.torch_input(q, "bf16"), bt, sl)
     torch.cuda.synchronize()
-    ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens, H, 256,
+    ref = O.attn_decode(kp, vp, cb, Hn.oracle_qjl(cache), q.astype(np.float64), table, lens, H, 256,
                         Hn.scale_of(d))
     err = Hn.attn_rel_err(out.cpu().numpy(), ref)
     print(f"  max rel err {err:.3e}", flush=True)
@@ -581,7 +581,7 @@ def test_v_code_widths(tq, d, vb):
     kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
     Hn.compare_encode_v(O.unpack_v(vp, aslots.cpu().numpy(), H, d, 256, vb), nv.astype(np.float64), cbv)
     for q, out, causal in ((q1, out1, False), (q4, out4, True), (q1, out1w, False)):
-        ref = O.attn_decode(kp, vp, cb, cache.qjl_host, q.astype(np.float64), table, lens1, H, 256,
+        ref = O.attn_decode(kp, vp, cb, Hn.oracle_qjl(cache), q.astype(np.float64), table, lens1, H, 256,
                             Hn.scale_of(d), causal_tail=causal, cb_v=cbv, v_bits=vb)
         err = Hn.attn_rel_err(out.cpu().numpy(), ref)
         print(f"  rows {q.shape[1] * 4} causal {causal}: max rel err {err:.3e}", flush=True)
@@ -603,7 +603,7 @@ def test_k_code_widths(tq, d, kb, vb):
     cache = tq.Cache(d, H, n_pages, k_bits=kb, v_bits=vb)
     cbk, cbv = O.codebook(d, kb), O.codebook(d, vb)
     assert np.array_equal(cache.k_levels.astype(np.float64), cbk.levels)
-    S = cache.qjl_host
+    S = Hn.oracle_qjl(cache)
     bt = torch.from_numpy(table).cuda()
     for b, L in enumerate(lens):
         t = np.arange(L)

@@ -226,6 +226,59 @@ def test_qjl_estimator_unbiased_monte_carlo():
     assert abs(ests.var() / var - 1) < 0.05
 
 
+def test_qjl_sign_step_end_to_end_monte_carlo():
+    """The whole K path of the reference, unchanged, over K independent draws of
+    S: O.encode(x, cb, S) writes the codes, norms and signs, O.rotate_query and
+    O.score read them back. The codes, r and gamma do not depend on S, so over
+    the draws the estimate has mean <q, x> exactly and the variance
+    (n^2/m)((pi/2)|q~|^2 gamma^2 - <q~, r>^2) of the QJL estimator. The query is
+    chosen with q~ close to r, where that variance is far below the (pi/2)
+    |q~|^2 gamma^2 / m that signs taken from any projection other than S r
+    (e.g. S^T r) would give, so a transposed or otherwise wrong projection in
+    the sign step fails the variance gate. AI Heartland, K-Cache圧縮 flow step 5
+    and the reason for QJL (inner-product scoring stays accurate)."""
+    d = 32
+    cb = O.codebook(d)
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal(d) * np.exp(rng.uniform(-0.7, 0.7, d))
+    base = O.encode(x, cb)                        # S-free part: codes, y, norm
+    r = base["y"] - cb.levels[base["idx"]]
+    gamma, n = np.linalg.norm(r), float(base["norm"])
+    q = O.fwht(r / gamma + 0.35 * rng.standard_normal(d) / math.sqrt(d))   # q~ = Pi q near r
+    qt = O.fwht(q)
+    K = 12000
+    ests = np.empty(K)
+    for k in range(K):
+        S = rng.standard_normal((d, d))
+        e = O.encode(x, cb, S)
+        qt_k, p_k = O.rotate_query(q, S)
+        ests[k] = O.score(qt_k, p_k, e["idx"], e["sign"], e["norm"], e["gamma"], cb, d)
+    var = n ** 2 / d * ((math.pi / 2) * (qt @ qt) * gamma ** 2 - (qt @ r) ** 2)
+    var_wrong = n ** 2 / d * (math.pi / 2) * (qt @ qt) * gamma ** 2
+    assert var < 0.6 * var_wrong                  # the gate separates the two
+    assert abs(ests.mean() - q @ x) < 4 * math.sqrt(var / K)
+    assert abs(ests.var() / var - 1) < 0.05
+
+
+def test_qjl_sign_orientation_with_a_triangular_projection():
+    """With S the upper-triangular all-ones matrix, (S r)_l is the suffix sum
+    r_l + ... + r_{d-1}, which differs from the prefix sums of r @ S: the sign
+    plane of O.encode must be [suffix sum >= 0] (sign bit 1 at zero, R6)."""
+    d = 16
+    cb = O.codebook(d)
+    rng = np.random.default_rng(5)
+    S = np.triu(np.ones((d, d)))
+    differs = 0
+    for _ in range(20):
+        x = rng.standard_normal(d)
+        e = O.encode(x, cb, S)
+        r = e["y"] - cb.levels[e["idx"]]
+        suffix = np.cumsum(r[::-1])[::-1]
+        assert np.array_equal(e["sign"], suffix >= 0)
+        differs += not np.array_equal(suffix >= 0, np.cumsum(r) >= 0)
+    assert differs >= 15                           # the two orientations are told apart
+
+
 def test_residual_energy_band():
     """E[gamma^2] ~ Lloyd-Max distortion of a unit vector (0.0345), sanity band."""
     cb = O.codebook(128)
