@@ -59,8 +59,10 @@ def check_codes(gidx, e, cb):
     return diff
 
 
-def compare_encode_k(gpu: dict, x64: np.ndarray, cb, S) -> dict:
-    """gpu: unpacked K records [n][H][...]; x64: the exact inputs [n][H][d]."""
+def compare_encode_k(gpu: dict, x64: np.ndarray, cb, S, rate_check: bool = True) -> dict:
+    """gpu: unpacked K records [n][H][...]; x64: the exact inputs [n][H][d].
+    rate_check=False leaves the exception-rate gate to a caller that sums the
+    counts over many calls (a short range has too few values for a rate)."""
     e = O.encode(x64, cb, S)
     code_diff = check_codes(gpu["idx"], e, cb)
     vec_cascade = code_diff.any(axis=-1)
@@ -81,9 +83,9 @@ def compare_encode_k(gpu: dict, x64: np.ndarray, cb, S) -> dict:
     assert okG.all(), "G sidecar mismatch"
     n_coded = gpu["idx"].size + gpu["sign"].size + 2 * gpu["N"].size
     exc = int(code_diff.sum() + sdiff.sum() + exN.sum() + exG.sum())
-    assert exc / n_coded < MAX_EXCEPTION_RATE, f"boundary exceptions {exc}/{n_coded}"
+    assert not rate_check or exc / n_coded < MAX_EXCEPTION_RATE, f"boundary exceptions {exc}/{n_coded}"
     return {"code_boundary": int(code_diff.sum()), "sign_boundary": int(sdiff.sum()),
-            "sidecar_midpoint": int(exN.sum() + exG.sum()), "values": n_coded}
+            "sidecar_midpoint": int(exN.sum() + exG.sum()), "values": n_coded, "exceptions": exc}
 
 
 def compare_encode_k_mse_only(gpu: dict, x64: np.ndarray, cb) -> dict:
@@ -106,16 +108,16 @@ def compare_encode_k_mse_only(gpu: dict, x64: np.ndarray, cb) -> dict:
             "values": n_coded}
 
 
-def compare_encode_v(gpu: dict, x64: np.ndarray, cb) -> dict:
+def compare_encode_v(gpu: dict, x64: np.ndarray, cb, rate_check: bool = True) -> dict:
     e = O.encode(x64, cb)
     code_diff = check_codes(gpu["idx"], e, cb)
     okN, exN = _fp16_match(gpu["N"], e["norm"])
     assert okN.all(), "N sidecar mismatch"
     n_coded = gpu["idx"].size + gpu["N"].size
     exc = int(code_diff.sum() + exN.sum())
-    assert exc / n_coded < MAX_EXCEPTION_RATE, f"boundary exceptions {exc}/{n_coded}"
+    assert not rate_check or exc / n_coded < MAX_EXCEPTION_RATE, f"boundary exceptions {exc}/{n_coded}"
     return {"code_boundary": int(code_diff.sum()), "sidecar_midpoint": int(exN.sum()),
-            "values": n_coded}
+            "values": n_coded, "exceptions": exc}
 
 
 def attn_rel_err(gpu_out: np.ndarray, ref_out: np.ndarray) -> float:
