@@ -70,13 +70,15 @@ typedef enum {
   TQ_EUNSUPPORTED = -2, /* valid request outside what the kernels implement       */
   TQ_EALIGN = -3,       /* pool not 256-byte aligned or I/O not 16-byte aligned    */
   TQ_EWORKSPACE = -4,   /* workspace smaller than *workspace_bytes (size written)  */
-  TQ_EHIP = -5          /* a HIP launch or runtime call failed                     */
+  TQ_EHIP = -5,         /* a HIP launch or runtime call failed                     */
+  TQ_ESCRATCH = -6      /* the call needs more than TQ_STATIC_SCRATCH_BYTES         */
 } tq_status;
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
 #define TQ_PAGE_SIZE 256   /* the only page size the kernels implement */
 #define TQ_MAX_GROUP 4096  /* max query rows per KV head per sequence (Hq/Hkv * n_q) */
+#define TQ_STATIC_SCRATCH_BYTES ((size_t)64 << 20)  /* scratch of tq_append_decode_static */
 
 /* Cache descriptor: plain data, owned by the caller, read by every call. */
 typedef struct {
@@ -278,6 +280,32 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
                      int32_t batch, int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
                      int32_t max_pages, const int32_t *seq_lens, int32_t causal_tail, float scale,
                      float *out, void *workspace, size_t *workspace_bytes, void *stream);
+
+/*
+ * tq_append_decode without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. The split partials and prepared queries
+ * live in a static device buffer of TQ_STATIC_SCRATCH_BYTES (64 MiB) that the
+ * library holds on every GPU it runs on until the process ends; the call itself
+ * allocates and frees nothing. The first call on a device (with that device
+ * current, as for every call) looks the buffer up once. A call whose workspace
+ * (the size tq_append_decode reports for the same arguments) exceeds
+ * TQ_STATIC_SCRATCH_BYTES returns TQ_ESCRATCH and launches nothing. The buffer
+ * holds decode and verify steps with a few query rows per KV head (for example
+ * 32 sequences of up to 16K tokens, or 4 sequences of 128K tokens at d = 256
+ * with 16 query rows per KV head); chunked prefill with hundreds of query rows
+ * per KV head needs the caller workspace of tq_append_decode.
+ * The buffer needs no initialisation and is scratch after the call. Every call
+ * on one GPU shares that GPU's buffer: calls that may overlap in time on one GPU
+ * (unordered streams, other host threads) race on it, so the caller must order
+ * them (one stream, or events). Arguments, results and other errors are those
+ * of tq_append_decode.
+ */
+int tq_append_decode_static(const tq_cache *c, const void *k_new, const void *v_new,
+                            int32_t kv_dtype, const int32_t *slots, int32_t n_new, const void *q,
+                            int32_t q_dtype, int32_t batch, int32_t n_q, int32_t n_q_heads,
+                            const int32_t *block_table, int32_t max_pages, const int32_t *seq_lens,
+                            int32_t causal_tail, float scale, float *out, void *stream);
 
 /*
  * The attention part of tq_attn_decode alone (one kernel launch), on queries

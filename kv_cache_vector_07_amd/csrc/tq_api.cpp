@@ -260,6 +260,7 @@ const char *tq_status_string(int32_t s) {
     case TQ_EALIGN: return "misaligned buffer";
     case TQ_EWORKSPACE: return "workspace too small";
     case TQ_EHIP: return "HIP runtime error";
+    case TQ_ESCRATCH: return "needs more than the static scratch (TQ_STATIC_SCRATCH_BYTES) holds";
     default: return "unknown status";
   }
 }
@@ -516,6 +517,18 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
                      int32_t batch, int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
                      int32_t max_pages, const int32_t *seq_lens, int32_t causal_tail, float scale,
                      float *out, void *workspace, size_t *workspace_bytes, void *stream) {
+  return tq::append_decode(c, k_new, v_new, kv_dtype, slots, n_new, q, q_dtype, batch, n_q,
+                           n_q_heads, block_table, max_pages, seq_lens, causal_tail, scale, out,
+                           workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+int tq::append_decode(const tq_cache *c, const void *k_new, const void *v_new, int32_t kv_dtype,
+                      const int32_t *slots, int32_t n_new, const void *q, int32_t q_dtype,
+                      int32_t batch, int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
+                      int32_t max_pages, const int32_t *seq_lens, int32_t causal_tail, float scale,
+                      float *out, void *workspace, size_t *workspace_bytes, void *stream) {
   int st = decode_checks(c, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
                          out, workspace_bytes);
   if (st) return st;
@@ -581,6 +594,8 @@ int tq_append_decode(const tq_cache *c, const void *k_new, const void *v_new, in
   return decode_run(c, prep, batch, n_q, n_q_heads, block_table, max_pages, seq_lens, causal_tail,
                     scale, out, ws, plan, s);
 }
+
+extern "C" {
 
 int tq_attn_decode_prepared(const tq_cache *c, const void *prep, int32_t batch, int32_t n_q,
                             int32_t n_q_heads, const int32_t *block_table, int32_t max_pages,

@@ -159,4 +159,12 @@ struct DenseArgs {
 };
 hipError_t launch_dense_split(const DenseArgs &a, int d, hipStream_t s);
 
+// The whole of tq_append_decode (checks, workspace sizing, launches), shared by
+// the entry point with a caller workspace and the one with the static scratch.
+int append_decode(const tq_cache *c, const void *k_new, const void *v_new, int32_t kv_dtype,
+                  const int32_t *slots, int32_t n_new, const void *q, int32_t q_dtype,
+                  int32_t batch, int32_t n_q, int32_t n_q_heads, const int32_t *block_table,
+                  int32_t max_pages, const int32_t *seq_lens, int32_t causal_tail, float scale,
+                  float *out, void *workspace, size_t *workspace_bytes, void *stream);
+
 }  // namespace tq

@@ -18,6 +18,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 _lib = None
 
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2, -3, -4, -5
+TQ_ESCRATCH = -6
+TQ_STATIC_SCRATCH_BYTES = 64 << 20
 TQ_F32, TQ_BF16 = 0, 1
 TQ_PAGE_SIZE = 256
 TQ_MAX_GROUP = 4096
@@ -26,7 +28,7 @@ EXPORTS = ("tq_k_page_bytes", "tq_v_page_bytes", "tq_k_page_bytes_bits", "tq_v_p
            "tq_build_codebook_sphere",
            "tq_encode_k",
            "tq_encode_v", "tq_query_prepare", "tq_attn_decode", "tq_attn_decode_window",
-           "tq_append_decode",
+           "tq_append_decode", "tq_append_decode_static",
            "tq_attn_decode_prepared", "tq_attn_decode_split", "tq_attn_decode_merge",
            "tq_dense_attn_decode", "tq_dequant", "tq_status_string")
 
@@ -78,6 +80,8 @@ def lib():
                                         vp, C.POINTER(sz), vp]
     L.tq_append_decode.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, vp, i32, vp,
                                    i32, f32, vp, vp, C.POINTER(sz), vp]
+    L.tq_append_decode_static.argtypes = [vp, vp, vp, i32, vp, i32, vp, i32, i32, i32, i32, vp, i32,
+                                          vp, i32, f32, vp, vp]
     L.tq_attn_decode_prepared.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp, vp,
                                           C.POINTER(sz), vp]
     L.tq_attn_decode_split.argtypes = [vp, vp, i32, i32, i32, vp, i32, vp, i32, f32, vp,
@@ -87,7 +91,8 @@ def lib():
     L.tq_dense_attn_decode.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp, f32,
                                        vp, vp, C.POINTER(sz), vp]
     for name in ("tq_build_codebook", "tq_build_codebook_sphere", "tq_encode_k", "tq_encode_v", "tq_query_prepare",
-                 "tq_attn_decode", "tq_attn_decode_window", "tq_append_decode", "tq_attn_decode_prepared",
+                 "tq_attn_decode", "tq_attn_decode_window", "tq_append_decode", "tq_append_decode_static",
+                 "tq_attn_decode_prepared",
                  "tq_attn_decode_split",
                  "tq_attn_decode_merge", "tq_dense_attn_decode", "tq_dequant"):
         getattr(L, name).restype = i32
@@ -310,6 +315,26 @@ def tq_append_decode(cache: Cache, k_new, v_new, slots, q, block_table, seq_lens
     size = C.c_size_t(ws.numel())
     st = L.tq_append_decode(*args(ws.data_ptr()), C.byref(size), _stream(stream))
     _check(st, "tq_append_decode")
+    return out
+
+
+def tq_append_decode_static(cache: Cache, k_new, v_new, slots, q, block_table, seq_lens,
+                            causal_tail: int = 0, scale=None, out=None, stream=None):
+    """tq_append_decode with the library's static device scratch instead of a
+    workspace: the call allocates nothing (out is allocated here only when not
+    given)."""
+    import torch
+    B, n_q, Hq, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(B, n_q, Hq, d, dtype=torch.float32, device=q.device)
+    n_new = int(slots.numel())
+    st = lib().tq_append_decode_static(cache.ref, k_new.data_ptr(), v_new.data_ptr(), _dtype_code(k_new),
+                                       slots.data_ptr(), n_new, q.data_ptr(), _dtype_code(q), B, n_q, Hq,
+                                       block_table.data_ptr(), int(block_table.shape[1]),
+                                       seq_lens.data_ptr(), int(causal_tail), scale, out.data_ptr(),
+                                       _stream(stream))
+    _check(st, "tq_append_decode_static")
     return out
 
 

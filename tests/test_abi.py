@@ -318,3 +318,18 @@ def test_prepare_validates_code_widths_and_codebooks(L):
     dsc = _desc(H=2)
     dsc.v_bits = 7
     assert prepare() == tq.TQ_EINVAL
+
+
+def test_static_scratch_entry_rejects_what_the_buffer_cannot_hold(L):
+    """tq_append_decode_static returns TQ_ESCRATCH, before any HIP call, when the
+    workspace tq_append_decode would need exceeds TQ_STATIC_SCRATCH_BYTES (here a
+    1024-token chunk: 4096 query rows per KV head); argument errors come first."""
+    dsc = _desc(H=8)
+    sz = C.c_size_t(0)
+    args = (C.byref(dsc), FAKE, FAKE, 1, FAKE, 1024, FAKE, 1, 1, 1024, 32, FAKE, 16, FAKE, 1, 0.1, FAKE)
+    assert L.tq_append_decode(*args, None, C.byref(sz), None) == tq.TQ_OK
+    assert sz.value > tq.TQ_STATIC_SCRATCH_BYTES
+    assert L.tq_append_decode_static(*args, None) == tq.TQ_ESCRATCH
+    assert tq.status_string(tq.TQ_ESCRATCH).startswith("needs more than the static scratch")
+    bad = (C.byref(dsc), FAKE, FAKE, 1, FAKE, 1, FAKE, 1, 1, 1, 30, FAKE, 16, FAKE, 0, 0.1, FAKE)
+    assert L.tq_append_decode_static(*bad, None) == tq.TQ_EINVAL        # 30 % 8 != 0
