@@ -630,9 +630,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
 }
 
 // One workgroup per (query row, KV head, sequence). Wave w takes splits
-// w, w + 4, ...: it issues the loads of up to 16 of them at once (the headers are
-// wave-uniform) and folds them with a running log-sum-exp; the four waves then
-// combine in LDS, and wave 0 applies the inverse rotation and writes the row.
+// w, w + 4, ..., 16 at a time: lane c loads the header (m, l, mU) of the c-th,
+// every lane loads its coordinates of all 16 (split indices past the last are
+// clamped, so every load is in bounds and none is branched around), and the
+// splits are folded in order with a running log-sum-exp, each header read from
+// its lane; the four waves then combine in LDS, and wave 0 applies the inverse
+// rotation and writes the row.
 template <int D, bool kRotate>
 __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
   constexpr int R = D / 64;
@@ -650,28 +653,25 @@ __global__ __launch_bounds__(256) void merge_kernel(DecodeArgs a) {
 #pragma unroll
   for (int r = 0; r < R; ++r) x[r] = 0.f;
   for (int base = wv; base < nsplit; base += 4 * CH) {
-    float4 hd[CH];
+    float4 hl = make_float4(-kFltMax, 0.f, -kFltMax, 0.f);
+    if (lane < CH && base + 4 * lane < nsplit)
+      hl = *reinterpret_cast<const float4 *>(part + (size_t)(base + 4 * lane) * stride);
     float v[CH][R];
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int sp = base + 4 * c;
-      if (sp < nsplit) {
-        const float *pr = part + (size_t)sp * stride;
-        hd[c] = *reinterpret_cast<const float4 *>(pr);
+      const float *pr = part + (size_t)min(base + 4 * c, nsplit - 1) * stride;
 #pragma unroll
-        for (int r = 0; r < R; ++r) v[c][r] = pr[kPartHead + lane + 64 * r];
-      } else {
-        hd[c] = make_float4(-kFltMax, 0.f, -kFltMax, 0.f);
-#pragma unroll
-        for (int r = 0; r < R; ++r) v[c][r] = 0.f;
-      }
+      for (int r = 0; r < R; ++r) v[c][r] = pr[kPartHead + lane + 64 * r];
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      if (hd[c].y > 0.f) {   // a split with no visible token has l = 0
-        const float mn = fmaxf(M, hd[c].x), mun = fmaxf(MU, hd[c].z);
-        l = l * __builtin_amdgcn_exp2f(M - mn) + hd[c].y * __builtin_amdgcn_exp2f(hd[c].x - mn);
-        const float f0 = __builtin_amdgcn_exp2f(MU - mun), f1 = __builtin_amdgcn_exp2f(hd[c].z - mun);
+      const float hy = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hl.y), c));
+      if (hy > 0.f) {   // a split with no visible token has l = 0 (as has one past the last)
+        const float hx = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hl.x), c));
+        const float hz = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, hl.z), c));
+        const float mn = fmaxf(M, hx), mun = fmaxf(MU, hz);
+        l = l * __builtin_amdgcn_exp2f(M - mn) + hy * __builtin_amdgcn_exp2f(hx - mn);
+        const float f0 = __builtin_amdgcn_exp2f(MU - mun), f1 = __builtin_amdgcn_exp2f(hz - mun);
 #pragma unroll
         for (int r = 0; r < R; ++r) x[r] = fmaf(x[r], f0, v[c][r] * f1);
         M = mn;
