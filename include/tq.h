@@ -93,7 +93,8 @@ typedef struct {
   float levels[8];      /* c[0..7], strictly ascending and odd, c[7-k] = -c[k]
                            (from tq_build_codebook); otherwise calls return
                            TQ_EINVAL                                              */
-  float thresholds[7];  /* t[0..6], midpoints, thresholds[3] == 0                 */
+  float thresholds[7];  /* t[0..6], midpoints, thresholds[3] == 0, strictly
+                           ascending (else TQ_EINVAL)                           */
   int32_t k_mse_only;   /* 0: K keeps the QJL stage ("K-Cache圧縮" steps 4-5, the
                            pages' K path). 1: keys without it, the ablation of
                            the pages' reason for QJL (inner-product scoring):
@@ -112,7 +113,8 @@ typedef struct {
                            TQ_EINVAL. The K code width is k_bits below.         */
   float v_levels[16];   /* with v_bits 2 or 4: the first 2^v_bits entries,
                            strictly ascending and odd (else TQ_EINVAL)          */
-  float v_thresholds[15]; /* with v_bits 2 or 4: the first 2^v_bits - 1         */
+  float v_thresholds[15]; /* with v_bits 2 or 4: the first 2^v_bits - 1,
+                           strictly ascending (else TQ_EINVAL)                  */
   int32_t k_bits;       /* K code width. 0 or 3: 3-bit K with levels and
                            thresholds above (the pages' 4.25 bits/dim). 2 or 4:
                            K codes of that width with k_levels and k_thresholds
@@ -122,7 +124,8 @@ typedef struct {
                            TQ_EINVAL.                                           */
   float k_levels[16];   /* with k_bits 2 or 4: the first 2^k_bits entries,
                            strictly ascending and odd (else TQ_EINVAL)          */
-  float k_thresholds[15]; /* with k_bits 2 or 4: the first 2^k_bits - 1         */
+  float k_thresholds[15]; /* with k_bits 2 or 4: the first 2^k_bits - 1,
+                           strictly ascending (else TQ_EINVAL)                  */
 } tq_cache;
 
 /* Bytes of one (page, KV head) section; 0 for unsupported d or P. */

@@ -38,12 +38,20 @@ int check_codebooks(const tq_cache *c) {
     }
     return true;
   };
-  if (!odd_increasing(c->levels, 8)) return TQ_EINVAL;
+  // thresholds strictly increasing (the encoders locate a code by binary search)
+  auto increasing = [](const float *t, int n) {
+    for (int k = 0; k < n; ++k)
+      if (!isfinite(t[k]) || (k > 0 && !(t[k] > t[k - 1]))) return false;
+    return true;
+  };
+  if (!odd_increasing(c->levels, 8) || !increasing(c->thresholds, 7)) return TQ_EINVAL;
   if (c->v_bits != 0 && c->v_bits != 2 && c->v_bits != 3 && c->v_bits != 4) return TQ_EINVAL;
-  if ((c->v_bits == 2 || c->v_bits == 4) && !odd_increasing(c->v_levels, 1 << c->v_bits))
+  if ((c->v_bits == 2 || c->v_bits == 4) &&
+      (!odd_increasing(c->v_levels, 1 << c->v_bits) || !increasing(c->v_thresholds, (1 << c->v_bits) - 1)))
     return TQ_EINVAL;
   if (c->k_bits != 0 && c->k_bits != 2 && c->k_bits != 3 && c->k_bits != 4) return TQ_EINVAL;
-  if ((c->k_bits == 2 || c->k_bits == 4) && !odd_increasing(c->k_levels, 1 << c->k_bits))
+  if ((c->k_bits == 2 || c->k_bits == 4) &&
+      (!odd_increasing(c->k_levels, 1 << c->k_bits) || !increasing(c->k_thresholds, (1 << c->k_bits) - 1)))
     return TQ_EINVAL;
   return TQ_OK;
 }

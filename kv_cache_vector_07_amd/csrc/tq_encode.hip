@@ -57,7 +57,7 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
   constexpr size_t KREC = (size_t)(KB + 1) * D / 8;
   constexpr size_t KCODES = (size_t)kPage * KREC;
   constexpr size_t KSEC = KCODES + 4 * kPage;
-  __shared__ float4 s_r[16 * VT][D / 4];    // residuals
+  __shared__ float4 s_r[16 * VT][D / 4 + 1];   // residuals (rows padded: no bank conflicts)
   __shared__ uint64_t s_code[VB][KB][R];    // code bit planes
   __shared__ uint16_t s_sign[VB][D / 16];   // sign bits, 16 rows of S per entry
   __shared__ float s_ng[VB][2];             // N, G
@@ -271,6 +271,405 @@ __device__ void encode_v_block(const EncodeArgs &a, int bx, int head) {
     }
     if (lane == 0) reinterpret_cast<uint16_t *>(sec + VCODES)[side_entry(off)] = f32_to_f16_bits(s_n[u]);
   }
+}
+
+// ------------------------------------------------------------------ bulk encode
+// Four lanes per vector: lane 4 v + p of a wave holds coordinates C p + e
+// (e = 0 .. C - 1, C = D / 4) of the wave's v-th vector, so the norm and all
+// but two rotation stages run in registers (the butterflies at distance C and
+// 2 C are the quad swaps lane ^ 1 and lane ^ 2), and the lane's code bits of
+// each 32-coordinate group are that group's plane words. A workgroup encodes 64
+// vectors, 16 per wave.
+
+// Loads the C coordinates of one vector this lane holds.
+template <int D, int DT>
+__device__ inline void load_quarter(const void *x, size_t base, int p, float (&y)[D / 4]) {
+  constexpr int C = D / 4;
+  if constexpr (DT == TQ_F32) {
+    const float4 *src = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(x) + base + C * p);
+#pragma unroll
+    for (int q = 0; q < C / 4; ++q) {
+      const float4 f = src[q];
+      y[4 * q] = f.x;
+      y[4 * q + 1] = f.y;
+      y[4 * q + 2] = f.z;
+      y[4 * q + 3] = f.w;
+    }
+  } else {
+    const uint4 *src = reinterpret_cast<const uint4 *>(reinterpret_cast<const uint16_t *>(x) + base + C * p);
+#pragma unroll
+    for (int q = 0; q < C / 8; ++q) {
+      const uint4 u = src[q];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        y[8 * q + 2 * k] = __uint_as_float(w[k] << 16);
+        y[8 * q + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+// Unnormalised Walsh-Hadamard butterflies over a vector spread over a quad of
+// lanes (coordinate C p + e in y[e] of lane p), distances 1, 2, ..., 2 C in
+// increasing order, each pair (a, b) -> (a + b, a - b).
+template <int D>
+__device__ inline void fwht_quad(float (&y)[D / 4], int p) {
+  constexpr int C = D / 4;
+#pragma unroll
+  for (int h = 1; h < C; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < C; ++e)
+      if (!(e & h)) {
+        const float a = y[e], b = y[e | h];
+        y[e] = a + b;
+        y[e | h] = a - b;
+      }
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const float o = xor_lane<1>(y[e]);
+    y[e] = (p & 1) ? o - y[e] : y[e] + o;
+  }
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    const float o = xor_lane<2>(y[e]);
+    y[e] = (p & 2) ? o - y[e] : y[e] + o;
+  }
+}
+
+// Steps 1-3 on a quad: norm (returned), y = Pi x / ||x|| (0 for a zero vector).
+template <int D>
+__device__ inline float front_quad(float (&y)[D / 4], int p) {
+  constexpr int C = D / 4;
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < C; ++e) ss = fmaf(y[e], y[e], ss);
+  ss += xor_lane<1>(ss);
+  ss += xor_lane<2>(ss);
+  const float n = sqrtf(ss);
+  const float inv = n > 0.f ? 1.0f / n : 0.f;
+#pragma unroll
+  for (int e = 0; e < C; ++e) y[e] *= inv;
+  fwht_quad<D>(y, p);
+#pragma unroll
+  for (int e = 0; e < C; ++e) y[e] *= rsqrt_dim<D>();
+  return n;
+}
+
+// Bitwise select: a where the mask m is all ones, b where it is zero (one
+// v_bfi_b32; written this way so that no select becomes a branch).
+__device__ inline uint32_t bsel(uint32_t m, uint32_t a, uint32_t b) { return (a & m) | (b & ~m); }
+__device__ inline uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ inline uint32_t ge_mask(float y, uint32_t t) {
+  return y >= __builtin_bit_cast(float, t) ? 0xFFFFFFFFu : 0u;
+}
+
+// Code = #{k : t_k <= y} (a tie goes to the upper cell) by binary search over
+// the ascending thresholds, NB-bit codes; m[j] is the all-ones mask of code bit
+// j (the bit planes), the code is returned.
+template <int NB>
+__device__ inline int code_bsearch(const Codebook &cb, float y, uint32_t (&m)[NB]) {
+  uint32_t T[(1 << NB) - 1];
+#pragma unroll
+  for (int k = 0; k < (1 << NB) - 1; ++k) T[k] = fbits(cb.thresholds[k]);
+  if constexpr (NB == 2) {
+    m[1] = ge_mask(y, T[1]);
+    m[0] = ge_mask(y, bsel(m[1], T[2], T[0]));
+  } else if constexpr (NB == 3) {
+    m[2] = ge_mask(y, T[3]);
+    m[1] = ge_mask(y, bsel(m[2], T[5], T[1]));
+    m[0] = ge_mask(y, bsel(m[2], bsel(m[1], T[6], T[4]), bsel(m[1], T[2], T[0])));
+  } else {
+    static_assert(NB == 4, "code width");
+    m[3] = ge_mask(y, T[7]);
+    m[2] = ge_mask(y, bsel(m[3], T[11], T[3]));
+    m[1] = ge_mask(y, bsel(m[3], bsel(m[2], T[13], T[9]), bsel(m[2], T[5], T[1])));
+    const uint32_t t0 = bsel(m[3], bsel(m[2], bsel(m[1], T[14], T[12]), bsel(m[1], T[10], T[8])),
+                             bsel(m[2], bsel(m[1], T[6], T[4]), bsel(m[1], T[2], T[0])));
+    m[0] = ge_mask(y, t0);
+  }
+  int idx = 0;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) idx |= (int)(m[j] & (1u << j));
+  return idx;
+}
+
+// c[code] from the bit-plane masks, by bitwise selects over the levels.
+template <int NB, int BASE = 0>
+__device__ inline uint32_t level_bits(const Codebook &cb, const uint32_t (&m)[NB]) {
+  if constexpr (NB == 0) {
+    return fbits(cb.levels[BASE]);
+  } else {
+    // the top remaining bit is m[NB - 1]
+    uint32_t mm[NB - 1 > 0 ? NB - 1 : 1];
+#pragma unroll
+    for (int j = 0; j + 1 < NB; ++j) mm[j] = m[j];
+    if constexpr (NB == 1) {
+      return bsel(m[0], fbits(cb.levels[BASE + 1]), fbits(cb.levels[BASE]));
+    } else {
+      const uint32_t lo = level_bits<NB - 1, BASE>(cb, reinterpret_cast<const uint32_t (&)[NB - 1]>(mm));
+      const uint32_t hi = level_bits<NB - 1, BASE + (1 << (NB - 1))>(cb, reinterpret_cast<const uint32_t (&)[NB - 1]>(mm));
+      return bsel(m[NB - 1], hi, lo);
+    }
+  }
+}
+
+// K encode of 64 vectors: codes, residual and G on quads; the residuals go to
+// LDS, where Z = R S^T runs on fp32 MFMA as in encode_k_block, and the signs
+// come back by ballot; each lane then stores its groups' record words.
+template <int D, int DT, int KB>
+__device__ void encode_k_bulk(const EncodeArgs &a, long blk) {
+  constexpr int C = D / 4;                  // coordinates per lane
+  constexpr int NGL = C / 32;               // 32-coordinate groups per lane: 1 or 2
+  constexpr int VB = 64, VT = 4;            // vectors per workgroup, 16-vector MFMA tiles
+  constexpr int RT = D / 16 / kWaves;       // 16-row tiles of S per wave: 2 or 4
+  constexpr size_t KREC = (size_t)(KB + 1) * D / 8;
+  constexpr size_t KCODES = (size_t)kPage * KREC;
+  constexpr size_t KSEC = KCODES + 4 * kPage;
+  __shared__ float4 s_r[VB][D / 4 + 1];     // residuals (rows padded: no bank conflicts)
+  __shared__ uint16_t s_sign[VB][D / 16];   // sign bits, 16 rows of S per entry
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l16 = lane & 15, kq = lane >> 4;
+  const int v = lane >> 2, p = lane & 3;
+  const int u = 16 * wave + v;              // this lane's vector in the workgroup
+  const long total = (long)a.n_tokens * a.n_heads;
+  const long v0 = blk * VB;
+  const int nv = (int)min((long)VB, total - v0);
+  const bool live = u < nv;
+
+  const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
+  const bool qjl = a.qjl != nullptr;        // MSE-only keys skip z = S r
+  constexpr bool kHoist = D == 128;
+  float4 sreg[kHoist ? RT * (D / 16) : 1];
+  if (kHoist && qjl) {
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int c = 0; c < D / 16; ++c)
+        sreg[t * (D / 16) + c] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
+  }
+
+  float y[C];
+  if (live) {
+    load_quarter<D, DT>(a.x, (size_t)(v0 + u) * D, p, y);
+  } else {
+#pragma unroll
+    for (int e = 0; e < C; ++e) y[e] = 0.f;
+  }
+  const float n = front_quad<D>(y, p);
+  uint32_t w[NGL][KB];
+#pragma unroll
+  for (int g = 0; g < NGL; ++g)
+#pragma unroll
+    for (int j = 0; j < KB; ++j) w[g][j] = 0u;
+  float rr = 0.f;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    uint32_t m[KB];
+    code_bsearch<KB>(a.cb, y[e], m);
+    y[e] -= __builtin_bit_cast(float, level_bits<KB>(a.cb, m));
+    rr = fmaf(y[e], y[e], rr);
+#pragma unroll
+    for (int j = 0; j < KB; ++j) w[e / 32][j] |= m[j] & (1u << (e % 32));
+  }
+  rr += xor_lane<1>(rr);
+  rr += xor_lane<2>(rr);
+  const float gm = sqrtf(rr);
+  // residuals of dead vectors are zero (their Z rows are not used)
+#pragma unroll
+  for (int q = 0; q < C / 4; ++q)
+    s_r[u][(C / 4) * p + q] = live ? make_float4(y[4 * q], y[4 * q + 1], y[4 * q + 2], y[4 * q + 3])
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
+
+  // Z tile (vector tile vt, row tile rt) = sum over i of R[16 vt + .][i] S[16 rt + .][i]
+  if (qjl) {
+    v4f acc[VT][RT];
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[vt][t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+      float4 bv[RT], av[VT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        if constexpr (kHoist)
+          bv[t] = sreg[t * (D / 16) + c];
+        else
+          bv[t] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
+      }
+#pragma unroll
+      for (int vt = 0; vt < VT; ++vt) av[vt] = s_r[16 * vt + l16][4 * c + kq];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+          for (int t = 0; t < RT; ++t)
+            acc[vt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[vt][m], bv[t][m], acc[vt][t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int vt = 0; vt < VT; ++vt)
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint64_t m = __ballot(acc[vt][t][r] >= 0.f);
+          const int uu = 16 * vt + 4 * kq + r;
+          if (l16 == 0) s_sign[uu][wave * RT + t] = (uint16_t)(m >> (16 * kq));
+        }
+  }
+  __syncthreads();
+
+  if (!live) return;
+  const long vec = v0 + u;
+  const long tok = vec / a.n_heads;
+  const int head = (int)(vec % a.n_heads);
+  const int slot = a.slots[tok];
+  uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * KSEC;
+  const int off = slot % kPage;
+  uint32_t *rec = reinterpret_cast<uint32_t *>(sec + (size_t)off * KREC);
+#pragma unroll
+  for (int g = 0; g < NGL; ++g) {
+    const int sg = NGL * p + g;             // coordinate group of these words
+    const uint32_t sw = qjl ? (uint32_t)s_sign[u][2 * sg] | ((uint32_t)s_sign[u][2 * sg + 1] << 16) : 0u;
+    if constexpr (KB == 3) {
+      reinterpret_cast<uint4 *>(rec)[sg] = make_uint4(w[g][0], w[g][1], w[g][2], sw);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KB; ++j) rec[(KB + 1) * sg + j] = w[g][j];
+      rec[(KB + 1) * sg + KB] = sw;
+    }
+  }
+  if (p == 0) {
+    reinterpret_cast<uint16_t *>(sec + KCODES)[side_entry(off)] = f32_to_f16_bits(n);
+    reinterpret_cast<uint16_t *>(sec + KCODES + 2 * kPage)[side_entry(off)] = f32_to_f16_bits(gm);
+  }
+}
+
+// V encode of 64 tokens of one KV head: codes on quads; each lane's plane
+// words go to LDS as [plane][group][token]. When the 64 slots are one whole
+// aligned 64-token block of a page, the block's words are assembled from there
+// and stored whole; otherwise each token's bits are set one by one with
+// atomics, leaving the neighbours in the same words intact.
+template <int D, int DT, int VBITS>
+__device__ void encode_v_bulk(const EncodeArgs &a, int bx, int head) {
+  constexpr int C = D / 4;
+  constexpr int NGL = C / 32;
+  constexpr int NGR = D / 32;               // 32-coordinate groups per vector
+  constexpr int TP = 64 + 4;                // token stride of a group row (padded)
+  constexpr size_t VCODES = (size_t)VBITS * D * kPage / 8;
+  constexpr size_t VSEC = VCODES + 2 * kPage;
+  __shared__ __attribute__((aligned(16))) uint32_t s_pl[VBITS][NGR][TP];
+  __shared__ int s_whole;
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int v = lane >> 2, p = lane & 3;
+  const int ut = 16 * wave + v;             // this lane's token in the workgroup
+  const int t0 = bx * 64;
+  const int nt = min(64, a.n_tokens - t0);
+  const bool live = ut < nt;
+  if (threadIdx.x == 0) {
+    const int s0 = a.slots[t0];
+    s_whole = (nt == 64 && (s0 & 63) == 0);
+  }
+  __syncthreads();
+  if (threadIdx.x < nt && a.slots[t0 + threadIdx.x] != a.slots[t0] + (int)threadIdx.x)
+    s_whole = 0;   // benign race: every writer stores 0
+
+  float y[C];
+  if (live) {
+    load_quarter<D, DT>(a.x, ((size_t)(t0 + ut) * a.n_heads + head) * D, p, y);
+  } else {
+#pragma unroll
+    for (int e = 0; e < C; ++e) y[e] = 0.f;
+  }
+  const float n = front_quad<D>(y, p);
+  uint32_t w[NGL][VBITS];
+#pragma unroll
+  for (int g = 0; g < NGL; ++g)
+#pragma unroll
+    for (int j = 0; j < VBITS; ++j) w[g][j] = 0u;
+#pragma unroll
+  for (int e = 0; e < C; ++e) {
+    uint32_t m[VBITS];
+    code_bsearch<VBITS>(a.cb, y[e], m);
+#pragma unroll
+    for (int j = 0; j < VBITS; ++j) w[e / 32][j] |= m[j] & (1u << (e % 32));
+  }
+#pragma unroll
+  for (int g = 0; g < NGL; ++g)
+#pragma unroll
+    for (int j = 0; j < VBITS; ++j) s_pl[j][NGL * p + g][ut] = w[g][j];
+  __syncthreads();
+
+  if (s_whole) {
+    const int s0 = a.slots[t0];
+    uint8_t *sec = a.pool + ((size_t)(s0 / kPage) * a.n_heads + head) * VSEC;
+    const int bofs = s0 % kPage;   // offset of the block in the page (a multiple of 64)
+    uint32_t *words = reinterpret_cast<uint32_t *>(sec) + (bofs >> 6) * 2 * VBITS * D;
+    // word e = j*2D + (16 k + nn)*(D/32) + kp; bit 8 r + 4 h + tau <- token
+    // 16 tau + 4 k + r, coordinate 32 kp + 16 h + nn: bit nn + 16 h of the
+    // token's group-kp word
+    for (int e = threadIdx.x; e < 2 * VBITS * D; e += 256) {
+      const int j = e / (2 * D), rem = e % (2 * D);
+      const int c = rem / NGR, kp = rem % NGR;
+      const int k = c >> 4, nn = c & 15;
+      const uint32_t *row = &s_pl[j][kp][4 * k];
+      uint32_t word = 0u;
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(row + 16 * tau);   // tokens 16 tau + 4 k + r
+        const uint32_t qs[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          word |= ((qs[r] >> nn) & 1u) << (8 * r + tau);
+          word |= ((qs[r] >> (nn + 16)) & 1u) << (8 * r + 4 + tau);
+        }
+      }
+      words[e] = word;
+    }
+    if (live && p == 0)
+      reinterpret_cast<uint16_t *>(sec + VCODES)[side_entry(bofs + ut)] = f32_to_f16_bits(n);
+    return;
+  }
+
+  if (!live) return;
+  const int slot = a.slots[t0 + ut];
+  uint8_t *sec = a.pool + ((size_t)(slot / kPage) * a.n_heads + head) * VSEC;
+  const int off = slot % kPage;
+  uint32_t *rows = reinterpret_cast<uint32_t *>(sec);
+  // coordinates i = 32 kp + 16 h + nn and i + 16 share a word: set and clear
+  // both bits with one atomic each
+#pragma unroll
+  for (int g = 0; g < NGL; ++g) {
+    const int kp = NGL * p + g;
+#pragma unroll
+    for (int j = 0; j < VBITS; ++j)
+#pragma unroll
+      for (int nn = 0; nn < 16; ++nn) {
+        const int i = 32 * kp + nn;
+        uint32_t *wd = rows + v_word<D, VBITS>(off, i, j);
+        const uint32_t b0 = 1u << v_bit(off, i), b1 = 1u << v_bit(off, i + 16);
+        const uint32_t set = ((w[g][j] >> nn) & 1u ? b0 : 0u) | ((w[g][j] >> (nn + 16)) & 1u ? b1 : 0u);
+        const uint32_t clr = (b0 | b1) & ~set;
+        if (set) atomicOr(wd, set);
+        if (clr) atomicAnd(wd, ~clr);
+      }
+  }
+  if (p == 0) reinterpret_cast<uint16_t *>(sec + VCODES)[side_entry(off)] = f32_to_f16_bits(n);
+}
+
+template <int D, int DT, int KB>
+__global__ __launch_bounds__(256) void encode_k_bulk_kernel(EncodeArgs a) {
+  encode_k_bulk<D, DT, KB>(a, blockIdx.x);
+}
+
+template <int D, int DT, int VBITS>
+__global__ __launch_bounds__(256) void encode_v_bulk_kernel(EncodeArgs a) {
+  encode_v_bulk<D, DT, VBITS>(a, blockIdx.x, blockIdx.y);
 }
 
 template <int D, int DT, int VPW, int KB>
@@ -606,8 +1005,9 @@ hipError_t by_dim_dtype(int d, int dtype, F &&f) {
 
 }  // namespace
 
-// Bulk calls use 16 vectors per wave; short appends (below 4096 vectors) one,
-// so that the work spreads over more workgroups.
+// Bulk calls (4096 vectors or more) use the quad kernels, 64 vectors per
+// workgroup; short appends use one vector per wave, so that the work spreads
+// over more workgroups and each vector's latency chain is short.
 hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
   const long total = (long)a.n_tokens * a.n_heads;
   return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
@@ -617,7 +1017,7 @@ hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
         hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 1, KB.value>), grid, dim3(256), 0, s, a);
       } else {
         const dim3 grid((unsigned)((total + 63) / 64));
-        hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 16, KB.value>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((encode_k_bulk_kernel<D.value, DT.value, KB.value>), grid, dim3(256), 0, s, a);
       }
     };
     if (a.bits == 2)
@@ -639,7 +1039,7 @@ hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s) {
         hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 1, VBITS.value>), grid, dim3(256), 0, s, a);
       } else {
         const dim3 grid((unsigned)((a.n_tokens + 63) / 64), (unsigned)a.n_heads);
-        hipLaunchKernelGGL((encode_v_kernel<D.value, DT.value, 16, VBITS.value>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((encode_v_bulk_kernel<D.value, DT.value, VBITS.value>), grid, dim3(256), 0, s, a);
       }
     };
     if (a.bits == 2)

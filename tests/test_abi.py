@@ -266,9 +266,12 @@ def test_v_widths_page_bytes_and_validation(L):
     assert decode() == tq.TQ_EINVAL
     dsc.v_bits = 2                                   # v_levels still zero: not increasing
     assert decode() == tq.TQ_EINVAL
-    lv, _, _ = tq.tq_build_codebook(128, 2, 1, with_qjl=False)
+    lv, th, _ = tq.tq_build_codebook(128, 2, 1, with_qjl=False)
     for k in range(4):
         dsc.v_levels[k] = float(lv[k])
+    assert decode() == tq.TQ_EINVAL                  # v_thresholds still zero: not ascending
+    for k in range(3):
+        dsc.v_thresholds[k] = float(th[k])
     assert decode() == tq.TQ_OK
     dsc.v_levels[0] = float(lv[0]) * 1.01           # no longer odd
     assert decode() == tq.TQ_EINVAL
@@ -290,9 +293,12 @@ def test_k_widths_page_bytes_validation_and_operand_size(L):
     assert decode() == tq.TQ_EINVAL
     dsc.k_bits = 4                                   # k_levels still zero: not increasing
     assert decode() == tq.TQ_EINVAL
-    lv, _, _ = tq.tq_build_codebook(128, 4, 1, with_qjl=False)
+    lv, th, _ = tq.tq_build_codebook(128, 4, 1, with_qjl=False)
     for k in range(16):
         dsc.k_levels[k] = float(lv[k])
+    assert decode() == tq.TQ_EINVAL                  # k_thresholds still zero: not ascending
+    for k in range(15):
+        dsc.k_thresholds[k] = float(th[k])
     assert decode() == tq.TQ_OK
     # the packed scoring operand has 9 MFMA operands per 128 coordinates instead of 5
     grp3 = 5 * (64 * 32 + 64 * 4) + 64
@@ -333,3 +339,17 @@ def test_static_scratch_entry_rejects_what_the_buffer_cannot_hold(L):
     assert tq.status_string(tq.TQ_ESCRATCH).startswith("needs more than the static scratch")
     bad = (C.byref(dsc), FAKE, FAKE, 1, FAKE, 1, FAKE, 1, 1, 1, 30, FAKE, 16, FAKE, 0, 0.1, FAKE)
     assert L.tq_append_decode_static(*bad, None) == tq.TQ_EINVAL        # 30 % 8 != 0
+
+
+def test_thresholds_must_ascend(L):
+    """The encoders find a code by binary search over the thresholds, so a
+    descriptor whose thresholds do not strictly ascend is rejected."""
+    dsc = _desc(H=2)
+    sz = C.c_size_t(0)
+    decode = lambda: L.tq_attn_decode(C.byref(dsc), FAKE, 1, 2, 1, 8, FAKE, 16, FAKE, 0, 0.1, FAKE,
+                                      None, C.byref(sz), None)
+    assert decode() == tq.TQ_OK
+    t1, t2 = dsc.thresholds[1], dsc.thresholds[2]
+    dsc.thresholds[1], dsc.thresholds[2] = t2, t1
+    assert decode() == tq.TQ_EINVAL
+    assert L.tq_encode_k(C.byref(dsc), FAKE, 1, FAKE, 4, None) == tq.TQ_EINVAL

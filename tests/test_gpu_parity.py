@@ -79,15 +79,18 @@ def test_encode_parity(tq, case):
     assert np.array_equal(a["N"].view(np.uint16), b["N"].view(np.uint16))
 
 
-def test_encode_deterministic_and_edge_vectors(tq):
-    d, H, n = 128, 2, 70
+@pytest.mark.parametrize("n", [70, 2100], ids=["append-path", "bulk-path"])
+def test_encode_deterministic_and_edge_vectors(tq, n):
+    """Zero, one-hot and fp16-overflowing vectors, on the short-append kernels
+    (n * H < 4096) and on the bulk ones."""
+    d, H = 128, 2
     rng = np.random.default_rng(9)
     k = rng.standard_normal((n, H, d)).astype(np.float32)
     k[3, 0] = 0.0                  # zero vector: N = 0, all codes 4
     k[5, 1] *= 1e4                 # norm above the fp16 range: N = +inf
     k[6, 0, :] = 0.0
     k[6, 0, 17] = 2.5              # one-hot vector
-    cache = tq.Cache(d, H, 2)
+    cache = tq.Cache(d, H, (n + 100 + 255) // 256)
     ts = torch.arange(n, dtype=torch.int32, device="cuda") + 100
     kt = torch.from_numpy(k).cuda()
     tq.tq_encode_k(cache, kt, ts)
