@@ -112,16 +112,51 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // per split, where a wave sees at most two blocks and the one-set kernel
 // (about 115 VGPRs against 180) finishes sooner.
 
-// Copies the packed scoring operand of a query group (NMU x 64 lanes x 32 bytes,
-// then NMU x 64 scale words) into LDS.
-template <int NMU>
-__device__ inline void stage_query(const uint8_t *grp, v8i *s_qop, int *s_qsc, int tid) {
-  const uint4 *src = reinterpret_cast<const uint4 *>(grp);
-  uint4 *dst = reinterpret_cast<uint4 *>(s_qop);
-  for (int e = tid; e < NMU * 128; e += 256) dst[e] = src[e];
-  const int *ssrc = reinterpret_cast<const int *>(grp + (size_t)NMU * 2048);
-  for (int e = tid; e < NMU * 64; e += 256) s_qsc[e] = ssrc[e];
-}
+// The packed scoring operand of the workgroup's query groups (per group NMU x
+// 64 lanes x 32 bytes, then NMU x 64 scale words), held in registers between
+// its loads and its copy into LDS. Every load is issued at once and none sits
+// under a branch (indices past the end are clamped and the values replaced), so
+// the block loads issued after them do not hold up the copy: loads complete in
+// order. A group past the last one gets zero operands and unit scales.
+template <int NMU, int NG>
+struct QueryStage {
+  static constexpr int NV = (NMU * 128 + 255) / 256, NS = (NMU * 64 + 255) / 256;
+  uint4 v[NG][NV];
+  int sc[NG][NS];
+
+  // seq: the (sequence, KV head)'s first group; groups rho0 .. rho0 + NG - 1 of QG
+  __device__ inline void load(const uint8_t *seq, size_t gbytes, int rho0, int QG, int tid) {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const uint8_t *grp = seq + (size_t)min(rho0 + gi, QG - 1) * gbytes;
+      const uint4 *src = reinterpret_cast<const uint4 *>(grp);
+      const int *ssrc = reinterpret_cast<const int *>(grp + (size_t)NMU * 2048);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) v[gi][i] = src[min(tid + 256 * i, NMU * 128 - 1)];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) sc[gi][i] = ssrc[min(tid + 256 * i, NMU * 64 - 1)];
+    }
+  }
+
+  // groups from QG - rho0 on are past the last one
+  __device__ inline void store(v8i *s_qop, int *s_qsc, int rho0, int QG, int tid) const {
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const bool live = rho0 + gi < QG;
+      uint4 *dst = reinterpret_cast<uint4 *>(s_qop + gi * NMU * 64);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = tid + 256 * i;
+        if (e < NMU * 128) dst[e] = live ? v[gi][i] : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int e = tid + 256 * i;
+        if (e < NMU * 64) s_qsc[gi * NMU * 64 + e] = live ? sc[gi][i] : 127;
+      }
+    }
+  }
+};
 
 template <int D, int VBITS, int KBITS>
 struct MfmaBlock {
@@ -151,42 +186,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   constexpr int NB = D / 16;                // 16-coordinate V column blocks
   constexpr int NR = NG * kMfmaMaxGroup;    // query rows of the workgroup
 
-  // the query operands live in LDS during the page loop; the same bytes then
-  // hold the per-wave V numerators for the final combine
+  // the query operands live in LDS during the page loop; the per-wave V
+  // numerators of the final combine have their own region, so a wave can write
+  // them while others still read query operands
   constexpr size_t QOP_BYTES = (size_t)NG * NMU * 64 * 32, QSC_BYTES = (size_t)NG * NMU * 64 * 4;
-  constexpr size_t WACC_BYTES = (size_t)4 * NR * D * 4;
-  constexpr size_t RAW = QOP_BYTES + QSC_BYTES > WACC_BYTES ? QOP_BYTES + QSC_BYTES : WACC_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char s_raw[RAW];
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[QOP_BYTES + QSC_BYTES];
+  __shared__ float s_wacc[4][NR][D];                // per wave: V numerator of each row
   __shared__ float s_wm[4][4][NR];                  // per wave: m, l, mU, sum U of each row
   v8i *s_qop = reinterpret_cast<v8i *>(s_raw);      // [group][mfma][lane]
   int *s_qsc = reinterpret_cast<int *>(s_raw + QOP_BYTES);
-  auto s_wacc = reinterpret_cast<float (*)[NR][D]>(s_raw);   // [wave][row][d]
 
   const int QG = a.plan.qgroups, WZ = a.plan.wg_per_seq;
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / WZ;
   const int rho0 = (blockIdx.z % WZ) * NG;           // first query group of the workgroup
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int n = lane & 15, kg = lane >> 4;   // scores: token 16 tau + n of query row kg
   const int lam = n & 3;                     // V weight operand: limb row / token of the quad
   const int H = a.n_kv_heads, g = a.n_q_heads / H;
-  const int L = a.seq_lens[b];
 
-  const uint8_t *grp0 = a.packed + (((size_t)b * H + kvh) * QG + rho0) * packed_group_bytes(D, KBITS);
-  float off1[NG], off2[NG];
-  int vis[NG];
+  // The start is a chain of latencies (arguments, then the packed query operand
+  // and the sequence's length and block table, then the first block), so the
+  // loads go out in that order, none under a branch, before anything waits.
+  const size_t gbytes = packed_group_bytes(D, KBITS);
+  const uint8_t *seq_grp = a.packed + ((size_t)b * H + kvh) * QG * gbytes;
+  QueryStage<NMU, NG> qs;
+  qs.load(seq_grp, gbytes, rho0, QG, tid);
+  float4 rc[NG];   // row constants {0, 0, sum q~, sum p} of this lane's query row
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int row = kMfmaMaxGroup * (rho0 + gi) + kg;   // query row of this lane in group gi
-    off1[gi] = off2[gi] = 0.f;
-    vis[gi] = 0;
-    if (row < a.plan.group) {
-      const float4 rc = reinterpret_cast<const float4 *>(grp0 + (size_t)gi * packed_group_bytes(D, KBITS) +
-                                                         (size_t)NMU * (2048 + 256))[kg];
-      off1[gi] = a.cb.levels[(1 << KBITS) - 1] * rc.z;
-      off2[gi] = rc.w * qjl_kappa<D>();
-      vis[gi] = a.causal_tail ? L - (a.n_q - 1 - row / g) : L;
-    }
-  }
+  for (int gi = 0; gi < NG; ++gi)
+    rc[gi] = reinterpret_cast<const float4 *>(seq_grp + (size_t)min(rho0 + gi, QG - 1) * gbytes +
+                                              (size_t)NMU * (2048 + 256))[kg];
+  // The sequence's length and first visible token and the block-table entries
+  // of the split's first two pages are loaded together (an entry past the
+  // sequence is read but not used; without a window the start is read from the
+  // lengths and dropped), and the empty asm keeps the compiler from sinking
+  // them past the branches below, one after another.
+  const int L = a.seq_lens[b];
+  const int s0raw = (a.seq_starts ? a.seq_starts : a.seq_lens)[b];
+  const int pgs = split * a.plan.pages_per_split;
+  const int32_t *brow = a.block_table + (size_t)b * a.max_pages;
+  const int physA = brow[min(pgs, a.max_pages - 1)];
+  const int physB = brow[min(pgs + 1, a.max_pages - 1)];
+  asm volatile("" ::"s"(L), "s"(s0raw), "s"(physA), "s"(physB));
+  auto phys_of = [&](int pg) { return pg == pgs ? physA : pg == pgs + 1 ? physB : brow[pg]; };
   // V weight operand: lane 16 kg + 4 q + lam takes the weight of query q, token
   // 16 tau + 4 kg + lam, which the score layout holds in lane 16 q + 4 kg + lam
   const int perm_addr = 4 * (16 * (n >> 2) + 4 * kg + lam);
@@ -252,31 +294,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   const int n_pages_seq = min((Lv + kPage - 1) / kPage, a.max_pages);
   // tokens before S0 are not visible (a window); pages wholly before it are
   // never read, so their block-table entries may point at recycled pages
-  const int S0 = a.seq_starts ? max(0, a.seq_starts[b]) : 0;
+  const int S0 = a.seq_starts ? max(0, s0raw) : 0;
   const int pg0 = max(split * a.plan.pages_per_split, S0 / kPage);
   int pg1 = min(split * a.plan.pages_per_split + a.plan.pages_per_split, n_pages_seq);
   const int blk0 = 64 * wave;
   // pages whose block of this wave holds no visible token are skipped (only the last can)
   if (pg1 > pg0 && blk0 >= Lv - (pg1 - 1) * kPage) --pg1;
 
-  // the query operands of the workgroup's groups (a group past the last one
-  // gets zero operands; its rows are masked)
-  auto stage = [&]() {
-#pragma unroll
-    for (int gi = 0; gi < NG; ++gi) {
-      if (rho0 + gi < QG) {
-        stage_query<NMU>(grp0 + (size_t)gi * packed_group_bytes(D, KBITS), s_qop + gi * NMU * 64,
-                         s_qsc + gi * NMU * 64, tid);
-      } else {
-        uint4 *dst = reinterpret_cast<uint4 *>(s_qop + gi * NMU * 64);
-        for (int e = tid; e < NMU * 128; e += 256) dst[e] = make_uint4(0u, 0u, 0u, 0u);
-        for (int e = tid; e < NMU * 64; e += 256) s_qsc[gi * NMU * 64 + e] = 127;
-      }
-    }
-  };
 
-  auto load_block = [&](MfmaBlock<D, VBITS, KBITS> &d, int pg) {
-    const int phys = a.block_table[(size_t)b * a.max_pages + pg];
+  auto load_block_at = [&](MfmaBlock<D, VBITS, KBITS> &d, int phys) {
     const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
     const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
 #pragma unroll
@@ -308,6 +334,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
         for (int c = 0; c < NCH; ++c) d.v[j][c] = vw[j * 2 * D * 4 / 16 + c];
     }
   };
+  auto load_block = [&](MfmaBlock<D, VBITS, KBITS> &d, int pg) { load_block_at(d, phys_of(pg)); };
+
+  // the first block's loads go out before anything waits for the query operand
+  // (at d = 128: at d = 256 its registers would be live across the copy). An
+  // empty split loads a block of page 0, which always exists, and never uses it.
+  constexpr bool kEarly = D == 128;
+  MfmaBlock<D, VBITS, KBITS> d0;
+  if constexpr (kEarly) load_block_at(d0, pg0 < pg1 ? phys_of(pg0) : 0);
+
+  float off1[NG], off2[NG];
+  int vis[NG];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int row = kMfmaMaxGroup * (rho0 + gi) + kg;   // query row of this lane in group gi
+    const bool live = row < a.plan.group;
+    off1[gi] = live ? a.cb.levels[(1 << KBITS) - 1] * rc[gi].z : 0.f;
+    off2[gi] = live ? rc[gi].w * qjl_kappa<D>() : 0.f;
+    vis[gi] = !live ? 0 : a.causal_tail ? L - (a.n_q - 1 - row / g) : L;
+  }
 
   auto process = [&](const MfmaBlock<D, VBITS, KBITS> &d, int pg) {
     // at d = 256 the query operand (20 MFMA operands, 80 registers) is read from
@@ -321,7 +366,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
 #pragma unroll
         for (int c = 0; c < NCH; ++c) vcur[j][c] = d.v[j][c];
     } else {
-      const int phys = a.block_table[(size_t)b * a.max_pages + pg];
+      const int phys = phys_of(pg);
       const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
       const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 2 * VBITS * D) + 4 * (D / 32) * lane);
 #pragma unroll
@@ -543,14 +588,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     }
   };
 
-  // the first block's loads go out before the query operand is staged, so the
-  // two fetches overlap
+  // the packed query operand is shared by the four waves: keep it in LDS
+  qs.store(s_qop, s_qsc, rho0, QG, tid);
+  __syncthreads();
   if constexpr (TWO_SETS) {
-    MfmaBlock<D, VBITS, KBITS> d0, d1;
-    if (pg0 < pg1) load_block(d0, pg0);
-    // the packed query operand is shared by the four waves: keep it in LDS
-    stage();
-    __syncthreads();
+    MfmaBlock<D, VBITS, KBITS> d1;
     for (int pg = pg0; pg < pg1; pg += 2) {
       if (pg + 1 < pg1) load_block(d1, pg + 1);
       process(d0, pg);
@@ -560,35 +602,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
     }
   } else {
     // one register set
-    stage();
-    __syncthreads();
     for (int pg = pg0; pg < pg1; ++pg) {
-      MfmaBlock<D, VBITS, KBITS> d0;
-      load_block(d0, pg);
+      if (!kEarly || pg > pg0) load_block(d0, pg);
       process(d0, pg);
     }
   }
 
   if constexpr (kLazyV) fold_v(0);
   // ---- combine the four waves into one partial per query row
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const float l_row = rowsum16(l_lane[gi]), us_row = rowsum16(us_lane[gi]);
-    if (n == 0) {
-      s_wm[wave][0][4 * gi + kg] = m_run[gi];
-      s_wm[wave][1][4 * gi + kg] = l_row;
-      s_wm[wave][2][4 * gi + kg] = mu_run[gi];
-      s_wm[wave][3][4 * gi + kg] = us_row;
-    }
-  }
-  __syncthreads();   // every wave is past the page loop: the query operands are dead
   {
     const float c7 = a.vcb.levels[(1 << VBITS) - 1];   // the V codebook's largest level
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
-      const float usq = s_wm[wave][3][4 * gi + kg];
+      // every lane of a DPP row (one query row) holds the row sums
+      const float l_row = rowsum16(l_lane[gi]), us_row = rowsum16(us_lane[gi]);
+      if (n == 0) {
+        s_wm[wave][0][4 * gi + kg] = m_run[gi];
+        s_wm[wave][1][4 * gi + kg] = l_row;
+        s_wm[wave][2][4 * gi + kg] = mu_run[gi];
+        s_wm[wave][3][4 * gi + kg] = us_row;
+      }
 #pragma unroll
-      for (int k = 0; k < NB; ++k) s_wacc[wave][4 * gi + kg][16 * k + n] = facc[gi][k] - c7 * usq;
+      for (int k = 0; k < NB; ++k) s_wacc[wave][4 * gi + kg][16 * k + n] = facc[gi][k] - c7 * us_row;
     }
   }
   __syncthreads();

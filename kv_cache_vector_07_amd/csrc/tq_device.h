@@ -214,8 +214,10 @@ __device__ inline float fp6_e2m3_round(float x, uint32_t &code) {
   const int e = min(2, max(0, __builtin_amdgcn_frexp_expf(a) - 1));
   const float k = __builtin_ldexpf(1.5f, 20 + e);
   const float q = fminf((a + k) - k, 7.5f);
-  // codes: 8 q below 2 (subnormals and the first binade alike), then 4 q + 8, 2 q + 16
-  const float cf = q < 2.f ? 8.f * q : (q < 4.f ? fmaf(4.f, q, 8.f) : fmaf(2.f, q, 16.f));
+  // codes: 8 q below 2 (subnormals and the first binade alike), then 4 q + 8,
+  // 2 q + 16, i.e. q 2^(3 - e) + 8 e. The three agree where the binades meet,
+  // so e taken before rounding gives the code of q, without branches.
+  const float cf = fmaf(q, __builtin_ldexpf(1.f, 3 - e), (float)(8 * e));
   code = (uint32_t)cf | (x < 0.f ? 0x20u : 0u);
   return x < 0.f ? -q : q;
 }

@@ -14,17 +14,20 @@ constexpr int kWaves = 4;      // waves per workgroup
 
 // Steps 1-3 for one vector: norm, rotation, codes (NT thresholds). Returns y
 // (rotated, unit norm) in y[], the codes in idx[] and the norm.
-template <int D, int DT, int NT = 7>
-__device__ inline float encode_front(const void *x, size_t base, const Codebook &cb,
-                                     float (&y)[D / 64], int (&idx)[D / 64]) {
-  constexpr int R = D / 64;
+template <int D, int DT>
+__device__ inline void load_vector(const void *x, size_t base, float (&y)[D / 64]) {
   const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int r = 0; r < D / 64; ++r) y[r] = load_elem<DT>(x, base + lane + 64 * r);
+}
+
+// The same steps on a vector already loaded into y[].
+template <int D, int NT = 7>
+__device__ inline float encode_front_loaded(const Codebook &cb, float (&y)[D / 64], int (&idx)[D / 64]) {
+  constexpr int R = D / 64;
   float ss = 0.f;
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    y[r] = load_elem<DT>(x, base + lane + 64 * r);
-    ss += y[r] * y[r];
-  }
+  for (int r = 0; r < R; ++r) ss += y[r] * y[r];
   ss = wave_sum(ss);
   const float n = sqrtf(ss);
   const float inv = n > 0.f ? 1.0f / n : 0.f;
@@ -39,35 +42,39 @@ __device__ inline float encode_front(const void *x, size_t base, const Codebook 
   return n;
 }
 
-// K encode: VPW vectors per wave (16 for bulk encodes, 1 for short appends
-// where latency rules). Each wave runs steps 1-4 on its vectors (codes by
-// ballot, residual into LDS); the QJL product Z = R S^T over the workgroup's
-// residuals then runs on fp32 MFMA (16x16x4), with S read from L2 once per
-// workgroup; signs come back by ballot. Rows of R past the last vector are
-// zero and their records are not written.
-typedef float v4f __attribute__((ext_vector_type(4)));
+template <int D, int DT, int NT = 7>
+__device__ inline float encode_front(const void *x, size_t base, const Codebook &cb,
+                                     float (&y)[D / 64], int (&idx)[D / 64]) {
+  load_vector<D, DT>(x, base, y);
+  return encode_front_loaded<D, NT>(cb, y, idx);
+}
 
-template <int D, int DT, int VPW, int KB>
-__device__ void encode_k_block(const EncodeArgs &a, long blk) {
+// K encode of short appends: one vector per workgroup. Wave 0 runs steps 1-4
+// (codes by ballot, residual into LDS); then wave w computes rows
+// 16 (RT w + t) + l16 of z = S r with lane FMAs: lane (l16, kq) holds
+// S[row][16 c + 4 kq + m] (read from L2 before the encode starts at d = 128),
+// the four lane groups' partial sums are added across lanes, and the signs come
+// back by ballot. Few vectors leave most of a 16-wide MFMA tile as padding, and
+// one vector per workgroup spreads a step's appends over more SIMDs.
+template <int D, int DT, int KB>
+__device__ void encode_k_block(const EncodeArgs &a, long vec) {
   constexpr int R = D / 64;
   constexpr int NWORD = (KB + 1) * D / 32;  // u32 words per K record: KB code planes + signs per 32
-  constexpr int VB = kWaves * VPW;          // vectors per workgroup
-  constexpr int VT = (VB + 15) / 16;        // 16-vector MFMA tiles
   constexpr int RT = D / 16 / kWaves;       // 16-row tiles of S per wave: 2 or 4
   constexpr size_t KREC = (size_t)(KB + 1) * D / 8;
   constexpr size_t KCODES = (size_t)kPage * KREC;
   constexpr size_t KSEC = KCODES + 4 * kPage;
-  __shared__ float4 s_r[16 * VT][D / 4 + 1];   // residuals (rows padded: no bank conflicts)
-  __shared__ uint64_t s_code[VB][KB][R];    // code bit planes
-  __shared__ uint16_t s_sign[VB][D / 16];   // sign bits, 16 rows of S per entry
-  __shared__ float s_ng[VB][2];             // N, G
+  __shared__ float4 s_r[D / 4];             // residual
+  __shared__ uint64_t s_code[KB][R];        // code bit planes
+  __shared__ uint16_t s_sign[D / 16];       // sign bits, 16 rows of S per entry
+  __shared__ float s_ng[2];                 // N, G
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int l16 = lane & 15, kq = lane >> 4;
-  const long total = (long)a.n_tokens * a.n_heads;
-  const long v0 = blk * VB;
-  const int nv = (int)min((long)VB, total - v0);
 
+  // the vector is loaded before S: loads complete in order
+  float y[R];
+  if (wave == 0) load_vector<D, DT>(a.x, (size_t)vec * D, y);
   // S rows of this wave's tiles: the loads do not depend on the data, so for
   // d = 128 they are all issued before the encode starts
   const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
@@ -82,81 +89,68 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
         sreg[t * (D / 16) + c] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
   }
 
-  for (int u = wave; u < 16 * VT; u += kWaves) {
-    float4 *rrow = s_r[u];
-    if (u >= nv) {
-      for (int e = lane; e < D / 4; e += 64) rrow[e] = make_float4(0.f, 0.f, 0.f, 0.f);
-      continue;
-    }
-    float y[R];
+  if (wave == 0) {
     int idx[R];
-    const float n = encode_front<D, DT, (1 << KB) - 1>(a.x, (size_t)(v0 + u) * D, a.cb, y, idx);
+    const float n = encode_front_loaded<D, (1 << KB) - 1>(a.cb, y, idx);
     float rr = 0.f;
 #pragma unroll
     for (int k = 0; k < R; ++k) {
       y[k] -= KB == 3 ? level_of(a.cb, idx[k]) : level_any(a.cb, idx[k]);
       rr += y[k] * y[k];
-      reinterpret_cast<float *>(rrow)[lane + 64 * k] = y[k];
+      reinterpret_cast<float *>(s_r)[lane + 64 * k] = y[k];
 #pragma unroll
       for (int j = 0; j < KB; ++j) {
         const uint64_t m = __ballot((idx[k] >> j) & 1);
-        if (lane == 0) s_code[u][j][k] = m;
+        if (lane == 0) s_code[j][k] = m;
       }
     }
     const float gm = sqrtf(wave_sum(rr));
     if (lane == 0) {
-      s_ng[u][0] = n;
-      s_ng[u][1] = gm;
+      s_ng[0] = n;
+      s_ng[1] = gm;
     }
   }
   __syncthreads();
 
-  // Z tile (vector tile vt, row tile rt) = sum over i of R[16 vt + .][i] S[16 rt + .][i].
-  // MFMA m of a 16-wide i step uses i = i0 + 4 kq + m in lane group kq, for A and B alike.
+  // z[t]: row 16 (RT wave + t) + l16 of S times the residual, this lane group's
+  // coordinates 16 c + 4 kq + m, then summed over the four lane groups
   if (qjl) {
-    v4f acc[VT][RT];
+    float z[RT];
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-      for (int t = 0; t < RT; ++t) acc[vt][t] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      float4 bv[RT], av[VT];
+    for (int t = 0; t < RT; ++t) z[t] = 0.f;
+    auto step = [&](int c) {
+      const float4 rv = s_r[4 * c + kq];
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
-        if constexpr (kHoist)
-          bv[t] = sreg[t * (D / 16) + c];
-        else
-          bv[t] = S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
+        const float4 bv = kHoist ? sreg[t * (D / 16) + c]
+                                 : S4[(size_t)(16 * (wave * RT + t) + l16) * (D / 4) + 4 * c + kq];
+        z[t] = fmaf(bv.x, rv.x, z[t]);
+        z[t] = fmaf(bv.y, rv.y, z[t]);
+        z[t] = fmaf(bv.z, rv.z, z[t]);
+        z[t] = fmaf(bv.w, rv.w, z[t]);
       }
+    };
+    if constexpr (kHoist) {
 #pragma unroll
-      for (int vt = 0; vt < VT; ++vt) av[vt] = s_r[16 * vt + l16][4 * c + kq];
-      // independent tiles between the dependent steps of one accumulator
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-          for (int t = 0; t < RT; ++t)
-            acc[vt][t] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[vt][m], bv[t][m], acc[vt][t], 0, 0, 0);
+      for (int c = 0; c < D / 16; ++c) step(c);
+    } else {
+      // at d = 256 the S loads go out four steps at a time (registers)
+#pragma unroll 4
+      for (int c = 0; c < D / 16; ++c) step(c);
     }
-    // lane (l16, kq), register r of a tile: vector 16 vt + 4 kq + r, row 16 rt + l16
 #pragma unroll
-    for (int vt = 0; vt < VT; ++vt)
-#pragma unroll
-      for (int t = 0; t < RT; ++t)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint64_t m = __ballot(acc[vt][t][r] >= 0.f);
-          const int u = 16 * vt + 4 * kq + r;
-          if (l16 == 0 && u < VB) s_sign[u][wave * RT + t] = (uint16_t)(m >> (16 * kq));
-        }
+    for (int t = 0; t < RT; ++t) {
+      float v = z[t];
+      v += xor_lane<16>(v);
+      v += xor_lane<32>(v);
+      const uint64_t m = __ballot(v >= 0.f);   // the four lane groups agree
+      if (lane == 0) s_sign[wave * RT + t] = (uint16_t)m;
+    }
   }
   __syncthreads();
 
-  // records: wave w writes vectors w, w + 4, ...
-  for (int u = wave; u < nv; u += kWaves) {
-    const long vec = v0 + u;
+  // the record, by wave 0
+  if (wave == 0) {
     const long tok = vec / a.n_heads;
     const int head = (int)(vec % a.n_heads);
     const int slot = a.slots[tok];
@@ -166,16 +160,16 @@ __device__ void encode_k_block(const EncodeArgs &a, long blk) {
       const int s = lane / (KB + 1), j = lane % (KB + 1);   // coordinate group, word in it
       uint32_t w;
       if (j < KB) {
-        const uint64_t m = s_code[u][j][s >> 1];
+        const uint64_t m = s_code[j][s >> 1];
         w = (s & 1) ? (uint32_t)(m >> 32) : (uint32_t)m;
       } else {
-        w = qjl ? (uint32_t)s_sign[u][2 * s] | ((uint32_t)s_sign[u][2 * s + 1] << 16) : 0u;
+        w = qjl ? (uint32_t)s_sign[2 * s] | ((uint32_t)s_sign[2 * s + 1] << 16) : 0u;
       }
       reinterpret_cast<uint32_t *>(sec + (size_t)off * KREC)[lane] = w;
     }
     if (lane == 0) {
-      reinterpret_cast<uint16_t *>(sec + KCODES)[side_entry(off)] = f32_to_f16_bits(s_ng[u][0]);
-      reinterpret_cast<uint16_t *>(sec + KCODES + 2 * kPage)[side_entry(off)] = f32_to_f16_bits(s_ng[u][1]);
+      reinterpret_cast<uint16_t *>(sec + KCODES)[side_entry(off)] = f32_to_f16_bits(s_ng[0]);
+      reinterpret_cast<uint16_t *>(sec + KCODES + 2 * kPage)[side_entry(off)] = f32_to_f16_bits(s_ng[1]);
     }
   }
 }
@@ -414,9 +408,12 @@ __device__ inline uint32_t level_bits(const Codebook &cb, const uint32_t (&m)[NB
   }
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 // K encode of 64 vectors: codes, residual and G on quads; the residuals go to
-// LDS, where Z = R S^T runs on fp32 MFMA as in encode_k_block, and the signs
-// come back by ballot; each lane then stores its groups' record words.
+// LDS, where Z = R S^T runs on fp32 MFMA (16x16x4 tiles: 16 vectors by 16 rows
+// of S, with S read from L2 once per workgroup), and the signs come back by
+// ballot; each lane then stores its groups' record words.
 template <int D, int DT, int KB>
 __device__ void encode_k_bulk(const EncodeArgs &a, long blk) {
   constexpr int C = D / 4;                  // coordinates per lane
@@ -672,9 +669,9 @@ __global__ __launch_bounds__(256) void encode_v_bulk_kernel(EncodeArgs a) {
   encode_v_bulk<D, DT, VBITS>(a, blockIdx.x, blockIdx.y);
 }
 
-template <int D, int DT, int VPW, int KB>
+template <int D, int DT, int KB>
 __global__ __launch_bounds__(256) void encode_k_kernel(EncodeArgs a) {
-  encode_k_block<D, DT, VPW, KB>(a, blockIdx.x);
+  encode_k_block<D, DT, KB>(a, blockIdx.x);
 }
 
 template <int D, int DT, int VPW, int VBITS>
@@ -683,38 +680,42 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
 }
 
 // ------------------------------------------------------------------ prepare
-// One workgroup per query row qq of a (sequence, KV head) group: rotate the
-// row, project it with S, write q~ and p, and on the MFMA path pack this row's
-// four limb rows of the fp6 scoring operand. The four waves split the m rows
-// of S, and every S load of a chunk is issued before the row is rotated.
-template <int D, int DT, int KB>
-__device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
+// kPrepPieces workgroups per query row qq of a (sequence, KV head) group: each
+// rotates the row and projects it with S (the four waves split the m rows of
+// S, and every S load of a chunk is issued before the row is rotated), then
+// packs its share of the row's four limb rows of the fp6 scoring operand;
+// piece 0 also writes q~, p and the row constants. Packing is a long chain of
+// dependent steps per lane, so it is spread over more SIMDs.
+constexpr int kPrepPieces = 4;
+
+// Rotation and projection of the row (the same for every key code width):
+// q~ into s_q, p = S q~ into s_p; piece 0 writes both to the query region.
+template <int D, int DT>
+__device__ void prepare_front(const PrepArgs &a, int qq, int kvh, int b, int piece, float *s_q, float *s_p) {
   constexpr int R = D / 64;
-  constexpr int NPK = k_planes(KB);    // key code planes (KB-bit codes), then the sign plane
-  constexpr int NMU = mfma_per_tile(D, KB);   // scoring MFMAs per 16-token tile
   constexpr int RPW = D / 4;         // rows of S per wave
   constexpr int LPR = 64 / RPW;      // lanes per row of S: 2 (d = 128) or 1 (d = 256)
   constexpr int EPL = D / LPR;       // elements of a row per lane
   constexpr int CH = 16;             // float4 loads in flight per lane
   constexpr int NCH = EPL / 4 / CH;  // chunks: 1 (d = 128) or 4 (d = 256)
-  __shared__ float s_q[D], s_p[D];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = a.n_q_heads / a.n_kv_heads, G = g * a.n_q;
+  const int g = a.n_q_heads / a.n_kv_heads;
   const int t = qq / g, hh = qq % g;
   const size_t row = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
   const int srow = wave * RPW + lane / LPR, part = lane % LPR;
   const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
   const size_t s_off = (size_t)srow * (D / 4) + part * (EPL / 4);   // this lane's part of its S row
   const bool qjl = a.qjl != nullptr;   // MSE-only keys: p = 0, S is not read
+  // the row is loaded first: loads complete in order, and the rotation, which
+  // needs the row, runs while the S loads are in flight
+  float v[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) v[r] = load_elem<DT>(a.q, row * D + lane + 64 * r);
   float4 sv[CH];
   if (qjl) {
 #pragma unroll
     for (int k = 0; k < CH; ++k) sv[k] = S4[s_off + k];
   }
-
-  float v[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) v[r] = load_elem<DT>(a.q, row * D + lane + 64 * r);
   fwht_wave<R>(v);
 #pragma unroll
   for (int r = 0; r < R; ++r) v[r] *= rsqrt_dim<D>();
@@ -723,7 +724,7 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       s_q[lane + 64 * r] = v[r];
-      dst[lane + 64 * r] = v[r];
+      if (piece == 0) dst[lane + 64 * r] = v[r];
     }
   }
   __syncthreads();
@@ -751,10 +752,20 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   if (LPR == 2) acc += __shfl_xor(acc, 1, 64);
   if (part == 0) {
     s_p[srow] = acc;
-    dst[D + srow] = acc;
+    if (piece == 0) dst[D + srow] = acc;
   }
-  if (a.packed == nullptr) return;
-  __syncthreads();
+}
+
+// This piece's share of the row's scoring operand (KB-bit key codes), from
+// s_q and s_p.
+template <int D, int KB>
+__device__ void prepare_pack(const PrepArgs &a, int qq, int kvh, int b, int piece, const float *s_q,
+                             const float *s_p) {
+  constexpr int R = D / 64;
+  constexpr int NPK = k_planes(KB);    // key code planes (KB-bit codes), then the sign plane
+  constexpr int NMU = mfma_per_tile(D, KB);   // scoring MFMAs per 16-token tile
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G = a.n_q_heads / a.n_kv_heads * a.n_q;
 
   // Scoring operand of this row for the fp6 x fp4 block-scaled MFMA
   // (16x16x128): MFMA mu = 5 c + pl scores coordinate chunk c (coordinates
@@ -789,70 +800,68 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
   uint8_t *opb = grp;                                                  // [mu][lane][32] bytes
   uint32_t *scl = reinterpret_cast<uint32_t *>(grp + (size_t)NMU * 2048);   // [mu][lane]
   const float kap2 = 2.f * qjl_kappa<D>();
-  // Half-wave h takes the (mu, block) tasks h, h + 8, ...: all of them in one
-  // pass, so their limb chains interleave. Fields are ORed into LDS dwords
-  // (field f of a lane's 32 sits at bits 6 f .. 6 f + 5 of its 192), then each
-  // packed dword is stored once.
-  constexpr int NTASK = NMU * 4, NT = (NTASK + 7) / 8;
-  __shared__ uint32_t s_pk[8][NT][4][6];                      // per half-wave: task, limb, dword
-  const int half = threadIdx.x >> 5, e = threadIdx.x & 31;
-  for (int z = e; z < NT * 4 * 6; z += 32) (&s_pk[half][0][0][0])[z] = 0u;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // Piece p takes the (MFMA, block pair) tasks p TP .. p TP + TP - 1 and its
+  // wave w the tasks w, w + 4, ... of them: two 32-slot blocks at a time, one
+  // per half-wave, as one branch-free block, so their limb chains interleave. Lane e of a half holds
+  // field e; the fields (field f at bits 6 f .. 6 f + 5 of the 192) are packed
+  // in registers: field pairs, then quads, are merged across lanes (a quad's 24
+  // bits in its first lane), and lane 4 j of each 16-lane row (j = 0, 1, 2)
+  // builds dword j of the row's 96 bits from its quad and the next, or (j = 3)
+  // a zero for dword 6 or 7. Every lane of a quad stores its first lane's dword
+  // and every lane of a half the block's scale: same address, same value.
+  constexpr int NTASK = NMU * 2;   // (mu, block pair) tasks
+  const int e = threadIdx.x & 31, hb = lane >> 5;
   const int fv = e >> 3, fm = e & 7;   // field e: bit 4 fm + fv of its plane word
-  const float val = fv == 0 ? 0.5f : fv == 1 ? 1.f : 2.f;
-  const int sh0 = (6 * e) & 31, dw0 = (6 * e) >> 5;   // where field e starts
+  const float ival = fv == 0 ? 2.f : fv == 1 ? 1.f : 0.5f;   // 1 / the key slot's value
+  const int prow = e >> 4, pj = (e & 15) >> 2;   // the lane's row and quad in it
+  const int pdw = pj < 3 ? 3 * prow + pj : 6 + prow;   // the dword quad pj of row prow writes
+  auto pack_task = [&](int task) {
+    const int mu = task >> 1, kb = 2 * (task & 1) + hb;
+    const int c = mu / (NPK + 1), pl = mu % (NPK + 1);
+    const int i = 32 * (kb + 4 * c) + 4 * fm + fv;
+    const float sqi = s_q[i], spi = s_p[i];   // both read: no branch on the plane
+    float r = (pl < NPK ? w[min(pl, NPK - 1)] * sqi : kap2 * spi) * ival;
+    // limb 0: the block scale 2^ex puts the block's largest value in [4, 8).
+    // Later limbs take their scale from the rounding bound of the previous one
+    // (no reduction): limb 0 leaves |r| <= 0.5 * 2^ex (0.25 from rounding in
+    // [4, 8), 0.5 where 7.75 .. 8 saturates to 7.5), so limb 1 uses ex - 3;
+    // a limb whose values stay below 4 leaves |r| <= 0.125 * 2^ex, so limbs 2
+    // and 3 use ex - 5. Every later limb value is then at most 4, no later limb
+    // saturates, and after four limbs |r| <= 2^(ex0 - 16), under 2^-18 of the
+    // block's largest value.
+    float mx = fabsf(r);
+    mx = fmaxf(mx, xor_lane<1>(mx));
+    mx = fmaxf(mx, xor_lane<2>(mx));
+    mx = fmaxf(mx, xor_lane<4>(mx));
+    mx = fmaxf(mx, xor_lane<8>(mx));
+    mx = fmaxf(mx, xor_lane<16>(mx));
+    const int ex0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 3 : 0;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int blkid = half + 8 * t;   // the same for both halves of a wave
-    if (blkid < NTASK) {
-      const int mu = blkid >> 2, kb = blkid & 3;
-      const int c = mu / (NPK + 1), pl = mu % (NPK + 1);
-      const int i = 32 * (kb + 4 * c) + 4 * fm + fv;
-      float r = (pl < NPK ? w[pl] * s_q[i] : kap2 * s_p[i]) / val;
-      // limb 0: the block scale 2^ex puts the block's largest value in [4, 8).
-      // Later limbs take their scale from the rounding bound of the previous one
-      // (no reduction): limb 0 leaves |r| <= 0.5 * 2^ex (0.25 from rounding in
-      // [4, 8), 0.5 where 7.75 .. 8 saturates to 7.5), so limb 1 uses ex - 3;
-      // a limb whose values stay below 4 leaves |r| <= 0.125 * 2^ex, so limbs 2
-      // and 3 use ex - 5. Every later limb value is then at most 4, no later limb
-      // saturates, and after four limbs |r| <= 2^(ex0 - 16), under 2^-18 of the
-      // block's largest value.
-      float mx = fabsf(r);
-      mx = fmaxf(mx, xor_lane<1>(mx));
-      mx = fmaxf(mx, xor_lane<2>(mx));
-      mx = fmaxf(mx, xor_lane<4>(mx));
-      mx = fmaxf(mx, xor_lane<8>(mx));
-      mx = fmaxf(mx, xor_lane<16>(mx));
-      const int ex0 = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) - 3 : 0;
-#pragma unroll
-      for (int limb = 0; limb < 4; ++limb) {
-        const int ex = max(-127, min(127, ex0 - (limb == 0 ? 0 : limb == 1 ? 3 : 3 + 5 * (limb - 1))));
-        uint32_t code;
-        const float qv = fp6_e2m3_round(__builtin_ldexpf(r, -ex), code);
-        r = fmaf(-qv, __builtin_ldexpf(1.f, ex), r);
-        atomicOr(&s_pk[half][t][limb][dw0], code << sh0);
-        if (sh0 > 26) atomicOr(&s_pk[half][t][limb][dw0 + 1], code >> (32 - sh0));
-        if (e == 0) scl[mu * 64 + 16 * kb + 4 * qloc + limb] = (uint32_t)(ex + 127);
-      }
+    for (int limb = 0; limb < 4; ++limb) {
+      const int ex = max(-127, min(127, ex0 - (limb == 0 ? 0 : limb == 1 ? 3 : 3 + 5 * (limb - 1))));
+      uint32_t code;
+      const float qv = fp6_e2m3_round(__builtin_ldexpf(r, -ex), code);
+      r = fmaf(-qv, __builtin_ldexpf(1.f, ex), r);
+      // pairs (lane 2 k), then quads (lane 4 k): fields 4 k .. 4 k + 3 in 24 bits
+      uint32_t pk = code | ((uint32_t)__builtin_amdgcn_mov_dpp((int)code, 0xB1, 0xF, 0xF, true) << 6);
+      pk |= (uint32_t)__builtin_amdgcn_mov_dpp((int)pk, 0x4E, 0xF, 0xF, true) << 12;
+      const uint32_t nx = (uint32_t)__shfl_down((int)pk, 4, 16);   // the next quad of the row
+      uint32_t word = pj < 3 ? (pk >> (8 * pj)) | (nx << (24 - 8 * pj)) : 0u;
+      word = (uint32_t)__builtin_amdgcn_mov_dpp((int)word, 0x00, 0xF, 0xF, true);   // quad_perm [0,0,0,0]
+      reinterpret_cast<uint32_t *>(opb)[((size_t)mu * 64 + 16 * kb + 4 * qloc + limb) * 8 + pdw] = word;
+      scl[mu * 64 + 16 * kb + 4 * qloc + limb] = (uint32_t)(ex + 127);
     }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // lane e < 24 stores dword e % 6 of limb e / 6; lanes 24..31 clear dwords 6 and 7
-  const int plimb = e < 24 ? e / 6 : (e - 24) >> 1;
-  const int pdw = e < 24 ? e % 6 : 6 + ((e - 24) & 1);
+  };
+  // every wave runs the same number of rounds; a task index past the piece's
+  // last is clamped to it, so that task is computed twice and stored twice with
+  // the same values, and all rounds stay one branch-free block
+  constexpr int TP = (NTASK + kPrepPieces - 1) / kPrepPieces, NT = (TP + 3) / 4;
+  const int tlast = min(NTASK, TP * (piece + 1)) - 1;
+  if (TP * piece <= tlast) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int blkid = half + 8 * t;
-    if (blkid < NTASK) {
-      const int mu = blkid >> 2, kb = blkid & 3;
-      const uint32_t word = e < 24 ? s_pk[half][t][plimb][pdw] : 0u;
-      reinterpret_cast<uint32_t *>(opb)[((size_t)mu * 64 + 16 * kb + 4 * qloc + plimb) * 8 + pdw] = word;
-    }
+    for (int t = 0; t < NT; ++t) pack_task(min(TP * piece + wave + 4 * t, tlast));
   }
+  if (piece != 0) return;
   // limb rows of rows Gr .. 3 of the group (no query): zero fields, unit scales
   if (qloc == 0 && Gr < kMfmaMaxGroup) {
     const int nrow = 4 * (kMfmaMaxGroup - Gr);
@@ -873,41 +882,56 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b) {
 }
 
 template <int D, int DT>
-__global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
+__device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b, int piece) {
+  __shared__ float s_q[D], s_p[D];
+  prepare_front<D, DT>(a, qq, kvh, b, piece, s_q, s_p);
+  if (a.packed == nullptr) return;
+  __syncthreads();
   // the K code width is uniform over the launch
   if (a.k_bits == 2)
-    prepare_row<D, DT, 2>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    prepare_pack<D, 2>(a, qq, kvh, b, piece, s_q, s_p);
   else if (a.k_bits == 4)
-    prepare_row<D, DT, 4>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    prepare_pack<D, 4>(a, qq, kvh, b, piece, s_q, s_p);
   else
-    prepare_row<D, DT, 3>(a, blockIdx.x, blockIdx.y, blockIdx.z);
+    prepare_pack<D, 3>(a, qq, kvh, b, piece, s_q, s_p);
+}
+
+template <int D, int DT>
+__global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
+  prepare_row<D, DT>(a, blockIdx.x / kPrepPieces, blockIdx.y, blockIdx.z, blockIdx.x % kPrepPieces);
 }
 
 // One launch for the work of a decode step that precedes the split-K decode:
-// workgroups [0, nk) encode the appended K vectors (one per wave), the next nv
+// workgroups [0, nk) encode the appended K vectors (one each), the next nv
 // encode the appended V vectors (one token per wave and KV head) and the rest
-// prepare one query row each. The three parts touch disjoint memory.
+// prepare the query rows (kPrepPieces workgroups each). The three parts touch
+// disjoint memory.
+// The workgroup counts come first and the query arguments next, so the role
+// test and the start of a query row read one or two kernel-argument lines.
 struct StepArgs {
-  EncodeArgs k, v;
+  int nk, nvx, nv, pad;   // K workgroups; V workgroups per KV head and in total
   PrepArgs p;
-  int nk, nvx, nv;   // K workgroups; V workgroups per KV head and in total
+  EncodeArgs k, v;
 };
 
 template <int D, int DT>
 __global__ __launch_bounds__(256) void step_prologue_kernel(StepArgs s) {
+  // both counts in one load, before the first branch
+  const int nk = s.nk, nv = s.nv;
+  asm volatile("" ::"s"(nk), "s"(nv));
   int id = blockIdx.x;
-  if (id < s.nk) {
+  if (id < nk) {
     // the K code width is uniform over the launch
     if (s.k.bits == 2)
-      encode_k_block<D, DT, 1, 2>(s.k, id);
+      encode_k_block<D, DT, 2>(s.k, id);
     else if (s.k.bits == 4)
-      encode_k_block<D, DT, 1, 4>(s.k, id);
+      encode_k_block<D, DT, 4>(s.k, id);
     else
-      encode_k_block<D, DT, 1, 3>(s.k, id);
+      encode_k_block<D, DT, 3>(s.k, id);
     return;
   }
-  id -= s.nk;
-  if (id < s.nv) {
+  id -= nk;
+  if (id < nv) {
     // the V code width is uniform over the launch
     if (s.v.bits == 2)
       encode_v_block<D, DT, 1, 2>(s.v, id % s.nvx, id / s.nvx);
@@ -917,15 +941,12 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(StepArgs s) {
       encode_v_block<D, DT, 1, 3>(s.v, id % s.nvx, id / s.nvx);
     return;
   }
-  id -= s.nv;
+  id -= nv;
+  const int piece = id % kPrepPieces;
+  id /= kPrepPieces;
   const int G = s.p.n_q * (s.p.n_q_heads / s.p.n_kv_heads);
   const int qq = id % G, kvh = (id / G) % s.p.n_kv_heads, b = id / (G * s.p.n_kv_heads);
-  if (s.p.k_bits == 2)
-    prepare_row<D, DT, 2>(s.p, qq, kvh, b);
-  else if (s.p.k_bits == 4)
-    prepare_row<D, DT, 4>(s.p, qq, kvh, b);
-  else
-    prepare_row<D, DT, 3>(s.p, qq, kvh, b);
+  prepare_row<D, DT>(s.p, qq, kvh, b, piece);
 }
 
 template <int D>
@@ -1013,8 +1034,8 @@ hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s) {
   return by_dim_dtype(d, a.dtype, [&](auto D, auto DT) {
     auto go = [&](auto KB) {
       if (total < 4096) {
-        const dim3 grid((unsigned)((total + kWaves - 1) / kWaves));
-        hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, 1, KB.value>), grid, dim3(256), 0, s, a);
+        const dim3 grid((unsigned)total);   // one vector per workgroup
+        hipLaunchKernelGGL((encode_k_kernel<D.value, DT.value, KB.value>), grid, dim3(256), 0, s, a);
       } else {
         const dim3 grid((unsigned)((total + 63) / 64));
         hipLaunchKernelGGL((encode_k_bulk_kernel<D.value, DT.value, KB.value>), grid, dim3(256), 0, s, a);
@@ -1053,7 +1074,7 @@ hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s) {
 }
 
 hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
-  const dim3 grid(a.n_q * (a.n_q_heads / a.n_kv_heads), a.n_kv_heads, a.batch);
+  const dim3 grid(a.n_q * (a.n_q_heads / a.n_kv_heads) * kPrepPieces, a.n_kv_heads, a.batch);
   if (d == 128) {
     if (a.dtype == TQ_F32)
       hipLaunchKernelGGL((prepare_kernel<128, TQ_F32>), grid, dim3(256), 0, s, a);
@@ -1075,14 +1096,15 @@ bool step_prologue_fits(const EncodeArgs &k, const PrepArgs &p) {
 hipError_t launch_step_prologue(const EncodeArgs &k, const EncodeArgs &v, const PrepArgs &p, int d,
                                 hipStream_t s) {
   StepArgs sa;
+  sa.pad = 0;
   sa.k = k;
   sa.v = v;
   sa.p = p;
-  sa.nk = (int)(((long)k.n_tokens * k.n_heads + kWaves - 1) / kWaves);
+  sa.nk = (int)((long)k.n_tokens * k.n_heads);   // one K vector per workgroup
   sa.nvx = (v.n_tokens + kWaves - 1) / kWaves;
   sa.nv = sa.nvx * v.n_heads;
   const long np = (long)p.n_q * p.n_q_heads * p.batch;   // query rows
-  const dim3 grid((unsigned)(sa.nk + sa.nv + np));
+  const dim3 grid((unsigned)(sa.nk + sa.nv + np * kPrepPieces));
   return by_dim_dtype(d, k.dtype, [&](auto D, auto DT) {
     hipLaunchKernelGGL((step_prologue_kernel<D.value, DT.value>), grid, dim3(256), 0, s, sa);
     return hipGetLastError();

@@ -55,12 +55,12 @@ struct DequantArgs {
 struct PrepArgs {
   const void *q;          // [batch][n_q][Hq][d]
   int dtype;
+  int k_bits;             // K code width: the number of key bit planes follows
   int batch, n_q, n_q_heads, n_kv_heads;
   const float *qjl;
   float *prep;            // [rows][2][d]: Pi q, then S Pi q
   uint8_t *packed;        // per (sequence, KV head, query group): operand + row constants (or null)
   Codebook cb;            // K
-  int k_bits;             // K code width: the number of key bit planes follows
 };
 
 // Bytes of the packed scoring operand of one query group of a (sequence, KV
