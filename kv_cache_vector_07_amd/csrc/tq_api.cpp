@@ -212,14 +212,16 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 namespace tq {
 
 DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages,
-                       int kb) {
+                       int kb, int vb) {
   DecodePlan p;
   p.group = n_q_heads / n_kv_heads * n_q;
   p.mfma = mfma_path(d, p.group);
-  p.qgroups = p.mfma ? query_groups(p.group) : 1;
-  // Several query groups of a (sequence, KV head) share a workgroup, so the key
-  // and V operands of a block are built once for all of them.
-  p.groups_per_wg = p.qgroups > 1 ? max_groups_per_wg(d) : 1;
+  p.wide = wide_path(d, p.group, kb, vb);
+  p.qgroups = !p.mfma ? 1 : p.wide ? (p.group + kWideRows - 1) / kWideRows : query_groups(p.group);
+  // Several 4-row query groups of a (sequence, KV head) share a workgroup, so
+  // the key and V operands of a block are built once for all of them; a wide
+  // group has a workgroup of its own.
+  p.groups_per_wg = p.qgroups > 1 && !p.wide ? max_groups_per_wg(d) : 1;
   p.wg_per_seq = (p.qgroups + p.groups_per_wg - 1) / p.groups_per_wg;
   // About 512 workgroups (two per CU, one occupancy round) so that every
   // workgroup streams several pages with its loads overlapped; whole pages per
@@ -232,7 +234,7 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
   p.n_split = (max_pages + pps - 1) / pps;
   p.partial_bytes =
       round_up((size_t)batch * n_kv_heads * p.n_split * p.group * (d + 4) * sizeof(float), 256);
-  p.prep_bytes = prep_region_bytes(d, batch, n_q, n_q_heads, n_kv_heads, kb);
+  p.prep_bytes = prep_region_bytes(d, batch, n_q, n_q_heads, n_kv_heads, kb, vb);
   return p;
 }
 
@@ -353,11 +355,9 @@ int tq_encode_v(const tq_cache *c, const void *v, int32_t dtype, const int32_t *
 // merge grid (rows, Hkv, batch); the second and third dimensions stay within
 // 65535.
 static bool grid_fits(const tq_cache *c, int32_t batch, int32_t n_q, int32_t n_q_heads) {
-  const int group = n_q_heads / c->n_kv_heads * n_q;
-  const int qg = tq::query_groups(group);
-  const int per_wg = qg > 1 ? tq::max_groups_per_wg(c->head_dim) : 1;
-  const long wz = (qg + per_wg - 1) / per_wg;
-  return c->n_kv_heads <= 65535 && (long)batch * wz <= 65535;
+  const tq::DecodePlan p = tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, 1,
+                                           k_bits_of(c), v_bits_of(c));
+  return c->n_kv_heads <= 65535 && (long)batch * p.wg_per_seq <= 65535;
 }
 
 static int prepare_checks(const tq_cache *c, int32_t dtype, int32_t batch, int32_t n_q,
@@ -384,8 +384,10 @@ static hipError_t run_prepare(const tq_cache *c, const void *q, int32_t dtype, i
   a.n_kv_heads = c->n_kv_heads;
   a.qjl = qjl_of(c);
   a.prep = (float *)prep;
-  const bool mfma = tq::mfma_path(c->head_dim, n_q_heads / c->n_kv_heads * n_q);
+  const int group = n_q_heads / c->n_kv_heads * n_q;
+  const bool mfma = tq::mfma_path(c->head_dim, group);
   a.packed = mfma ? prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads) : nullptr;
+  a.wide = tq::wide_path(c->head_dim, group, k_bits_of(c), v_bits_of(c));
   a.cb = codebook_of(c);
   a.k_bits = k_bits_of(c);
   return tq::launch_prepare(a, c->head_dim, s);
@@ -397,7 +399,8 @@ int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t ba
   if (st) return st;
   if (!prep_bytes) return TQ_EINVAL;
   const size_t need =
-      tq::prep_region_bytes(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, k_bits_of(c));
+      tq::prep_region_bytes(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, k_bits_of(c),
+                            v_bits_of(c));
   if (!prep) {
     *prep_bytes = need;
     return TQ_OK;
@@ -482,7 +485,7 @@ static int attn_decode_impl(const tq_cache *c, const void *q, int32_t dtype, int
   if (dtype != TQ_F32 && dtype != TQ_BF16) return TQ_EUNSUPPORTED;
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
-                      k_bits_of(c));
+                      k_bits_of(c), v_bits_of(c));
   size_t need = plan.partial_bytes + plan.prep_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -545,7 +548,7 @@ int tq::append_decode(const tq_cache *c, const void *k_new, const void *v_new, i
   if (n_new < 0) return TQ_EINVAL;
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
-                      k_bits_of(c));
+                      k_bits_of(c), v_bits_of(c));
   size_t need = plan.partial_bytes + plan.prep_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -589,6 +592,7 @@ int tq::append_decode(const tq_cache *c, const void *k_new, const void *v_new, i
   pa.qjl = qjl_of(c);
   pa.prep = (float *)prep;
   pa.packed = prep + tq::prep_float_bytes(c->head_dim, batch, n_q, n_q_heads);
+  pa.wide = plan.wide;
   pa.cb = codebook_of(c);
   pa.k_bits = k_bits_of(c);
   if (n_new > 0 && tq::step_prologue_fits(ek, pa)) {
@@ -614,7 +618,7 @@ int tq_attn_decode_prepared(const tq_cache *c, const void *prep, int32_t batch, 
   if (st) return st;
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
-                      k_bits_of(c));
+                      k_bits_of(c), v_bits_of(c));
   size_t need = plan.partial_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -640,7 +644,7 @@ int tq_attn_decode_split(const tq_cache *c, const void *prep, int32_t batch, int
   if (st) return st;
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
-                      k_bits_of(c));
+                      k_bits_of(c), v_bits_of(c));
   size_t need = plan.partial_bytes;
   if (!workspace) {
     *workspace_bytes = need;
@@ -671,7 +675,7 @@ int tq_attn_decode_merge(const tq_cache *c, int32_t batch, int32_t n_q, int32_t 
   if (!aligned(out, 16) || !aligned(workspace, 256)) return TQ_EALIGN;
   tq::DecodePlan plan =
       tq::plan_decode(c->head_dim, batch, n_q, n_q_heads, c->n_kv_heads, max_pages,
-                      k_bits_of(c));
+                      k_bits_of(c), v_bits_of(c));
   if (workspace_bytes < plan.partial_bytes) return TQ_EWORKSPACE;
   tq::DecodeArgs a = decode_args(c, nullptr, batch, n_q, n_q_heads, nullptr, max_pages, nullptr, 0,
                                  0.f, out, (uint8_t *)workspace, plan);

@@ -664,6 +664,479 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   }
 }
 
+// Everything one 64-token block of a wave needs (key record words, sidecars,
+// V words), loaded before the block is processed.
+template <int D>
+struct WideBlock {
+  uint32_t kw[4][D / 128][4];   // key words of coordinate groups kg + 4 c of tokens 16 tau + n
+  uint2 g, nk, nv;              // G, N^K, N^V of side entries 4 n + tau
+  uint4 v[3][D / 128];          // V words of plane j: coordinate pairs kp
+};
+
+// ------------------------------------------------------------- wide groups
+// Sixteen distinct query rows per workgroup (3-bit K and V codes). Each wave
+// owns 64-token blocks as in decode_mfma_kernel, but every operand built from
+// the keys and the V bits serves all 16 rows:
+//
+// Scores: the A operand of scaled MFMA (mu, l) holds limb l of the 16 rows
+// (fp6, E8M0 block scales per row), so the four limb MFMAs of a key operand
+// accumulate into one result and the sum over limbs comes out of the MFMA.
+// Output lane (n, kg) holds rows 4 kg + r (r = 0..3) of token 16 tau + n: one
+// DPP row of 16 lanes holds four query rows, each with its own online softmax.
+//
+// V: per block and row the weights are scaled by a power of two that puts their
+// largest in [0.5, 1), then (times each plane weight) taken in fixed point
+// below 2^23 as three balanced int8 limbs, each with its own int32 sums; the
+// block's sums are folded into fp32 with the scale undone (per block, as the
+// scales differ). The weight operand of lane (m, kgA) is row m at tokens
+// 16 tau + 4 kgA + r: a 4x4 transpose inside each quad of the score layout
+// and a lane permutation (kg <-> kgA, one ds_bpermute per weight) bring the
+// weights there, and byte permutes pack the limbs.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void decode_wide_kernel(DecodeArgs a) {
+  constexpr int VBITS = 3, KBITS = 3;
+  constexpr int NPK = 4;                       // key code planes (then the sign plane)
+  constexpr int NMU = mfma_per_tile(D, KBITS);
+  constexpr int NOP = 4 * NMU;                 // (mu, limb) query operands
+  constexpr int NCH = D / 128;
+  constexpr int KREC = (KBITS + 1) * D / 8;
+  constexpr size_t KCODES = (size_t)kPage * KREC;
+  constexpr size_t KSEC = KCODES + 4 * kPage;
+  constexpr size_t VCODES = (size_t)VBITS * D * kPage / 8;
+  constexpr size_t VSEC = VCODES + 2 * kPage;
+  constexpr int NB = D / 16;
+  constexpr int RW = kWideRows;
+  // the query operands live in LDS during the page loop, without the two zero
+  // dwords of each lane's 32 bytes (fp6 fields fill six): dwords 0-3 and 4-5 in
+  // planes of their own (conflict-free 16- and 8-byte reads), then the scale
+  // words. The same bytes then hold the per-wave V numerators for the final
+  // combine. At d = 256 that keeps two workgroups per CU.
+  constexpr size_t Q16_BYTES = (size_t)NOP * 64 * 16, Q8_BYTES = (size_t)NOP * 64 * 8;
+  constexpr size_t QSC_BYTES = (size_t)NOP * 64 * 4;
+  constexpr size_t QALL = Q16_BYTES + Q8_BYTES + QSC_BYTES;
+  constexpr size_t WACC_BYTES = (size_t)4 * RW * D * 4;
+  constexpr size_t RAW = QALL > WACC_BYTES ? QALL : WACC_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char s_raw[RAW];
+  __shared__ float s_wm[4][4][RW];                  // per wave: m, l, mU, sum U of each row
+  uint4 *s_q16 = reinterpret_cast<uint4 *>(s_raw);  // [operand][lane]
+  uint2 *s_q8 = reinterpret_cast<uint2 *>(s_raw + Q16_BYTES);
+  int *s_qsc = reinterpret_cast<int *>(s_raw + Q16_BYTES + Q8_BYTES);
+  auto s_wacc = reinterpret_cast<float (*)[RW][D]>(s_raw);   // [wave][row][d], after the loop
+
+  const int QG = a.plan.qgroups;
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z / QG, rho = blockIdx.z % QG;
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int n = lane & 15, kg = lane >> 4;
+  const int H = a.n_kv_heads, g = a.n_q_heads / H, G = a.plan.group;
+  const int row0 = RW * rho;   // first query row of the workgroup
+
+  // loads first, none under a branch: the group's packed operand and row
+  // constants, then the sequence's length and start and the split's first
+  // block-table entries
+  const size_t gbytes = packed_group_bytes_wide(D);
+  const uint8_t *grp = a.packed + (((size_t)b * H + kvh) * QG + rho) * gbytes;
+  QueryStage<NOP, 1> qs;
+  qs.load(grp, gbytes, 0, 1, tid);
+  const float4 *rcp = reinterpret_cast<const float4 *>(grp + (size_t)NOP * (2048 + 256));
+  const float4 rcA = rcp[2 * kg], rcB = rcp[2 * kg + 1];   // {sum q~, sum p} of rows 4 kg .. 4 kg + 3
+  const int L = a.seq_lens[b];
+  const int s0raw = (a.seq_starts ? a.seq_starts : a.seq_lens)[b];
+  const int pgs = split * a.plan.pages_per_split;
+  const int32_t *brow = a.block_table + (size_t)b * a.max_pages;
+  const int physA = brow[min(pgs, a.max_pages - 1)];
+  asm volatile("" ::"s"(L), "s"(s0raw), "s"(physA));
+  auto phys_of = [&](int pg) { return pg == pgs ? physA : brow[pg]; };
+
+  // Lv: one past the last token any row of the workgroup sees
+  const int row_last = min(row0 + RW, G) - 1;
+  const int Lv = a.causal_tail ? L - (a.n_q - 1 - row_last / g) : L;
+  const int n_pages_seq = min((Lv + kPage - 1) / kPage, a.max_pages);
+  const int S0 = a.seq_starts ? max(0, s0raw) : 0;
+  const int pg0 = max(pgs, S0 / kPage);
+  int pg1 = min(pgs + a.plan.pages_per_split, n_pages_seq);
+  const int blk0 = 64 * wave;
+  if (pg1 > pg0 && blk0 >= Lv - (pg1 - 1) * kPage) --pg1;
+
+  // this lane's rows 4 kg + r
+  const float c7k = a.cb.levels[(1 << KBITS) - 1];
+  float off1[4], off2[4];
+  int vis[4];
+  {
+    const float sqv[4] = {rcA.x, rcA.z, rcB.x, rcB.z}, spv[4] = {rcA.y, rcA.w, rcB.y, rcB.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = row0 + 4 * kg + r;
+      const bool live = row < G;
+      off1[r] = live ? c7k * sqv[r] : 0.f;
+      off2[r] = live ? spv[r] * qjl_kappa<D>() : 0.f;
+      vis[r] = !live ? 0 : a.causal_tail ? L - (a.n_q - 1 - row / g) : L;
+    }
+  }
+  const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
+  float wpl[4];
+  plane_weights(a.vcb, wpl);
+  float wmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) wmax = fmaxf(wmax, fabsf(wpl[j]));
+  // weight X = U' * 2^-tau * (w_j / wmax) * kFix with U' < 1 the block-scaled
+  // weight (|X| <= kFix, so X + 0x8080 keeps its top byte in int8), 2^tau being
+  // the value the V bit of token 16 tau + 4 k + r takes in byte r of the B operand
+  constexpr float kFix = 8355000.f;
+  float cx[4], half[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    half[j] = wpl[j] < 0.f ? -0.5f : 0.5f;   // round to nearest with a truncating convert
+    cx[j] = wpl[j] / wmax * kFix;
+  }
+  const float delta_u = wmax / kFix;
+  // source lane of the weight transpose (kg <-> kgA): lane 16 a + 4 b + c reads lane 16 b + 4 a + c
+  const int tr_addr = 4 * (16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + (lane & 3));
+  const int rq = lane & 3;   // the lane's place in its quad
+
+  float m_run[4], mu_run[4], l_lane[4], us_lane[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    m_run[r] = mu_run[r] = -kFltMax;
+    l_lane[r] = us_lane[r] = 0.f;
+  }
+  v4f facc[NB];
+#pragma unroll
+  for (int k = 0; k < NB; ++k) facc[k] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto load_block_at = [&](WideBlock<D> &d, int phys) {
+    const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
+    const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint8_t *rec = ks + (size_t)(blk0 + 16 * tau + n) * KREC;
+        const uint4 u = reinterpret_cast<const uint4 *>(rec)[kg + 4 * c];
+        d.kw[tau][c][0] = u.x;
+        d.kw[tau][c][1] = u.y;
+        d.kw[tau][c][2] = u.z;
+        d.kw[tau][c][3] = u.w;
+      }
+    const int se = blk0 + 4 * n;   // side entries of tokens 16 tau + n, tau = 0..3
+    d.g = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * kPage + 2 * se);
+    d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * se);
+    d.nv = *reinterpret_cast<const uint2 *>(vs + VCODES + 2 * se);
+    const uint4 *vw = reinterpret_cast<const uint4 *>(vs + (size_t)4 * (wave * 2 * VBITS * D) + 4 * (D / 32) * lane);
+#pragma unroll
+    for (int j = 0; j < VBITS; ++j)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) d.v[j][c] = vw[j * 2 * D * 4 / 16 + c];
+  };
+
+  // ---- scores of the 16 rows: c1 (code planes) and c2 (signs) per tile
+  auto score_mfma = [&](const WideBlock<D> &d, v4f (&c1)[4], v4f (&c2)[4]) {
+    // the query operands are read from LDS where they are used (an opaque lane
+    // offset keeps them from being hoisted out of the page loop)
+    int qo = lane;
+    asm volatile("" : "+v"(qo));
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) c1[tau] = c2[tau] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+      for (int j = 0; j <= NPK; ++j) {
+        v8i op[4];
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          const uint32_t *w = d.kw[tau][c];
+          const uint32_t pl = j == 0 ? w[0] : j == 1 ? w[1] : j == 2 ? w[2] : j == 3 ? (w[0] ^ w[1] ^ w[2]) : w[3];
+          op[tau] = v8i{(int)(pl & 0x11111111u), (int)(pl & 0x22222222u), (int)(pl & 0x44444444u),
+                        (int)((pl >> 1) & 0x44444444u), 0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int limb = 0; limb < 4; ++limb) {
+          const int o = ((NPK + 1) * c + j) * 4 + limb;
+          const uint4 q16 = s_q16[o * 64 + qo];
+          const uint2 q8 = s_q8[o * 64 + qo];
+          const v8i qop = v8i{(int)q16.x, (int)q16.y, (int)q16.z, (int)q16.w, (int)q8.x, (int)q8.y, 0, 0};
+          const int qsc = s_qsc[o * 64 + qo];
+#pragma unroll
+          for (int tau = 0; tau < 4; ++tau) {
+            if (j < NPK)
+              c1[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op[tau], c1[tau], 2, 4, 0, qsc, 0, 127);
+            else
+              c2[tau] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qop, op[tau], c2[tau], 2, 4, 0, qsc, 0, 127);
+          }
+        }
+      }
+    }
+  };
+
+  // the rest of a block: scores, softmax, weights, V
+  auto finish = [&](const WideBlock<D> &d, int pg, const v4f (&c1)[4], const v4f (&c2)[4]) {
+    const uint4 (&vcur)[VBITS][NCH] = d.v;
+    const int tok0 = pg * kPage;
+    const int ntok = min(kPage, L - tok0);
+    float sc[4][4], sv[4][4];   // [tau][row r]
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      const int sh = 16 * (tau & 1);
+      const float Gt = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.g.y : d.g.x) >> sh));
+      const float N = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nk.y : d.nk.x) >> sh));
+      const float lnv = __builtin_amdgcn_logf(f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nv.y : d.nv.x) >> sh)));
+      const int tok = blk0 + 16 * tau + n;
+      const bool in_page = tok < ntok && tok0 + tok >= S0;
+      const float sN = scale2 * N;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const bool valid = in_page && tok0 + tok < vis[r];   // vis = 0 for rows past the group
+        const float sco = sN * fmaf(Gt, c2[tau][r] - off2[r], c1[tau][r] - off1[r]);
+        sc[tau][r] = valid ? sco : kNegInf;
+        sv[tau][r] = valid ? sco + lnv : kNegInf;   // + log2 N^V
+      }
+    }
+
+    // ---- online softmax of this wave, per row (lazy references, as in decode_mfma_kernel)
+    {
+      float smax[4], vmax[4];
+      bool move = false;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        smax[r] = fmaxf(fmaxf(sc[0][r], sc[1][r]), fmaxf(sc[2][r], sc[3][r]));
+        vmax[r] = fmaxf(fmaxf(sv[0][r], sv[1][r]), fmaxf(sv[2][r], sv[3][r]));
+        move |= smax[r] > m_run[r] + kSlack || vmax[r] > mu_run[r] + kSlack;
+      }
+      if (__any(move)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float m_new = fmaxf(m_run[r], rowmax16(smax[r]));
+          const float mu_new = fmaxf(mu_run[r], rowmax16(vmax[r]));
+          const float alpha = __builtin_amdgcn_exp2f(m_run[r] - m_new);
+          const float alphaU = __builtin_amdgcn_exp2f(mu_run[r] - mu_new);
+#pragma unroll
+          for (int k = 0; k < NB; ++k) facc[k][r] *= alphaU;
+          l_lane[r] *= alpha;
+          us_lane[r] *= alphaU;
+          m_run[r] = m_new;
+          mu_run[r] = mu_new;
+        }
+      }
+    }
+    float U[4][4];   // [tau][row r]
+    float dsc[4];    // per row: delta_u * 2^E, 2^-E the block's weight scale
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float ps = 0.f, us = 0.f, um = 0.f;
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        ps += __builtin_amdgcn_exp2f(sc[tau][r] - m_run[r]);
+        U[tau][r] = __builtin_amdgcn_exp2f(sv[tau][r] - mu_run[r]);
+        us += U[tau][r];
+        um = fmaxf(um, U[tau][r]);
+      }
+      l_lane[r] += ps;
+      us_lane[r] += us;
+      // the block's largest weight of the row, as m 2^E with m in [0.5, 1) (E = 0 if none)
+      const float bm = rowmax16(um);
+      const int E = bm > 0.f ? __builtin_amdgcn_frexp_expf(bm) : 0;
+      dsc[r] = __builtin_amdgcn_ldexpf(delta_u, E);
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) U[tau][r] = __builtin_amdgcn_ldexpf(U[tau][r], -E);
+    }
+
+    // ---- weights to the V operand layout. Transpose inside each quad (lane q
+    // of the quad gets slot q of lanes 0..3: rows 4 kg + q, tokens 16 tau + 4 (n >> 2) + r),
+    // then lane 16 a + 4 b + c takes lane 16 b + 4 a + c.
+    float T[4][4];   // [tau][r]: row (lane & 15), token 16 tau + 4 (lane >> 4) + r
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau) {
+      float s1[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float o = dppf<0x4E>(U[tau][r ^ 2]);   // quad_perm [2,3,0,1]
+        s1[r] = ((r ^ rq) & 2) ? o : U[tau][r];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float o = dppf<0xB1>(s1[r ^ 1]);       // quad_perm [1,0,3,2]
+        const float t = ((r ^ rq) & 1) ? o : s1[r];
+        T[tau][r] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(tr_addr, __builtin_bit_cast(int, t)));
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) T[tau][r] = __builtin_amdgcn_ldexpf(T[tau][r], -tau);
+
+    // ---- V: chunks of column blocks; per chunk the four planes in turn, each
+    // with three limbs. A chunk's int32 sums start at zero and are folded with
+    // the row's scale.
+    auto vword = [&](int j, int kp) -> uint32_t {
+      const uint4 &u = vcur[j][kp >> 2];
+      const int e = kp & 3;
+      return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
+    };
+    // weight limbs of plane j: bytes r = limb l of the weight of token
+    // 16 tau + 4 kgA + r. Y = X + 0x8080; limbs: bytes 0 and 1 of Y with their
+    // top bit flipped, then byte 2 (signed): X = b0 + 256 b1 + 65536 b2.
+    auto build_a = [&](int j, v4i (&Aj)[3]) {
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+          uint32_t Y[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Y[r] = (uint32_t)(int)fmaf(T[tau][r], cx[j], half[j]) + 0x8080u;
+          const uint32_t t01 = __builtin_amdgcn_perm(Y[1], Y[0], 0x05010400u);   // Y0.b0 Y1.b0 Y0.b1 Y1.b1
+          const uint32_t t23 = __builtin_amdgcn_perm(Y[3], Y[2], 0x05010400u);
+          const uint32_t u01 = __builtin_amdgcn_perm(Y[1], Y[0], 0x06020602u);   // Y0.b2 Y1.b2 (twice)
+          const uint32_t u23 = __builtin_amdgcn_perm(Y[3], Y[2], 0x06020602u);
+          Aj[0][tau] = (int)(__builtin_amdgcn_perm(t23, t01, 0x05040100u) ^ 0x80808080u);
+          Aj[1][tau] = (int)(__builtin_amdgcn_perm(t23, t01, 0x07060302u) ^ 0x80808080u);
+          Aj[2][tau] = (int)__builtin_amdgcn_perm(u23, u01, 0x05040100u);
+        }
+    };
+    // the four planes' limbs, built once for all column chunks
+    v4i Aall[4][3];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) build_a(j, Aall[j]);
+    // column blocks per chunk: 8 (at d = 128 4, to stay within 256 registers)
+    constexpr int CBK = D == 128 ? 4 : 8;
+#pragma unroll
+    for (int ch = 0; ch < NB / CBK; ++ch) {
+      v4i vacc[3][CBK];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        const v4i (&Aj)[3] = Aall[j];
+#pragma unroll
+        for (int kq = 0; kq < CBK / 2; ++kq) {
+          const int kp = (CBK / 2) * ch + kq;
+          const uint32_t wj = j < 3 ? vword(j, kp) : vword(0, kp) ^ vword(1, kp) ^ vword(2, kp);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const uint32_t w = wj >> (4 * h);
+            v4i bop;   // VGPR tau, byte r: token 16 tau + 4 k + r, bit value 2^tau
+            bop.x = (int)(w & 0x01010101u);
+            bop.y = (int)(w & 0x02020202u);
+            bop.z = (int)(w & 0x04040404u);
+            bop.w = (int)(w & 0x08080808u);
+#pragma unroll
+            for (int l = 0; l < 3; ++l)
+              vacc[l][2 * kq + h] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                  Aj[l], bop, j == 0 ? v4i{0, 0, 0, 0} : vacc[l][2 * kq + h], 0, 0, 0);
+          }
+        }
+      }
+      // a limb row gains at most 64 tokens x 4 planes x 128 x 8 = 2^18 per block,
+      // so b0 + 256 b1 stays exact in int32
+#pragma unroll
+      for (int k = 0; k < CBK; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float lo = (float)(vacc[0][k][r] + (vacc[1][k][r] << 8));
+          facc[CBK * ch + k][r] = fmaf(dsc[r], fmaf(65536.f, (float)vacc[2][k][r], lo), facc[CBK * ch + k][r]);
+        }
+    }
+  };
+
+  // the query operand (shared by the four waves, kept in LDS) is loaded first,
+  // then the first block, then the operand is copied into LDS. At d = 256 (one
+  // wave per SIMD) a second register set takes each block's loads one block ahead.
+  constexpr bool kTwo = D == 256;
+  WideBlock<D> d0;
+  load_block_at(d0, pg0 < pg1 ? phys_of(pg0) : 0);
+  {
+    // uint4 e of the operands: operand e >> 7, lane (e >> 1) & 63, half e & 1
+#pragma unroll
+    for (int i = 0; i < QueryStage<NOP, 1>::NV; ++i) {
+      const int e = tid + 256 * i;
+      if (e < NOP * 128) {
+        const int o64 = (e >> 7) * 64 + ((e >> 1) & 63);
+        if (e & 1)
+          s_q8[o64] = make_uint2(qs.v[0][i].x, qs.v[0][i].y);
+        else
+          s_q16[o64] = qs.v[0][i];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < QueryStage<NOP, 1>::NS; ++i) {
+      const int e = tid + 256 * i;
+      if (e < NOP * 64) s_qsc[e] = qs.sc[0][i];
+    }
+  }
+  __syncthreads();
+  if constexpr (kTwo) {
+    WideBlock<D> d1;
+    auto process = [&](const WideBlock<D> &d, int pg) {
+      v4f c1[4], c2[4];
+      score_mfma(d, c1, c2);
+      finish(d, pg, c1, c2);
+    };
+    for (int pg = pg0; pg < pg1; pg += 2) {
+      if (pg + 1 < pg1) load_block_at(d1, phys_of(pg + 1));
+      process(d0, pg);
+      if (pg + 1 >= pg1) break;
+      if (pg + 2 < pg1) load_block_at(d0, phys_of(pg + 2));
+      process(d1, pg + 1);
+    }
+  } else {
+    for (int pg = pg0; pg < pg1; ++pg) {
+      if (pg > pg0) load_block_at(d0, phys_of(pg));
+      v4f a1[4], a2[4];
+      score_mfma(d0, a1, a2);
+      finish(d0, pg, a1, a2);
+    }
+  }
+
+  // ---- combine the four waves into one partial per query row
+  __syncthreads();   // every wave is past the page loop: the query operands are dead
+  {
+    const float c7 = a.vcb.levels[(1 << VBITS) - 1];   // the V codebook's largest level
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float l_row = rowsum16(l_lane[r]), us_row = rowsum16(us_lane[r]);
+      if (n == 0) {
+        s_wm[wave][0][4 * kg + r] = m_run[r];
+        s_wm[wave][1][4 * kg + r] = l_row;
+        s_wm[wave][2][4 * kg + r] = mu_run[r];
+        s_wm[wave][3][4 * kg + r] = us_row;
+      }
+#pragma unroll
+      for (int k = 0; k < NB; ++k) s_wacc[wave][4 * kg + r][16 * k + n] = facc[k][r] - c7 * us_row;
+    }
+  }
+  __syncthreads();
+  const int nsplit = a.plan.n_split;
+  const int nrow = min(RW, G - row0);
+  const size_t pbase = (((size_t)b * H + kvh) * nsplit + split) * G + row0;
+  for (int qq = wave; qq < nrow; qq += 4) {
+    float M = kNegInf, MU = kNegInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      if (s_wm[w][1][qq] > 0.f) {
+        M = fmaxf(M, s_wm[w][0][qq]);
+        MU = fmaxf(MU, s_wm[w][2][qq]);
+      }
+    float lsum = 0.f, fw[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bool live = s_wm[w][1][qq] > 0.f;
+      lsum += live ? s_wm[w][1][qq] * __builtin_amdgcn_exp2f(s_wm[w][0][qq] - M) : 0.f;
+      fw[w] = live ? __builtin_amdgcn_exp2f(s_wm[w][2][qq] - MU) : 0.f;
+    }
+    float *pr = a.partials + (pbase + qq) * (D + kPartHead);
+    if (lane == 0) {
+      pr[0] = M;
+      pr[1] = lsum;
+      pr[2] = MU;
+      pr[3] = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < D / 64; ++r) {
+      const int i = lane + 64 * r;
+      float x = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x = fmaf(fw[w], s_wacc[w][qq][i], x);
+      pr[kPartHead + i] = x;
+    }
+  }
+}
+
 // One workgroup per (query row, KV head, sequence). Wave w takes splits
 // w, w + 4, ..., 16 at a time: lane c loads the header (m, l, mU) of the c-th,
 // every lane loads its coordinates of all 16 (split indices past the last are
@@ -780,6 +1253,12 @@ template <int D>
 hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
   const int G = a.plan.group;
   if (!a.plan.mfma || G > TQ_MAX_GROUP) return hipErrorInvalidValue;
+  if (a.plan.wide) {
+    if (a.k_bits != 3 || a.v_bits != 3 || a.plan.wg_per_seq != a.plan.qgroups) return hipErrorInvalidValue;
+    const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.qgroups);
+    hipLaunchKernelGGL((decode_wide_kernel<D>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   auto by_k = [&](auto VB) -> hipError_t {
     switch (a.k_bits) {
       case 2: return launch_split_bits<D, VB.value, 2>(a, s);
@@ -798,10 +1277,13 @@ hipError_t launch_split_dim(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int kb) {
+size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int kb, int vb) {
   size_t bytes = prep_float_bytes(d, batch, n_q, n_q_heads);
   const int group = n_q_heads / n_kv_heads * n_q;
-  if (mfma_path(d, group))
+  if (wide_path(d, group, kb, vb))
+    bytes += ((size_t)batch * n_kv_heads * ((group + kWideRows - 1) / kWideRows) * packed_group_bytes_wide(d) +
+              255) / 256 * 256;
+  else if (mfma_path(d, group))
     bytes += ((size_t)batch * n_kv_heads * query_groups(group) * packed_group_bytes(d, kb) + 255) / 256 * 256;
   return bytes;
 }

@@ -680,12 +680,13 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
 }
 
 // ------------------------------------------------------------------ prepare
-// kPrepPieces workgroups per query row qq of a (sequence, KV head) group: each
-// rotates the row and projects it with S (the four waves split the m rows of
-// S, and every S load of a chunk is issued before the row is rotated), then
-// packs its share of the row's four limb rows of the fp6 scoring operand;
-// piece 0 also writes q~, p and the row constants. Packing is a long chain of
-// dependent steps per lane, so it is spread over more SIMDs.
+// One or kPrepPieces workgroups per query row qq of a (sequence, KV head)
+// group (a.pieces): each rotates the row and projects it with S (the four
+// waves split the m rows of S, and every S load of a chunk is issued before the
+// row is rotated), then packs its share of the kPrepPieces shares of the row's
+// fp6 scoring operand; piece 0 also writes q~, p and the row constants. Packing
+// is a long chain of dependent steps per lane, so with few rows it is spread
+// over more SIMDs; with many rows one workgroup per row saves the S reads.
 constexpr int kPrepPieces = 4;
 
 // Rotation and projection of the row (the same for every key code width):
@@ -757,8 +758,10 @@ __device__ void prepare_front(const PrepArgs &a, int qq, int kvh, int b, int pie
 }
 
 // This piece's share of the row's scoring operand (KB-bit key codes), from
-// s_q and s_p.
-template <int D, int KB>
+// s_q and s_p. In a 4-row group the operand of MFMA mu holds the row's four
+// limbs on rows 4 qloc + limb; in a 16-row (wide) group limb l of every row
+// has an operand of its own, (mu, l), with the row on row qloc.
+template <int D, int KB, bool WIDE>
 __device__ void prepare_pack(const PrepArgs &a, int qq, int kvh, int b, int piece, const float *s_q,
                              const float *s_p) {
   constexpr int R = D / 64;
@@ -793,12 +796,20 @@ __device__ void prepare_pack(const PrepArgs &a, int qq, int kvh, int b, int piec
   }
   sq = wave_sum(sq);
   sp = wave_sum(sp);
-  // query group rho = qq / 4 has its own operand; this row is its row group qloc
-  const int QG = query_groups(G), rho = qq / kMfmaMaxGroup, qloc = qq % kMfmaMaxGroup;
-  const int Gr = min(kMfmaMaxGroup, G - kMfmaMaxGroup * rho);   // rows of the group
-  uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * packed_group_bytes(D, KB);
-  uint8_t *opb = grp;                                                  // [mu][lane][32] bytes
-  uint32_t *scl = reinterpret_cast<uint32_t *>(grp + (size_t)NMU * 2048);   // [mu][lane]
+  // query group rho = qq / RG has its own operand; this row is its row qloc
+  constexpr int RG = WIDE ? kWideRows : kMfmaMaxGroup;   // rows per query group
+  constexpr int NOP = WIDE ? 4 * NMU : NMU;              // MFMA operands per group
+  static_assert(!WIDE || KB == 3, "wide groups take 3-bit keys");
+  const int QG = (G + RG - 1) / RG, rho = qq / RG, qloc = qq % RG;
+  const int Gr = min(RG, G - RG * rho);   // rows of the group
+  const size_t gbytes = WIDE ? packed_group_bytes_wide(D) : packed_group_bytes(D, KB);
+  uint8_t *grp = a.packed + (((size_t)b * a.n_kv_heads + kvh) * QG + rho) * gbytes;
+  uint8_t *opb = grp;                                                  // [operand][lane][32] bytes
+  uint32_t *scl = reinterpret_cast<uint32_t *>(grp + (size_t)NOP * 2048);   // [operand][lane]
+  // where limb `limb` of this row's k-block kb sits: operand and lane
+  auto op_lane = [&](int mu, int kb, int limb) {
+    return WIDE ? (mu * 4 + limb) * 64 + 16 * kb + qloc : mu * 64 + 16 * kb + 4 * qloc + limb;
+  };
   const float kap2 = 2.f * qjl_kappa<D>();
   // Piece p takes the (MFMA, block pair) tasks p TP .. p TP + TP - 1 and its
   // wave w the tasks w, w + 4, ... of them: two 32-slot blocks at a time, one
@@ -848,35 +859,42 @@ __device__ void prepare_pack(const PrepArgs &a, int qq, int kvh, int b, int piec
       const uint32_t nx = (uint32_t)__shfl_down((int)pk, 4, 16);   // the next quad of the row
       uint32_t word = pj < 3 ? (pk >> (8 * pj)) | (nx << (24 - 8 * pj)) : 0u;
       word = (uint32_t)__builtin_amdgcn_mov_dpp((int)word, 0x00, 0xF, 0xF, true);   // quad_perm [0,0,0,0]
-      reinterpret_cast<uint32_t *>(opb)[((size_t)mu * 64 + 16 * kb + 4 * qloc + limb) * 8 + pdw] = word;
-      scl[mu * 64 + 16 * kb + 4 * qloc + limb] = (uint32_t)(ex + 127);
+      reinterpret_cast<uint32_t *>(opb)[(size_t)op_lane(mu, kb, limb) * 8 + pdw] = word;
+      scl[op_lane(mu, kb, limb)] = (uint32_t)(ex + 127);
     }
   };
   // every wave runs the same number of rounds; a task index past the piece's
   // last is clamped to it, so that task is computed twice and stored twice with
   // the same values, and all rounds stay one branch-free block
   constexpr int TP = (NTASK + kPrepPieces - 1) / kPrepPieces, NT = (TP + 3) / 4;
-  const int tlast = min(NTASK, TP * (piece + 1)) - 1;
-  if (TP * piece <= tlast) {
+  const int per = kPrepPieces / a.pieces;   // shares of this workgroup
+  for (int sh = piece * per; sh < piece * per + per; ++sh) {
+    const int tlast = min(NTASK, TP * (sh + 1)) - 1;
+    if (TP * sh <= tlast) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) pack_task(min(TP * piece + wave + 4 * t, tlast));
-  }
-  if (piece != 0) return;
-  // limb rows of rows Gr .. 3 of the group (no query): zero fields, unit scales
-  if (qloc == 0 && Gr < kMfmaMaxGroup) {
-    const int nrow = 4 * (kMfmaMaxGroup - Gr);
-    for (int t = threadIdx.x; t < NMU * 4 * nrow * 32; t += 256) {
-      const int byte = t & 31, rest = t >> 5;
-      const int row = 4 * Gr + rest % nrow, lg = (rest / nrow) & 3, mu = rest / nrow / 4;
-      opb[((size_t)mu * 64 + 16 * lg + row) * 32 + byte] = 0;
-      if (byte == 0) scl[mu * 64 + 16 * lg + row] = 127u;
+      for (int t = 0; t < NT; ++t) pack_task(min(TP * sh + wave + 4 * t, tlast));
     }
   }
-  float *rc = reinterpret_cast<float *>(grp + (size_t)NMU * (2048 + 256));
-  if (threadIdx.x < 4) {
+  if (piece != 0) return;
+  // MFMA rows of the group's rows Gr .. RG - 1 (no query): zero fields, unit
+  // scales (operand rows 4 r + limb of a 4-row group, row r of a wide one)
+  constexpr int RPR = WIDE ? 1 : 4;   // MFMA rows per query row in one operand
+  if (qloc == 0 && Gr < RG) {
+    const int nrow = RPR * (RG - Gr);
+    for (int t = threadIdx.x; t < NOP * 4 * nrow * 32; t += 256) {
+      const int byte = t & 31, rest = t >> 5;
+      const int row = RPR * Gr + rest % nrow, lg = (rest / nrow) & 3, op = rest / nrow / 4;
+      opb[((size_t)op * 64 + 16 * lg + row) * 32 + byte] = 0;
+      if (byte == 0) scl[op * 64 + 16 * lg + row] = 127u;
+    }
+  }
+  // row constants: {0, 0, sum q~, sum p} per row of a 4-row group, {sum q~, sum p} of a wide one
+  constexpr int RCW = WIDE ? 2 : 4;
+  float *rc = reinterpret_cast<float *>(grp + (size_t)NOP * (2048 + 256));
+  if (threadIdx.x < RCW) {
     const float cv[4] = {0.f, 0.f, sq, sp};
-    rc[4 * qloc + threadIdx.x] = cv[threadIdx.x];
-  } else if (qloc == 0 && threadIdx.x < 4 * kMfmaMaxGroup && threadIdx.x >= 4 * Gr) {
+    rc[RCW * qloc + threadIdx.x] = cv[4 - RCW + threadIdx.x];
+  } else if (qloc == 0 && threadIdx.x < RCW * RG && threadIdx.x >= RCW * Gr) {
     rc[threadIdx.x] = 0.f;
   }
 }
@@ -887,18 +905,20 @@ __device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b, int piece
   prepare_front<D, DT>(a, qq, kvh, b, piece, s_q, s_p);
   if (a.packed == nullptr) return;
   __syncthreads();
-  // the K code width is uniform over the launch
-  if (a.k_bits == 2)
-    prepare_pack<D, 2>(a, qq, kvh, b, piece, s_q, s_p);
+  // the K code width and the group width are uniform over the launch
+  if (a.wide)
+    prepare_pack<D, 3, true>(a, qq, kvh, b, piece, s_q, s_p);
+  else if (a.k_bits == 2)
+    prepare_pack<D, 2, false>(a, qq, kvh, b, piece, s_q, s_p);
   else if (a.k_bits == 4)
-    prepare_pack<D, 4>(a, qq, kvh, b, piece, s_q, s_p);
+    prepare_pack<D, 4, false>(a, qq, kvh, b, piece, s_q, s_p);
   else
-    prepare_pack<D, 3>(a, qq, kvh, b, piece, s_q, s_p);
+    prepare_pack<D, 3, false>(a, qq, kvh, b, piece, s_q, s_p);
 }
 
 template <int D, int DT>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
-  prepare_row<D, DT>(a, blockIdx.x / kPrepPieces, blockIdx.y, blockIdx.z, blockIdx.x % kPrepPieces);
+  prepare_row<D, DT>(a, blockIdx.x / a.pieces, blockIdx.y, blockIdx.z, blockIdx.x % a.pieces);
 }
 
 // One launch for the work of a decode step that precedes the split-K decode:
@@ -942,8 +962,8 @@ __global__ __launch_bounds__(256) void step_prologue_kernel(StepArgs s) {
     return;
   }
   id -= nv;
-  const int piece = id % kPrepPieces;
-  id /= kPrepPieces;
+  const int piece = id % s.p.pieces;
+  id /= s.p.pieces;
   const int G = s.p.n_q * (s.p.n_q_heads / s.p.n_kv_heads);
   const int qq = id % G, kvh = (id / G) % s.p.n_kv_heads, b = id / (G * s.p.n_kv_heads);
   prepare_row<D, DT>(s.p, qq, kvh, b, piece);
@@ -1073,18 +1093,27 @@ hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s) {
   });
 }
 
+// Workgroups per query row: kPrepPieces while the rows are few (the launch is
+// latency-bound), else one (each workgroup reads S).
+static int prep_pieces(const PrepArgs &a) {
+  const long rows = (long)a.n_q * a.n_q_heads * a.batch;
+  return rows <= 256 ? kPrepPieces : 1;
+}
+
 hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
-  const dim3 grid(a.n_q * (a.n_q_heads / a.n_kv_heads) * kPrepPieces, a.n_kv_heads, a.batch);
+  PrepArgs pa = a;
+  pa.pieces = prep_pieces(a);
+  const dim3 grid(a.n_q * (a.n_q_heads / a.n_kv_heads) * pa.pieces, a.n_kv_heads, a.batch);
   if (d == 128) {
     if (a.dtype == TQ_F32)
-      hipLaunchKernelGGL((prepare_kernel<128, TQ_F32>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prepare_kernel<128, TQ_F32>), grid, dim3(256), 0, s, pa);
     else
-      hipLaunchKernelGGL((prepare_kernel<128, TQ_BF16>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prepare_kernel<128, TQ_BF16>), grid, dim3(256), 0, s, pa);
   } else {
     if (a.dtype == TQ_F32)
-      hipLaunchKernelGGL((prepare_kernel<256, TQ_F32>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prepare_kernel<256, TQ_F32>), grid, dim3(256), 0, s, pa);
     else
-      hipLaunchKernelGGL((prepare_kernel<256, TQ_BF16>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((prepare_kernel<256, TQ_BF16>), grid, dim3(256), 0, s, pa);
   }
   return hipGetLastError();
 }
@@ -1100,11 +1129,12 @@ hipError_t launch_step_prologue(const EncodeArgs &k, const EncodeArgs &v, const 
   sa.k = k;
   sa.v = v;
   sa.p = p;
+  sa.p.pieces = prep_pieces(p);
   sa.nk = (int)((long)k.n_tokens * k.n_heads);   // one K vector per workgroup
   sa.nvx = (v.n_tokens + kWaves - 1) / kWaves;
   sa.nv = sa.nvx * v.n_heads;
   const long np = (long)p.n_q * p.n_q_heads * p.batch;   // query rows
-  const dim3 grid((unsigned)(sa.nk + sa.nv + np * kPrepPieces));
+  const dim3 grid((unsigned)(sa.nk + sa.nv + np * sa.p.pieces));
   return by_dim_dtype(d, k.dtype, [&](auto D, auto DT) {
     hipLaunchKernelGGL((step_prologue_kernel<D.value, DT.value>), grid, dim3(256), 0, s, sa);
     return hipGetLastError();

@@ -60,6 +60,8 @@ struct PrepArgs {
   const float *qjl;
   float *prep;            // [rows][2][d]: Pi q, then S Pi q
   uint8_t *packed;        // per (sequence, KV head, query group): operand + row constants (or null)
+  int wide;               // the packed operand is in 16-row groups (else 4-row groups)
+  int pieces;             // workgroups per query row (set at launch)
   Codebook cb;            // K
 };
 
@@ -86,11 +88,25 @@ __host__ __device__ inline int max_groups_per_wg(int d) { return d == 128 ? 2 : 
 __host__ __device__ inline bool mfma_path(int d, int group) {
   return (d == 128 || d == 256) && group <= TQ_MAX_GROUP;
 }
+// Wide query groups: 16 distinct query rows per scoring MFMA (one fp6 limb of
+// each row per MFMA, the four limbs accumulating in one result) and per V
+// MFMA (weights as two int8 limbs, each with its own int32 sums), for 16 or
+// more rows per KV head with 3-bit K and V codes. Packed operand of a wide
+// group: per scoring MFMA mu and limb, 64 lanes x 32 bytes, then the scale
+// words of the same operands (64 per operand), then 16 rows x {sum q~, sum p}.
+constexpr int kWideRows = 16;
+__host__ __device__ inline bool wide_path(int d, int group, int kb, int vb) {
+  return mfma_path(d, group) && group >= kWideRows && kb == 3 && vb == 3;
+}
+__host__ __device__ inline size_t packed_group_bytes_wide(int d) {
+  return (size_t)mfma_per_tile(d, 3) * 4 * (64 * 32 + 64 * 4) + kWideRows * 8;
+}
 
 // Split-K plan of one decode call.
 struct DecodePlan {
   int group;              // query rows per (sequence, KV head) = Hq/Hkv * n_q
-  int qgroups;            // MFMA query groups of 4 rows (MFMA path)
+  bool wide;              // query groups of 16 rows (wide_path), else of 4
+  int qgroups;            // MFMA query groups of 4 (or 16) rows (MFMA path)
   int groups_per_wg;      // query groups one decode workgroup serves: 1 or 2
   int wg_per_seq;         // decode workgroups per (split, KV head, sequence)
   int pages_per_split;
@@ -102,7 +118,7 @@ struct DecodePlan {
 
 // Query region of a decode call: [rows][2][d] float32, then (MFMA path) the
 // packed operands of the B*Hkv groups.
-size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int kb = 3);
+size_t prep_region_bytes(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int kb, int vb);
 inline size_t prep_float_bytes(int d, int batch, int n_q, int n_q_heads) {
   return ((size_t)batch * n_q * n_q_heads * 2 * d * sizeof(float) + 255) / 256 * 256;
 }
@@ -128,7 +144,7 @@ struct DecodeArgs {
 };
 
 DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads, int max_pages,
-                       int kb = 3);
+                       int kb, int vb);
 
 hipError_t launch_encode_k(const EncodeArgs &a, int d, hipStream_t s);
 hipError_t launch_encode_v(const EncodeArgs &a, int d, hipStream_t s);

@@ -111,10 +111,14 @@ def test_dequant_and_prepare_validation(L):
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 7, FAKE, C.byref(sz), None) == tq.TQ_EINVAL
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE + 16, C.byref(sz), None) == tq.TQ_EALIGN
     assert L.tq_query_prepare(r, FAKE, 0, 2, 1, 8, FAKE, None, None) == tq.TQ_EINVAL
-    # 16 rows per KV head: four query groups of 4 rows, each with its own operand
+    # 16 rows per KV head (3-bit K and V): one wide query group per (sequence, KV
+    # head), whose operand holds each of the 5 scoring MFMAs once per fp6 limb
+    # (4 x 5 operands, 32 query bytes and a scale word per lane each), then 16 x 2
+    # row constants
     sz16 = C.c_size_t(0)
     assert L.tq_query_prepare(r, FAKE, 0, 2, 2, 16, None, C.byref(sz16), None) == tq.TQ_OK
-    assert sz16.value == 2 * 2 * 16 * 2 * 128 * 4 + 2 * 2 * 4 * grp
+    wide = 4 * 5 * (64 * 32 + 64 * 4) + 16 * 2 * 4
+    assert sz16.value == 2 * 2 * 16 * 2 * 128 * 4 + (2 * 2 * 1 * wide + 255) // 256 * 256
 
 
 def _decode(L, dsc, ws=None, size=None, B=2, nq=1, Hq=8, maxp=16, causal=0, q=FAKE):
@@ -138,8 +142,10 @@ def test_decode_validation_and_workspace(L):
     assert _decode(L, dsc, Hq=7)[0] == tq.TQ_EINVAL                # Hq not a multiple of Hkv
     assert _decode(L, dsc, Hq=8, nq=1025)[0] == tq.TQ_EUNSUPPORTED   # 4 * 1025 rows > 4096
     assert _decode(L, dsc, Hq=8, nq=1024)[0] == tq.TQ_OK
-    # batch x workgroups per sequence must fit the third grid dimension (65535)
-    assert _decode(L, dsc, B=128, Hq=8, nq=1024)[0] == tq.TQ_EUNSUPPORTED
+    # batch x workgroups per sequence must fit the third grid dimension (65535):
+    # 4096 rows per KV head are 256 wide groups of 16 rows
+    assert _decode(L, dsc, B=255, Hq=8, nq=1024)[0] == tq.TQ_OK
+    assert _decode(L, dsc, B=256, Hq=8, nq=1024)[0] == tq.TQ_EUNSUPPORTED
     assert _decode(L, dsc, causal=2)[0] == tq.TQ_EINVAL
     assert _decode(L, dsc, B=0)[0] == tq.TQ_EINVAL
     assert _decode(L, dsc, maxp=0)[0] == tq.TQ_EINVAL

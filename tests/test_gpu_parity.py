@@ -724,3 +724,84 @@ def test_dense_baseline_parity(tq, d, Hq, nq, lens):
     err = Hn.attn_rel_err(out, ref)
     print(f"  max rel err {err:.3e}", flush=True)
     assert err <= Hn.ATTN_TOL
+
+
+def _fp6_e2m3(code):
+    """Value of OCP fp6 e2m3 codes (sign bit 5; 1/8 steps below 2, then 1/4, 1/2)."""
+    m = code & 0x1F
+    v = np.where(m < 16, m / 8.0, np.where(m < 24, 2.0 + (m - 16) / 4.0, 4.0 + (m - 24) / 2.0))
+    return np.where(code & 0x20, -v, v)
+
+
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("n_q", [1, 5])
+def test_query_operand_layout(tq, d, n_q):
+    """The packed scoring operand reconstructs its inputs. Per 32-slot block of
+    MFMA mu (coordinate chunk c = mu // 5, plane pl = mu % 5), slot f holds
+    y_i / value(f) as four fp6 limbs with E8M0 scales, i = 32 (block + 4 c) +
+    4 (f & 7) + (f >> 3), value 0.5, 1, 2, 2 for f >> 3 = 0..3, and y = w_pl q~_i
+    (code planes) or 2 kappa p_i (signs); the limbs sum to it within 2^-17 of the
+    block's largest term. With 4 rows per KV head (n_q = 1) a query group has 4
+    rows and MFMA mu holds row r's limbs on rows 4 r + limb; with 20 (n_q = 5)
+    the rows form wide groups of 16 (the second one ragged), and limb l of row r
+    sits on row r of operand (mu, l). Rows past the group are zero with unit
+    scales; q~ and p come from the same buffer (checked against the oracle in
+    test_query_prepare_parity)."""
+    B, Hkv, Hq = 2, 2, 8
+    g = Hq // Hkv
+    G = g * n_q
+    cache = tq.Cache(d, Hkv, 1)
+    q = np.random.default_rng(40 + n_q).standard_normal((B, n_q, Hq, d)).astype(np.float32)
+    prep = tq.tq_query_prepare(cache, torch.from_numpy(q).cuda())
+    torch.cuda.synchronize()
+    rows = tq.prepared_rows(prep, q.shape).cpu().numpy().astype(np.float64)
+    raw = prep.cpu().numpy()
+    wide = G >= 16
+    NMU = 5 * d // 128
+    RG = 16 if wide else 4
+    NOP = 4 * NMU if wide else NMU
+    QG = -(-G // RG)
+    gbytes = NOP * (2048 + 256) + (16 * 8 if wide else 64)
+    off0 = -(-(B * n_q * Hq * 2 * d * 4) // 256) * 256
+    lv = cache.k_levels.astype(np.float64)
+    a2 = 0.25 * (lv[4] + lv[5] + lv[6] + lv[7])
+    w = [2 * (0.5 * (lv[5] + lv[7]) - a2), 2 * (0.5 * (lv[6] + lv[7]) - a2), 2 * a2,
+         2 * (0.5 * (lv[4] + lv[7]) - a2)]
+    kap2 = 2 * math.sqrt(math.pi / 2) / d
+    f = np.arange(32)
+    fv, fm = f >> 3, f & 7
+    val = np.where(fv == 0, 0.5, np.where(fv == 1, 1.0, 2.0))
+    worst = 0.0
+    for b in range(B):
+        for kvh in range(Hkv):
+            for rho in range(QG):
+                grp = raw[off0 + ((b * Hkv + kvh) * QG + rho) * gbytes:][:gbytes]
+                ops = grp[:NOP * 2048].reshape(NOP, 64, 32)
+                scl = grp[NOP * 2048:NOP * 2304].view(np.uint32).reshape(NOP, 64)
+                for qloc in range(RG):
+                    qq = rho * RG + qloc
+                    lanes = [(mu, kb, [((mu * 4 + l) if wide else mu,
+                                        16 * kb + (qloc if wide else 4 * qloc + l)) for l in range(4)])
+                             for mu in range(NMU) for kb in range(4)]
+                    for mu, kb, where in lanes:
+                        recon = np.zeros(32)
+                        for o, lane in where:
+                            bits = int.from_bytes(ops[o, lane, :24].tobytes(), "little")
+                            codes = np.array([(bits >> (6 * k)) & 63 for k in range(32)])
+                            assert not ops[o, lane, 24:].any()
+                            recon += _fp6_e2m3(codes) * 2.0 ** (int(scl[o, lane]) - 127)
+                        if qq >= G:
+                            assert not recon.any()
+                            assert all(int(scl[o, lane]) == 127 for o, lane in where)
+                            continue
+                        t, hh = qq // g, qq % g
+                        qt = rows[b, t, kvh * g + hh, 0]
+                        p = rows[b, t, kvh * g + hh, 1]
+                        c, pl = mu // 5, mu % 5
+                        i = 32 * (kb + 4 * c) + 4 * fm + fv
+                        y = (w[pl] * qt[i] if pl < 4 else kap2 * p[i]) / val
+                        den = max(np.max(np.abs(y)), 1e-30)
+                        err = np.max(np.abs(recon - y)) / den
+                        worst = max(worst, err)
+                        assert err < 2.0 ** -17, (b, kvh, qq, mu, kb, err)
+    print(f"[operand layout] d={d} rows={G} wide={wide}: worst limb-sum error {worst:.2e} of block max")

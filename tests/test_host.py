@@ -95,14 +95,18 @@ def test_split_workspace_follows_the_plan(d):
     """The prepared call's workspace is the split partials alone:
     B * Hkv * n_split * rows * (d + 4) floats, rounded up to 256 B, with
     n_split = ceil(max_pages / pps) and pps = clamp(ceil(B Hkv max_pages W / 512), 1, 256)
-    (W = workgroups per sequence)."""
+    (W = workgroups per sequence: one per wide group of 16 rows when there are 16
+    rows or more, else one per one or two (d = 128) groups of 4)."""
     dsc = _desc(d)
     for B, nq, Hq, maxp in [(1, 1, 32, 128), (1, 1, 16, 391), (32, 1, 32, 64), (4, 4, 32, 512),
                             (1, 512, 32, 130), (2, 1, 8, 1)]:
         rows = Hq // 8 * nq
-        qg = (rows + 3) // 4
-        per_wg = (2 if d == 128 else 1) if qg > 1 else 1
-        wz = (qg + per_wg - 1) // per_wg
+        if rows >= 16:
+            wz = (rows + 15) // 16
+        else:
+            qg = (rows + 3) // 4
+            per_wg = (2 if d == 128 else 1) if qg > 1 else 1
+            wz = (qg + per_wg - 1) // per_wg
         pps = min(256, max(1, -(-(B * 8 * maxp * wz) // 512)))
         n_split = -(-maxp // pps)
         want = -(-(B * 8 * n_split * rows * (d + 4) * 4) // 256) * 256
