@@ -223,11 +223,13 @@ DecodePlan plan_decode(int d, int batch, int n_q, int n_q_heads, int n_kv_heads,
   // group has a workgroup of its own.
   p.groups_per_wg = p.qgroups > 1 && !p.wide ? max_groups_per_wg(d) : 1;
   p.wg_per_seq = (p.qgroups + p.groups_per_wg - 1) / p.groups_per_wg;
-  // About 512 workgroups (two per CU, one occupancy round) so that every
-  // workgroup streams several pages with its loads overlapped; whole pages per
-  // split; at most 256 pages (65536 tokens) per split.
+  // About 512 workgroups (two per CU, one occupancy round), or 768 for the
+  // one-group kernel at d = 128 (three per CU), so that every workgroup streams
+  // several pages with its loads overlapped; whole pages per split; at most 256
+  // pages (65536 tokens) per split.
+  const long target = d == 128 && !p.wide && p.groups_per_wg == 1 ? 768 : 512;
   long work = (long)batch * n_kv_heads * max_pages * p.wg_per_seq;
-  int pps = (int)((work + 511) / 512);
+  int pps = (int)((work + target - 1) / target);
   if (pps < 1) pps = 1;
   if (pps > 256) pps = 256;
   p.pages_per_split = pps;

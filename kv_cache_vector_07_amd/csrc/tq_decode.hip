@@ -104,13 +104,11 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // n_split * Hkv a multiple of 8 they land on the same XCD and share its L2.
 // With a causal tail a workgroup stops at the last token its rows can see.
 //
-// With TWO_SETS (d = 128, one group, more than two pages per split),
-// everything one block needs (key records, sidecars, V words) is loaded one
-// block ahead; two register sets alternate between even and odd pages so that
-// no copy is needed. Otherwise the block's loads are issued at its start: at
-// d = 256 to keep two waves per SIMD, and at d = 128 with two pages or fewer
-// per split, where a wave sees at most two blocks and the one-set kernel
-// (about 115 VGPRs against 180) finishes sooner.
+// A block's loads are issued at its start (the first block's before the query
+// operand is staged), into one register set: at d = 128 with one group that
+// leaves three waves per SIMD (under 170 VGPRs), which hides the load latency
+// better than loading one block ahead into a second set at two waves per SIMD;
+// at d = 256 one set keeps two waves per SIMD.
 
 // The packed scoring operand of the workgroup's query groups (per group NMU x
 // 64 lanes x 32 bytes, then NMU x 64 scale words), held in registers between
@@ -171,9 +169,8 @@ struct MfmaBlock {
 // NG query groups (4 rows each) share a workgroup: the key and V operands of a
 // block are built once and each MFMA operand of the keys or V bits meets the NG
 // query operands in turn. NG = 1 gives each group its own workgroup.
-template <int D, int NG, int VBITS, int KBITS, bool TWO_SETS>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2 : 1))) void decode_mfma_kernel(DecodeArgs a) {
-  static_assert(!TWO_SETS || (D == 128 && NG == 1), "two register sets only at d = 128 with one group");
+template <int D, int NG, int VBITS, int KBITS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? (D == 128 ? 3 : 2) : 1))) void decode_mfma_kernel(DecodeArgs a) {
   constexpr int NPK = k_planes(KBITS);      // key code planes (then the sign plane)
   constexpr int NMU = mfma_per_tile(D, KBITS);   // scaled MFMAs per 16-token scoring tile
   constexpr int NCH = D / 128;              // 128-coordinate chunks per token
@@ -591,21 +588,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? 2
   // the packed query operand is shared by the four waves: keep it in LDS
   qs.store(s_qop, s_qsc, rho0, QG, tid);
   __syncthreads();
-  if constexpr (TWO_SETS) {
-    MfmaBlock<D, VBITS, KBITS> d1;
-    for (int pg = pg0; pg < pg1; pg += 2) {
-      if (pg + 1 < pg1) load_block(d1, pg + 1);
-      process(d0, pg);
-      if (pg + 1 >= pg1) break;
-      if (pg + 2 < pg1) load_block(d0, pg + 2);
-      process(d1, pg + 1);
-    }
-  } else {
-    // one register set
-    for (int pg = pg0; pg < pg1; ++pg) {
-      if (!kEarly || pg > pg0) load_block(d0, pg);
-      process(d0, pg);
-    }
+  for (int pg = pg0; pg < pg1; ++pg) {
+    if (!kEarly || pg > pg0) load_block(d0, pg);
+    process(d0, pg);
   }
 
   if constexpr (kLazyV) fold_v(0);
@@ -1232,15 +1217,11 @@ hipError_t launch_split_bits(const DecodeArgs &a, hipStream_t s) {
   const dim3 grid(a.plan.n_split, a.n_kv_heads, a.batch * a.plan.wg_per_seq);
   switch (a.plan.groups_per_wg) {
     case 1:
-      // loads one block ahead pay off once a wave sees more than two blocks
-      if (D == 128 && a.plan.pages_per_split > 2)
-        hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS, KBITS, D == 128>), grid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS, KBITS, false>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((decode_mfma_kernel<D, 1, VBITS, KBITS>), grid, dim3(256), 0, s, a);
       break;
     case 2:
       if constexpr (D == 128) {
-        hipLaunchKernelGGL((decode_mfma_kernel<D, 2, VBITS, KBITS, false>), grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL((decode_mfma_kernel<D, 2, VBITS, KBITS>), grid, dim3(256), 0, s, a);
         break;
       }
       return hipErrorInvalidValue;

@@ -94,7 +94,8 @@ def _prepared_ws(dsc, B, nq, Hq, maxp):
 def test_split_workspace_follows_the_plan(d):
     """The prepared call's workspace is the split partials alone:
     B * Hkv * n_split * rows * (d + 4) floats, rounded up to 256 B, with
-    n_split = ceil(max_pages / pps) and pps = clamp(ceil(B Hkv max_pages W / 512), 1, 256)
+    n_split = ceil(max_pages / pps) and pps = clamp(ceil(B Hkv max_pages W / T), 1, 256)
+    (T = 768 for a single group of 4 rows at d = 128, else 512)
     (W = workgroups per sequence: one per wide group of 16 rows when there are 16
     rows or more, else one per one or two (d = 128) groups of 4)."""
     dsc = _desc(d)
@@ -107,7 +108,9 @@ def test_split_workspace_follows_the_plan(d):
             qg = (rows + 3) // 4
             per_wg = (2 if d == 128 else 1) if qg > 1 else 1
             wz = (qg + per_wg - 1) // per_wg
-        pps = min(256, max(1, -(-(B * 8 * maxp * wz) // 512)))
+        # 768 workgroups for the one-group kernel at d = 128, else 512
+        target = 768 if d == 128 and rows <= 4 else 512
+        pps = min(256, max(1, -(-(B * 8 * maxp * wz) // target)))
         n_split = -(-maxp // pps)
         want = -(-(B * 8 * n_split * rows * (d + 4) * 4) // 256) * 256
         assert _prepared_ws(dsc, B, nq, Hq, maxp) == want, (B, nq, Hq, maxp)
