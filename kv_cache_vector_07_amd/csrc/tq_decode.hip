@@ -678,7 +678,7 @@ struct WideBlock {
 // and a lane permutation (kg <-> kgA, one ds_bpermute per weight) bring the
 // weights there, and byte permutes pack the limbs.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 2 : 1))) void decode_wide_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_wide_kernel(DecodeArgs a) {
   constexpr int VBITS = 3, KBITS = 3;
   constexpr int NPK = 4;                       // key code planes (then the sign plane)
   constexpr int NMU = mfma_per_tile(D, KBITS);
@@ -703,6 +703,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
   constexpr size_t RAW = QALL > WACC_BYTES ? QALL : WACC_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char s_raw[RAW];
   __shared__ float s_wm[4][4][RW];                  // per wave: m, l, mU, sum U of each row
+  __shared__ float4 s_rc[RW];                       // per row: code and sign offsets, visible length
   uint4 *s_q16 = reinterpret_cast<uint4 *>(s_raw);  // [operand][lane]
   uint2 *s_q8 = reinterpret_cast<uint2 *>(s_raw + Q16_BYTES);
   int *s_qsc = reinterpret_cast<int *>(s_raw + Q16_BYTES + Q8_BYTES);
@@ -756,6 +757,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
       off2[r] = live ? spv[r] * qjl_kappa<D>() : 0.f;
       vis[r] = !live ? 0 : a.causal_tail ? L - (a.n_q - 1 - row / g) : L;
     }
+  }
+  // the row constants are read from LDS where they are used, which keeps them
+  // out of the registers of the page loop
+  if (wave == 0 && n == 0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s_rc[4 * kg + r] = make_float4(off1[r], off2[r], __int_as_float(vis[r]), 0.f);
   }
   const float scale2 = a.scale * 1.4426950408889634f;   // scores in log2 units
   float wpl[4];
@@ -857,6 +864,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
     const uint4 (&vcur)[VBITS][NCH] = d.v;
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
+    int ro = 4 * kg;
+    asm volatile("" : "+v"(ro));
+    float4 rcr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rcr[r] = s_rc[ro + r];
     float sc[4][4], sv[4][4];   // [tau][row r]
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
@@ -869,8 +881,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
       const float sN = scale2 * N;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const bool valid = in_page && tok0 + tok < vis[r];   // vis = 0 for rows past the group
-        const float sco = sN * fmaf(Gt, c2[tau][r] - off2[r], c1[tau][r] - off1[r]);
+        const bool valid = in_page && tok0 + tok < __float_as_int(rcr[r].z);   // 0 for rows past the group
+        const float sco = sN * fmaf(Gt, c2[tau][r] - rcr[r].y, c1[tau][r] - rcr[r].x);
         sc[tau][r] = valid ? sco : kNegInf;
         sv[tau][r] = valid ? sco + lnv : kNegInf;   // + log2 N^V
       }
@@ -979,8 +991,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
     v4i Aall[4][3];
 #pragma unroll
     for (int j = 0; j < 4; ++j) build_a(j, Aall[j]);
-    // column blocks per chunk: 8 (at d = 128 4, to stay within 256 registers)
-    constexpr int CBK = D == 128 ? 4 : 8;
+    // column blocks per chunk: 4 at d = 128, 2 at d = 256 (two waves per SIMD
+    // need at most 256 registers)
+    constexpr int CBK = D == 128 ? 4 : 2;
 #pragma unroll
     for (int ch = 0; ch < NB / CBK; ++ch) {
       v4i vacc[3][CBK];
@@ -1020,9 +1033,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
   };
 
   // the query operand (shared by the four waves, kept in LDS) is loaded first,
-  // then the first block, then the operand is copied into LDS. At d = 256 (one
-  // wave per SIMD) a second register set takes each block's loads one block ahead.
-  constexpr bool kTwo = D == 256;
+  // then the first block, then the operand is copied into LDS
   WideBlock<D> d0;
   load_block_at(d0, pg0 < pg1 ? phys_of(pg0) : 0);
   {
@@ -1045,27 +1056,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 128 ? 
     }
   }
   __syncthreads();
-  if constexpr (kTwo) {
-    WideBlock<D> d1;
-    auto process = [&](const WideBlock<D> &d, int pg) {
-      v4f c1[4], c2[4];
-      score_mfma(d, c1, c2);
-      finish(d, pg, c1, c2);
-    };
-    for (int pg = pg0; pg < pg1; pg += 2) {
-      if (pg + 1 < pg1) load_block_at(d1, phys_of(pg + 1));
-      process(d0, pg);
-      if (pg + 1 >= pg1) break;
-      if (pg + 2 < pg1) load_block_at(d0, phys_of(pg + 2));
-      process(d1, pg + 1);
-    }
-  } else {
-    for (int pg = pg0; pg < pg1; ++pg) {
-      if (pg > pg0) load_block_at(d0, phys_of(pg));
-      v4f a1[4], a2[4];
-      score_mfma(d0, a1, a2);
-      finish(d0, pg, a1, a2);
-    }
+  for (int pg = pg0; pg < pg1; ++pg) {
+    if (pg > pg0) load_block_at(d0, phys_of(pg));
+    v4f a1[4], a2[4];
+    score_mfma(d0, a1, a2);
+    finish(d0, pg, a1, a2);
   }
 
   // ---- combine the four waves into one partial per query row
