@@ -499,7 +499,7 @@ def prefill_attention(wl, chunk, tm, log):
     Reported against the time its MFMA instructions need at the published
     rates (16 clocks per 16x16x128 fp6 x fp4 and per 16x16x64 int8 MFMA on
     1024 SIMDs at 2.4 GHz), counted over the 64-token blocks each workgroup's
-    rows can see."""
+    rows can see, for the kernel the row count selects."""
     import torch
     from kv_cache_vector_07_amd import inputs as I
     w, lens = wl.w, wl.lens
@@ -536,15 +536,22 @@ def prefill_attention(wl, chunk, tm, log):
         if r:
             raise RuntimeError(f"prefill attention launch failed with status {r}")
     ms, runs = tm.median(run, 4, warm=3)
-    # MFMA instructions: per visible 64-token block and query group of 4 rows,
-    # 4 tiles x 5 d/128 fp6 x fp4 MFMAs and 4 planes x d/16 int8 MFMAs
-    per_blk = 4 * 5 * (d // 128) + 4 * (d // 16)
-    groups = (rows + 3) // 4
+    # MFMA instructions per visible 64-token block. Wide groups (16 rows or
+    # more, 3-bit K and V): per 16 rows, 4 tiles x 5 d/128 x 4 limbs fp6 x fp4
+    # MFMAs and 4 planes x 3 limbs x d/16 int8 MFMAs. Narrow groups of 4 rows:
+    # 4 tiles x 5 d/128 fp6 x fp4 MFMAs and 4 planes x d/16 int8 MFMAs.
+    wide = rows >= 16 and wl.kbits == 3 and wl.vbits == 3
+    RW = 16 if wide else 4
+    if wide:
+        per_blk = 4 * 5 * (d // 128) * 4 + 4 * 3 * (d // 16)
+    else:
+        per_blk = 4 * 5 * (d // 128) + 4 * (d // 16)
+    groups = (rows + RW - 1) // RW
     blocks = 0
     useful = 0
     for L in lens:
         for gi in range(groups):
-            t_last = min(4 * gi + 3, rows - 1) // g
+            t_last = min(RW * gi + RW - 1, rows - 1) // g
             vis = int(L) - (chunk - 1 - t_last)
             blocks += (vis + 63) // 64
         t = np.arange(chunk)
