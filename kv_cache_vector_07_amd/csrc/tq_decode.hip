@@ -770,15 +770,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   float wmax = 0.f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) wmax = fmaxf(wmax, fabsf(wpl[j]));
-  // weight X = U' * 2^-tau * (w_j / wmax) * kFix with U' < 1 the block-scaled
-  // weight (|X| <= kFix, so X + 0x8080 keeps its top byte in int8), 2^tau being
-  // the value the V bit of token 16 tau + 4 k + r takes in byte r of the B operand
+  // weight X = U' * 2^-tau * (|w_j| / wmax) * kFix with U' < 1 the block-scaled
+  // weight, 2^tau being the value the V bit of token 16 tau + 4 k + r takes in
+  // byte r of the B operand. A plane with a negative weight is taken as its
+  // complement, w p = |w| (1 - p) + w, so X >= 0 and the constant w joins the
+  // offset: the levels are sum_j |w_j| p'_j - c_eff with c_eff = c7 - sum of the
+  // negative w_j. With 0 <= X <= kFix, X + 0x8080 < 2^23: it is exact in the
+  // mantissa of 2^23 + 0x8080 + X (round to nearest), and its top byte is int8.
   constexpr float kFix = 8355000.f;
-  float cx[4], half[4];
+  constexpr float kMagic = 8421504.f;   // 2^23 + 0x8080
+  float cx[4], c_eff = a.vcb.levels[(1 << VBITS) - 1];
+  uint32_t flip[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    half[j] = wpl[j] < 0.f ? -0.5f : 0.5f;   // round to nearest with a truncating convert
-    cx[j] = wpl[j] / wmax * kFix;
+    cx[j] = fabsf(wpl[j]) / wmax * kFix;
+    flip[j] = wpl[j] < 0.f ? 0xFFFFFFFFu : 0u;
+    c_eff -= wpl[j] < 0.f ? wpl[j] : 0.f;
   }
   const float delta_u = wmax / kFix;
   // source lane of the weight transpose (kg <-> kgA): lane 16 a + 4 b + c reads lane 16 b + 4 a + c
@@ -970,14 +977,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
       return e == 0 ? u.x : e == 1 ? u.y : e == 2 ? u.z : u.w;
     };
     // weight limbs of plane j: bytes r = limb l of the weight of token
-    // 16 tau + 4 kgA + r. Y = X + 0x8080; limbs: bytes 0 and 1 of Y with their
-    // top bit flipped, then byte 2 (signed): X = b0 + 256 b1 + 65536 b2.
+    // 16 tau + 4 kgA + r. Y = X + 0x8080 (low three bytes of the float
+    // 2^23 + 0x8080 + X); limbs: bytes 0 and 1 of Y with their top bit flipped,
+    // then byte 2 (in [0, 127]): X = b0 + 256 b1 + 65536 b2.
     auto build_a = [&](int j, v4i (&Aj)[3]) {
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) {
           uint32_t Y[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Y[r] = (uint32_t)(int)fmaf(T[tau][r], cx[j], half[j]) + 0x8080u;
+          for (int r = 0; r < 4; ++r) Y[r] = __float_as_uint(fmaf(T[tau][r], cx[j], kMagic));
           const uint32_t t01 = __builtin_amdgcn_perm(Y[1], Y[0], 0x05010400u);   // Y0.b0 Y1.b0 Y0.b1 Y1.b1
           const uint32_t t23 = __builtin_amdgcn_perm(Y[3], Y[2], 0x05010400u);
           const uint32_t u01 = __builtin_amdgcn_perm(Y[1], Y[0], 0x06020602u);   // Y0.b2 Y1.b2 (twice)
@@ -1004,7 +1012,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
 #pragma unroll
         for (int kq = 0; kq < CBK / 2; ++kq) {
           const int kp = (CBK / 2) * ch + kq;
-          const uint32_t wj = j < 3 ? vword(j, kp) : vword(0, kp) ^ vword(1, kp) ^ vword(2, kp);
+          const uint32_t wj = (j < 3 ? vword(j, kp) : vword(0, kp) ^ vword(1, kp) ^ vword(2, kp)) ^ flip[j];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const uint32_t w = wj >> (4 * h);
@@ -1066,7 +1074,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // ---- combine the four waves into one partial per query row
   __syncthreads();   // every wave is past the page loop: the query operands are dead
   {
-    const float c7 = a.vcb.levels[(1 << VBITS) - 1];   // the V codebook's largest level
+    const float c7 = c_eff;   // the V levels' offset (the largest level, less the flipped planes' weights)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float l_row = rowsum16(l_lane[r]), us_row = rowsum16(us_lane[r]);
