@@ -736,6 +736,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
   // Lv: one past the last token any row of the workgroup sees
   const int row_last = min(row0 + RW, G) - 1;
   const int Lv = a.causal_tail ? L - (a.n_q - 1 - row_last / g) : L;
+  // one past the last token the workgroup's first row (the one that sees least) sees
+  const int vis_first = a.causal_tail ? L - (a.n_q - 1 - row0 / g) : L;
   const int n_pages_seq = min((Lv + kPage - 1) / kPage, a.max_pages);
   const int S0 = a.seq_starts ? max(0, s0raw) : 0;
   const int pg0 = max(pgs, S0 / kPage);
@@ -833,8 +835,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     // offset keeps them from being hoisted out of the page loop)
     int qo = lane;
     asm volatile("" : "+v"(qo));
+    // the accumulators start at minus the rows' code and sign offsets, so the
+    // MFMAs leave the offset-corrected sums
+    {
+      int ro = 4 * kg;
+      asm volatile("" : "+v"(ro));
+      float4 rcr[4];
 #pragma unroll
-    for (int tau = 0; tau < 4; ++tau) c1[tau] = c2[tau] = v4f{0.f, 0.f, 0.f, 0.f};
+      for (int r = 0; r < 4; ++r) rcr[r] = s_rc[ro + r];
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        c1[tau] = v4f{-rcr[0].x, -rcr[1].x, -rcr[2].x, -rcr[3].x};
+        c2[tau] = v4f{-rcr[0].y, -rcr[1].y, -rcr[2].y, -rcr[3].y};
+      }
+    }
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
 #pragma unroll
@@ -871,27 +885,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const uint4 (&vcur)[VBITS][NCH] = d.v;
     const int tok0 = pg * kPage;
     const int ntok = min(kPage, L - tok0);
-    int ro = 4 * kg;
-    asm volatile("" : "+v"(ro));
-    float4 rcr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) rcr[r] = s_rc[ro + r];
     float sc[4][4], sv[4][4];   // [tau][row r]
+    float sN[4], lnv[4];
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       const int sh = 16 * (tau & 1);
       const float Gt = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.g.y : d.g.x) >> sh));
       const float N = f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nk.y : d.nk.x) >> sh));
-      const float lnv = __builtin_amdgcn_logf(f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nv.y : d.nv.x) >> sh)));
-      const int tok = blk0 + 16 * tau + n;
-      const bool in_page = tok < ntok && tok0 + tok >= S0;
-      const float sN = scale2 * N;
+      lnv[tau] = __builtin_amdgcn_logf(f16_bits_to_f32((uint16_t)(((tau >> 1) ? d.nv.y : d.nv.x) >> sh)));
+      sN[tau] = scale2 * N;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool valid = in_page && tok0 + tok < __float_as_int(rcr[r].z);   // 0 for rows past the group
-        const float sco = sN * fmaf(Gt, c2[tau][r] - rcr[r].y, c1[tau][r] - rcr[r].x);
-        sc[tau][r] = valid ? sco : kNegInf;
-        sv[tau][r] = valid ? sco + lnv : kNegInf;   // + log2 N^V
+      for (int r = 0; r < 4; ++r) sc[tau][r] = sN[tau] * fmaf(Gt, c2[tau][r], c1[tau][r]);
+    }
+    // a block that every row of the workgroup sees whole (inside the page and
+    // the window, before the first row's causal end) needs no mask
+    if (tok0 + blk0 >= S0 && tok0 + blk0 + 64 <= vis_first) {
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[tau][r] = sc[tau][r] + lnv[tau];   // + log2 N^V
+    } else {
+      int ro = 4 * kg;
+      asm volatile("" : "+v"(ro));
+      int visr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) visr[r] = __float_as_int(s_rc[ro + r].z);
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const int tok = blk0 + 16 * tau + n;
+        const bool in_page = tok < ntok && tok0 + tok >= S0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool valid = in_page && tok0 + tok < visr[r];   // 0 for rows past the group
+          sv[tau][r] = valid ? sc[tau][r] + lnv[tau] : kNegInf;
+          sc[tau][r] = valid ? sc[tau][r] : kNegInf;
+        }
       }
     }
 
