@@ -686,13 +686,18 @@ __global__ __launch_bounds__(256) void encode_v_kernel(EncodeArgs a) {
 // row is rotated), then packs its share of the kPrepPieces shares of the row's
 // fp6 scoring operand; piece 0 also writes q~, p and the row constants. Packing
 // is a long chain of dependent steps per lane, so with few rows it is spread
-// over more SIMDs; with many rows one workgroup per row saves the S reads.
+// over more SIMDs; with many rows a workgroup takes kPrepRows rows and reads S
+// once for them.
 constexpr int kPrepPieces = 4;
+constexpr int kPrepRows = 4;
 
-// Rotation and projection of the row (the same for every key code width):
-// q~ into s_q, p = S q~ into s_p; piece 0 writes both to the query region.
-template <int D, int DT>
-__device__ void prepare_front(const PrepArgs &a, int qq, int kvh, int b, int piece, float *s_q, float *s_p) {
+// Rotation and projection of NRW consecutive rows qq0 .. qq0 + NRW - 1 of a
+// (sequence, KV head) group, of which the first nr exist (the same for every key
+// code width): q~ of row i into s_q[i], p = S q~ into s_p[i]; piece 0 writes both
+// to the query region. The S loads are shared by the NRW rows.
+template <int D, int DT, int NRW>
+__device__ void prepare_front(const PrepArgs &a, int qq0, int nr, int kvh, int b, int piece, float (*s_q)[D],
+                              float (*s_p)[D]) {
   constexpr int R = D / 64;
   constexpr int RPW = D / 4;         // rows of S per wave
   constexpr int LPR = 64 / RPW;      // lanes per row of S: 2 (d = 128) or 1 (d = 256)
@@ -701,38 +706,52 @@ __device__ void prepare_front(const PrepArgs &a, int qq, int kvh, int b, int pie
   constexpr int NCH = EPL / 4 / CH;  // chunks: 1 (d = 128) or 4 (d = 256)
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = a.n_q_heads / a.n_kv_heads;
-  const int t = qq / g, hh = qq % g;
-  const size_t row = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
+  size_t row[NRW];
+#pragma unroll
+  for (int i = 0; i < NRW; ++i) {
+    const int qq = qq0 + min(i, nr - 1);   // rows past the group repeat the last one (not written)
+    const int t = qq / g, hh = qq % g;
+    row[i] = ((size_t)b * a.n_q + t) * a.n_q_heads + kvh * g + hh;
+  }
   const int srow = wave * RPW + lane / LPR, part = lane % LPR;
   const float4 *S4 = reinterpret_cast<const float4 *>(a.qjl);
   const size_t s_off = (size_t)srow * (D / 4) + part * (EPL / 4);   // this lane's part of its S row
   const bool qjl = a.qjl != nullptr;   // MSE-only keys: p = 0, S is not read
-  // the row is loaded first: loads complete in order, and the rotation, which
-  // needs the row, runs while the S loads are in flight
-  float v[R];
+  // the rows are loaded first: loads complete in order, and the rotation, which
+  // needs the rows, runs while the S loads are in flight
+  float v[NRW][R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) v[r] = load_elem<DT>(a.q, row * D + lane + 64 * r);
+  for (int i = 0; i < NRW; ++i)
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[i][r] = load_elem<DT>(a.q, row[i] * D + lane + 64 * r);
   float4 sv[CH];
   if (qjl) {
 #pragma unroll
     for (int k = 0; k < CH; ++k) sv[k] = S4[s_off + k];
   }
-  fwht_wave<R>(v);
 #pragma unroll
-  for (int r = 0; r < R; ++r) v[r] *= rsqrt_dim<D>();
-  float *dst = a.prep + row * 2 * D;
+  for (int i = 0; i < NRW; ++i) {
+    fwht_wave<R>(v[i]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) v[i][r] *= rsqrt_dim<D>();
+  }
   if (wave == 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      s_q[lane + 64 * r] = v[r];
-      if (piece == 0) dst[lane + 64 * r] = v[r];
+    for (int i = 0; i < NRW; ++i) {
+      float *dst = a.prep + row[i] * 2 * D;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        s_q[i][lane + 64 * r] = v[i][r];
+        if (piece == 0 && i < nr) dst[lane + 64 * r] = v[i][r];
+      }
     }
   }
   __syncthreads();
 
   // p_l = sum_i S[l][i] q~_i
-  const float4 *q4 = reinterpret_cast<const float4 *>(s_q) + part * (EPL / 4);
-  float acc = 0.f;
+  float acc[NRW];
+#pragma unroll
+  for (int i = 0; i < NRW; ++i) acc[i] = 0.f;
   if (qjl) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -741,19 +760,26 @@ __device__ void prepare_front(const PrepArgs &a, int qq, int kvh, int b, int pie
         for (int k = 0; k < CH; ++k) sv[k] = S4[s_off + c * CH + k];
       }
 #pragma unroll
-      for (int k = 0; k < CH; ++k) {
-        const float4 qv = q4[c * CH + k];
-        acc = fmaf(sv[k].x, qv.x, acc);
-        acc = fmaf(sv[k].y, qv.y, acc);
-        acc = fmaf(sv[k].z, qv.z, acc);
-        acc = fmaf(sv[k].w, qv.w, acc);
+      for (int i = 0; i < NRW; ++i) {
+        const float4 *q4 = reinterpret_cast<const float4 *>(s_q[i]) + part * (EPL / 4);
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+          const float4 qv = q4[c * CH + k];
+          acc[i] = fmaf(sv[k].x, qv.x, acc[i]);
+          acc[i] = fmaf(sv[k].y, qv.y, acc[i]);
+          acc[i] = fmaf(sv[k].z, qv.z, acc[i]);
+          acc[i] = fmaf(sv[k].w, qv.w, acc[i]);
+        }
       }
     }
   }
-  if (LPR == 2) acc += __shfl_xor(acc, 1, 64);
-  if (part == 0) {
-    s_p[srow] = acc;
-    if (piece == 0) dst[D + srow] = acc;
+#pragma unroll
+  for (int i = 0; i < NRW; ++i) {
+    if (LPR == 2) acc[i] += __shfl_xor(acc[i], 1, 64);
+    if (part == 0) {
+      s_p[i][srow] = acc[i];
+      if (piece == 0 && i < nr) a.prep[row[i] * 2 * D + D + srow] = acc[i];
+    }
   }
 }
 
@@ -899,26 +925,42 @@ __device__ void prepare_pack(const PrepArgs &a, int qq, int kvh, int b, int piec
   }
 }
 
-template <int D, int DT>
-__device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b, int piece) {
-  __shared__ float s_q[D], s_p[D];
-  prepare_front<D, DT>(a, qq, kvh, b, piece, s_q, s_p);
+// Rows qq0 .. qq0 + nr - 1 (nr <= NRW) of one (sequence, KV head) group.
+template <int D, int DT, int NRW>
+__device__ void prepare_rows(const PrepArgs &a, int qq0, int nr, int kvh, int b, int piece) {
+  __shared__ float s_q[NRW][D], s_p[NRW][D];
+  prepare_front<D, DT, NRW>(a, qq0, nr, kvh, b, piece, s_q, s_p);
   if (a.packed == nullptr) return;
   __syncthreads();
-  // the K code width and the group width are uniform over the launch
-  if (a.wide)
-    prepare_pack<D, 3, true>(a, qq, kvh, b, piece, s_q, s_p);
-  else if (a.k_bits == 2)
-    prepare_pack<D, 2, false>(a, qq, kvh, b, piece, s_q, s_p);
-  else if (a.k_bits == 4)
-    prepare_pack<D, 4, false>(a, qq, kvh, b, piece, s_q, s_p);
-  else
-    prepare_pack<D, 3, false>(a, qq, kvh, b, piece, s_q, s_p);
+  for (int i = 0; i < nr; ++i) {
+    // the K code width and the group width are uniform over the launch
+    if (a.wide)
+      prepare_pack<D, 3, true>(a, qq0 + i, kvh, b, piece, s_q[i], s_p[i]);
+    else if (a.k_bits == 2)
+      prepare_pack<D, 2, false>(a, qq0 + i, kvh, b, piece, s_q[i], s_p[i]);
+    else if (a.k_bits == 4)
+      prepare_pack<D, 4, false>(a, qq0 + i, kvh, b, piece, s_q[i], s_p[i]);
+    else
+      prepare_pack<D, 3, false>(a, qq0 + i, kvh, b, piece, s_q[i], s_p[i]);
+  }
 }
 
 template <int D, int DT>
+__device__ void prepare_row(const PrepArgs &a, int qq, int kvh, int b, int piece) {
+  prepare_rows<D, DT, 1>(a, qq, 1, kvh, b, piece);
+}
+
+// Workgroup x of a (sequence, KV head): with pieces > 1, piece x % pieces of
+// row x / pieces; else rows kPrepRows x .. kPrepRows x + kPrepRows - 1.
+template <int D, int DT>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepArgs a) {
-  prepare_row<D, DT>(a, blockIdx.x / a.pieces, blockIdx.y, blockIdx.z, blockIdx.x % a.pieces);
+  if (a.pieces > 1) {
+    prepare_row<D, DT>(a, blockIdx.x / a.pieces, blockIdx.y, blockIdx.z, blockIdx.x % a.pieces);
+  } else {
+    const int G = a.n_q * (a.n_q_heads / a.n_kv_heads);
+    const int qq0 = kPrepRows * blockIdx.x;
+    prepare_rows<D, DT, kPrepRows>(a, qq0, min(kPrepRows, G - qq0), blockIdx.y, blockIdx.z, 0);
+  }
 }
 
 // One launch for the work of a decode step that precedes the split-K decode:
@@ -1103,7 +1145,8 @@ static int prep_pieces(const PrepArgs &a) {
 hipError_t launch_prepare(const PrepArgs &a, int d, hipStream_t s) {
   PrepArgs pa = a;
   pa.pieces = prep_pieces(a);
-  const dim3 grid(a.n_q * (a.n_q_heads / a.n_kv_heads) * pa.pieces, a.n_kv_heads, a.batch);
+  const int G = a.n_q * (a.n_q_heads / a.n_kv_heads);   // rows per (sequence, KV head)
+  const dim3 grid(pa.pieces > 1 ? G * pa.pieces : (G + kPrepRows - 1) / kPrepRows, a.n_kv_heads, a.batch);
   if (d == 128) {
     if (a.dtype == TQ_F32)
       hipLaunchKernelGGL((prepare_kernel<128, TQ_F32>), grid, dim3(256), 0, s, pa);

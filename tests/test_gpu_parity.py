@@ -388,8 +388,9 @@ def test_speculative_verify_and_rollback(tq):
     assert torch.equal(before, after)
 
 
-@pytest.mark.parametrize("d,H,Hq,C", [(128, 2, 8, 128), (256, 8, 8, 200)],
-                         ids=["d128-512rows-fused-prologue", "d256-200rows-separate-encode"])
+@pytest.mark.parametrize("d,H,Hq,C", [(128, 2, 8, 128), (256, 8, 8, 200), (128, 2, 6, 67)],
+                         ids=["d128-512rows-fused-prologue", "d256-200rows-separate-encode",
+                              "d128-201rows-ragged-groups"])
 def test_chunked_prefill_attention(tq, d, H, Hq, C):
     """Chunked prefill: C new tokens per sequence are appended (encoded) and their
     C x Hq/Hkv query rows attend causally over the compressed history and the
