@@ -526,6 +526,56 @@ def test_mse_only_keys_encode_and_decode(tq, d):
     assert err <= Hn.ATTN_TOL
 
 
+@pytest.mark.parametrize("d", [128, 256])
+@pytest.mark.parametrize("Hq", [8, 32], ids=["4rows", "16rows"])
+@pytest.mark.parametrize("mse", [False, True], ids=["qjl", "mse-only"])
+def test_codebook_with_a_negative_parity_weight(tq, d, Hq, mse):
+    """An odd codebook whose parity plane weighs less than nothing
+    (c4 + c7 < c5 + c6): the 16-row kernel takes that plane's V bits
+    complemented. Groups of 4 and of 16 rows, with and without the QJL stage,
+    against the reference on the same codebook (float32 levels, midpoint
+    thresholds)."""
+    H, lens = 2, [700, 300]
+    c = (np.array([0.3, 0.9, 1.4, 1.9]) / np.sqrt(d)).astype(np.float32)
+    levels = np.concatenate([-c[::-1], c]).astype(np.float32)
+    thr = (0.5 * (levels[:-1].astype(np.float64) + levels[1:])).astype(np.float32)
+    thr[3] = 0.0
+    assert 0.5 * (float(c[0]) + float(c[3]) - float(c[1]) - float(c[2])) < 0   # parity plane weight
+    S = tq.tq_build_codebook(d, 3, 777)[2]
+    cb = O.Codebook(d, levels.astype(np.float64), thr.astype(np.float64), levels.astype(np.float64),
+                    thr.astype(np.float64), 0)
+    print(f"[negative parity weight] d={d} rows={Hq // H} mse_only={mse}", flush=True)
+    w = I.Workload(f"npw{d}", len(lens), Hq, H, d, "bf16", "outlier", 91, fixed_len=1)
+    table, n_pages = I.page_table(w, np.asarray(lens), shuffle=True)
+    cache = tq.Cache(d, H, n_pages, codebook=(levels, thr, S), k_mse_only=mse)
+    bt = torch.from_numpy(table).cuda()
+    S64 = None if mse else S.astype(np.float64)
+    for b, L in enumerate(lens):
+        k = I.kv_tokens(w, "k", b, 0, L)
+        v = I.kv_tokens(w, "v", b, 0, L)
+        t = np.arange(L)
+        slots = (table[b][t // 256].astype(np.int64) * 256 + t % 256).astype(np.int32)
+        ts = torch.from_numpy(slots).cuda()
+        tq.tq_encode_k(cache, Hn.torch_input(k, "bf16"), ts)
+        tq.tq_encode_v(cache, Hn.torch_input(v, "bf16"), ts)
+        torch.cuda.synchronize()
+        kp, vp = cache.k_pool.cpu().numpy(), cache.v_pool.cpu().numpy()
+        uk = O.unpack_k(kp, slots, H, d, 256)
+        if mse:
+            Hn.compare_encode_k_mse_only(uk, k.astype(np.float64), cb)
+        else:
+            Hn.compare_encode_k(uk, k.astype(np.float64), cb, S64)
+        Hn.compare_encode_v(O.unpack_v(vp, slots, H, d, 256), v.astype(np.float64), cb)
+    q = I.queries(w, 0)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = tq.tq_attn_decode(cache, Hn.torch_input(q, "bf16"), bt, sl)
+    torch.cuda.synchronize()
+    ref = O.attn_decode(kp, vp, cb, S64, q.astype(np.float64), table, lens, H, 256, Hn.scale_of(d))
+    err = Hn.attn_rel_err(out.cpu().numpy(), ref)
+    print(f"  max rel err {err:.3e}", flush=True)
+    assert err <= Hn.ATTN_TOL
+
+
 def _decode_wide_table(tq, cache, q, bt, sl):
     """Decode with the block table padded to 72 columns (the padding is never
     read): two sequences x 8 KV heads x 72 pages make 3 pages per split, so at
