@@ -299,9 +299,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? (
   if (pg1 > pg0 && blk0 >= Lv - (pg1 - 1) * kPage) --pg1;
 
 
-  auto load_block_at = [&](MfmaBlock<D, VBITS, KBITS> &d, int phys) {
+  // a block's key words (read by the score MFMAs) and the rest (sidecars and V
+  // words, read after them) load separately
+  auto load_keys_at = [&](MfmaBlock<D, VBITS, KBITS> &d, int phys) {
     const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
-    const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
@@ -319,6 +320,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? (
           for (int j = 0; j <= KBITS; ++j) d.kw[tau][c][j] = r32[j];
         }
       }
+  };
+  auto load_rest_at = [&](MfmaBlock<D, VBITS, KBITS> &d, int phys) {
+    const uint8_t *ks = a.k_pool + ((size_t)phys * H + kvh) * KSEC;
+    const uint8_t *vs = a.v_pool + ((size_t)phys * H + kvh) * VSEC;
     const int se = blk0 + 4 * n;   // side entries of tokens 16 tau + n, tau = 0..3
     d.g = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * kPage + 2 * se);
     d.nk = *reinterpret_cast<const uint2 *>(ks + KCODES + 2 * se);
@@ -330,6 +335,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? (
 #pragma unroll
         for (int c = 0; c < NCH; ++c) d.v[j][c] = vw[j * 2 * D * 4 / 16 + c];
     }
+  };
+  auto load_block_at = [&](MfmaBlock<D, VBITS, KBITS> &d, int phys) {
+    load_keys_at(d, phys);
+    load_rest_at(d, phys);
   };
   auto load_block = [&](MfmaBlock<D, VBITS, KBITS> &d, int pg) { load_block_at(d, phys_of(pg)); };
 
@@ -351,7 +360,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? (
     vis[gi] = !live ? 0 : a.causal_tail ? L - (a.n_q - 1 - row / g) : L;
   }
 
-  auto process = [&](const MfmaBlock<D, VBITS, KBITS> &d, int pg) {
+  // At d = 128 block pg + 1 loads while block pg is processed, into the same
+  // registers: its key words once the score MFMAs have been issued, the rest at
+  // the end (the last block loads itself again, so the loop has no branch).
+  constexpr bool kRot = D == 128 && KBITS + VBITS <= 7;
+  auto process = [&](MfmaBlock<D, VBITS, KBITS> &d, int pg, int phys_next) {
     // at d = 256 the query operand (20 MFMA operands, 80 registers) is read from
     // LDS where it is used: an opaque lane offset keeps it from being hoisted
     int qo = lane;
@@ -422,6 +435,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? (
         }
       }
     }
+    if constexpr (kRot) load_keys_at(d, phys_next);
 #pragma unroll
     for (int tau = 0; tau < 4; ++tau) {
       const int sh = 16 * (tau & 1);
@@ -583,14 +597,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NG == 1 ? (
       for (int gi = 0; gi < NG; ++gi) fold_v(gi);
     }
     }
+    if constexpr (kRot) load_rest_at(d, phys_next);
   };
 
   // the packed query operand is shared by the four waves: keep it in LDS
   qs.store(s_qop, s_qsc, rho0, QG, tid);
   __syncthreads();
   for (int pg = pg0; pg < pg1; ++pg) {
-    if (!kEarly || pg > pg0) load_block(d0, pg);
-    process(d0, pg);
+    if (!kEarly || (!kRot && pg > pg0)) load_block(d0, pg);
+    process(d0, pg, kRot ? phys_of(min(pg + 1, pg1 - 1)) : 0);
   }
 
   if constexpr (kLazyV) fold_v(0);
