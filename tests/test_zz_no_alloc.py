@@ -1,7 +1,8 @@
 """tq_append_decode_static (the decode step with the library's static device
 scratch, for callers that cannot allocate) against tq_append_decode with a
-caller workspace: two calls in a row, the second with a smaller input. Both
-entry points run the same kernels, so outputs and pools must be bit-equal."""
+caller workspace: three calls in a row, each smaller than the one before (the
+first with 16 query rows per KV head). Both entry points run the same kernels, so
+outputs and pools must be bit-equal."""
 
 import ctypes as C
 import math
@@ -60,14 +61,21 @@ def test_static_scratch_entry_matches_caller_workspace():
     lens = [1500, 700, 2100]
     table, n_pages = I.page_table(w, np.asarray(lens), shuffle=True)
     caches, bt = _caches(tq, w, lens, n_pages, table)
-    # first call: 3 sequences, 2 query tokens (8 causal rows per KV head)
-    print("[no-alloc] call 1: B=3, n_q=2, L=[1500, 700, 2100]", flush=True)
+    # first call: 3 sequences, 4 query tokens (16 causal rows per KV head: the
+    # 16-row kernel)
+    print("[no-alloc] call 1: B=3, n_q=4, L=[1500, 700, 2100]", flush=True)
+    ref, got = _step(tq, caches, w, bt, lens, 3, 4, 2)
+    assert np.array_equal(ref, got) and np.abs(ref).max() > 0
+    assert torch.equal(caches[0].k_pool, caches[1].k_pool) and torch.equal(caches[0].v_pool, caches[1].v_pool)
+    # then smaller calls, each after one that left more in the scratch: 3
+    # sequences with 2 query tokens (8 causal rows per KV head, groups of 4)
+    print("[no-alloc] call 2: B=3, n_q=2, L=[1500, 700, 2100]", flush=True)
     ref, got = _step(tq, caches, w, bt, lens, 3, 2, 0)
     assert np.array_equal(ref, got) and np.abs(ref).max() > 0
     assert torch.equal(caches[0].k_pool, caches[1].k_pool) and torch.equal(caches[0].v_pool, caches[1].v_pool)
-    # second call, smaller: 1 sequence, 1 query token; the scratch keeps the
-    # first call's contents, which the second must not depend on
-    print("[no-alloc] call 2: B=1, n_q=1, L=[1500]", flush=True)
+    # 1 sequence, 1 query token; the scratch keeps the earlier calls' contents,
+    # which this one must not depend on
+    print("[no-alloc] call 3: B=1, n_q=1, L=[1500]", flush=True)
     ref, got = _step(tq, caches, w, bt, lens, 1, 1, 1)
     assert np.array_equal(ref, got) and np.abs(ref).max() > 0
     assert torch.equal(caches[0].k_pool, caches[1].k_pool) and torch.equal(caches[0].v_pool, caches[1].v_pool)
