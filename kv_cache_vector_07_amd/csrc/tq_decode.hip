@@ -97,18 +97,19 @@ __device__ inline uint32_t quad_byte_transpose(uint32_t d, int lam) {
 // reference moves, and once at the end. (Folding only at a rescale also fits at
 // d = 128 but measured slower there.)
 //
-// Up to TQ_MAX_GROUP query rows per KV head (a few for decode and verify, a
-// whole chunk's for chunked prefill) run as query groups of 4 rows (4 rows x 4
-// limbs fill the 16 MFMA rows). At d = 128 two groups share a workgroup; the
+// Query rows per KV head run as query groups of 4 rows (4 rows x 4 limbs fill
+// the 16 MFMA rows); with 16 rows or more and 3-bit codes decode_wide_kernel
+// below takes them instead. At d = 128 two groups share a workgroup; the
 // workgroups of one split sit in blockIdx.z, n_split * Hkv apart, so with
 // n_split * Hkv a multiple of 8 they land on the same XCD and share its L2.
 // With a causal tail a workgroup stops at the last token its rows can see.
 //
-// A block's loads are issued at its start (the first block's before the query
-// operand is staged), into one register set: at d = 128 with one group that
-// leaves three waves per SIMD (under 170 VGPRs), which hides the load latency
-// better than loading one block ahead into a second set at two waves per SIMD;
-// at d = 256 one set keeps two waves per SIMD.
+// One register set holds a block's loads (the first block's go out before the
+// query operand is staged): at d = 128 with one group that leaves three waves
+// per SIMD (under 170 VGPRs). There the next block's key words are loaded as
+// soon as the score MFMAs have read the current ones, and its sidecars and V
+// words after the V MFMAs; at d = 256 a block's loads go out at its start, and
+// one set keeps two waves per SIMD.
 
 // The packed scoring operand of the workgroup's query groups (per group NMU x
 // 64 lanes x 32 bytes, then NMU x 64 scale words), held in registers between
