@@ -541,15 +541,15 @@ def test_codebook_with_a_negative_parity_weight(tq, d, Hq, mse):
     thr = (0.5 * (levels[:-1].astype(np.float64) + levels[1:])).astype(np.float32)
     thr[3] = 0.0
     assert 0.5 * (float(c[0]) + float(c[3]) - float(c[1]) - float(c[2])) < 0   # parity plane weight
-    S = tq.tq_build_codebook(d, 3, 777)[2]
+    S = tq.tq_build_codebook(d, 3, 12345)[2]   # the cache's QJL seed: oracle_qjl checks it
     cb = O.Codebook(d, levels.astype(np.float64), thr.astype(np.float64), levels.astype(np.float64),
                     thr.astype(np.float64), 0)
     print(f"[negative parity weight] d={d} rows={Hq // H} mse_only={mse}", flush=True)
     w = I.Workload(f"npw{d}", len(lens), Hq, H, d, "bf16", "outlier", 91, fixed_len=1)
     table, n_pages = I.page_table(w, np.asarray(lens), shuffle=True)
-    cache = tq.Cache(d, H, n_pages, codebook=(levels, thr, S), k_mse_only=mse)
+    cache = tq.Cache(d, H, n_pages, qjl_seed=12345, codebook=(levels, thr, S), k_mse_only=mse)
     bt = torch.from_numpy(table).cuda()
-    S64 = None if mse else S.astype(np.float64)
+    S64 = None if mse else Hn.oracle_qjl(cache)   # the oracle's own S, equal to the cache's
     for b, L in enumerate(lens):
         k = I.kv_tokens(w, "k", b, 0, L)
         v = I.kv_tokens(w, "v", b, 0, L)
