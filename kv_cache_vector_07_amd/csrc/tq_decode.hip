@@ -805,7 +805,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     flip[j] = wpl[j] < 0.f ? 0xFFFFFFFFu : 0u;
     c_eff -= wpl[j] < 0.f ? wpl[j] : 0.f;
   }
-  const float delta_u = wmax / kFix;
+  float delta_u = wmax / kFix;
+  if constexpr (D == 256) {
+    // these are the same in every lane: scalar registers free vector ones
+    // (at d = 256 that takes the kernel's register spills out of the page loop)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cx[j] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, cx[j])));
+      flip[j] = (uint32_t)__builtin_amdgcn_readfirstlane((int)flip[j]);
+    }
+    c_eff = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, c_eff)));
+    delta_u = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, delta_u)));
+  }
   // source lane of the weight transpose (kg <-> kgA): lane 16 a + 4 b + c reads lane 16 b + 4 a + c
   const int tr_addr = 4 * (16 * ((lane >> 2) & 3) + 4 * (lane >> 4) + (lane & 3));
   const int rq = lane & 3;   // the lane's place in its quad
