@@ -229,9 +229,10 @@ int tq_query_prepare(const tq_cache *c, const void *q, int32_t dtype, int32_t ba
  * ceil(L_b / P) pages must lie in [0, n_pages) (device data, not checked);
  * later entries are never read, and tokens past max_pages * P are not seen.
  * L_b <= 0 or an empty visible range gives a zero row. Hq / Hkv * n_q must not
- * exceed TQ_MAX_GROUP, and batch * ceil(ceil(rows / 4) / k) must not exceed
- * 65535, with rows = Hq / Hkv * n_q and k = 2 at d = 128 when rows > 4, else 1
- * (TQ_EUNSUPPORTED).
+ * exceed TQ_MAX_GROUP, and batch * W must not exceed 65535 (TQ_EUNSUPPORTED),
+ * with rows = Hq / Hkv * n_q and W the workgroups per sequence and KV head:
+ * ceil(rows / 16) with 16 rows or more and 3-bit K and V codes, else
+ * ceil(ceil(rows / 4) / k) with k = 2 at d = 128 when rows > 4, else 1.
  * Workspace: call with workspace == NULL to get the size in *workspace_bytes
  * (nothing is launched). It holds split partials and the prepared queries; its
  * contents need no initialisation and are scratch after the call. Calls that
